@@ -1,0 +1,136 @@
+"""Block manager: per-sequence block tables, on-demand allocation, fork and copy-on-write.
+
+Follows:
+* agentalpha.top Q32, answer part 2 (PagedAttention的解决方案): the KV cache is cut
+  into fixed-size blocks (16 tokens by default) allocated on demand; each request
+  keeps a block table from logical block to physical block (its example: logical
+  0 -> physical 5, logical 1 -> physical 12); a new token either lands in the
+  current block or opens a new one, and stored data never moves.
+* agentalpha.top Q32, answer part 3 (Copy-on-Write) and ohmygp.com "破局思路"
+  (写时共享): sequences that share a prefix map their logical blocks to the same
+  physical blocks, a reference count tracks the sharers, and a block is copied
+  only when one sharer writes into it.
+* data.6616ai.com "PagedAttention：把虚拟内存搬进 KV Cache": blocks are requested one
+  at a time as a request grows; shared prefix blocks are refcounted and copied
+  only at divergence.
+
+Readings where the pages leave the policy open (all stated in the design notes):
+* the free list starts in a caller-given order and hands out blocks from its
+  front; a block whose count drops to zero goes to its back;
+* a sequence added with n tokens receives ceil(n / B) blocks at once;
+* appending at position ``pos``: when ``pos % B == 0`` a fresh block is opened;
+  otherwise, when the tail block is shared (count > 1), the writer takes a fresh
+  block, the pair (old tail -> fresh) is emitted for copying, and the old tail
+  loses one reference; the last remaining sharer writes in place;
+* a batch step visits sequences in the order given (ascending ids).
+"""
+from __future__ import annotations
+
+import collections
+from typing import Dict, List, Optional, Sequence, Tuple
+
+
+class OutOfBlocks(RuntimeError):
+    pass
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, block_size: int, free_order: Sequence[int]):
+        order = [int(x) for x in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("free_order must be a permutation of range(num_blocks)")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        self.free = collections.deque(order)
+        self.refcount = [0] * self.num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lens: Dict[int, int] = {}
+
+    # -- allocation -----------------------------------------------------------
+    def _take(self) -> int:
+        if not self.free:
+            raise OutOfBlocks("no free block")
+        blk = self.free.popleft()
+        self.refcount[blk] = 1
+        return blk
+
+    def add_seq(self, seq: int, num_tokens: int) -> None:
+        """Register ``seq`` holding ``num_tokens`` tokens: ceil(n/B) fresh blocks."""
+        if seq in self.tables:
+            raise ValueError(f"sequence {seq} exists")
+        nblk = -(-int(num_tokens) // self.block_size)
+        if nblk > len(self.free):
+            raise OutOfBlocks("not enough free blocks")
+        self.tables[seq] = [self._take() for _ in range(nblk)]
+        self.lens[seq] = int(num_tokens)
+
+    def fork(self, parent: int, child: int) -> None:
+        """``child`` shares every block of ``parent``; each shared block gains a reference."""
+        if child in self.tables:
+            raise ValueError(f"sequence {child} exists")
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        for blk in self.tables[child]:
+            self.refcount[blk] += 1
+
+    def append_slot(self, seq: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+        """Reserve the slot of the next token of ``seq``.
+
+        Returns (slot, cow) where slot = physical_block * B + offset and cow is
+        (src_block, dst_block) when the write lands in a shared block, else None.
+        """
+        B = self.block_size
+        table = self.tables[seq]
+        pos = self.lens[seq]
+        cow = None
+        if pos % B == 0:
+            table.append(self._take())
+        else:
+            tail = table[-1]
+            if self.refcount[tail] > 1:
+                fresh = self._take()
+                self.refcount[tail] -= 1
+                table[-1] = fresh
+                cow = (tail, fresh)
+        slot = table[pos // B] * B + pos % B
+        self.lens[seq] = pos + 1
+        return slot, cow
+
+    def step(self, seqs: Sequence[int]) -> Tuple[List[int], List[Tuple[int, int]]]:
+        """One decode step: append a slot for each sequence in order; collect CoW pairs."""
+        slots, pairs = [], []
+        for s in seqs:
+            slot, cow = self.append_slot(int(s))
+            slots.append(slot)
+            if cow is not None:
+                pairs.append(cow)
+        return slots, pairs
+
+    def free_seq(self, seq: int) -> None:
+        """Drop ``seq``; blocks whose count reaches zero return to the back of the free list."""
+        for blk in self.tables.pop(seq):
+            self.refcount[blk] -= 1
+            if self.refcount[blk] == 0:
+                self.free.append(blk)
+        del self.lens[seq]
+
+    # -- lookups --------------------------------------------------------------
+    def slot_of(self, seq: int, pos: int) -> int:
+        """Slot of logical position ``pos``: block table[pos // B], offset pos % B."""
+        B = self.block_size
+        return self.tables[seq][pos // B] * B + pos % B
+
+    def slots(self, seq: int, pos0: int, count: int) -> List[int]:
+        return [self.slot_of(seq, p) for p in range(pos0, pos0 + count)]
+
+    def block_table(self, seq: int) -> List[int]:
+        return list(self.tables[seq])
+
+    def block_tables(self, seqs: Sequence[int], width: int, pad: int) -> List[List[int]]:
+        rows = []
+        for s in seqs:
+            t = self.tables[int(s)]
+            if len(t) > width:
+                raise ValueError("table wider than width")
+            rows.append(t + [pad] * (width - len(t)))
+        return rows

@@ -1,0 +1,12 @@
+"""Seeded synthetic inputs for the paged KV-cache decode path.
+
+This package draws context lengths, free-list orders and N(0,1) values, and lists
+the block-manager operations (prefill, fork, decode steps) that a workload
+performs.  It holds none of the method's arithmetic: no slot resolution, no
+attention, no copy-on-write decision.  The oracle side and the HIP side of every
+test and of the benchmark consume the same arrays from here.
+"""
+from .workloads import (  # noqa: F401
+    DTYPES, NAN_BITS, Workload, normal_bits, skewed_lengths,
+    tiny_fp32, mha_bf16, gqa_bf16, cow_fp16, long_bf16, by_name, WORKLOADS,
+)

@@ -1,0 +1,254 @@
+"""Workload definitions and seeded generators.
+
+Every random draw comes from ``numpy.random.Generator(PCG64)`` seeded by a tuple
+of integers, so a tensor can be regenerated on its own (one sequence's context,
+one decode step's new tokens) without drawing the rest.  Values are drawn in
+fp32 and rounded to the storage type with a round-to-nearest-even cast; the
+arrays handed out are the raw storage bits (uint16 for bf16/fp16, uint32 for
+fp32), so both sides see identical bytes.
+
+Length mix: the interview post (ohmygp.com, "用模拟把浪费率算出来") simulates
+request lengths drawn 70% from [32, 512), 25% from [512, 2048) and 5% from
+[2048, 4096).  ``skewed_lengths`` draws from that mix, optionally with every
+range scaled by an integer factor (factor 2 gives lengths up to 8191).
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import dataclasses
+import math
+import os
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+# storage dtype name -> (numpy bits dtype, torch dtype, element bytes)
+DTYPES: Dict[str, Tuple[type, torch.dtype, int]] = {
+    "f32": (np.uint32, torch.float32, 4),
+    "f16": (np.uint16, torch.float16, 2),
+    "bf16": (np.uint16, torch.bfloat16, 2),
+}
+
+# quiet-NaN bit patterns used to poison pool memory that no sequence owns
+NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
+
+# seed-tuple tags for the different value streams of one workload
+_TAG_CTX_K, _TAG_CTX_V, _TAG_STEP_K, _TAG_STEP_V, _TAG_Q = 1, 2, 3, 4, 5
+
+
+def _gen_threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def normal_bits(key: Sequence[int], shape: Sequence[int], dtype: str) -> np.ndarray:
+    """N(0,1) values of ``shape`` as raw ``dtype`` storage bits, from seed tuple ``key``."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    rng = np.random.default_rng(list(key))
+    x = rng.standard_normal(size=n, dtype=np.float32)
+    bits_np, tdt, _ = DTYPES[dtype]
+    if dtype == "f32":
+        return x.view(np.uint32).reshape(shape)
+    t = torch.from_numpy(x).to(tdt)  # round-to-nearest-even
+    return t.view(torch.int16).numpy().view(np.uint16).reshape(shape)
+
+
+def skewed_lengths(rng: np.random.Generator, n: int, factor: int = 1) -> np.ndarray:
+    """Lengths from the interview post's skewed mix, every range scaled by ``factor``."""
+    r = rng.random(n)
+    u = rng.random(n)
+    short = factor * 32 + np.floor(u * (480 * factor))
+    mid = factor * 512 + np.floor(u * (1536 * factor))
+    long_ = factor * 2048 + np.floor(u * (2048 * factor))
+    return np.where(r < 0.7, short, np.where(r < 0.95, mid, long_)).astype(np.int64)
+
+
+@dataclasses.dataclass
+class Workload:
+    """One decode workload: shapes, pool, block-manager operations and value seeds.
+
+    Operations, replayed in this order by both sides:
+      1. ``prefill``: for each (seq, n): add the sequence with n tokens and write
+         their K/V (positions 0..n-1) from ``context_kv(seq, n)``.
+      2. ``forks``: for each (parent, child): the child shares the parent's blocks.
+      3. ``steps``: each entry is a list of sequence ids, ascending; every listed
+         sequence appends one token; the step's copy-on-write pairs are copied
+         before the step's tokens are written.  The last step is the measured one.
+      4. attention over ``batch`` (output row i is sequence ``batch[i]``) with
+         queries ``queries()``.
+    """
+
+    name: str
+    seed: int
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    scale: float
+    free_order: np.ndarray
+    prefill: List[Tuple[int, int]]
+    forks: List[Tuple[int, int]]
+    steps: List[List[int]]
+    batch: np.ndarray
+    context_lens: np.ndarray  # length of each batch sequence after the last step
+    notes: str = ""
+
+    # ---- shapes -------------------------------------------------------------
+    @property
+    def num_seqs(self) -> int:
+        return int(len(self.batch))
+
+    @property
+    def elem_bytes(self) -> int:
+        return DTYPES[self.dtype][2]
+
+    def kv_bytes_logical(self) -> int:
+        """K+V bytes that attention reads: each context token once per KV head."""
+        return int(2 * int(self.context_lens.sum()) * self.num_kv_heads * self.head_dim * self.elem_bytes)
+
+    # ---- values -------------------------------------------------------------
+    def context_kv(self, seq: int, n: int) -> Tuple[np.ndarray, np.ndarray]:
+        shape = (n, self.num_kv_heads, self.head_dim)
+        return (normal_bits((self.seed, _TAG_CTX_K, seq), shape, self.dtype),
+                normal_bits((self.seed, _TAG_CTX_V, seq), shape, self.dtype))
+
+    def all_context_kv(self, threads: Optional[int] = None) -> Dict[int, Tuple[np.ndarray, np.ndarray]]:
+        """Context K/V of every prefilled sequence, drawn on a thread pool."""
+        threads = threads or _gen_threads()
+        jobs = [(s, n) for s, n in self.prefill]
+        out: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
+        with _cf.ThreadPoolExecutor(threads) as ex:
+            futs = {}
+            for s, n in jobs:
+                shape = (n, self.num_kv_heads, self.head_dim)
+                futs[ex.submit(normal_bits, (self.seed, _TAG_CTX_K, s), shape, self.dtype)] = (s, 0)
+                futs[ex.submit(normal_bits, (self.seed, _TAG_CTX_V, s), shape, self.dtype)] = (s, 1)
+            parts: Dict[Tuple[int, int], np.ndarray] = {}
+            for f in _cf.as_completed(futs):
+                parts[futs[f]] = f.result()
+        for s, _ in jobs:
+            out[s] = (parts[(s, 0)], parts[(s, 1)])
+        return out
+
+    def step_kv(self, step: int) -> Tuple[np.ndarray, np.ndarray]:
+        shape = (len(self.steps[step]), self.num_kv_heads, self.head_dim)
+        return (normal_bits((self.seed, _TAG_STEP_K, step), shape, self.dtype),
+                normal_bits((self.seed, _TAG_STEP_V, step), shape, self.dtype))
+
+    def queries(self) -> np.ndarray:
+        return normal_bits((self.seed, _TAG_Q), (self.num_seqs, self.num_q_heads, self.head_dim), self.dtype)
+
+
+def _decode_workload(name: str, seed: int, dtype: str, lengths: np.ndarray, hq: int, hkv: int,
+                     d: int, block: int, rng: np.random.Generator, num_blocks: Optional[int] = None,
+                     width: Optional[int] = None, slack: float = 1.1, notes: str = "") -> Workload:
+    """Batch decode: each sequence holds len-1 context tokens, the step writes token len-1."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    n = len(lengths)
+    need = int(sum(-(-int(L) // block) for L in lengths))
+    if num_blocks is None:
+        num_blocks = int(math.ceil(slack * need))
+    if width is None:
+        width = int(max(1, max(-(-int(L) // block) for L in lengths)))
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    return Workload(
+        name=name, seed=seed, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        block_size=block, num_blocks=num_blocks, max_blocks_per_seq=width,
+        scale=1.0 / math.sqrt(d), free_order=free_order,
+        prefill=[(b, int(lengths[b]) - 1) for b in range(n)], forks=[],
+        steps=[list(range(n))], batch=np.arange(n, dtype=np.int32),
+        context_lens=lengths.astype(np.int32), notes=notes)
+
+
+def tiny_fp32(seed: int = 1000, num_seqs: int = 4) -> Workload:
+    """4 sequences, lengths U{1..64}, 8 q = 8 kv heads, D=64, B=16, pool of 64 blocks, fp32."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(1, 65, size=num_seqs)
+    return _decode_workload("tiny_fp32", seed, "f32", lengths, 8, 8, 64, 16, rng,
+                            num_blocks=64, width=4)
+
+
+def mha_bf16(seed: int = 1001, num_seqs: int = 64, max_len: Optional[int] = None) -> Workload:
+    """MHA 32 q = 32 kv heads, D=128, B=16, skewed mix, pool = need + 10%, bf16."""
+    rng = np.random.default_rng(seed)
+    lengths = skewed_lengths(rng, num_seqs, 1)
+    if max_len is not None:
+        lengths = np.minimum(lengths, max_len)
+    return _decode_workload("mha_bf16", seed, "bf16", lengths, 32, 32, 128, 16, rng,
+                            width=256 if max_len is None else None)
+
+
+def gqa_bf16(seed: int = 1002, num_seqs: int = 256, max_len: Optional[int] = None) -> Workload:
+    """GQA 32 q over 8 kv heads (4 per group), D=128, B=16, skewed mix x2 (up to 8191), bf16."""
+    rng = np.random.default_rng(seed)
+    lengths = skewed_lengths(rng, num_seqs, 2)
+    if max_len is not None:
+        lengths = np.minimum(lengths, max_len)
+    return _decode_workload("gqa_bf16", seed, "bf16", lengths, 32, 8, 128, 16, rng,
+                            width=512 if max_len is None else None)
+
+
+def long_bf16(block_size: int = 16, seed: int = 1004, num_seqs: int = 8, context: int = 131072) -> Workload:
+    """Long context: every sequence holds ``context`` tokens, 32 q / 8 kv heads, D=128, bf16.
+
+    The pool holds exactly the blocks the batch needs (65536 at B=16, 32768 at B=32
+    for 8 x 131072 tokens), placed by a random permutation.
+    """
+    rng = np.random.default_rng(seed)
+    lengths = np.full(num_seqs, context, dtype=np.int64)
+    need = num_seqs * (-(-context // block_size))
+    return _decode_workload(f"long_bf16_b{block_size}", seed, "bf16", lengths, 32, 8, 128, block_size,
+                            rng, num_blocks=need, width=-(-context // block_size))
+
+
+def cow_fp16(prompt_len: int = 1020, seed: int = 1003, num_prompts: int = 64, samples: int = 4,
+             max_suffix: int = 256) -> Workload:
+    """Parallel sampling: prompts of ``prompt_len`` tokens, each forked into ``samples`` samples.
+
+    Sample i of prompt k is sequence ``samples*k + i``; sample 0 is the prompt's own
+    sequence.  Each sample has generated s ~ U{0..max_suffix} tokens before the
+    measured step (one decode step per token, all samples stepping together), then
+    the measured step appends one more token to every sample.  32 q / 8 kv heads,
+    D=128, B=16, fp16.
+    """
+    rng = np.random.default_rng(seed)
+    block = 16
+    n = num_prompts * samples
+    suffix = rng.integers(0, max_suffix + 1, size=n)
+    lengths = prompt_len + suffix + 1
+    full_shared = prompt_len // block
+    need = num_prompts * (-(-prompt_len // block))
+    need += int(sum(-(-int(L) // block) - full_shared for L in lengths))
+    num_blocks = int(math.ceil(1.1 * need))
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    steps: List[List[int]] = []
+    for tau in range(int(suffix.max()) if n else 0):
+        steps.append([i for i in range(n) if suffix[i] > tau])
+    steps.append(list(range(n)))
+    width = -(-(prompt_len + max_suffix + 1) // block)
+    return Workload(
+        name=f"cow_fp16_p{prompt_len}", seed=seed, dtype="f16", num_q_heads=32, num_kv_heads=8,
+        head_dim=128, block_size=block, num_blocks=num_blocks, max_blocks_per_seq=width,
+        scale=1.0 / math.sqrt(128), free_order=free_order,
+        prefill=[(samples * k, prompt_len) for k in range(num_prompts)],
+        forks=[(samples * k, samples * k + i) for k in range(num_prompts) for i in range(1, samples)],
+        steps=steps, batch=np.arange(n, dtype=np.int32), context_lens=lengths.astype(np.int32),
+        notes=f"suffix lengths {suffix.tolist()}")
+
+
+WORKLOADS = {
+    "tiny_fp32": tiny_fp32,
+    "mha_bf16": mha_bf16,
+    "gqa_bf16": gqa_bf16,
+    "cow_fp16_p1020": lambda **kw: cow_fp16(1020, **kw),
+    "cow_fp16_p1024": lambda **kw: cow_fp16(1024, **kw),
+    "long_bf16_b16": lambda **kw: long_bf16(16, **kw),
+    "long_bf16_b32": lambda **kw: long_bf16(32, **kw),
+}
+
+
+def by_name(name: str, **kw) -> Workload:
+    return WORKLOADS[name](**kw)
