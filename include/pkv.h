@@ -1,0 +1,207 @@
+/*
+ * pkv.h -- paged KV cache for decode on AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * The method (pages: agentalpha.top "Q32：vLLM PagedAttention 原理", data.6616ai.com
+ * "vLLM" article, ohmygp.com "batch-008-day-02-interview-1"): the KV cache is cut
+ * into fixed-size physical blocks (16 tokens by default) that may sit anywhere in a
+ * pool; each sequence's block table maps its logical blocks to physical ones; a new
+ * token takes one slot and opens a new block only when the current one is full;
+ * sequences sharing a prefix share refcounted blocks, and a shared block is copied
+ * only when a sharer writes into it; attention reads K/V by block index.
+ *
+ * Conventions for every call below.
+ *  - Device pointers are caller-owned device memory (e.g. torch tensors); the
+ *    library never allocates or frees on these paths and keeps no pointer after the
+ *    call returns.  Host pointers are marked "host".
+ *  - Kernels are enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and run asynchronously; a PKV_OK return means the launch was accepted.
+ *  - A call returns a pkv_status.  On failure nothing is enqueued and
+ *    pkv_last_error() returns a message for the calling thread.
+ *  - Preconditions marked "device" are not checked on the host (that would need a
+ *    device->host sync); violating them is undefined behaviour.
+ *
+ * KV pool layout (the pages do not fix one).  Let X = 16 / element_bytes (8 for
+ * bf16/fp16, 4 for fp32), H = num_kv_heads, D = head_dim, B = block_size.
+ *  - K pool: [num_blocks][H][D / X][B][X]: element (block, head, offset, d) at
+ *    ((((block * H + head) * (D / X) + d / X) * B + offset) * X + d % X).
+ *  - V pool: [num_blocks][H][D][B]: element (block, head, offset, d) at
+ *    (((block * H + head) * D + d) * B + offset).
+ *  One (block, head) tile of K or V is B * D * element_bytes contiguous bytes.
+ *  A slot is physical_block * B + offset.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, unknown sequence */
+  PKV_ERR_UNSUPPORTED = 2,   /* a valid shape or dtype this build has no kernel for */
+  PKV_ERR_WORKSPACE = 3,     /* workspace smaller than the required size */
+  PKV_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch */
+  PKV_ERR_OUT_OF_BLOCKS = 5  /* block manager: no free block left */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Shape and element type of a K/V pool pair.  Supported: head_dim in {64, 128},
+ * block_size in {16, 32}, any num_kv_heads >= 1, num_blocks >= 1. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pkv_dtype */
+} pkv_pool_desc;
+
+/* Library version string and status names.  Never NULL. */
+const char* pkv_version(void);
+const char* pkv_status_string(int32_t status);
+/* Message of the calling thread's most recent failure ("" if none). */
+const char* pkv_last_error(void);
+
+/* Bytes of one pool (K or V) for `pool`; 0 if the descriptor is invalid. */
+size_t pkv_pool_bytes(const pkv_pool_desc* pool);
+
+/*
+ * KV write: store each new token's K and V in its slot.
+ * Pages: agentalpha.top Q32 answer part 2 (a new token lands in the current block
+ * or opens a new one; nothing stored moves); ohmygp.com "破局思路" (one slot per
+ * decoded token; a new block only when the current one is full).
+ *   k_new, v_new  device, [num_tokens][H][D] contiguous, pool dtype, 16-byte aligned.
+ *   slot_mapping  device int64 [num_tokens]; token t goes to block slot/B, offset
+ *                 slot%B; slot < 0 skips the token (padding).
+ *   k_pool, v_pool device, layout above, 16-byte aligned; only the written slots change.
+ * Device preconditions: every slot < num_blocks * B; non-negative slots distinct.
+ * num_tokens == 0 enqueues nothing.  Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
+ */
+int32_t pkv_paged_kv_write(const pkv_pool_desc* pool, void* k_pool, void* v_pool,
+                           const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/*
+ * Copy-on-write block copy: for each pair (src, dst), block dst of the K pool and of
+ * the V pool (all heads, all slots) becomes a copy of block src.
+ * Pages: agentalpha.top Q32 answer part 3 (copy a shared block only when a sharer
+ * writes into it); data.6616ai.com "PagedAttention：把虚拟内存搬进 KV Cache" (refcounted
+ * shared prefix, copied only at divergence); ohmygp.com "破局思路" (写时共享).
+ *   src_dst_pairs device int64 [num_pairs][2].
+ * Device preconditions: ids < num_blocks; destinations distinct; no destination is
+ * also a source (a source may repeat).  num_pairs == 0 enqueues nothing.
+ * Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
+ */
+int32_t pkv_copy_blocks(const pkv_pool_desc* pool, void* k_pool, void* v_pool,
+                        const int64_t* src_dst_pairs, int32_t num_pairs, void* stream);
+
+/* Context tokens per split-context partition of the attention pass. */
+#define PKV_PARTITION_TOKENS 512
+
+/* Workspace bytes pkv_paged_attention_decode needs for these sizes (0 on bad input):
+ * fp32 partial results of every (sequence, query head, partition). */
+size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                           int32_t max_blocks_per_seq, int32_t block_size);
+
+/*
+ * Decode attention over the paged pool, one query token per sequence.
+ * Pages: data.6616ai.com "PagedAttention：把虚拟内存搬进 KV Cache" (the attention
+ * kernel reads K/V by block index: logically contiguous, physically scattered);
+ * agentalpha.top Q32 follow-up 3 (blockwise, FlashAttention-style loading adapted to
+ * non-contiguous blocks by pointer indexing).  For each sequence b and query head h,
+ * with G = num_q_heads / H and kv head g = h / G:
+ *     s_j = scale * dot(q[b][h], K[b, j, g])   for 0 <= j < context_lens[b]
+ *     out[b][h] = sum_j softmax(s)_j * V[b, j, g]
+ * where token j of sequence b sits in block block_tables[b][j / B] at offset j % B.
+ * Long contexts are split into PKV_PARTITION_TOKENS-token partitions whose partial
+ * results are merged with log-sum-exp weights (in `workspace`).
+ *   q, out        device [num_seqs][num_q_heads][D], pool dtype, contiguous, 16-byte aligned.
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries at index
+ *                 >= ceil(context_lens[b] / B) are never read.
+ *   context_lens  device int32 [num_seqs]; 0 gives a zero output row.
+ *   workspace     device, >= pkv_paged_attention_workspace_bytes(...), 256-byte aligned;
+ *                 contents on entry do not matter.
+ * num_q_heads must be a multiple of H.  Accumulation is fp32; the output is rounded
+ * to the pool dtype.  The reduction order depends only on logical token positions,
+ * so results do not depend on the physical placement of blocks.
+ * Device preconditions: context_lens[b] <= max_blocks_per_seq * B; table entries that
+ * are read are < num_blocks.  num_seqs == 0 enqueues nothing.
+ * Errors: INVALID_ARG, UNSUPPORTED (dtype/head_dim/block_size/group size), WORKSPACE, LAUNCH.
+ */
+int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                   void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two passes of pkv_paged_attention_decode, exposed separately (same arguments,
+ * same results when called in this order on one stream) so that each pass can be
+ * timed on its own.  The partition pass writes the final output for sequences of
+ * at most one partition and partial results for the others; the merge pass combines
+ * the partials of multi-partition sequences.
+ */
+int32_t pkv_paged_attention_partitions(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                       void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, float scale,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+int32_t pkv_paged_attention_merge(const pkv_pool_desc* pool, void* out, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, const void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side block manager: block tables, on-demand allocation, fork and
+ * copy-on-write decisions.  Pages: agentalpha.top Q32 answer parts 2-3;
+ * data.6616ai.com "PagedAttention：把虚拟内存搬进 KV Cache"; ohmygp.com "破局思路".
+ * Policy:
+ *  - the free list starts as `free_order` (host, a permutation of 0..num_blocks-1)
+ *    and hands out blocks from its front; freed blocks go to its back;
+ *  - add_seq(seq, n) gives a new sequence ceil(n / B) blocks;
+ *  - append_slot at position pos: pos % B == 0 opens a fresh block; otherwise, if the
+ *    tail block is shared (refcount > 1), the writer takes a fresh block, reports
+ *    (old tail, fresh) as a copy pair and drops one reference to the old tail;
+ *    the slot is table[pos / B] * B + pos % B;
+ *  - fork(parent, child): the child shares all of the parent's blocks (+1 reference each);
+ *  - free_seq drops one reference per block; blocks reaching zero become free.
+ * Sequence ids are any non-negative int32.  A pkv_bm is not thread-safe.
+ * Every call is host-only and synchronous.  Errors: INVALID_ARG (unknown or duplicate
+ * sequence, bad sizes), OUT_OF_BLOCKS (the state is unchanged when it is returned).
+ */
+typedef struct pkv_bm pkv_bm;
+
+int32_t pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pkv_bm** out);
+void pkv_bm_destroy(pkv_bm* bm);
+int32_t pkv_bm_add_seq(pkv_bm* bm, int32_t seq, int32_t num_tokens);
+int32_t pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child);
+/* Reserve the next token's slot; cow_src and cow_dst receive -1 when no copy is needed. */
+int32_t pkv_bm_append_slot(pkv_bm* bm, int32_t seq, int64_t* slot, int32_t* cow_src, int32_t* cow_dst);
+/* One decode step over `seqs` (host, n entries, visited in order): slots_out (host, n)
+ * receives each slot, pairs_out (host, [n][2] capacity) the copy pairs in order,
+ * *num_pairs their count.  On OUT_OF_BLOCKS the sequences before the failing one
+ * have been appended. */
+int32_t pkv_bm_step(pkv_bm* bm, const int32_t* seqs, int32_t n, int64_t* slots_out,
+                    int64_t* pairs_out, int32_t* num_pairs);
+int32_t pkv_bm_free_seq(pkv_bm* bm, int32_t seq);
+int32_t pkv_bm_seq_len(const pkv_bm* bm, int32_t seq, int32_t* len);
+/* Slots of positions pos0 .. pos0+count-1 of `seq` (host out, count entries). */
+int32_t pkv_bm_slots(const pkv_bm* bm, int32_t seq, int32_t pos0, int32_t count, int64_t* out);
+/* The block table of `seq` into out (host, cap entries); *n = its length. */
+int32_t pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t cap, int32_t* n);
+/* Tables of `seqs` (host, n) as a host int32 [n][width] matrix padded with `pad`. */
+int32_t pkv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t width,
+                            int32_t pad, int32_t* out);
+/* Reference count of `block` (-1 if out of range), number of free blocks. */
+int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
+int32_t pkv_bm_num_free(const pkv_bm* bm);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

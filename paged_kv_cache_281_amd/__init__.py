@@ -1,0 +1,291 @@
+"""Paged KV-cache decode for AMD Instinct MI355X (gfx950).
+
+A thin Python binding of ``libpkv.so`` (C ABI declared in ``include/pkv.h``).
+This module only marshals arguments -- torch tensors become device pointers and
+the current HIP stream -- and raises on a non-zero status.  Every step of the
+path runs in the library's HIP kernels; there is no fallback: if the library is
+missing, every call raises.
+
+Pool tensors use the library's physical layout, with X = 16 / element_bytes:
+  K pool ``[num_blocks, num_kv_heads, head_dim // X, block_size, X]``
+  V pool ``[num_blocks, num_kv_heads, head_dim, block_size]``
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+__all__ = [
+    "load", "library_path", "PoolDesc", "alloc_pools", "pool_desc", "paged_kv_write", "copy_blocks",
+    "workspace_bytes", "alloc_workspace", "paged_attention_decode", "paged_attention_partitions",
+    "paged_attention_merge", "BlockManager", "PkvError", "PARTITION_TOKENS", "DTYPE_CODES",
+]
+
+PARTITION_TOKENS = 512
+DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_c_i32, _c_i64, _c_vp, _c_sz, _c_f = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+
+_LIB = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", _c_i32), ("block_size", _c_i32), ("num_kv_heads", _c_i32),
+                ("head_dim", _c_i32), ("dtype", _c_i32)]
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+
+def load():
+    """Load libpkv.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m paged_kv_cache_281_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    sig = {
+        "pkv_version": ([], ctypes.c_char_p),
+        "pkv_status_string": ([_c_i32], ctypes.c_char_p),
+        "pkv_last_error": ([], ctypes.c_char_p),
+        "pkv_pool_bytes": ([P(PoolDesc)], _c_sz),
+        "pkv_paged_kv_write": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp], _c_i32),
+        "pkv_copy_blocks": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_i32, _c_vp], _c_i32),
+        "pkv_paged_attention_workspace_bytes": ([_c_i32, _c_i32, _c_i32, _c_i32, _c_i32], _c_sz),
+        "pkv_paged_attention_decode": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
+                                        _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_paged_attention_partitions": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
+                                            _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_paged_attention_merge": ([P(PoolDesc), _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_sz, _c_vp],
+                                      _c_i32),
+        "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
+        "pkv_bm_destroy": ([_c_vp], None),
+        "pkv_bm_add_seq": ([_c_vp, _c_i32, _c_i32], _c_i32),
+        "pkv_bm_fork": ([_c_vp, _c_i32, _c_i32], _c_i32),
+        "pkv_bm_append_slot": ([_c_vp, _c_i32, P(_c_i64), P(_c_i32), P(_c_i32)], _c_i32),
+        "pkv_bm_step": ([_c_vp, _c_vp, _c_i32, _c_vp, _c_vp, P(_c_i32)], _c_i32),
+        "pkv_bm_free_seq": ([_c_vp, _c_i32], _c_i32),
+        "pkv_bm_seq_len": ([_c_vp, _c_i32, P(_c_i32)], _c_i32),
+        "pkv_bm_slots": ([_c_vp, _c_i32, _c_i32, _c_i32, _c_vp], _c_i32),
+        "pkv_bm_block_table": ([_c_vp, _c_i32, _c_vp, _c_i32, P(_c_i32)], _c_i32),
+        "pkv_bm_block_tables": ([_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp], _c_i32),
+        "pkv_bm_refcount": ([_c_vp, _c_i32], _c_i32),
+        "pkv_bm_num_free": ([_c_vp], _c_i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _LIB = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load()
+        raise PkvError(status, f"{lib.pkv_status_string(status).decode()}: {lib.pkv_last_error().decode()}")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+# ---- pools ------------------------------------------------------------------------
+def pool_shapes(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype):
+    x = 16 // torch.empty((), dtype=dtype).element_size()
+    return ((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+            (num_blocks, num_kv_heads, head_dim, block_size))
+
+
+def alloc_pools(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+                device="cuda") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Uninitialised K and V pools in the library's layout."""
+    ks, vs = pool_shapes(num_blocks, block_size, num_kv_heads, head_dim, dtype)
+    return torch.empty(ks, dtype=dtype, device=device), torch.empty(vs, dtype=dtype, device=device)
+
+
+def pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor) -> PoolDesc:
+    _require(k_pool.dim() == 5 and v_pool.dim() == 4, "K pool must be 5-D and V pool 4-D")
+    nb, h, dx, B, x = k_pool.shape
+    _require(k_pool.dtype in DTYPE_CODES and v_pool.dtype == k_pool.dtype, "unsupported or mismatched pool dtype")
+    _require(x * k_pool.element_size() == 16, "K pool last dimension must span 16 bytes")
+    _require(tuple(v_pool.shape) == (nb, h, dx * x, B), "V pool shape does not match the K pool")
+    _require(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
+    _require(k_pool.is_cuda and v_pool.is_cuda, "pools must be device tensors")
+    return PoolDesc(nb, B, h, dx * x, DTYPE_CODES[k_pool.dtype])
+
+
+# ---- kernels ------------------------------------------------------------------------
+def paged_kv_write(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   slot_mapping: torch.Tensor) -> None:
+    """Store token t's K/V ``[num_kv_heads, head_dim]`` in slot ``slot_mapping[t]`` (negative: skip)."""
+    d = pool_desc(k_pool, v_pool)
+    T = k_new.shape[0]
+    for t in (k_new, v_new):
+        _require(tuple(t.shape) == (T, d.num_kv_heads, d.head_dim), "k_new/v_new must be [T, Hkv, D]")
+        _require(t.dtype == k_pool.dtype and t.is_contiguous() and t.device == k_pool.device, "k_new/v_new dtype/layout/device")
+    _require(slot_mapping.dtype == torch.int64 and tuple(slot_mapping.shape) == (T,) and slot_mapping.is_contiguous()
+             and slot_mapping.device == k_pool.device, "slot_mapping must be a contiguous int64 [T] device tensor")
+    _check(load().pkv_paged_kv_write(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                                     _ptr(slot_mapping), T, _stream(k_pool.device)))
+
+
+def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor) -> None:
+    """For each row (src, dst) of the int64 ``[P, 2]`` device tensor, block dst becomes a copy of src."""
+    d = pool_desc(k_pool, v_pool)
+    _require(pairs.dtype == torch.int64 and pairs.dim() == 2 and pairs.shape[1] == 2 and pairs.is_contiguous()
+             and pairs.device == k_pool.device, "pairs must be a contiguous int64 [P, 2] device tensor")
+    _check(load().pkv_copy_blocks(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0],
+                                  _stream(k_pool.device)))
+
+
+def workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_blocks_per_seq: int, block_size: int) -> int:
+    return int(load().pkv_paged_attention_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                                                          block_size))
+
+
+def alloc_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_blocks_per_seq: int, block_size: int,
+                    device="cuda") -> torch.Tensor:
+    n = workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _attn_args(q, k_pool, v_pool, block_tables, context_lens, out, workspace):
+    d = pool_desc(k_pool, v_pool)
+    _require(q.dim() == 3 and q.shape[2] == d.head_dim and q.dtype == k_pool.dtype and q.is_contiguous()
+             and q.device == k_pool.device, "q must be a contiguous [N, Hq, D] device tensor of the pool dtype")
+    N, Hq, _ = q.shape
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == N
+             and block_tables.is_contiguous() and block_tables.device == k_pool.device,
+             "block_tables must be a contiguous int32 [N, W] device tensor")
+    _require(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (N,) and context_lens.is_contiguous()
+             and context_lens.device == k_pool.device, "context_lens must be a contiguous int32 [N] device tensor")
+    W = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous() and out.device == q.device,
+             "out must match q")
+    if workspace is None:
+        workspace = alloc_workspace(N, Hq, d.head_dim, W, d.block_size, device=q.device)
+    return d, N, Hq, W, out, workspace
+
+
+def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """softmax(scale * q K^T) V per sequence and query head, K/V read through the block tables."""
+    d, N, Hq, W, out, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, out, workspace)
+    _check(load().pkv_paged_attention_decode(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq,
+                                             _ptr(block_tables), W, _ptr(context_lens), float(scale), _ptr(ws),
+                                             ws.numel(), _stream(q.device)))
+    return out
+
+
+def paged_attention_partitions(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace) -> None:
+    """First pass of ``paged_attention_decode`` (per-partition results)."""
+    d, N, Hq, W, out, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, out, workspace)
+    _check(load().pkv_paged_attention_partitions(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N,
+                                                 Hq, _ptr(block_tables), W, _ptr(context_lens), float(scale),
+                                                 _ptr(ws), ws.numel(), _stream(q.device)))
+
+
+def paged_attention_merge(q, k_pool, v_pool, block_tables, context_lens, out, workspace) -> None:
+    """Second pass of ``paged_attention_decode`` (log-sum-exp merge of partitions)."""
+    d, N, Hq, W, out, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, out, workspace)
+    _check(load().pkv_paged_attention_merge(ctypes.byref(d), _ptr(out), N, Hq, W, _ptr(context_lens), _ptr(ws),
+                                            ws.numel(), _stream(q.device)))
+
+
+# ---- host block manager ----------------------------------------------------------------
+class BlockManager:
+    """Host-side block manager of libpkv (tables, on-demand allocation, fork, copy-on-write)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Sequence[int]):
+        self._lib = load()
+        order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+        _require(order.shape == (num_blocks,), "free_order must hold num_blocks entries")
+        h = _c_vp()
+        _check(self._lib.pkv_bm_create(num_blocks, block_size, order.ctypes.data, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pkv_bm_destroy(h)
+            self._h = None
+
+    def add_seq(self, seq: int, num_tokens: int) -> None:
+        _check(self._lib.pkv_bm_add_seq(self._h, seq, num_tokens))
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(self._lib.pkv_bm_fork(self._h, parent, child))
+
+    def append_slot(self, seq: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+        slot, src, dst = _c_i64(), _c_i32(), _c_i32()
+        _check(self._lib.pkv_bm_append_slot(self._h, seq, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def step(self, seqs: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+        s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        n = len(s)
+        slots = np.empty(n, dtype=np.int64)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int64)
+        npairs = _c_i32()
+        _check(self._lib.pkv_bm_step(self._h, s.ctypes.data, n, slots.ctypes.data, pairs.ctypes.data,
+                                     ctypes.byref(npairs)))
+        return slots, pairs[:npairs.value].copy()
+
+    def free_seq(self, seq: int) -> None:
+        _check(self._lib.pkv_bm_free_seq(self._h, seq))
+
+    def seq_len(self, seq: int) -> int:
+        n = _c_i32()
+        _check(self._lib.pkv_bm_seq_len(self._h, seq, ctypes.byref(n)))
+        return n.value
+
+    def slots(self, seq: int, pos0: int, count: int) -> np.ndarray:
+        out = np.empty(count, dtype=np.int64)
+        _check(self._lib.pkv_bm_slots(self._h, seq, pos0, count, out.ctypes.data))
+        return out
+
+    def block_table(self, seq: int) -> List[int]:
+        n = _c_i32()
+        cap = self.num_blocks
+        out = np.empty(cap, dtype=np.int32)
+        _check(self._lib.pkv_bm_block_table(self._h, seq, out.ctypes.data, cap, ctypes.byref(n)))
+        return out[:n.value].tolist()
+
+    def block_tables(self, seqs: Sequence[int], width: int, pad: int) -> np.ndarray:
+        s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        out = np.empty((len(s), width), dtype=np.int32)
+        _check(self._lib.pkv_bm_block_tables(self._h, s.ctypes.data, len(s), width, pad, out.ctypes.data))
+        return out
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pkv_bm_refcount(self._h, block))
+
+    def num_free(self) -> int:
+        return int(self._lib.pkv_bm_num_free(self._h))

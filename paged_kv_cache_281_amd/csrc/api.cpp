@@ -1,0 +1,243 @@
+// C ABI of libpkv: argument validation, workspace sizing and dispatch to the
+// gfx950 kernels.  No entry point allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t launch_status(int rc, const char* what) {
+  if (rc == 0) return PKV_OK;
+  if (rc < 0) return set_error(PKV_ERR_UNSUPPORTED, what);
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s: launch failed: %s", what, hipGetErrorString(static_cast<hipError_t>(rc)));
+  return set_error(PKV_ERR_LAUNCH, buf);
+}
+
+int32_t check_pool(const pkv_pool_desc* pool, const char* who) {
+  char buf[256];
+  if (!pool) {
+    std::snprintf(buf, sizeof(buf), "%s: null pool descriptor", who);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (pool->num_blocks <= 0 || pool->block_size <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0) {
+    std::snprintf(buf, sizeof(buf), "%s: pool sizes must be positive", who);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (elem_bytes(pool->dtype) == 0) {
+    std::snprintf(buf, sizeof(buf), "%s: unknown dtype %d", who, pool->dtype);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (pool->head_dim != 64 && pool->head_dim != 128) {
+    std::snprintf(buf, sizeof(buf), "%s: head_dim %d unsupported (64 or 128)", who, pool->head_dim);
+    return set_error(PKV_ERR_UNSUPPORTED, buf);
+  }
+  if (pool->block_size != 16 && pool->block_size != 32) {
+    std::snprintf(buf, sizeof(buf), "%s: block_size %d unsupported (16 or 32)", who, pool->block_size);
+    return set_error(PKV_ERR_UNSUPPORTED, buf);
+  }
+  return PKV_OK;
+}
+
+struct AttnCheck {
+  int32_t status;
+  AttnArgs args;
+};
+
+size_t workspace_bytes_for(int64_t n, int64_t hq, int64_t d, int64_t parts) {
+  // partial outputs [n][hq][parts][d] then (max, sum) pairs [n][hq][parts][2], 256-byte aligned
+  const size_t o = static_cast<size_t>(n * hq * parts * d) * sizeof(float);
+  const size_t o_al = (o + 255) / 256 * 256;
+  return o_al + static_cast<size_t>(n * hq * parts * 2) * sizeof(float);
+}
+
+AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                          void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          float scale, const void* workspace, size_t workspace_bytes, bool need_pools) {
+  AttnCheck c{PKV_OK, {}};
+  char buf[256];
+  if ((c.status = check_pool(pool, who)) != PKV_OK) return c;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) {
+    std::snprintf(buf, sizeof(buf), "%s: num_seqs >= 0, num_q_heads > 0, max_blocks_per_seq > 0 required", who);
+    c.status = set_error(PKV_ERR_INVALID_ARG, buf);
+    return c;
+  }
+  if (num_q_heads % pool->num_kv_heads != 0) {
+    std::snprintf(buf, sizeof(buf), "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who, num_q_heads,
+                  pool->num_kv_heads);
+    c.status = set_error(PKV_ERR_INVALID_ARG, buf);
+    return c;
+  }
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (!attn_supported(pool->dtype, pool->head_dim, pool->block_size, group)) {
+    std::snprintf(buf, sizeof(buf), "%s: no kernel for dtype %d, head_dim %d, block_size %d, group %d", who,
+                  pool->dtype, pool->head_dim, pool->block_size, group);
+    c.status = set_error(PKV_ERR_UNSUPPORTED, buf);
+    return c;
+  }
+  const int64_t parts = max_partitions(max_blocks_per_seq, pool->block_size);
+  if (num_seqs > 65535 || parts > 65535) {
+    std::snprintf(buf, sizeof(buf), "%s: num_seqs and partitions per sequence must be <= 65535", who);
+    c.status = set_error(PKV_ERR_UNSUPPORTED, buf);
+    return c;
+  }
+  if (num_seqs > 0) {
+    if ((need_pools && (!k_pool || !v_pool || !q || !block_tables)) || !out || !context_lens) {
+      std::snprintf(buf, sizeof(buf), "%s: null pointer argument", who);
+      c.status = set_error(PKV_ERR_INVALID_ARG, buf);
+      return c;
+    }
+    if (!aligned(out, 16) || (need_pools && (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(q, 16))) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4)) {
+      std::snprintf(buf, sizeof(buf), "%s: misaligned pointer (pools, q, out need 16 bytes)", who);
+      c.status = set_error(PKV_ERR_INVALID_ARG, buf);
+      return c;
+    }
+  }
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, pool->head_dim, parts);
+  if (num_seqs > 0 && (workspace_bytes < need || !workspace || !aligned(workspace, 256))) {
+    std::snprintf(buf, sizeof(buf), "%s: workspace of %zu bytes (256-byte aligned) needed, got %zu", who, need,
+                  workspace_bytes);
+    c.status = set_error(PKV_ERR_WORKSPACE, buf);
+    return c;
+  }
+  AttnArgs& a = c.args;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.out = out;
+  a.q = q;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  const size_t o = static_cast<size_t>(static_cast<int64_t>(num_seqs) * num_q_heads * parts * pool->head_dim) *
+                   sizeof(float);
+  a.ws_o = static_cast<float*>(const_cast<void*>(workspace));
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + (o + 255) / 256 * 256);
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.block_size = pool->block_size;
+  a.dtype = pool->dtype;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_parts = static_cast<int32_t>(parts);
+  a.scale = scale;
+  return c;
+}
+
+}  // namespace
+
+int32_t set_error(int32_t status, const char* msg) {
+  g_last_error = msg ? msg : "";
+  return status;
+}
+
+}  // namespace pkv
+
+using pkv::set_error;
+
+extern "C" {
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+const char* pkv_status_string(int32_t status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_LAUNCH: return "PKV_ERR_LAUNCH";
+    case PKV_ERR_OUT_OF_BLOCKS: return "PKV_ERR_OUT_OF_BLOCKS";
+    default: return "PKV_ERR_UNKNOWN";
+  }
+}
+
+const char* pkv_last_error(void) { return pkv::g_last_error.c_str(); }
+
+size_t pkv_pool_bytes(const pkv_pool_desc* pool) {
+  if (!pool || pool->num_blocks <= 0 || pool->block_size <= 0 || pool->num_kv_heads <= 0 || pool->head_dim <= 0)
+    return 0;
+  const int eb = pkv::elem_bytes(pool->dtype);
+  return static_cast<size_t>(pool->num_blocks) * pool->num_kv_heads * pool->block_size * pool->head_dim * eb;
+}
+
+int32_t pkv_paged_kv_write(const pkv_pool_desc* pool, void* k_pool, void* v_pool, const void* k_new,
+                           const void* v_new, const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
+  int32_t st = pkv::check_pool(pool, "pkv_paged_kv_write");
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return set_error(PKV_ERR_INVALID_ARG, "pkv_paged_kv_write: negative num_tokens");
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
+    return set_error(PKV_ERR_INVALID_ARG, "pkv_paged_kv_write: null pointer argument");
+  if (!pkv::aligned(k_pool, 16) || !pkv::aligned(v_pool, 16) || !pkv::aligned(k_new, 16) ||
+      !pkv::aligned(v_new, 16) || !pkv::aligned(slot_mapping, 8))
+    return set_error(PKV_ERR_INVALID_ARG, "pkv_paged_kv_write: misaligned pointer");
+  return pkv::launch_status(pkv::launch_kv_write(*pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream),
+                            "pkv_paged_kv_write");
+}
+
+int32_t pkv_copy_blocks(const pkv_pool_desc* pool, void* k_pool, void* v_pool, const int64_t* src_dst_pairs,
+                        int32_t num_pairs, void* stream) {
+  int32_t st = pkv::check_pool(pool, "pkv_copy_blocks");
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return set_error(PKV_ERR_INVALID_ARG, "pkv_copy_blocks: negative num_pairs");
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src_dst_pairs) return set_error(PKV_ERR_INVALID_ARG, "pkv_copy_blocks: null pointer argument");
+  if (!pkv::aligned(k_pool, 16) || !pkv::aligned(v_pool, 16) || !pkv::aligned(src_dst_pairs, 8))
+    return set_error(PKV_ERR_INVALID_ARG, "pkv_copy_blocks: misaligned pointer");
+  return pkv::launch_status(pkv::launch_copy_blocks(*pool, k_pool, v_pool, src_dst_pairs, num_pairs, stream),
+                            "pkv_copy_blocks");
+}
+
+size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                           int32_t max_blocks_per_seq, int32_t block_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;
+  return pkv::workspace_bytes_for(num_seqs, num_q_heads, head_dim, pkv::max_partitions(max_blocks_per_seq, block_size));
+}
+
+int32_t pkv_paged_attention_partitions(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
+                                       const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, float scale, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  pkv::AttnCheck c = pkv::check_attention("pkv_paged_attention_partitions", pool, k_pool, v_pool, out, q, num_seqs,
+                                          num_q_heads, block_tables, max_blocks_per_seq, context_lens, scale,
+                                          workspace, workspace_bytes, true);
+  if (c.status != PKV_OK) return c.status;
+  if (num_seqs == 0) return PKV_OK;
+  return pkv::launch_status(pkv::launch_attn_partitions(c.args, stream), "pkv_paged_attention_partitions");
+}
+
+int32_t pkv_paged_attention_merge(const pkv_pool_desc* pool, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens, const void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  pkv::AttnCheck c = pkv::check_attention("pkv_paged_attention_merge", pool, nullptr, nullptr, out, nullptr, num_seqs,
+                                          num_q_heads, nullptr, max_blocks_per_seq, context_lens, 1.0f, workspace,
+                                          workspace_bytes, false);
+  if (c.status != PKV_OK) return c.status;
+  if (num_seqs == 0) return PKV_OK;
+  return pkv::launch_status(pkv::launch_attn_merge(c.args, stream), "pkv_paged_attention_merge");
+}
+
+int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
+                                   const void* q, int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = pkv_paged_attention_partitions(pool, k_pool, v_pool, out, q, num_seqs, num_q_heads, block_tables,
+                                              max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes,
+                                              stream);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  return pkv_paged_attention_merge(pool, out, num_seqs, num_q_heads, max_blocks_per_seq, context_lens, workspace,
+                                   workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+// Host-side block manager: block tables, on-demand allocation, fork, copy-on-write.
+//
+// Pages: agentalpha.top "Q32：vLLM PagedAttention 原理", answer part 2 (fixed-size
+// blocks handed out on demand; a per-request table from logical to physical block)
+// and part 3 (shared blocks are copied only when a sharer writes); data.6616ai.com
+// vLLM article, "PagedAttention：把虚拟内存搬进 KV Cache" (blocks requested one at a
+// time as a request grows; refcounted prefix sharing); ohmygp.com interview post,
+// "破局思路" (one slot per decoded token, a new block only when the current one is
+// full; copy on write into a shared block).
+//
+// The free list is a ring buffer over all block ids: allocation pops from the
+// front, release pushes to the back.  Tables are per-sequence vectors.
+#include <cstdint>
+#include <cstring>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+struct pkv_bm {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> ring;      // free list storage, capacity num_blocks
+  int64_t head = 0;               // index of the next block to hand out
+  int64_t count = 0;              // number of free blocks
+  std::vector<int32_t> refcount;  // per physical block
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t len = 0;
+  };
+  std::unordered_map<int32_t, Seq> seqs;
+
+  int32_t take() {
+    int32_t b = ring[head];
+    head = (head + 1) % num_blocks;
+    --count;
+    refcount[b] = 1;
+    return b;
+  }
+  void give_back(int32_t b) {
+    ring[(head + count) % num_blocks] = b;
+    ++count;
+  }
+};
+
+namespace {
+
+int32_t bad(const char* msg) { return pkv::set_error(PKV_ERR_INVALID_ARG, msg); }
+
+pkv_bm::Seq* find(pkv_bm* bm, int32_t seq) {
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? nullptr : &it->second;
+}
+const pkv_bm::Seq* find(const pkv_bm* bm, int32_t seq) {
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? nullptr : &it->second;
+}
+
+int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pkv_bm** out) {
+  if (!out || !free_order) return bad("pkv_bm_create: null pointer");
+  if (num_blocks <= 0 || block_size <= 0) return bad("pkv_bm_create: num_blocks and block_size must be positive");
+  std::vector<char> seen(num_blocks, 0);
+  for (int32_t i = 0; i < num_blocks; ++i) {
+    int32_t b = free_order[i];
+    if (b < 0 || b >= num_blocks || seen[b]) return bad("pkv_bm_create: free_order is not a permutation");
+    seen[b] = 1;
+  }
+  auto* bm = new pkv_bm;
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->ring.assign(free_order, free_order + num_blocks);
+  bm->head = 0;
+  bm->count = num_blocks;
+  bm->refcount.assign(num_blocks, 0);
+  *out = bm;
+  return PKV_OK;
+}
+
+void pkv_bm_destroy(pkv_bm* bm) { delete bm; }
+
+int32_t pkv_bm_add_seq(pkv_bm* bm, int32_t seq, int32_t num_tokens) {
+  if (!bm) return bad("pkv_bm_add_seq: null manager");
+  if (seq < 0 || num_tokens < 0) return bad("pkv_bm_add_seq: negative sequence id or token count");
+  if (find(bm, seq)) return bad("pkv_bm_add_seq: sequence already exists");
+  int64_t need = div_up(num_tokens, bm->block_size);
+  if (need > bm->count) return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_add_seq: not enough free blocks");
+  pkv_bm::Seq s;
+  s.table.reserve(need);
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->take());
+  s.len = num_tokens;
+  bm->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
+}
+
+int32_t pkv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child) {
+  if (!bm) return bad("pkv_bm_fork: null manager");
+  if (child < 0) return bad("pkv_bm_fork: negative sequence id");
+  const pkv_bm::Seq* p = find(bm, parent);
+  if (!p) return bad("pkv_bm_fork: unknown parent");
+  if (find(bm, child)) return bad("pkv_bm_fork: child already exists");
+  pkv_bm::Seq c = *p;
+  for (int32_t b : c.table) ++bm->refcount[b];
+  bm->seqs.emplace(child, std::move(c));
+  return PKV_OK;
+}
+
+int32_t pkv_bm_append_slot(pkv_bm* bm, int32_t seq, int64_t* slot, int32_t* cow_src, int32_t* cow_dst) {
+  if (!bm || !slot || !cow_src || !cow_dst) return bad("pkv_bm_append_slot: null pointer");
+  pkv_bm::Seq* s = find(bm, seq);
+  if (!s) return bad("pkv_bm_append_slot: unknown sequence");
+  const int32_t B = bm->block_size;
+  const int32_t pos = s->len;
+  *cow_src = -1;
+  *cow_dst = -1;
+  if (pos % B == 0) {
+    if (bm->count == 0) return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_append_slot: no free block");
+    s->table.push_back(bm->take());
+  } else {
+    int32_t tail = s->table.back();
+    if (bm->refcount[tail] > 1) {
+      if (bm->count == 0) return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_append_slot: no free block");
+      int32_t fresh = bm->take();
+      --bm->refcount[tail];
+      s->table.back() = fresh;
+      *cow_src = tail;
+      *cow_dst = fresh;
+    }
+  }
+  *slot = static_cast<int64_t>(s->table[pos / B]) * B + pos % B;
+  s->len = pos + 1;
+  return PKV_OK;
+}
+
+int32_t pkv_bm_step(pkv_bm* bm, const int32_t* seqs, int32_t n, int64_t* slots_out, int64_t* pairs_out,
+                    int32_t* num_pairs) {
+  if (!bm || !num_pairs || (n > 0 && (!seqs || !slots_out || !pairs_out))) return bad("pkv_bm_step: null pointer");
+  if (n < 0) return bad("pkv_bm_step: negative count");
+  *num_pairs = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t src, dst;
+    int32_t st = pkv_bm_append_slot(bm, seqs[i], &slots_out[i], &src, &dst);
+    if (st != PKV_OK) return st;
+    if (src >= 0) {
+      pairs_out[2 * *num_pairs] = src;
+      pairs_out[2 * *num_pairs + 1] = dst;
+      ++*num_pairs;
+    }
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_bm_free_seq(pkv_bm* bm, int32_t seq) {
+  if (!bm) return bad("pkv_bm_free_seq: null manager");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return bad("pkv_bm_free_seq: unknown sequence");
+  for (int32_t b : it->second.table) {
+    if (--bm->refcount[b] == 0) bm->give_back(b);
+  }
+  bm->seqs.erase(it);
+  return PKV_OK;
+}
+
+int32_t pkv_bm_seq_len(const pkv_bm* bm, int32_t seq, int32_t* len) {
+  if (!bm || !len) return bad("pkv_bm_seq_len: null pointer");
+  const pkv_bm::Seq* s = find(bm, seq);
+  if (!s) return bad("pkv_bm_seq_len: unknown sequence");
+  *len = s->len;
+  return PKV_OK;
+}
+
+int32_t pkv_bm_slots(const pkv_bm* bm, int32_t seq, int32_t pos0, int32_t count, int64_t* out) {
+  if (!bm || (count > 0 && !out)) return bad("pkv_bm_slots: null pointer");
+  const pkv_bm::Seq* s = find(bm, seq);
+  if (!s) return bad("pkv_bm_slots: unknown sequence");
+  if (pos0 < 0 || count < 0 || static_cast<int64_t>(pos0) + count > s->len)
+    return bad("pkv_bm_slots: positions outside the sequence");
+  const int32_t B = bm->block_size;
+  for (int32_t i = 0; i < count; ++i) {
+    int32_t pos = pos0 + i;
+    out[i] = static_cast<int64_t>(s->table[pos / B]) * B + pos % B;
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t cap, int32_t* n) {
+  if (!bm || !n || (cap > 0 && !out)) return bad("pkv_bm_block_table: null pointer");
+  const pkv_bm::Seq* s = find(bm, seq);
+  if (!s) return bad("pkv_bm_block_table: unknown sequence");
+  *n = static_cast<int32_t>(s->table.size());
+  if (*n > cap) return bad("pkv_bm_block_table: capacity too small");
+  if (*n) std::memcpy(out, s->table.data(), sizeof(int32_t) * *n);
+  return PKV_OK;
+}
+
+int32_t pkv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t width, int32_t pad,
+                            int32_t* out) {
+  if (!bm || (n > 0 && (!seqs || !out))) return bad("pkv_bm_block_tables: null pointer");
+  if (n < 0 || width < 0) return bad("pkv_bm_block_tables: negative size");
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq* s = find(bm, seqs[i]);
+    if (!s) return bad("pkv_bm_block_tables: unknown sequence");
+    if (static_cast<int64_t>(s->table.size()) > width) return bad("pkv_bm_block_tables: table wider than width");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq* s = find(bm, seqs[i]);
+    int32_t* row = out + static_cast<int64_t>(i) * width;
+    int32_t k = static_cast<int32_t>(s->table.size());
+    if (k) std::memcpy(row, s->table.data(), sizeof(int32_t) * k);
+    for (int32_t j = k; j < width; ++j) row[j] = pad;
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->refcount[block];
+}
+
+int32_t pkv_bm_num_free(const pkv_bm* bm) { return bm ? static_cast<int32_t>(bm->count) : -1; }
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Device-side helpers for the gfx950 kernels: raw vector types, element traits,
+// MFMA / dot2 wrappers and wave-level shuffles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pkv {
+
+typedef unsigned int u32;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+
+// exp2 on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ float shfl_idx(float v, int src) { return __shfl(v, src, 64); }
+__device__ __forceinline__ u32 shfl_idx_u(u32 v, int src) {
+  return static_cast<u32>(__shfl(static_cast<int>(v), src, 64));
+}
+
+// Element traits.  Storage is handled as raw bits; arithmetic is fp32.
+struct BF16 {
+  static constexpr int kBytes = 2;
+  typedef uint16_t Bits;
+  __device__ static __forceinline__ u32 pack2(float a, float b) {
+    bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(u32, v);
+  }
+  __device__ static __forceinline__ float lo(u32 w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ float hi(u32 w) { return __uint_as_float(w & 0xffff0000u); }
+  __device__ static __forceinline__ float dot2(u32 a, u32 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+  }
+  // 16x16x32 MFMA, A/B = 8 elements per lane
+  __device__ static __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // 16x16x16 MFMA, A/B = 4 elements per lane
+  __device__ static __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ Bits from_float(float f) {
+    return __builtin_bit_cast(Bits, static_cast<__bf16>(f));
+  }
+};
+
+struct F16 {
+  static constexpr int kBytes = 2;
+  typedef uint16_t Bits;
+  __device__ static __forceinline__ u32 pack2(float a, float b) {
+    f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(u32, v);
+  }
+  __device__ static __forceinline__ float lo(u32 w) {
+    return static_cast<float>(__builtin_bit_cast(f16x2, w)[0]);
+  }
+  __device__ static __forceinline__ float hi(u32 w) {
+    return static_cast<float>(__builtin_bit_cast(f16x2, w)[1]);
+  }
+  __device__ static __forceinline__ float dot2(u32 a, u32 b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+  }
+  __device__ static __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ Bits from_float(float f) {
+    return __builtin_bit_cast(Bits, static_cast<_Float16>(f));
+  }
+};
+
+struct F32 {
+  static constexpr int kBytes = 4;
+  typedef float Bits;
+  __device__ static __forceinline__ Bits from_float(float f) { return f; }
+};
+
+}  // namespace pkv

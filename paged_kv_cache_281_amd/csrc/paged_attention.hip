@@ -1,0 +1,634 @@
+// Decode attention over a paged KV pool, for gfx950 (CDNA4).
+//
+// Pages: data.6616ai.com vLLM article, "PagedAttention：把虚拟内存搬进 KV Cache" (the
+// attention kernel reads K/V by block index: logically contiguous, physically
+// scattered); agentalpha.top "Q32：vLLM PagedAttention 原理", follow-up 3 (blockwise,
+// FlashAttention-style loading adapted to scattered blocks through pointer
+// indexing); data.6616ai.com "可能的追问" (the cost is table lookups and
+// non-contiguous access); data.6616ai.com "PagedAttention 之外" and ohmygp.com
+// "先搞清敌人" (decode is bound by memory, not compute).
+//
+// Work split.  A workgroup (4 waves) owns one (sequence, kv head [, group of up to
+// 16 query heads], partition of PKV_PARTITION_TOKENS context tokens).  It stages
+// the partition's block-table entries in LDS, then each wave walks every 4th
+// 16-token unit of the partition with a register double buffer (the next unit's K
+// and V loads are in flight while the current unit is computed), keeping an online
+// softmax (running max in log2 units, running sum, rescaled output).  The four
+// waves' states are merged in LDS.  A sequence that fits in one partition gets its
+// final output here; longer ones leave (max, sum, normalised output) per partition
+// in the workspace for the merge kernel, which weights partition p by
+// exp2(m_p - M) * l_p.
+//
+// Loads.  With the pool layout of pkv.h one (block, kv head) tile is contiguous:
+// K as [D/X][B][X] 16-byte chunks, V as [D][B].  Lane (r = lane/16, m = lane%16)
+// reads K chunk (4i + r) of token m of the unit, so every K load instruction covers
+// four 256-byte runs; it reads V row (16c + m), tokens 4r..4r+3, so every V load
+// instruction covers 512 contiguous bytes.  The physical block id comes from LDS and
+// is made wave-uniform, so tile addresses are scalar.
+//
+// Grouped-query heads (2..16 query heads per kv head, bf16/fp16) use MFMA: the
+// scores S^T[token][head] of a 16-token unit are a 16x16x32 MFMA chain over D (K
+// fragment as A, the group's queries zero-padded to 16 columns as B), and
+// O^T[d][head] += V^T[d][token] P^T[token][head] is a 16x16x16 MFMA per 16 d whose B
+// operand is the score accumulator's own register layout, rounded to the pool type.
+// One query head per kv head (and fp32 pools) use the vector ALU: bf16/fp16 dot
+// products with v_dot2 (fp32 accumulate), fp32 with FMAs.
+//
+// NaN safety: scores of tokens past the context are replaced by -inf (select, not
+// arithmetic) and V elements of those tokens are zeroed before they meet p = 0.
+// The per-token reduction order depends only on logical positions, so the result
+// does not depend on where the blocks sit.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kPT = PKV_PARTITION_TOKENS;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+struct Params {
+  const char* q;
+  const char* kp;
+  const char* vp;
+  char* out;
+  float* ws_o;
+  float* ws_ml;
+  const int* tables;
+  const int* ctx;
+  int Hq, Hkv, G, NHG, W, Pmax;
+  float scale_log2;
+};
+
+template <class T, int D>
+__device__ __forceinline__ void zero_rows(const Params& P, int b, int hq0, int nrows) {
+  typedef typename T::Bits Bits;
+  Bits* o = reinterpret_cast<Bits*>(P.out) + (static_cast<int64_t>(b) * P.Hq + hq0) * D;
+  for (int i = threadIdx.x; i < nrows * D; i += kThreads) o[i] = T::from_float(0.f);
+}
+
+// Merge the four waves' (max, sum, output) in LDS; store the final row or the partials.
+template <class T, int D, int GMAX>
+__device__ __forceinline__ void combine_and_store(const Params& P, const float (*s_m)[GMAX],
+                                                  const float (*s_l)[GMAX], const float (*s_o)[GMAX][D + 4],
+                                                  int b, int hq0, int gcur, int p, int np) {
+  typedef typename T::Bits Bits;
+  for (int idx = threadIdx.x; idx < gcur * D; idx += kThreads) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(s_m[w][g] - M);
+      num += f * s_o[w][g][d];
+      den += f * s_l[w][g];
+    }
+    const int64_t row = static_cast<int64_t>(b) * P.Hq + hq0 + g;
+    if (np == 1) {
+      reinterpret_cast<Bits*>(P.out)[row * D + d] = T::from_float(num / den);
+    } else {
+      const int64_t pr = row * P.Pmax + p;
+      P.ws_o[pr * D + d] = num / den;
+      if (d == 0) {
+        P.ws_ml[2 * pr] = M;
+        P.ws_ml[2 * pr + 1] = den;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// MFMA partition kernel: bf16/fp16 pools, 2..16 query heads per workgroup.
+// grid = (num_kv_heads * head_groups, max_partitions, num_seqs)
+// ---------------------------------------------------------------------------------
+template <class T, int D, int B, int GMAX>
+__global__ __launch_bounds__(kThreads) void attn_partition_mfma(Params P) {
+  constexpr int EB = T::kBytes;
+  static_assert(EB == 2, "MFMA path is for 16-bit pools");
+  constexpr int KI = D / 32;   // 16x16x32 steps over head_dim
+  constexpr int NC = D / 16;   // 16x16x16 products per unit (16 d each)
+  constexpr int SUB = B / 16;  // 16-token units per block
+  constexpr int BPP = kPT / B;
+  constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
+
+  __shared__ int s_tab[BPP];
+  __shared__ float s_m[kWaves][GMAX];
+  __shared__ float s_l[kWaves][GMAX];
+  __shared__ float s_o[kWaves][GMAX][D + 4];
+
+  const int hy = blockIdx.x;
+  const int p = blockIdx.y;
+  const int b = blockIdx.z;
+  const int kvh = hy / P.NHG;
+  const int hg = hy - kvh * P.NHG;
+  const int hq0 = kvh * P.G + hg * 16;
+  const int gcur = min(16, P.G - hg * 16);
+  const int L = P.ctx[b];
+  if (L <= 0) {
+    if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
+    return;
+  }
+  const int np = (L + kPT - 1) / kPT;
+  if (p >= np) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int r = lane >> 4;
+  const int m = lane & 15;
+  const int ntok = min(kPT, L - p * kPT);
+  const int nunits = (ntok + 15) >> 4;
+  const int nblk = (ntok + B - 1) / B;
+
+  if (tid < nblk) s_tab[tid] = P.tables[static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP + tid];
+
+  const bool hv = m < gcur;
+  u32x4 qf[KI];
+  {
+    const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + (hv ? m : 0)) * D * EB;
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki) {
+      qf[ki] = hv ? *reinterpret_cast<const u32x4*>(qrow + (4 * ki + r) * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
+
+  const char* kbase = P.kp + kvh * TILE;
+  const char* vbase = P.vp + kvh * TILE;
+  const int64_t bstride = static_cast<int64_t>(P.Hkv) * TILE;
+  const int koff = (r * B + m) * 16;       // + ki * 4 * B * 16 + sub * 256
+  const int voff = (m * B + 4 * r) * EB;   // + c * 16 * B * EB + sub * 16 * EB
+
+  auto load = [&](int u, u32x4 (&kf)[KI], u32x2 (&vf)[NC]) {
+    const int bi = u / SUB;
+    const int sub = u - bi * SUB;
+    const int blk = __builtin_amdgcn_readfirstlane(s_tab[bi]);
+    const char* kt = kbase + blk * bstride + sub * 256;
+    const char* vt = vbase + blk * bstride + sub * 16 * EB;
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki) kf[ki] = *reinterpret_cast<const u32x4*>(kt + koff + ki * 4 * B * 16);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vf[c] = *reinterpret_cast<const u32x2*>(vt + voff + c * 16 * B * EB);
+  };
+
+  float m_run = kNegInf;
+  float l_part = 0.f;
+  f32x4 o[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int u, const u32x4 (&kf)[KI], u32x2 (&vf)[NC]) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki) acc = T::mfma_k32(kf[ki], qf[ki], acc);
+    float s0 = acc[0] * P.scale_log2, s1 = acc[1] * P.scale_log2;
+    float s2 = acc[2] * P.scale_log2, s3 = acc[3] * P.scale_log2;
+    if (16 * u + 16 > ntok) {
+      const int t0 = 16 * u + 4 * r;
+      s0 = (t0 + 0 < ntok) ? s0 : kNegInf;
+      s1 = (t0 + 1 < ntok) ? s1 : kNegInf;
+      s2 = (t0 + 2 < ntok) ? s2 : kNegInf;
+      s3 = (t0 + 3 < ntok) ? s3 : kNegInf;
+      const u32 mlo = (t0 + 0 < ntok ? 0x0000ffffu : 0u) | (t0 + 1 < ntok ? 0xffff0000u : 0u);
+      const u32 mhi = (t0 + 2 < ntok ? 0x0000ffffu : 0u) | (t0 + 3 < ntok ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        vf[c][0] &= mlo;
+        vf[c][1] &= mhi;
+      }
+    }
+    float mx = fmaxf(fmaxf(s0, s1), fmaxf(s2, s3));
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - mn);
+    const u32 p01 = T::pack2(fast_exp2(s0 - mn), fast_exp2(s1 - mn));
+    const u32 p23 = T::pack2(fast_exp2(s2 - mn), fast_exp2(s3 - mn));
+    l_part = l_part * alpha + ((T::lo(p01) + T::hi(p01)) + (T::lo(p23) + T::hi(p23)));
+    const u32x2 pb = {p01, p23};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      o[c] *= alpha;
+      o[c] = T::mfma_k16(vf[c], pb, o[c]);
+    }
+    m_run = mn;
+  };
+
+  {
+    u32x4 ka[KI], kb[KI];
+    u32x2 va[NC], vb[NC];
+    int u = w;
+    if (u < nunits) {
+      load(u, ka, va);
+      while (true) {
+        const int u1 = u + kWaves;
+        if (u1 < nunits) load(u1, kb, vb);
+        compute(u, ka, va);
+        if (u1 >= nunits) break;
+        const int u2 = u1 + kWaves;
+        if (u2 < nunits) load(u2, ka, va);
+        compute(u1, kb, vb);
+        if (u2 >= nunits) break;
+        u = u2;
+      }
+    }
+  }
+
+  float l = l_part;
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+  if (hv) {
+    if (r == 0) {
+      s_m[w][m] = m_run;
+      s_l[w][m] = l;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_o[w][m][16 * c + 4 * r + j] = o[c][j];
+    }
+  }
+  __syncthreads();
+  combine_and_store<T, D, GMAX>(P, s_m, s_l, s_o, b, hq0, gcur, p, np);
+}
+
+// ---------------------------------------------------------------------------------
+// Vector-ALU partition kernel: one query head per kv head (any pool type), or fp32
+// pools with G query heads per kv head.  grid = (num_kv_heads, max_partitions, num_seqs)
+// ---------------------------------------------------------------------------------
+template <class T, int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
+  constexpr int EB = T::kBytes;
+  constexpr int X = 16 / EB;
+  constexpr int NCH = D / X;
+  constexpr int KL = NCH / 4;  // K chunks per lane per unit: r, r+4, r+8, ...
+  constexpr int NV = D / 16;   // V rows per lane per unit: m, m+16, ...
+  constexpr int SUB = B / 16;
+  constexpr int BPP = kPT / B;
+  constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
+  typedef typename std::conditional<EB == 2, u32x2, u32x4>::type VVec;  // 4 tokens of one V row
+
+  __shared__ int s_tab[BPP];
+  __shared__ float s_m[kWaves][G];
+  __shared__ float s_l[kWaves][G];
+  __shared__ float s_o[kWaves][G][D + 4];
+
+  const int kvh = blockIdx.x;
+  const int p = blockIdx.y;
+  const int b = blockIdx.z;
+  const int hq0 = kvh * G;
+  const int L = P.ctx[b];
+  if (L <= 0) {
+    if (p == 0) zero_rows<T, D>(P, b, hq0, G);
+    return;
+  }
+  const int np = (L + kPT - 1) / kPT;
+  if (p >= np) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int r = lane >> 4;
+  const int m = lane & 15;
+  const int ntok = min(kPT, L - p * kPT);
+  const int nunits = (ntok + 15) >> 4;
+  const int nblk = (ntok + B - 1) / B;
+
+  if (tid < nblk) s_tab[tid] = P.tables[static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP + tid];
+
+  // queries: lane keeps chunks r + 4i of every head (fp32 pools: pre-scaled floats)
+  u32x4 qw[G][KL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + g) * D * EB;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + (r + 4 * i) * 16);
+      if constexpr (EB == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(__uint_as_float(v[e]) * P.scale_log2);
+      }
+      qw[g][i] = v;
+    }
+  }
+  __syncthreads();
+
+  const char* kbase = P.kp + kvh * TILE;
+  const char* vbase = P.vp + kvh * TILE;
+  const int64_t bstride = static_cast<int64_t>(P.Hkv) * TILE;
+  const int koff = (r * B + m) * 16;      // + i * 4 * B * 16 + sub * 256
+  const int voff = (m * B + 4 * r) * EB;  // + c * 16 * B * EB + sub * 16 * EB
+
+  auto load = [&](int u, u32x4 (&kf)[KL], VVec (&vf)[NV]) {
+    const int bi = u / SUB;
+    const int sub = u - bi * SUB;
+    const int blk = __builtin_amdgcn_readfirstlane(s_tab[bi]);
+    const char* kt = kbase + blk * bstride + sub * 256;
+    const char* vt = vbase + blk * bstride + sub * 16 * EB;
+#pragma unroll
+    for (int i = 0; i < KL; ++i) kf[i] = *reinterpret_cast<const u32x4*>(kt + koff + i * 4 * B * 16);
+#pragma unroll
+    for (int c = 0; c < NV; ++c) vf[c] = *reinterpret_cast<const VVec*>(vt + voff + c * 16 * B * EB);
+  };
+
+  float m_run[G], l_part[G], o[G][NV];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = kNegInf;
+    l_part[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) o[g][c] = 0.f;
+  }
+  const int src_row = (lane & 48) | (4 * r);  // lane holding token 4r of this row
+
+  auto compute = [&](int u, const u32x4 (&kf)[KL], VVec (&vf)[NV]) {
+    float s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        if constexpr (EB == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part = T::dot2(kf[i][e], qw[g][i][e], part);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part = fmaf(__uint_as_float(kf[i][e]), __uint_as_float(qw[g][i][e]), part);
+        }
+      }
+      part += shfl_xor(part, 16);
+      part += shfl_xor(part, 32);
+      s[g] = (EB == 2) ? part * P.scale_log2 : part;
+    }
+    const bool tail = 16 * u + 16 > ntok;
+    if (tail) {
+      const bool valid = 16 * u + m < ntok;
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[g] = valid ? s[g] : kNegInf;
+      const int t0 = 16 * u + 4 * r;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        if constexpr (EB == 2) {
+          const u32 mlo = (t0 + 0 < ntok ? 0x0000ffffu : 0u) | (t0 + 1 < ntok ? 0xffff0000u : 0u);
+          const u32 mhi = (t0 + 2 < ntok ? 0x0000ffffu : 0u) | (t0 + 3 < ntok ? 0xffff0000u : 0u);
+          vf[c][0] &= mlo;
+          vf[c][1] &= mhi;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vf[c][e] = (t0 + e < ntok) ? vf[c][e] : 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = s[g];
+      mx = fmaxf(mx, shfl_xor(mx, 1));
+      mx = fmaxf(mx, shfl_xor(mx, 2));
+      mx = fmaxf(mx, shfl_xor(mx, 4));
+      mx = fmaxf(mx, shfl_xor(mx, 8));
+      const float mn = fmaxf(m_run[g], mx);
+      const float alpha = fast_exp2(m_run[g] - mn);
+      float pr = fast_exp2(s[g] - mn);
+      m_run[g] = mn;
+      if constexpr (EB == 2) {
+        pr = T::lo(T::pack2(pr, 0.f));  // probabilities in the pool type, as the product uses them
+        const float other = shfl_xor(pr, 1);
+        const u32 pw = (m & 1) ? T::pack2(other, pr) : T::pack2(pr, other);  // (p[2k], p[2k+1])
+        const u32 pp0 = shfl_idx_u(pw, src_row);
+        const u32 pp1 = shfl_idx_u(pw, src_row + 2);
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          float acc = o[g][c] * alpha;
+          acc = T::dot2(vf[c][0], pp0, acc);
+          acc = T::dot2(vf[c][1], pp1, acc);
+          o[g][c] = acc;
+        }
+      } else {
+        float pt[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pt[e] = shfl_idx(pr, src_row + e);
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          float acc = o[g][c] * alpha;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = fmaf(pt[e], __uint_as_float(vf[c][e]), acc);
+          o[g][c] = acc;
+        }
+      }
+      l_part[g] = l_part[g] * alpha + pr;
+    }
+  };
+
+  {
+    u32x4 ka[KL], kb[KL];
+    VVec va[NV], vb[NV];
+    int u = w;
+    if (u < nunits) {
+      load(u, ka, va);
+      while (true) {
+        const int u1 = u + kWaves;
+        if (u1 < nunits) load(u1, kb, vb);
+        compute(u, ka, va);
+        if (u1 >= nunits) break;
+        const int u2 = u1 + kWaves;
+        if (u2 < nunits) load(u2, ka, va);
+        compute(u1, kb, vb);
+        if (u2 >= nunits) break;
+        u = u2;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float l = l_part[g];
+    l += shfl_xor(l, 1);
+    l += shfl_xor(l, 2);
+    l += shfl_xor(l, 4);
+    l += shfl_xor(l, 8);
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      float v = o[g][c];
+      v += shfl_xor(v, 16);
+      v += shfl_xor(v, 32);
+      o[g][c] = v;
+    }
+    if (lane < 16) {
+      if (m == 0) {
+        s_m[w][g] = m_run[g];
+        s_l[w][g] = l;
+      }
+#pragma unroll
+      for (int c = 0; c < NV; ++c) s_o[w][g][16 * c + m] = o[g][c];
+    }
+  }
+  __syncthreads();
+  combine_and_store<T, D, G>(P, s_m, s_l, s_o, b, hq0, G, p, np);
+}
+
+// ---------------------------------------------------------------------------------
+// Merge kernel: log-sum-exp combination of partition partials.  grid = (Hq, N)
+// ---------------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(kThreads) void attn_merge(Params P) {
+  typedef typename T::Bits Bits;
+  constexpr int NCOL = D / 4;
+  constexpr int NG = kThreads / NCOL;
+  __shared__ float s_red[kWaves];
+  __shared__ f32x4 s_acc[NG][NCOL];
+
+  const int hq = blockIdx.x;
+  const int b = blockIdx.y;
+  const int L = P.ctx[b];
+  const int np = (L + kPT - 1) / kPT;
+  if (np <= 1) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int64_t row = static_cast<int64_t>(b) * P.Hq + hq;
+  const float* ml = P.ws_ml + row * P.Pmax * 2;
+  const float* po = P.ws_o + row * P.Pmax * D;
+
+  float mx = kNegInf;
+  for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, ml[2 * i]);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, shfl_xor(mx, k));
+  if (lane == 0) s_red[w] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+
+  float den = 0.f;
+  for (int i = tid; i < np; i += kThreads) den += fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) den += shfl_xor(den, k);
+  if (lane == 0) s_red[w] = den;
+  __syncthreads();
+  const float DEN = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+
+  const int col = tid % NCOL;
+  const int grp = tid / NCOL;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = grp; i < np; i += NG) {
+    const float wgt = fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(po + static_cast<int64_t>(i) * D + col * 4);
+    acc += wgt * v;
+  }
+  s_acc[grp][col] = acc;
+  __syncthreads();
+  if (tid < NCOL) {
+    f32x4 sum = s_acc[0][tid];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) sum += s_acc[g][tid];
+    Bits* o = reinterpret_cast<Bits*>(P.out) + row * D + tid * 4;
+    const float inv = 1.f / DEN;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = T::from_float(sum[e] * inv);
+  }
+}
+
+Params make_params(const AttnArgs& a) {
+  Params P;
+  P.q = static_cast<const char*>(a.q);
+  P.kp = static_cast<const char*>(a.k_pool);
+  P.vp = static_cast<const char*>(a.v_pool);
+  P.out = static_cast<char*>(a.out);
+  P.ws_o = a.ws_o;
+  P.ws_ml = a.ws_ml;
+  P.tables = a.block_tables;
+  P.ctx = a.context_lens;
+  P.Hq = a.num_q_heads;
+  P.Hkv = a.num_kv_heads;
+  P.G = a.num_q_heads / a.num_kv_heads;
+  P.NHG = (P.G + 15) / 16;
+  P.W = a.max_blocks_per_seq;
+  P.Pmax = a.max_parts;
+  P.scale_log2 = a.scale * kLog2e;
+  return P;
+}
+
+template <class T, int D, int B>
+int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
+  const Params P = make_params(a);
+  const dim3 block(kThreads);
+  const bool valu = (T::kBytes == 4) || P.G == 1;
+  if (valu) {
+    const dim3 grid(a.num_kv_heads, a.max_parts, a.num_seqs);
+    switch (P.G) {
+      case 1: hipLaunchKernelGGL((attn_partition_valu<T, D, B, 1>), grid, block, 0, s, P); break;
+      case 2:
+        if constexpr (T::kBytes == 4) { hipLaunchKernelGGL((attn_partition_valu<T, D, B, 2>), grid, block, 0, s, P); break; }
+        return -1;
+      case 4:
+        if constexpr (T::kBytes == 4) { hipLaunchKernelGGL((attn_partition_valu<T, D, B, 4>), grid, block, 0, s, P); break; }
+        return -1;
+      default: return -1;
+    }
+  } else if constexpr (T::kBytes == 2) {
+    const dim3 grid(a.num_kv_heads * P.NHG, a.max_parts, a.num_seqs);
+    if (P.G <= 4) {
+      hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 4>), grid, block, 0, s, P);
+    } else if (P.G <= 8) {
+      hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 8>), grid, block, 0, s, P);
+    } else {
+      hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 16>), grid, block, 0, s, P);
+    }
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+template <class T, int D>
+int launch_merge_t(const AttnArgs& a, hipStream_t s) {
+  const Params P = make_params(a);
+  hipLaunchKernelGGL((attn_merge<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kThreads), 0, s, P);
+  return static_cast<int>(hipGetLastError());
+}
+
+template <class T>
+int launch_partitions_d(const AttnArgs& a, hipStream_t s) {
+  if (a.head_dim == 64) return a.block_size == 16 ? launch_partitions_t<T, 64, 16>(a, s) : launch_partitions_t<T, 64, 32>(a, s);
+  return a.block_size == 16 ? launch_partitions_t<T, 128, 16>(a, s) : launch_partitions_t<T, 128, 32>(a, s);
+}
+
+template <class T>
+int launch_merge_d(const AttnArgs& a, hipStream_t s) {
+  return a.head_dim == 64 ? launch_merge_t<T, 64>(a, s) : launch_merge_t<T, 128>(a, s);
+}
+
+}  // namespace
+
+bool attn_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
+  if (head_dim != 64 && head_dim != 128) return false;
+  if (block_size != 16 && block_size != 32) return false;
+  if (group < 1) return false;
+  if (dtype == PKV_F32) return group == 1 || group == 2 || group == 4;
+  return dtype == PKV_F16 || dtype == PKV_BF16;
+}
+
+int launch_attn_partitions(const AttnArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (a.dtype) {
+    case PKV_F32: return launch_partitions_d<F32>(a, s);
+    case PKV_F16: return launch_partitions_d<F16>(a, s);
+    case PKV_BF16: return launch_partitions_d<BF16>(a, s);
+    default: return -1;
+  }
+}
+
+int launch_attn_merge(const AttnArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (a.dtype) {
+    case PKV_F32: return launch_merge_d<F32>(a, s);
+    case PKV_F16: return launch_merge_d<F16>(a, s);
+    case PKV_BF16: return launch_merge_d<BF16>(a, s);
+    default: return -1;
+  }
+}
+
+}  // namespace pkv

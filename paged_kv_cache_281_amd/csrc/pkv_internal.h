@@ -1,0 +1,56 @@
+// Internal declarations shared by the host-side translation units of libpkv.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Records `msg` as the calling thread's last error and returns `status`.
+int32_t set_error(int32_t status, const char* msg);
+
+// Element bytes of a pkv_dtype, 0 if unknown.
+inline int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+// Partitions of PKV_PARTITION_TOKENS tokens needed for max_blocks_per_seq blocks.
+inline int64_t max_partitions(int64_t max_blocks_per_seq, int64_t block_size) {
+  return (max_blocks_per_seq * block_size + PKV_PARTITION_TOKENS - 1) / PKV_PARTITION_TOKENS;
+}
+
+// Kernel launchers (defined in the .hip files).  They assume validated arguments
+// and return a hipError_t value as int.
+int launch_kv_write(const pkv_pool_desc& pool, void* k_pool, void* v_pool, const void* k_new,
+                    const void* v_new, const int64_t* slots, int32_t num_tokens, void* stream);
+int launch_copy_blocks(const pkv_pool_desc& pool, void* k_pool, void* v_pool, const int64_t* pairs,
+                       int32_t num_pairs, void* stream);
+
+struct AttnArgs {
+  const void* k_pool;
+  const void* v_pool;
+  void* out;
+  const void* q;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_o;   // [num_seqs][num_q_heads][max_partitions][head_dim]
+  float* ws_ml;  // [num_seqs][num_q_heads][max_partitions][2]: running max (log2 units), sum
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
+  int32_t max_blocks_per_seq, max_parts;
+  float scale;
+};
+
+// Returns -1 when no kernel exists for the shape/dtype/group size, else a hipError_t.
+int launch_attn_partitions(const AttnArgs& a, void* stream);
+int launch_attn_merge(const AttnArgs& a, void* stream);
+// Whether a partition kernel exists for this configuration.
+bool attn_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
+
+}  // namespace pkv

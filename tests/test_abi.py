@@ -1,0 +1,92 @@
+"""The C-ABI library loads and exports every declared symbol; host-side paths (CPU only)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(pkv_lib):
+    names = _declared_functions()
+    assert len(names) >= 20
+    lib = ctypes.CDLL(pkv_lib.library_path())
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version(pkv_lib):
+    lib = pkv_lib.load()
+    assert lib.pkv_version().decode().startswith("pkv")
+    assert lib.pkv_status_string(0) == b"PKV_OK"
+    assert lib.pkv_status_string(5) == b"PKV_ERR_OUT_OF_BLOCKS"
+
+
+def test_workspace_and_pool_sizes(pkv_lib):
+    lib = pkv_lib.load()
+    # 8 sequences x 32 heads x 256 partitions x 128 floats, then (max, sum) pairs
+    n = lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 8192, 16)
+    parts = 8192 * 16 // 512
+    o = 8 * 32 * parts * 128 * 4
+    assert n == (o + 255) // 256 * 256 + 8 * 32 * parts * 2 * 4
+    assert lib.pkv_paged_attention_workspace_bytes(-1, 32, 128, 8, 16) == 0
+    d = pkv_lib.PoolDesc(65536, 16, 8, 128, 2)
+    assert lib.pkv_pool_bytes(ctypes.byref(d)) == 2 * 2 ** 30
+
+
+def test_host_side_argument_errors(pkv_lib):
+    """Invalid arguments are rejected on the host, before any device work."""
+    lib = pkv_lib.load()
+    P = pkv_lib.PoolDesc
+    fake = ctypes.c_void_p(0x1000)
+    st = lib.pkv_paged_kv_write(None, fake, fake, fake, fake, fake, 4, None)
+    assert st == 1 and b"null pool" in lib.pkv_last_error()
+    st = lib.pkv_paged_kv_write(ctypes.byref(P(64, 24, 8, 128, 2)), fake, fake, fake, fake, fake, 4, None)
+    assert st == 2 and b"block_size" in lib.pkv_last_error()
+    st = lib.pkv_paged_kv_write(ctypes.byref(P(64, 16, 8, 96, 2)), fake, fake, fake, fake, fake, 4, None)
+    assert st == 2
+    st = lib.pkv_paged_kv_write(ctypes.byref(P(64, 16, 8, 128, 7)), fake, fake, fake, fake, fake, 4, None)
+    assert st == 1
+    st = lib.pkv_paged_kv_write(ctypes.byref(P(64, 16, 8, 128, 2)), fake, fake, ctypes.c_void_p(0x1008), fake,
+                                fake, 4, None)
+    assert st == 1 and b"misaligned" in lib.pkv_last_error()
+    assert lib.pkv_paged_kv_write(ctypes.byref(P(64, 16, 8, 128, 2)), None, None, None, None, None, 0, None) == 0
+    assert lib.pkv_copy_blocks(ctypes.byref(P(64, 16, 8, 128, 2)), fake, fake, None, 3, None) == 1
+    assert lib.pkv_copy_blocks(ctypes.byref(P(64, 16, 8, 128, 2)), None, None, None, 0, None) == 0
+    d = ctypes.byref(P(64, 16, 8, 128, 2))
+    # num_q_heads not a multiple of num_kv_heads
+    st = lib.pkv_paged_attention_decode(d, fake, fake, fake, fake, 4, 12, fake, 4, fake, 1.0, fake, 1 << 20, None)
+    assert st == 1 and b"multiple" in lib.pkv_last_error()
+    # workspace too small
+    st = lib.pkv_paged_attention_decode(d, fake, fake, fake, fake, 4, 32, fake, 4, fake, 1.0, fake, 16, None)
+    assert st == 3
+    # fp32 with 8 query heads per kv head has no kernel
+    st = lib.pkv_paged_attention_decode(ctypes.byref(P(64, 16, 4, 128, 0)), fake, fake, fake, fake, 4, 32, fake, 4,
+                                        fake, 1.0, fake, 1 << 24, None)
+    assert st == 2
+    assert lib.pkv_paged_attention_decode(d, None, None, None, None, 0, 32, None, 4, None, 1.0, None, 0, None) == 0
+
+
+def test_block_manager_errors(pkv_lib):
+    bm = pkv_lib.BlockManager(4, 16, [3, 1, 0, 2])
+    bm.add_seq(0, 17)
+    with pytest.raises(pkv_lib.PkvError) as e:
+        bm.add_seq(0, 1)
+    assert e.value.status == 1
+    with pytest.raises(pkv_lib.PkvError) as e:
+        bm.add_seq(1, 64)
+    assert e.value.status == 5
+    assert bm.num_free() == 2  # the failed call changed nothing
+    with pytest.raises(pkv_lib.PkvError):
+        bm.fork(7, 8)
+    with pytest.raises(pkv_lib.PkvError):
+        pkv_lib.BlockManager(4, 16, [0, 1, 1, 2])
+    assert bm.refcount(99) == -1
