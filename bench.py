@@ -1,0 +1,273 @@
+"""Benchmark of one paged decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the copy-on-write block
+copies of the step (if any), the KV write of the step's new tokens (slots from
+the host block manager), the partition pass of paged attention and the
+log-sum-exp merge.  Inputs are seeded synthetic data already resident in HBM.
+
+Prints one JSON line.  ``value`` is KV GB/s over the whole step (attention's
+algorithmic K+V bytes / step time); ``roofline`` describes the dominant kernel
+(the attention partition pass) against MI355X's 8 TB/s HBM peak; ``cpu_baseline``
+times the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV GB/s (% of HBM peak) + decode tokens/sec, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+PARTITION_TOKENS = 512
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_attention.hip")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, lens):
+    """Bytes the attention partition pass must move, by item (see the design notes)."""
+    e = w.elem_bytes
+    H, D, B, Hq = w.num_kv_heads, w.head_dim, w.block_size, w.num_q_heads
+    G = Hq // H
+    groups = H * max(1, -(-G // 16)) if G > 1 and w.dtype != "f32" else H
+    lens = np.asarray(lens, dtype=np.int64)
+    kv = int(2 * lens.sum() * H * D * e)
+    q = int(len(lens) * Hq * D * e)
+    parts = -(-lens // PARTITION_TOKENS)
+    single = parts <= 1
+    out = int(single.sum() * Hq * D * e)
+    partials = int(parts[~single].sum() * Hq * (D + 2) * 4)
+    tables = int(groups * (-(-lens // B)).sum() * 4 + len(lens) * 4)
+    return {"kv": kv, "q": q, "out": out, "partials": partials, "tables": tables,
+            "total": kv + q + out + partials + tables}
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch of the partition kernel from a committed rocprofv3 PMC
+    summary, if its kernel source hash matches the current source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_partition_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if not h or not t or h.group(1) != cur:
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(w, ctx, target_s):
+    """The fp64 oracle (as it stands) on a bounded sample: the measured step's KV write
+    and attention for the first sequences of the batch, until ``target_s`` elapses."""
+    import synth
+    from oracle.attention import paged_attention_decode as oracle_attention
+    from oracle.kv_cache import paged_kv_write as oracle_write
+    from oracle.replay import replay as oracle_replay
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    ora = oracle_replay(w, synth.NAN_BITS[w.dtype], context=ctx)
+    q = w.queries()
+    k_new, v_new = w.step_kv(len(w.steps) - 1)
+    done, kv_bytes = 0, 0
+    t0 = time.perf_counter()
+    for b in range(w.num_seqs):
+        oracle_write(ora.pool, k_new[b:b + 1], v_new[b:b + 1], ora.last_slots[b:b + 1])
+        oracle_attention(q, w.dtype, ora.pool, ora.block_tables, ora.context_lens, w.scale, seqs=[b])
+        done += 1
+        kv_bytes += 2 * int(ora.context_lens[b]) * w.num_kv_heads * w.head_dim * w.elem_bytes
+        if time.perf_counter() - t0 > target_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": kv_bytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "tokens_per_s": done / el,
+            "sample": f"KV write + attention of the first {done} of {w.num_seqs} sequences of the batch "
+                      f"({kv_bytes / 1e9:.3f} GB of KV) in {el:.1f} s; fp64 NumPy, BLAS threads {threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-reps", type=int, default=10,
+                    help="extra partition-pass timings, each after a 512 MiB cache flush")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path runs on one GPU, see the design notes for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "reps": 5}))
+        return
+
+    import paged_kv_cache_281_amd as pkv
+    import synth
+    pkv.load()
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    ti = {"f32": (np.int32, torch.int32), "f16": (np.int16, torch.int16), "bf16": (np.int16, torch.int16)}
+
+    w = synth.by_name(args.workload)
+    log(f"workload {w.name}: N={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
+        f"B={w.block_size} {w.dtype} tokens={int(w.context_lens.sum())}")
+    t = time.perf_counter()
+    ctx = w.all_context_kv()
+    log(f"generated context values in {time.perf_counter() - t:.1f} s")
+    npi, tint = ti[w.dtype]
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(npi)).to(dev).view(tdt[w.dtype])
+
+    # ---- set-up: every operation before the measured step ----------------------------
+    bm = pkv.BlockManager(w.num_blocks, w.block_size, w.free_order)
+    kp, vp = pkv.alloc_pools(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, tdt[w.dtype], dev)
+    kp.view(tint).fill_(0)
+    vp.view(tint).fill_(0)
+    for seq, n in w.prefill:
+        bm.add_seq(seq, n)
+        if n:
+            k, v = ctx.pop(seq)
+            pkv.paged_kv_write(kp, vp, up(k), up(v), torch.from_numpy(bm.slots(seq, 0, n)).to(dev))
+    for p, c in w.forks:
+        bm.fork(p, c)
+    for i, seqs in enumerate(w.steps[:-1]):
+        slots, pairs = bm.step(seqs)
+        if len(pairs):
+            pkv.copy_blocks(kp, vp, torch.from_numpy(pairs).to(dev))
+        k, v = w.step_kv(i)
+        pkv.paged_kv_write(kp, vp, up(k), up(v), torch.from_numpy(slots).to(dev))
+    # the measured step: host block manager once (its cost is reported separately)
+    th = time.perf_counter()
+    slots, pairs = bm.step(w.steps[-1])
+    host_bm_us = (time.perf_counter() - th) * 1e6
+    k_new, v_new = (up(x) for x in w.step_kv(len(w.steps) - 1))
+    slots_d = torch.from_numpy(slots).to(dev)
+    pairs_d = torch.from_numpy(pairs).to(dev)
+    tables = torch.from_numpy(bm.block_tables(w.batch, w.max_blocks_per_seq, 0)).to(dev)
+    lens_np = np.asarray([bm.seq_len(int(s)) for s in w.batch], dtype=np.int32)
+    lens = torch.from_numpy(lens_np).to(dev)
+    q = up(w.queries())
+    out = torch.empty_like(q)
+    ws = pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_blocks_per_seq, w.block_size, dev)
+    torch.cuda.synchronize()
+    log(f"set-up done; step has {len(pairs)} copy pairs, {len(slots)} new tokens")
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        if len(pairs):
+            pkv.copy_blocks(kp, vp, pairs_d)
+        pkv.paged_kv_write(kp, vp, k_new, v_new, slots_d)
+        if e is not None:
+            e[1].record(stream)
+        pkv.paged_attention_partitions(q, kp, vp, tables, lens, w.scale, out, ws)
+        if e is not None:
+            e[2].record(stream)
+        pkv.paged_attention_merge(q, kp, vp, tables, lens, out, ws)
+        if e is not None:
+            e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    write_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    part_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    merge_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    log(f"step {ms_step:.4f} ms (copy+write {write_ms:.4f}, partitions {part_ms:.4f}, merge {merge_ms:.4f})")
+
+    # partition pass after flushing L2 / MALL with a 512 MiB write (outside the events)
+    flushed = []
+    if args.flush_reps > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.flush_reps):
+            scratch.fill_(1)
+            e0.record(stream)
+            pkv.paged_attention_partitions(q, kp, vp, tables, lens, w.scale, out, ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            flushed.append(e0.elapsed_time(e1))
+        del scratch
+        pkv.paged_attention_merge(q, kp, vp, tables, lens, out, ws)
+        torch.cuda.synchronize()
+
+    ab = algorithmic_bytes(w, lens_np)
+    kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
+    achieved = ab["total"] / (part_ms * 1e-3) / 1e9
+    traffic = stored_traffic(args.workload)
+    res = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "context_tokens": int(lens_np.sum()), "max_context": int(lens_np.max()),
+                   "partition_tokens": PARTITION_TOKENS, "copy_pairs": int(len(pairs)),
+                   "kv_bytes": ab["kv"]},
+        "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "attention_kv_gbs": round(ab["kv"] / ((part_ms + merge_ms) * 1e-3) / 1e9, 2),
+        "kernel_ms": {"copy_and_write": round(write_ms, 5), "attn_partitions": round(part_ms, 5),
+                      "attn_merge": round(merge_ms, 5)},
+        "attn_partitions_ms_after_cache_flush": round(float(np.median(flushed)), 5) if flushed else None,
+        "host_block_manager_step_us": round(host_bm_us, 1),
+        "roofline": {"kernel": "attn_partition", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": ab},
+    }
+    if not args.no_cpu_baseline:
+        del kp, vp
+        torch.cuda.empty_cache()
+        log("timing the oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(w, w.all_context_kv(), args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,7 +44,8 @@ class PoolDesc(ctypes.Structure):
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+    """The in-tree libpkv.so, or the file named by the PKV_LIBRARY environment variable."""
+    return os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 
 def load():

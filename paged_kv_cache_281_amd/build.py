@@ -29,18 +29,23 @@ def _hipcc() -> str:
 def _flags(debug: bool):
     f = [f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
          # no packed-fp32 instructions in device code
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in VGPRs: the online-softmax rescale works on them with VALU ops
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
     f += ["-O1", "-g", "-DPKV_DEBUG=1"] if debug else ["-O3"]
     return f
 
 
-def build(debug: bool = False, jobs: int = 8, verbose: bool = False) -> str:
-    """Compile every source under csrc/ and link libpkv.so; returns the library path."""
+def build(debug: bool = False, jobs: int = 8, verbose: bool = False, extra_flags=(), out: str = None) -> str:
+    """Compile every source under csrc/ and link libpkv.so (or ``out``); returns its path."""
     hipcc = _hipcc()
-    out_dir = os.path.join(HERE, "_build", "debug" if debug else "release")
+    tag = "debug" if debug else "release"
+    if extra_flags:
+        tag += "-" + str(abs(hash(tuple(extra_flags))))
+    out_dir = os.path.join(HERE, "_build", tag)
     os.makedirs(out_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    flags = _flags(debug)
+    flags = _flags(debug) + list(extra_flags)
 
     def compile_one(src):
         obj = os.path.join(out_dir, os.path.basename(src) + ".o")
@@ -56,7 +61,7 @@ def build(debug: bool = False, jobs: int = 8, verbose: bool = False) -> str:
 
     with cf.ThreadPoolExecutor(max(1, jobs)) as ex:
         objs = list(ex.map(compile_one, sources))
-    lib = LIB if not debug else os.path.join(HERE, "libpkv_debug.so")
+    lib = out or (LIB if not debug else os.path.join(HERE, "libpkv_debug.so"))
     tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)

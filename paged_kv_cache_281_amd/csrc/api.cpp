@@ -54,10 +54,8 @@ struct AttnCheck {
 };
 
 size_t workspace_bytes_for(int64_t n, int64_t hq, int64_t d, int64_t parts) {
-  // partial outputs [n][hq][parts][d] then (max, sum) pairs [n][hq][parts][2], 256-byte aligned
-  const size_t o = static_cast<size_t>(n * hq * parts * d) * sizeof(float);
-  const size_t o_al = (o + 255) / 256 * 256;
-  return o_al + static_cast<size_t>(n * hq * parts * 2) * sizeof(float);
+  // partial outputs, (max, sum) pairs, the task list and counters
+  return workspace_layout(n, hq, d, parts).total;
 }
 
 AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
@@ -86,8 +84,9 @@ AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void
     return c;
   }
   const int64_t parts = max_partitions(max_blocks_per_seq, pool->block_size);
-  if (num_seqs > 65535 || parts > 65535) {
-    std::snprintf(buf, sizeof(buf), "%s: num_seqs and partitions per sequence must be <= 65535", who);
+  if (num_seqs > 65535 || parts > 65535 || static_cast<int64_t>(num_seqs) * parts * num_q_heads > (int64_t{1} << 23)) {
+    std::snprintf(buf, sizeof(buf), "%s: num_seqs and partitions per sequence must be <= 65535 and "
+                  "num_seqs * partitions * num_q_heads <= 2^23", who);
     c.status = set_error(PKV_ERR_UNSUPPORTED, buf);
     return c;
   }
@@ -118,10 +117,12 @@ AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void
   a.q = q;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  const size_t o = static_cast<size_t>(static_cast<int64_t>(num_seqs) * num_q_heads * parts * pool->head_dim) *
-                   sizeof(float);
-  a.ws_o = static_cast<float*>(const_cast<void*>(workspace));
-  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + (o + 255) / 256 * 256);
+  const WorkspaceLayout L = workspace_layout(num_seqs, num_q_heads, pool->head_dim, parts);
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  a.ws_o = reinterpret_cast<float*>(ws + L.o);
+  a.ws_ml = reinterpret_cast<float*>(ws + L.ml);
+  a.tasks = reinterpret_cast<int*>(ws + L.tasks);
+  a.counters = reinterpret_cast<int*>(ws + L.counters);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;

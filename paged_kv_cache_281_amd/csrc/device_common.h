@@ -25,6 +25,49 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Reductions across the four 16-lane rows of a wave with the gfx950 lane-swap
+// instructions (no LDS traffic).  xor16: rows (0,1) and (2,3); xor32: rows (0,2), (1,3).
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Reductions within each 16-lane row through DPP: partners lane^15, lane^7, lane^3,
+// lane^1 (row mirror, half-row mirror, two quad permutations) span the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<0x140>(v));  // row_mirror
+  v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp<0x1B>(v));   // quad_perm [3,2,1,0]
+  v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0x140>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x1B>(v);
+  v += dpp<0xB1>(v);
+  return v;
+}
+
+// True in every lane when `pred` holds in any active lane (wave-uniform).
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 __device__ __forceinline__ float shfl_idx(float v, int src) { return __shfl(v, src, 64); }
 __device__ __forceinline__ u32 shfl_idx_u(u32 v, int src) {
   return static_cast<u32>(__shfl(static_cast<int>(v), src, 64));

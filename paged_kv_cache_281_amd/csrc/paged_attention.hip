@@ -13,7 +13,8 @@
 // the partition's block-table entries in LDS, then each wave walks every 4th
 // 16-token unit of the partition with a register double buffer (the next unit's K
 // and V loads are in flight while the current unit is computed), keeping an online
-// softmax (running max in log2 units, running sum, rescaled output).  The four
+// softmax (running max in log2 units, running sum, rescaled output).  Items are
+// taken from a device-built task list ordered longest first (plan kernel).  The four
 // waves' states are merged in LDS.  A sequence that fits in one partition gets its
 // final output here; longer ones leave (max, sum, normalised output) per partition
 // in the workspace for the merge kernel, which weights partition p by
@@ -40,6 +41,8 @@
 // does not depend on where the blocks sit.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -59,9 +62,58 @@ struct Params {
   float* ws_ml;
   const int* tables;
   const int* ctx;
-  int Hq, Hkv, G, NHG, W, Pmax;
+  const int* tasks;     // (sequence * Pmax + partition) items, longest first
+  const int* counters;  // counters[0] = number of items
+  int Hq, Hkv, G, NHG, W, Pmax, Lmax;
   float scale_log2;
 };
+
+// Context length of sequence b, clamped to what its table can address (longer
+// values break the caller's contract; clamping keeps every access in bounds).
+__device__ __forceinline__ int context_len(const Params& P, int b) { return min(max(P.ctx[b], 0), P.Lmax); }
+
+// ---------------------------------------------------------------------------------
+// Plan kernel (one workgroup): lists every (sequence, partition) item, longest first
+// so that the short tail partitions of a skewed batch run last.  Items are bucketed
+// by their number of 16-token units (full partitions first); an empty sequence gets
+// one item, which writes its zero output.  Only the order within a bucket depends
+// on timing, and no result depends on the order.
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void attn_plan(Params P, int N, int* __restrict__ tasks, int* __restrict__ counters) {
+  constexpr int NB = kPT / 16;
+  __shared__ int cnt[NB + 1];
+  __shared__ int off[NB + 1];
+  const int tid = threadIdx.x;
+  if (tid <= NB) cnt[tid] = 0;
+  __syncthreads();
+  for (int b = tid; b < N; b += blockDim.x) {
+    const int L = context_len(P, b);
+    const int full = L / kPT;
+    const int rem = L - full * kPT;
+    if (full) atomicAdd(&cnt[NB], full);
+    if (rem || L == 0) atomicAdd(&cnt[rem ? (rem + 15) >> 4 : 1], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int k = NB; k >= 1; --k) {
+      off[k] = acc;
+      acc += cnt[k];
+    }
+    counters[0] = acc;
+  }
+  __syncthreads();
+  for (int b = tid; b < N; b += blockDim.x) {
+    const int L = context_len(P, b);
+    const int full = L / kPT;
+    const int rem = L - full * kPT;
+    if (full) {
+      const int s = atomicAdd(&off[NB], full);
+      for (int q = 0; q < full; ++q) tasks[s + q] = b * P.Pmax + q;
+    }
+    if (rem || L == 0) tasks[atomicAdd(&off[rem ? (rem + 15) >> 4 : 1], 1)] = b * P.Pmax + full;
+  }
+}
 
 template <class T, int D>
 __device__ __forceinline__ void zero_rows(const Params& P, int b, int hq0, int nrows) {
@@ -103,12 +155,117 @@ __device__ __forceinline__ void combine_and_store(const Params& P, const float (
   }
 }
 
+// Runs load/compute over this wave's units w, w+NW, w+2*NW, ... with three register
+// buffers: while unit i is computed, units i+1 and i+2 are in flight.  Loads in the
+// steady-state loop are unconditional, so each compute waits only for its own data.
+template <int NW, class Buf, class Load, class Compute>
+__device__ __forceinline__ void pipeline3(int w, int nunits, Load&& load, Compute&& compute) {
+  const int n = nunits > w ? (nunits - w + NW - 1) / NW : 0;
+  Buf A, B, C;
+  if (n > 0) load(w, A);
+  if (n > 1) load(w + NW, B);
+  int i = 0;
+  for (; i + 4 < n; i += 3) {
+    const int u = w + i * NW;
+    load(u + 2 * NW, C);
+    compute(u, A);
+    load(u + 3 * NW, A);
+    compute(u + NW, B);
+    load(u + 4 * NW, B);
+    compute(u + 2 * NW, C);
+  }
+  const int r = n - i;
+  const int u = w + i * NW;
+  if (r == 4) {
+    load(u + 2 * NW, C);
+    compute(u, A);
+    load(u + 3 * NW, A);
+    compute(u + NW, B);
+    compute(u + 2 * NW, C);
+    compute(u + 3 * NW, A);
+  } else if (r == 3) {
+    load(u + 2 * NW, C);
+    compute(u, A);
+    compute(u + NW, B);
+    compute(u + 2 * NW, C);
+  } else if (r == 2) {
+    compute(u, A);
+    compute(u + NW, B);
+  } else if (r == 1) {
+    compute(u, A);
+  }
+}
+
+// Two-buffer variant: while unit i is computed, unit i+1 is in flight.  The
+// scheduling fences keep each prefetch issued before the compute it overlaps.
+#define PKV_FENCE() __builtin_amdgcn_sched_barrier(0)
+template <int NW, class Buf, class Load, class Compute>
+__device__ __forceinline__ void pipeline2(int w, int nunits, Load&& load, Compute&& compute) {
+  const int n = nunits > w ? (nunits - w + NW - 1) / NW : 0;
+  Buf A, B;
+  if (n > 0) load(w, A);
+  int i = 0;
+  for (; i + 2 < n; i += 2) {
+    const int u = w + i * NW;
+    load(u + NW, B);
+    PKV_FENCE();
+    compute(u, A);
+    PKV_FENCE();
+    load(u + 2 * NW, A);
+    PKV_FENCE();
+    compute(u + NW, B);
+    PKV_FENCE();
+  }
+  const int u = w + i * NW;
+  if (n - i == 2) {
+    load(u + NW, B);
+    PKV_FENCE();
+    compute(u, A);
+    PKV_FENCE();
+    compute(u + NW, B);
+  } else if (n - i == 1) {
+    compute(u, A);
+  }
+}
+
+#ifndef PKV_STAGES
+#define PKV_STAGES 2
+#endif
+template <int NW, class Buf, class Load, class Compute>
+__device__ __forceinline__ void pipeline(int w, int nunits, Load&& load, Compute&& compute) {
+  if constexpr (PKV_STAGES == 3) {
+    pipeline3<NW, Buf>(w, nunits, load, compute);
+  } else {
+    pipeline2<NW, Buf>(w, nunits, load, compute);
+  }
+}
+
+// Loads of K/V tiles: every byte is read once per decode step, so they are issued
+// non-temporal (streamed through the caches without displacing the block tables,
+// queries and partial results that are reused).
+template <class V>
+__device__ __forceinline__ V load_stream(const char* p) {
+#ifdef PKV_CACHED_LOADS
+  return *reinterpret_cast<const V*>(p);
+#else
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+#endif
+}
+
+// A running max is only raised (and the accumulators rescaled) when a new score
+// exceeds it by more than this many log2 units; until then probabilities are taken
+// against the stale max and stay below 2^kRescaleLog2 (no overflow in fp32/bf16/fp16).
+constexpr float kRescaleLog2 = 8.f;
+
 // ---------------------------------------------------------------------------------
 // MFMA partition kernel: bf16/fp16 pools, 2..16 query heads per workgroup.
 // grid = (num_kv_heads * head_groups, max_partitions, num_seqs)
 // ---------------------------------------------------------------------------------
 template <class T, int D, int B, int GMAX>
-__global__ __launch_bounds__(kThreads) void attn_partition_mfma(Params P) {
+#ifndef PKV_MFMA_WAVES_PER_EU
+#define PKV_MFMA_WAVES_PER_EU 1
+#endif
+__global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partition_mfma(Params P) {
   constexpr int EB = T::kBytes;
   static_assert(EB == 2, "MFMA path is for 16-bit pools");
   constexpr int KI = D / 32;   // 16x16x32 steps over head_dim
@@ -116,20 +273,28 @@ __global__ __launch_bounds__(kThreads) void attn_partition_mfma(Params P) {
   constexpr int SUB = B / 16;  // 16-token units per block
   constexpr int BPP = kPT / B;
   constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
+  struct Buf {
+    u32x4 k[KI];
+    u32x2 v[NC];
+  };
 
   __shared__ int s_tab[BPP];
   __shared__ float s_m[kWaves][GMAX];
   __shared__ float s_l[kWaves][GMAX];
   __shared__ float s_o[kWaves][GMAX][D + 4];
 
-  const int hy = blockIdx.x;
-  const int p = blockIdx.y;
-  const int b = blockIdx.z;
+  const int HY = P.Hkv * P.NHG;
+  const int t = blockIdx.x / HY;
+  const int hy = blockIdx.x - t * HY;
+  if (t >= P.counters[0]) return;
+  const int item = P.tasks[t];
+  const int b = item / P.Pmax;
+  const int p = item - b * P.Pmax;
   const int kvh = hy / P.NHG;
   const int hg = hy - kvh * P.NHG;
   const int hq0 = kvh * P.G + hg * 16;
   const int gcur = min(16, P.G - hg * 16);
-  const int L = P.ctx[b];
+  const int L = context_len(P, b);
   if (L <= 0) {
     if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
     return;
@@ -139,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_mfma(Params P) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;
   const int m = lane & 15;
   const int ntok = min(kPT, L - p * kPT);
@@ -165,16 +330,16 @@ __global__ __launch_bounds__(kThreads) void attn_partition_mfma(Params P) {
   const int koff = (r * B + m) * 16;       // + ki * 4 * B * 16 + sub * 256
   const int voff = (m * B + 4 * r) * EB;   // + c * 16 * B * EB + sub * 16 * EB
 
-  auto load = [&](int u, u32x4 (&kf)[KI], u32x2 (&vf)[NC]) {
+  auto load = [&](int u, Buf& f) {
     const int bi = u / SUB;
     const int sub = u - bi * SUB;
     const int blk = __builtin_amdgcn_readfirstlane(s_tab[bi]);
     const char* kt = kbase + blk * bstride + sub * 256;
     const char* vt = vbase + blk * bstride + sub * 16 * EB;
 #pragma unroll
-    for (int ki = 0; ki < KI; ++ki) kf[ki] = *reinterpret_cast<const u32x4*>(kt + koff + ki * 4 * B * 16);
+    for (int ki = 0; ki < KI; ++ki) f.k[ki] = load_stream<u32x4>(kt + koff + ki * 4 * B * 16);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vf[c] = *reinterpret_cast<const u32x2*>(vt + voff + c * 16 * B * EB);
+    for (int c = 0; c < NC; ++c) f.v[c] = load_stream<u32x2>(vt + voff + c * 16 * B * EB);
   };
 
   float m_run = kNegInf;
@@ -183,10 +348,10 @@ __global__ __launch_bounds__(kThreads) void attn_partition_mfma(Params P) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int u, const u32x4 (&kf)[KI], u32x2 (&vf)[NC]) {
+  auto compute = [&](int u, Buf& f) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ki = 0; ki < KI; ++ki) acc = T::mfma_k32(kf[ki], qf[ki], acc);
+    for (int ki = 0; ki < KI; ++ki) acc = T::mfma_k32(f.k[ki], qf[ki], acc);
     float s0 = acc[0] * P.scale_log2, s1 = acc[1] * P.scale_log2;
     float s2 = acc[2] * P.scale_log2, s3 = acc[3] * P.scale_log2;
     if (16 * u + 16 > ntok) {
@@ -199,50 +364,33 @@ __global__ __launch_bounds__(kThreads) void attn_partition_mfma(Params P) {
       const u32 mhi = (t0 + 2 < ntok ? 0x0000ffffu : 0u) | (t0 + 3 < ntok ? 0xffff0000u : 0u);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        vf[c][0] &= mlo;
-        vf[c][1] &= mhi;
+        f.v[c][0] &= mlo;
+        f.v[c][1] &= mhi;
       }
     }
     float mx = fmaxf(fmaxf(s0, s1), fmaxf(s2, s3));
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float mn = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - mn);
-    const u32 p01 = T::pack2(fast_exp2(s0 - mn), fast_exp2(s1 - mn));
-    const u32 p23 = T::pack2(fast_exp2(s2 - mn), fast_exp2(s3 - mn));
-    l_part = l_part * alpha + ((T::lo(p01) + T::hi(p01)) + (T::lo(p23) + T::hi(p23)));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
+    if (wave_any(mx > m_run + kRescaleLog2)) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - mn);
+      l_part *= alpha;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) o[c] *= alpha;
+      m_run = mn;
+    }
+    const u32 p01 = T::pack2(fast_exp2(s0 - m_run), fast_exp2(s1 - m_run));
+    const u32 p23 = T::pack2(fast_exp2(s2 - m_run), fast_exp2(s3 - m_run));
+    l_part += (T::lo(p01) + T::hi(p01)) + (T::lo(p23) + T::hi(p23));
     const u32x2 pb = {p01, p23};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      o[c] *= alpha;
-      o[c] = T::mfma_k16(vf[c], pb, o[c]);
-    }
-    m_run = mn;
+    for (int c = 0; c < NC; ++c) o[c] = T::mfma_k16(f.v[c], pb, o[c]);
   };
 
-  {
-    u32x4 ka[KI], kb[KI];
-    u32x2 va[NC], vb[NC];
-    int u = w;
-    if (u < nunits) {
-      load(u, ka, va);
-      while (true) {
-        const int u1 = u + kWaves;
-        if (u1 < nunits) load(u1, kb, vb);
-        compute(u, ka, va);
-        if (u1 >= nunits) break;
-        const int u2 = u1 + kWaves;
-        if (u2 < nunits) load(u2, ka, va);
-        compute(u1, kb, vb);
-        if (u2 >= nunits) break;
-        u = u2;
-      }
-    }
-  }
+  pipeline<kWaves, Buf>(w, nunits, load, compute);
 
-  float l = l_part;
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
+  float l = sum_xor16(l_part);
+  l = sum_xor32(l);
   if (hv) {
     if (r == 0) {
       s_m[w][m] = m_run;
@@ -273,17 +421,24 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   constexpr int BPP = kPT / B;
   constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
   typedef typename std::conditional<EB == 2, u32x2, u32x4>::type VVec;  // 4 tokens of one V row
+  struct Buf {
+    u32x4 k[KL];
+    VVec v[NV];
+  };
 
   __shared__ int s_tab[BPP];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ float s_o[kWaves][G][D + 4];
 
-  const int kvh = blockIdx.x;
-  const int p = blockIdx.y;
-  const int b = blockIdx.z;
+  const int t = blockIdx.x / P.Hkv;
+  const int kvh = blockIdx.x - t * P.Hkv;
+  if (t >= P.counters[0]) return;
+  const int item = P.tasks[t];
+  const int b = item / P.Pmax;
+  const int p = item - b * P.Pmax;
   const int hq0 = kvh * G;
-  const int L = P.ctx[b];
+  const int L = context_len(P, b);
   if (L <= 0) {
     if (p == 0) zero_rows<T, D>(P, b, hq0, G);
     return;
@@ -293,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;
   const int m = lane & 15;
   const int ntok = min(kPT, L - p * kPT);
@@ -325,16 +480,16 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   const int koff = (r * B + m) * 16;      // + i * 4 * B * 16 + sub * 256
   const int voff = (m * B + 4 * r) * EB;  // + c * 16 * B * EB + sub * 16 * EB
 
-  auto load = [&](int u, u32x4 (&kf)[KL], VVec (&vf)[NV]) {
+  auto load = [&](int u, Buf& f) {
     const int bi = u / SUB;
     const int sub = u - bi * SUB;
     const int blk = __builtin_amdgcn_readfirstlane(s_tab[bi]);
     const char* kt = kbase + blk * bstride + sub * 256;
     const char* vt = vbase + blk * bstride + sub * 16 * EB;
 #pragma unroll
-    for (int i = 0; i < KL; ++i) kf[i] = *reinterpret_cast<const u32x4*>(kt + koff + i * 4 * B * 16);
+    for (int i = 0; i < KL; ++i) f.k[i] = load_stream<u32x4>(kt + koff + i * 4 * B * 16);
 #pragma unroll
-    for (int c = 0; c < NV; ++c) vf[c] = *reinterpret_cast<const VVec*>(vt + voff + c * 16 * B * EB);
+    for (int c = 0; c < NV; ++c) f.v[c] = load_stream<VVec>(vt + voff + c * 16 * B * EB);
   };
 
   float m_run[G], l_part[G], o[G][NV];
@@ -347,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   }
   const int src_row = (lane & 48) | (4 * r);  // lane holding token 4r of this row
 
-  auto compute = [&](int u, const u32x4 (&kf)[KL], VVec (&vf)[NV]) {
+  auto compute = [&](int u, Buf& f) {
     float s[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -356,18 +511,17 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
       for (int i = 0; i < KL; ++i) {
         if constexpr (EB == 2) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) part = T::dot2(kf[i][e], qw[g][i][e], part);
+          for (int e = 0; e < 4; ++e) part = T::dot2(f.k[i][e], qw[g][i][e], part);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) part = fmaf(__uint_as_float(kf[i][e]), __uint_as_float(qw[g][i][e]), part);
+          for (int e = 0; e < 4; ++e) part = fmaf(__uint_as_float(f.k[i][e]), __uint_as_float(qw[g][i][e]), part);
         }
       }
-      part += shfl_xor(part, 16);
-      part += shfl_xor(part, 32);
+      part = sum_xor16(part);
+      part = sum_xor32(part);
       s[g] = (EB == 2) ? part * P.scale_log2 : part;
     }
-    const bool tail = 16 * u + 16 > ntok;
-    if (tail) {
+    if (16 * u + 16 > ntok) {
       const bool valid = 16 * u + m < ntok;
 #pragma unroll
       for (int g = 0; g < G; ++g) s[g] = valid ? s[g] : kNegInf;
@@ -377,37 +531,36 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
         if constexpr (EB == 2) {
           const u32 mlo = (t0 + 0 < ntok ? 0x0000ffffu : 0u) | (t0 + 1 < ntok ? 0xffff0000u : 0u);
           const u32 mhi = (t0 + 2 < ntok ? 0x0000ffffu : 0u) | (t0 + 3 < ntok ? 0xffff0000u : 0u);
-          vf[c][0] &= mlo;
-          vf[c][1] &= mhi;
+          f.v[c][0] &= mlo;
+          f.v[c][1] &= mhi;
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vf[c][e] = (t0 + e < ntok) ? vf[c][e] : 0u;
+          for (int e = 0; e < 4; ++e) f.v[c][e] = (t0 + e < ntok) ? f.v[c][e] : 0u;
         }
       }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float mx = s[g];
-      mx = fmaxf(mx, shfl_xor(mx, 1));
-      mx = fmaxf(mx, shfl_xor(mx, 2));
-      mx = fmaxf(mx, shfl_xor(mx, 4));
-      mx = fmaxf(mx, shfl_xor(mx, 8));
-      const float mn = fmaxf(m_run[g], mx);
-      const float alpha = fast_exp2(m_run[g] - mn);
-      float pr = fast_exp2(s[g] - mn);
-      m_run[g] = mn;
+      const float mx = row_max16(s[g]);
+      if (wave_any(mx > m_run[g] + kRescaleLog2)) {
+        const float mn = fmaxf(m_run[g], mx);
+        const float alpha = fast_exp2(m_run[g] - mn);
+        l_part[g] *= alpha;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) o[g][c] *= alpha;
+        m_run[g] = mn;
+      }
+      float pr = fast_exp2(s[g] - m_run[g]);
       if constexpr (EB == 2) {
         pr = T::lo(T::pack2(pr, 0.f));  // probabilities in the pool type, as the product uses them
-        const float other = shfl_xor(pr, 1);
+        const float other = dpp<0xB1>(pr);  // lane ^ 1
         const u32 pw = (m & 1) ? T::pack2(other, pr) : T::pack2(pr, other);  // (p[2k], p[2k+1])
         const u32 pp0 = shfl_idx_u(pw, src_row);
         const u32 pp1 = shfl_idx_u(pw, src_row + 2);
 #pragma unroll
         for (int c = 0; c < NV; ++c) {
-          float acc = o[g][c] * alpha;
-          acc = T::dot2(vf[c][0], pp0, acc);
-          acc = T::dot2(vf[c][1], pp1, acc);
-          o[g][c] = acc;
+          float acc = T::dot2(f.v[c][0], pp0, o[g][c]);
+          o[g][c] = T::dot2(f.v[c][1], pp1, acc);
         }
       } else {
         float pt[4];
@@ -415,50 +568,23 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
         for (int e = 0; e < 4; ++e) pt[e] = shfl_idx(pr, src_row + e);
 #pragma unroll
         for (int c = 0; c < NV; ++c) {
-          float acc = o[g][c] * alpha;
+          float acc = o[g][c];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = fmaf(pt[e], __uint_as_float(vf[c][e]), acc);
+          for (int e = 0; e < 4; ++e) acc = fmaf(pt[e], __uint_as_float(f.v[c][e]), acc);
           o[g][c] = acc;
         }
       }
-      l_part[g] = l_part[g] * alpha + pr;
+      l_part[g] += pr;
     }
   };
 
-  {
-    u32x4 ka[KL], kb[KL];
-    VVec va[NV], vb[NV];
-    int u = w;
-    if (u < nunits) {
-      load(u, ka, va);
-      while (true) {
-        const int u1 = u + kWaves;
-        if (u1 < nunits) load(u1, kb, vb);
-        compute(u, ka, va);
-        if (u1 >= nunits) break;
-        const int u2 = u1 + kWaves;
-        if (u2 < nunits) load(u2, ka, va);
-        compute(u1, kb, vb);
-        if (u2 >= nunits) break;
-        u = u2;
-      }
-    }
-  }
+  pipeline<kWaves, Buf>(w, nunits, load, compute);
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float l = l_part[g];
-    l += shfl_xor(l, 1);
-    l += shfl_xor(l, 2);
-    l += shfl_xor(l, 4);
-    l += shfl_xor(l, 8);
+    const float l = row_sum16(l_part[g]);
 #pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      float v = o[g][c];
-      v += shfl_xor(v, 16);
-      v += shfl_xor(v, 32);
-      o[g][c] = v;
-    }
+    for (int c = 0; c < NV; ++c) o[g][c] = sum_xor32(sum_xor16(o[g][c]));
     if (lane < 16) {
       if (m == 0) {
         s_m[w][g] = m_run[g];
@@ -485,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge(Params P) {
 
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int L = P.ctx[b];
+  const int L = context_len(P, b);
   const int np = (L + kPT - 1) / kPT;
   if (np <= 1) return;
   const int tid = threadIdx.x;
@@ -543,12 +669,15 @@ Params make_params(const AttnArgs& a) {
   P.ws_ml = a.ws_ml;
   P.tables = a.block_tables;
   P.ctx = a.context_lens;
+  P.tasks = a.tasks;
+  P.counters = a.counters;
   P.Hq = a.num_q_heads;
   P.Hkv = a.num_kv_heads;
   P.G = a.num_q_heads / a.num_kv_heads;
   P.NHG = (P.G + 15) / 16;
   P.W = a.max_blocks_per_seq;
   P.Pmax = a.max_parts;
+  P.Lmax = a.max_blocks_per_seq * a.block_size;
   P.scale_log2 = a.scale * kLog2e;
   return P;
 }
@@ -556,10 +685,12 @@ Params make_params(const AttnArgs& a) {
 template <class T, int D, int B>
 int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
   const Params P = make_params(a);
+  hipLaunchKernelGGL(attn_plan, dim3(1), dim3(1024), 0, s, P, a.num_seqs, a.tasks, a.counters);
   const dim3 block(kThreads);
+  const int64_t items = static_cast<int64_t>(a.num_seqs) * a.max_parts;
   const bool valu = (T::kBytes == 4) || P.G == 1;
   if (valu) {
-    const dim3 grid(a.num_kv_heads, a.max_parts, a.num_seqs);
+    const dim3 grid(static_cast<unsigned>(items * a.num_kv_heads));
     switch (P.G) {
       case 1: hipLaunchKernelGGL((attn_partition_valu<T, D, B, 1>), grid, block, 0, s, P); break;
       case 2:
@@ -571,7 +702,7 @@ int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
       default: return -1;
     }
   } else if constexpr (T::kBytes == 2) {
-    const dim3 grid(a.num_kv_heads * P.NHG, a.max_parts, a.num_seqs);
+    const dim3 grid(static_cast<unsigned>(items * a.num_kv_heads * P.NHG));
     if (P.G <= 4) {
       hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 4>), grid, block, 0, s, P);
     } else if (P.G <= 8) {
