@@ -2,8 +2,9 @@
 
 A step is one pass of the whole hot path over one batch: the copy-on-write block
 copies of the step (if any), the KV write of the step's new tokens (slots from
-the host block manager), the partition pass of paged attention and the
-log-sum-exp merge.  Inputs are seeded synthetic data already resident in HBM.
+the host block manager), and paged attention (plan pass, then the partition pass
+whose last finisher per row does the log-sum-exp merge).  Inputs are seeded
+synthetic data already resident in HBM.
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole step (attention's
 algorithmic K+V bytes / step time); ``roofline`` describes the dominant kernel
@@ -47,7 +48,7 @@ def algorithmic_bytes(w, lens):
     parts = -(-lens // PARTITION_TOKENS)
     single = parts <= 1
     out = int(single.sum() * Hq * D * e)
-    partials = int(parts[~single].sum() * Hq * (D + 2) * 4)
+    partials = int(2 * parts[~single].sum() * Hq * (D + 2) * 4)  # written, then read by the merge
     tables = int(groups * (-(-lens // B)).sum() * 4 + len(lens) * 4)
     return {"kv": kv, "q": q, "out": out, "partials": partials, "tables": tables,
             "total": kv + q + out + partials + tables}
@@ -181,23 +182,20 @@ def main():
     log(f"set-up done; step has {len(pairs)} copy pairs, {len(slots)} new tokens")
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
     def step(e=None):
-        if e is not None:
-            e[0].record(stream)
         if len(pairs):
             pkv.copy_blocks(kp, vp, pairs_d)
         pkv.paged_kv_write(kp, vp, k_new, v_new, slots_d)
+        pkv.paged_attention_plan(q, kp, vp, tables, lens, ws)
         if e is not None:
-            e[1].record(stream)
+            e[0].record(stream)
         pkv.paged_attention_partitions(q, kp, vp, tables, lens, w.scale, out, ws)
         if e is not None:
-            e[2].record(stream)
-        pkv.paged_attention_merge(q, kp, vp, tables, lens, out, ws)
-        if e is not None:
-            e[3].record(stream)
+            e[1].record(stream)
 
+    # timed region: exactly `steps` steps; events bracket the partition kernel in each
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -207,17 +205,31 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    write_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    part_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    merge_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    log(f"step {ms_step:.4f} ms (copy+write {write_ms:.4f}, partitions {part_ms:.4f}, merge {merge_ms:.4f})")
+    part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
 
-    # partition pass after flushing L2 / MALL with a 512 MiB write (outside the events)
+    # outside the timed region: the other passes on their own, then the partition
+    # pass after flushing L2 / MALL with a 512 MiB write
+    def timed(fn, reps=10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    copy_ms = timed(lambda: pkv.copy_blocks(kp, vp, pairs_d)) if len(pairs) else 0.0
+    write_ms = timed(lambda: pkv.paged_kv_write(kp, vp, k_new, v_new, slots_d))
+    plan_ms = timed(lambda: pkv.paged_attention_plan(q, kp, vp, tables, lens, ws))
+    log(f"step {ms_step:.4f} ms (partitions {part_ms:.4f}; alone: copy {copy_ms:.4f}, write {write_ms:.4f}, "
+        f"plan {plan_ms:.4f})")
     flushed = []
     if args.flush_reps > 0:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(args.flush_reps):
+            pkv.paged_attention_plan(q, kp, vp, tables, lens, ws)
             scratch.fill_(1)
             e0.record(stream)
             pkv.paged_attention_partitions(q, kp, vp, tables, lens, w.scale, out, ws)
@@ -225,8 +237,6 @@ def main():
             torch.cuda.synchronize()
             flushed.append(e0.elapsed_time(e1))
         del scratch
-        pkv.paged_attention_merge(q, kp, vp, tables, lens, out, ws)
-        torch.cuda.synchronize()
 
     ab = algorithmic_bytes(w, lens_np)
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
@@ -252,9 +262,9 @@ def main():
                    "kv_bytes": ab["kv"]},
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
-        "attention_kv_gbs": round(ab["kv"] / ((part_ms + merge_ms) * 1e-3) / 1e9, 2),
-        "kernel_ms": {"copy_and_write": round(write_ms, 5), "attn_partitions": round(part_ms, 5),
-                      "attn_merge": round(merge_ms, 5)},
+        "attention_kv_gbs": round(ab["kv"] / ((plan_ms + part_ms) * 1e-3) / 1e9, 2),
+        "kernel_ms": {"attn_partitions": round(part_ms, 5), "copy_blocks_alone": round(copy_ms, 5),
+                      "kv_write_alone": round(write_ms, 5), "attn_plan_alone": round(plan_ms, 5)},
         "attn_partitions_ms_after_cache_flush": round(float(np.median(flushed)), 5) if flushed else None,
         "host_block_manager_step_us": round(host_bm_us, 1),
         "roofline": {"kernel": "attn_partition", "bound": "hbm", "achieved": round(achieved, 2),

@@ -103,7 +103,8 @@ int32_t pkv_copy_blocks(const pkv_pool_desc* pool, void* k_pool, void* v_pool,
 #define PKV_PARTITION_TOKENS 512
 
 /* Workspace bytes pkv_paged_attention_decode needs for these sizes (0 on bad input):
- * fp32 partial results of every (sequence, query head, partition). */
+ * fp32 partial results of every (sequence, query head, partition), the task list and
+ * per-row counters. */
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                            int32_t max_blocks_per_seq, int32_t block_size);
 
@@ -118,7 +119,9 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  *     out[b][h] = sum_j softmax(s)_j * V[b, j, g]
  * where token j of sequence b sits in block block_tables[b][j / B] at offset j % B.
  * Long contexts are split into PKV_PARTITION_TOKENS-token partitions whose partial
- * results are merged with log-sum-exp weights (in `workspace`).
+ * results are merged with log-sum-exp weights (in `workspace`).  Context lengths above
+ * max_blocks_per_seq * B break the contract; they are clamped to it (no access goes
+ * past the table row).
  *   q, out        device [num_seqs][num_q_heads][D], pool dtype, contiguous, 16-byte aligned.
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries at index
  *                 >= ceil(context_lens[b] / B) are never read.
@@ -140,20 +143,25 @@ int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool
 
 /*
  * The two passes of pkv_paged_attention_decode, exposed separately (same arguments,
- * same results when called in this order on one stream) so that each pass can be
- * timed on its own.  The partition pass writes the final output for sequences of
- * at most one partition and partial results for the others; the merge pass combines
- * the partials of multi-partition sequences.
+ * same results when called in this order on one stream with the same workspace and
+ * context_lens) so that each pass can be timed on its own:
+ *  - plan: lists the (sequence, partition) items in the workspace, longest first, and
+ *    clears the per-row completion counters;
+ *  - partitions: one workgroup per item and kv-head group; writes the final output of
+ *    sequences that fit one partition and partial results of the others; the
+ *    workgroup that completes the last partition of a row merges that row's partials
+ *    with log-sum-exp weights.
+ * A partitions pass without a preceding plan pass on that workspace gives undefined
+ * output values (but stays within the buffers).  Errors as pkv_paged_attention_decode.
  */
+int32_t pkv_paged_attention_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 int32_t pkv_paged_attention_partitions(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
                                        void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* context_lens, float scale,
                                        void* workspace, size_t workspace_bytes, void* stream);
-int32_t pkv_paged_attention_merge(const pkv_pool_desc* pool, void* out, int32_t num_seqs,
-                                  int32_t num_q_heads, int32_t max_blocks_per_seq,
-                                  const int32_t* context_lens, const void* workspace,
-                                  size_t workspace_bytes, void* stream);
 
 /*
  * Host-side block manager: block tables, on-demand allocation, fork and

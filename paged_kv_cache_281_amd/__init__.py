@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "load", "library_path", "PoolDesc", "alloc_pools", "pool_desc", "paged_kv_write", "copy_blocks",
     "workspace_bytes", "alloc_workspace", "paged_attention_decode", "paged_attention_partitions",
-    "paged_attention_merge", "BlockManager", "PkvError", "PARTITION_TOKENS", "DTYPE_CODES",
+    "paged_attention_plan", "BlockManager", "PkvError", "PARTITION_TOKENS", "DTYPE_CODES",
 ]
 
 PARTITION_TOKENS = 512
@@ -70,8 +70,7 @@ def load():
                                         _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
         "pkv_paged_attention_partitions": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
                                             _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
-        "pkv_paged_attention_merge": ([P(PoolDesc), _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_sz, _c_vp],
-                                      _c_i32),
+        "pkv_paged_attention_plan": ([P(PoolDesc), _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_sz, _c_vp], _c_i32),
         "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
         "pkv_bm_destroy": ([_c_vp], None),
         "pkv_bm_add_seq": ([_c_vp, _c_i32, _c_i32], _c_i32),
@@ -204,19 +203,19 @@ def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
     return out
 
 
+def paged_attention_plan(q, k_pool, v_pool, block_tables, context_lens, workspace) -> None:
+    """First pass of ``paged_attention_decode``: the (sequence, partition) task list."""
+    d, N, Hq, W, _, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, q, workspace)
+    _check(load().pkv_paged_attention_plan(ctypes.byref(d), N, Hq, W, _ptr(context_lens), _ptr(ws), ws.numel(),
+                                           _stream(q.device)))
+
+
 def paged_attention_partitions(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace) -> None:
-    """First pass of ``paged_attention_decode`` (per-partition results)."""
+    """Second pass of ``paged_attention_decode`` (partitions, with the merge of split rows)."""
     d, N, Hq, W, out, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, out, workspace)
     _check(load().pkv_paged_attention_partitions(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N,
                                                  Hq, _ptr(block_tables), W, _ptr(context_lens), float(scale),
                                                  _ptr(ws), ws.numel(), _stream(q.device)))
-
-
-def paged_attention_merge(q, k_pool, v_pool, block_tables, context_lens, out, workspace) -> None:
-    """Second pass of ``paged_attention_decode`` (log-sum-exp merge of partitions)."""
-    d, N, Hq, W, out, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, out, workspace)
-    _check(load().pkv_paged_attention_merge(ctypes.byref(d), _ptr(out), N, Hq, W, _ptr(context_lens), _ptr(ws),
-                                            ws.numel(), _stream(q.device)))
 
 
 # ---- host block manager ----------------------------------------------------------------

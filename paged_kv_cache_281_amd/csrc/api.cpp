@@ -61,7 +61,8 @@ size_t workspace_bytes_for(int64_t n, int64_t hq, int64_t d, int64_t parts) {
 AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
                           void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                          float scale, const void* workspace, size_t workspace_bytes, bool need_pools) {
+                          float scale, const void* workspace, size_t workspace_bytes, bool need_pools,
+                          bool need_out = true) {
   AttnCheck c{PKV_OK, {}};
   char buf[256];
   if ((c.status = check_pool(pool, who)) != PKV_OK) return c;
@@ -91,12 +92,13 @@ AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void
     return c;
   }
   if (num_seqs > 0) {
-    if ((need_pools && (!k_pool || !v_pool || !q || !block_tables)) || !out || !context_lens) {
+    if ((need_pools && (!k_pool || !v_pool || !q || !block_tables)) || (need_out && !out) || !context_lens) {
       std::snprintf(buf, sizeof(buf), "%s: null pointer argument", who);
       c.status = set_error(PKV_ERR_INVALID_ARG, buf);
       return c;
     }
-    if (!aligned(out, 16) || (need_pools && (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(q, 16))) ||
+    if ((need_out && !aligned(out, 16)) ||
+        (need_pools && (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(q, 16))) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4)) {
       std::snprintf(buf, sizeof(buf), "%s: misaligned pointer (pools, q, out need 16 bytes)", who);
       c.status = set_error(PKV_ERR_INVALID_ARG, buf);
@@ -123,6 +125,7 @@ AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void
   a.ws_ml = reinterpret_cast<float*>(ws + L.ml);
   a.tasks = reinterpret_cast<int*>(ws + L.tasks);
   a.counters = reinterpret_cast<int*>(ws + L.counters);
+  a.done = reinterpret_cast<int*>(ws + L.done);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
@@ -218,27 +221,26 @@ int32_t pkv_paged_attention_partitions(const pkv_pool_desc* pool, const void* k_
   return pkv::launch_status(pkv::launch_attn_partitions(c.args, stream), "pkv_paged_attention_partitions");
 }
 
-int32_t pkv_paged_attention_merge(const pkv_pool_desc* pool, void* out, int32_t num_seqs, int32_t num_q_heads,
-                                  int32_t max_blocks_per_seq, const int32_t* context_lens, const void* workspace,
-                                  size_t workspace_bytes, void* stream) {
-  pkv::AttnCheck c = pkv::check_attention("pkv_paged_attention_merge", pool, nullptr, nullptr, out, nullptr, num_seqs,
-                                          num_q_heads, nullptr, max_blocks_per_seq, context_lens, 1.0f, workspace,
-                                          workspace_bytes, false);
+int32_t pkv_paged_attention_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  pkv::AttnCheck c = pkv::check_attention("pkv_paged_attention_plan", pool, nullptr, nullptr, nullptr, nullptr,
+                                          num_seqs, num_q_heads, nullptr, max_blocks_per_seq, context_lens, 1.0f,
+                                          workspace, workspace_bytes, false, false);
   if (c.status != PKV_OK) return c.status;
   if (num_seqs == 0) return PKV_OK;
-  return pkv::launch_status(pkv::launch_attn_merge(c.args, stream), "pkv_paged_attention_merge");
+  return pkv::launch_status(pkv::launch_attn_plan(c.args, stream), "pkv_paged_attention_plan");
 }
 
 int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
                                    const void* q, int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
                                    int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  int32_t st = pkv_paged_attention_partitions(pool, k_pool, v_pool, out, q, num_seqs, num_q_heads, block_tables,
-                                              max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes,
-                                              stream);
+  int32_t st = pkv_paged_attention_plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, context_lens, workspace,
+                                        workspace_bytes, stream);
   if (st != PKV_OK || num_seqs == 0) return st;
-  return pkv_paged_attention_merge(pool, out, num_seqs, num_q_heads, max_blocks_per_seq, context_lens, workspace,
-                                   workspace_bytes, stream);
+  return pkv_paged_attention_partitions(pool, k_pool, v_pool, out, q, num_seqs, num_q_heads, block_tables,
+                                        max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

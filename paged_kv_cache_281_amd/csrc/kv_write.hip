@@ -32,15 +32,16 @@ __global__ __launch_bounds__(256) void kv_write_kernel(char* __restrict__ k_pool
   const int64_t th = idx / nch;
   const int h = static_cast<int>(th % H);
   const int64_t t = th / H;
+  // the source vectors do not depend on the slot: issue all three loads together
+  const int64_t src = ((t * H + h) * D + static_cast<int64_t>(c) * X) * EB;
+  const u32x4 kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_new + src));
+  const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_new + src));
   const int64_t slot = slots[t];
   if (slot < 0) return;
   const int64_t blk = slot / B;
   const int off = static_cast<int>(slot % B);
-  const int64_t src = ((t * H + h) * D + static_cast<int64_t>(c) * X) * EB;
-  const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + src);
   const int64_t tile = (blk * H + h) * static_cast<int64_t>(D) * B;  // elements
   *reinterpret_cast<u32x4*>(k_pool + (tile + (static_cast<int64_t>(c) * B + off) * X) * EB) = kv;
-  const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + src);
   const int64_t vrow = tile + static_cast<int64_t>(c) * X * B + off;  // element (d = c*X, off)
   if constexpr (EB == 4) {
 #pragma unroll

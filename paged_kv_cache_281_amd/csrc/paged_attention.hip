@@ -17,8 +17,8 @@
 // taken from a device-built task list ordered longest first (plan kernel).  The four
 // waves' states are merged in LDS.  A sequence that fits in one partition gets its
 // final output here; longer ones leave (max, sum, normalised output) per partition
-// in the workspace for the merge kernel, which weights partition p by
-// exp2(m_p - M) * l_p.
+// in the workspace, and the workgroup that completes a row's last partition merges
+// them, weighting partition p by exp2(m_p - M) * l_p.
 //
 // Loads.  With the pool layout of pkv.h one (block, kv head) tile is contiguous:
 // K as [D/X][B][X] 16-byte chunks, V as [D][B].  Lane (r = lane/16, m = lane%16)
@@ -64,7 +64,8 @@ struct Params {
   const int* ctx;
   const int* tasks;     // (sequence * Pmax + partition) items, longest first
   const int* counters;  // counters[0] = number of items
-  int Hq, Hkv, G, NHG, W, Pmax, Lmax;
+  int* done;            // [N * Hq]: partitions finished per (sequence, first head of a group)
+  int N, Hq, Hkv, G, NHG, W, Pmax, Lmax;
   float scale_log2;
 };
 
@@ -79,12 +80,14 @@ __device__ __forceinline__ int context_len(const Params& P, int b) { return min(
 // one item, which writes its zero output.  Only the order within a bucket depends
 // on timing, and no result depends on the order.
 // ---------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void attn_plan(Params P, int N, int* __restrict__ tasks, int* __restrict__ counters) {
+__global__ __launch_bounds__(1024) void attn_plan(Params P, int* __restrict__ tasks, int* __restrict__ counters) {
+  const int N = P.N;
   constexpr int NB = kPT / 16;
   __shared__ int cnt[NB + 1];
   __shared__ int off[NB + 1];
   const int tid = threadIdx.x;
   if (tid <= NB) cnt[tid] = 0;
+  for (int i = tid; i < N * P.Hq; i += blockDim.x) P.done[i] = 0;
   __syncthreads();
   for (int b = tid; b < N; b += blockDim.x) {
     const int L = context_len(P, b);
@@ -113,6 +116,15 @@ __global__ __launch_bounds__(1024) void attn_plan(Params P, int N, int* __restri
     }
     if (rem || L == 0) tasks[atomicAdd(&off[rem ? (rem + 15) >> 4 : 1], 1)] = b * P.Pmax + full;
   }
+}
+
+// Device-scope (relaxed) stores and loads of the partition partials: coherent across
+// the XCDs' separate L2 caches without a cache write-back or invalidation.
+__device__ __forceinline__ void store_device(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_device(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class T, int D>
@@ -145,11 +157,13 @@ __device__ __forceinline__ void combine_and_store(const Params& P, const float (
     if (np == 1) {
       reinterpret_cast<Bits*>(P.out)[row * D + d] = T::from_float(num / den);
     } else {
+      // partials are read by whichever workgroup merges the row, possibly on another
+      // XCD: device-scope stores write through to the coherent level
       const int64_t pr = row * P.Pmax + p;
-      P.ws_o[pr * D + d] = num / den;
+      store_device(&P.ws_o[pr * D + d], num / den);
       if (d == 0) {
-        P.ws_ml[2 * pr] = M;
-        P.ws_ml[2 * pr + 1] = den;
+        store_device(&P.ws_ml[2 * pr], M);
+        store_device(&P.ws_ml[2 * pr + 1], den);
       }
     }
   }
@@ -252,10 +266,109 @@ __device__ __forceinline__ V load_stream(const char* p) {
 #endif
 }
 
+// Rows split into at most this many partitions are merged inside the partition
+// kernel by their last finisher; longer rows (long contexts) are merged by a separate
+// kernel that spreads each row over a whole workgroup.
+constexpr int kFuseMaxParts = 32;
+
+// The query fragments of the MFMA path are kept in LDS (re-read per unit), which
+// lowers register use enough for three waves per SIMD.
+#ifndef PKV_Q_IN_REGS
+#define PKV_Q_IN_LDS 1
+#endif
+
 // A running max is only raised (and the accumulators rescaled) when a new score
 // exceeds it by more than this many log2 units; until then probabilities are taken
 // against the stale max and stay below 2^kRescaleLog2 (no overflow in fp32/bf16/fp16).
 constexpr float kRescaleLog2 = 8.f;
+
+// ---------------------------------------------------------------------------------
+// Log-sum-exp merge of the partition partials of one (sequence, query head) row, by
+// the calling workgroup: M = max_p m_p, w_p = exp2(m_p - M) * l_p,
+// out = sum_p w_p * o_p / sum_p w_p.
+// ---------------------------------------------------------------------------------
+template <int D>
+struct MergeSmem {
+  static constexpr int NCOL = D / 4;
+  static constexpr int NG = kThreads / NCOL;
+  float red[kWaves];
+  f32x4 acc[NG][NCOL];
+};
+
+// kCoherent: the partials were stored by other workgroups of the running kernel, so
+// they are read with device-scope loads; after a kernel boundary plain loads suffice.
+template <class T, int D, bool kCoherent>
+__device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, MergeSmem<D>& sm) {
+  typedef typename T::Bits Bits;
+  constexpr int NCOL = MergeSmem<D>::NCOL;
+  constexpr int NG = MergeSmem<D>::NG;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const float* ml = P.ws_ml + row * P.Pmax * 2;
+  const float* po = P.ws_o + row * P.Pmax * D;
+
+  auto ld = [](const float* p) { return kCoherent ? load_device(p) : *p; };
+  float mx = kNegInf;
+  for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, ld(&ml[2 * i]));
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, shfl_xor(mx, k));
+  if (lane == 0) sm.red[w] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
+  __syncthreads();
+
+  float den = 0.f;
+  for (int i = tid; i < np; i += kThreads) den += fast_exp2(ld(&ml[2 * i]) - M) * ld(&ml[2 * i + 1]);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) den += shfl_xor(den, k);
+  if (lane == 0) sm.red[w] = den;
+  __syncthreads();
+  const float DEN = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+
+  const int col = tid % NCOL;
+  const int grp = tid / NCOL;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = grp; i < np; i += NG) {
+    const float wgt = fast_exp2(ld(&ml[2 * i]) - M) * ld(&ml[2 * i + 1]);
+    const float* src = po + static_cast<int64_t>(i) * D + col * 4;
+    f32x4 v;
+    if constexpr (kCoherent) {
+      v = f32x4{load_device(src), load_device(src + 1), load_device(src + 2), load_device(src + 3)};
+    } else {
+      v = *reinterpret_cast<const f32x4*>(src);
+    }
+    acc += wgt * v;
+  }
+  sm.acc[grp][col] = acc;
+  __syncthreads();
+  if (tid < NCOL) {
+    f32x4 sum = sm.acc[0][tid];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) sum += sm.acc[g][tid];
+    Bits* o = reinterpret_cast<Bits*>(P.out) + row * D + tid * 4;
+    const float inv = 1.f / DEN;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = T::from_float(sum[e] * inv);
+  }
+  __syncthreads();
+}
+
+// After a partition's partials are stored: the workgroup that finishes a row's last
+// partition (device-scope counter, zeroed by the plan pass) merges its query heads.
+// Every thread waits until its device-scope partial stores have completed before the
+// workgroup's count is added, so the merging workgroup, whose device-scope loads are
+// issued after it has read the final count, sees every partition's partials.
+template <class T, int D>
+__device__ __forceinline__ void finish_rows(const Params& P, int b, int hq0, int nrows, int np,
+                                           MergeSmem<D>& sm, int& s_last) {
+  __builtin_amdgcn_s_waitcnt(0);  // all of this thread's memory operations have completed
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&P.done[static_cast<int64_t>(b) * P.Hq + hq0], 1) == np - 1;
+  __syncthreads();
+  if (!s_last) return;
+  for (int g = 0; g < nrows; ++g) merge_row<T, D, true>(P, static_cast<int64_t>(b) * P.Hq + hq0 + g, np, sm);
+}
 
 // ---------------------------------------------------------------------------------
 // MFMA partition kernel: bf16/fp16 pools, 2..16 query heads per workgroup.
@@ -282,12 +395,15 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   __shared__ float s_m[kWaves][GMAX];
   __shared__ float s_l[kWaves][GMAX];
   __shared__ float s_o[kWaves][GMAX][D + 4];
+  __shared__ MergeSmem<D> s_merge;
+  __shared__ int s_last;
 
   const int HY = P.Hkv * P.NHG;
   const int t = blockIdx.x / HY;
   const int hy = blockIdx.x - t * HY;
   if (t >= P.counters[0]) return;
   const int item = P.tasks[t];
+  if (item < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
   const int b = item / P.Pmax;
   const int p = item - b * P.Pmax;
   const int kvh = hy / P.NHG;
@@ -314,6 +430,16 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   if (tid < nblk) s_tab[tid] = P.tables[static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP + tid];
 
   const bool hv = m < gcur;
+#ifdef PKV_Q_IN_LDS
+  // query fragments live in LDS (lane-major, conflict-free) and are re-read per unit
+  __shared__ u32x4 s_q[KI][64];
+  if (w == 0) {
+    const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + (hv ? m : 0)) * D * EB;
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki)
+      s_q[ki][lane] = hv ? *reinterpret_cast<const u32x4*>(qrow + (4 * ki + r) * 16) : u32x4{0u, 0u, 0u, 0u};
+  }
+#else
   u32x4 qf[KI];
   {
     const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + (hv ? m : 0)) * D * EB;
@@ -322,6 +448,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
       qf[ki] = hv ? *reinterpret_cast<const u32x4*>(qrow + (4 * ki + r) * 16) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+#endif
   __syncthreads();
 
   const char* kbase = P.kp + kvh * TILE;
@@ -351,7 +478,13 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   auto compute = [&](int u, Buf& f) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ki = 0; ki < KI; ++ki) acc = T::mfma_k32(f.k[ki], qf[ki], acc);
+    for (int ki = 0; ki < KI; ++ki) {
+#ifdef PKV_Q_IN_LDS
+      acc = T::mfma_k32(f.k[ki], s_q[ki][lane], acc);
+#else
+      acc = T::mfma_k32(f.k[ki], qf[ki], acc);
+#endif
+    }
     float s0 = acc[0] * P.scale_log2, s1 = acc[1] * P.scale_log2;
     float s2 = acc[2] * P.scale_log2, s3 = acc[3] * P.scale_log2;
     if (16 * u + 16 > ntok) {
@@ -404,6 +537,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   }
   __syncthreads();
   combine_and_store<T, D, GMAX>(P, s_m, s_l, s_o, b, hq0, gcur, p, np);
+  if (np > 1 && np <= kFuseMaxParts) finish_rows<T, D>(P, b, hq0, gcur, np, s_merge, s_last);
 }
 
 // ---------------------------------------------------------------------------------
@@ -430,11 +564,14 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ float s_o[kWaves][G][D + 4];
+  __shared__ MergeSmem<D> s_merge;
+  __shared__ int s_last;
 
   const int t = blockIdx.x / P.Hkv;
   const int kvh = blockIdx.x - t * P.Hkv;
   if (t >= P.counters[0]) return;
   const int item = P.tasks[t];
+  if (item < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
   const int b = item / P.Pmax;
   const int p = item - b * P.Pmax;
   const int hq0 = kvh * G;
@@ -596,67 +733,18 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   }
   __syncthreads();
   combine_and_store<T, D, G>(P, s_m, s_l, s_o, b, hq0, G, p, np);
+  if (np > 1 && np <= kFuseMaxParts) finish_rows<T, D>(P, b, hq0, G, np, s_merge, s_last);
 }
 
-// ---------------------------------------------------------------------------------
-// Merge kernel: log-sum-exp combination of partition partials.  grid = (Hq, N)
-// ---------------------------------------------------------------------------------
+// Merge kernel for rows of more than kFuseMaxParts partitions.  grid = (Hq, N)
 template <class T, int D>
-__global__ __launch_bounds__(kThreads) void attn_merge(Params P) {
-  typedef typename T::Bits Bits;
-  constexpr int NCOL = D / 4;
-  constexpr int NG = kThreads / NCOL;
-  __shared__ float s_red[kWaves];
-  __shared__ f32x4 s_acc[NG][NCOL];
-
+__global__ __launch_bounds__(kThreads) void attn_merge_long(Params P) {
+  __shared__ MergeSmem<D> s_merge;
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int L = context_len(P, b);
-  const int np = (L + kPT - 1) / kPT;
-  if (np <= 1) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int64_t row = static_cast<int64_t>(b) * P.Hq + hq;
-  const float* ml = P.ws_ml + row * P.Pmax * 2;
-  const float* po = P.ws_o + row * P.Pmax * D;
-
-  float mx = kNegInf;
-  for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, ml[2 * i]);
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, shfl_xor(mx, k));
-  if (lane == 0) s_red[w] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  __syncthreads();
-
-  float den = 0.f;
-  for (int i = tid; i < np; i += kThreads) den += fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) den += shfl_xor(den, k);
-  if (lane == 0) s_red[w] = den;
-  __syncthreads();
-  const float DEN = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-
-  const int col = tid % NCOL;
-  const int grp = tid / NCOL;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i = grp; i < np; i += NG) {
-    const float wgt = fast_exp2(ml[2 * i] - M) * ml[2 * i + 1];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(po + static_cast<int64_t>(i) * D + col * 4);
-    acc += wgt * v;
-  }
-  s_acc[grp][col] = acc;
-  __syncthreads();
-  if (tid < NCOL) {
-    f32x4 sum = s_acc[0][tid];
-#pragma unroll
-    for (int g = 1; g < NG; ++g) sum += s_acc[g][tid];
-    Bits* o = reinterpret_cast<Bits*>(P.out) + row * D + tid * 4;
-    const float inv = 1.f / DEN;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = T::from_float(sum[e] * inv);
-  }
+  const int np = (context_len(P, b) + kPT - 1) / kPT;
+  if (np <= kFuseMaxParts) return;
+  merge_row<T, D, false>(P, static_cast<int64_t>(b) * P.Hq + hq, np, s_merge);
 }
 
 Params make_params(const AttnArgs& a) {
@@ -671,6 +759,8 @@ Params make_params(const AttnArgs& a) {
   P.ctx = a.context_lens;
   P.tasks = a.tasks;
   P.counters = a.counters;
+  P.done = a.done;
+  P.N = a.num_seqs;
   P.Hq = a.num_q_heads;
   P.Hkv = a.num_kv_heads;
   P.G = a.num_q_heads / a.num_kv_heads;
@@ -685,7 +775,6 @@ Params make_params(const AttnArgs& a) {
 template <class T, int D, int B>
 int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
   const Params P = make_params(a);
-  hipLaunchKernelGGL(attn_plan, dim3(1), dim3(1024), 0, s, P, a.num_seqs, a.tasks, a.counters);
   const dim3 block(kThreads);
   const int64_t items = static_cast<int64_t>(a.num_seqs) * a.max_parts;
   const bool valu = (T::kBytes == 4) || P.G == 1;
@@ -711,13 +800,9 @@ int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 16>), grid, block, 0, s, P);
     }
   }
-  return static_cast<int>(hipGetLastError());
-}
-
-template <class T, int D>
-int launch_merge_t(const AttnArgs& a, hipStream_t s) {
-  const Params P = make_params(a);
-  hipLaunchKernelGGL((attn_merge<T, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kThreads), 0, s, P);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_parts <= kFuseMaxParts) return static_cast<int>(e);
+  hipLaunchKernelGGL((attn_merge_long<T, D>), dim3(a.num_q_heads, a.num_seqs), block, 0, s, P);
   return static_cast<int>(hipGetLastError());
 }
 
@@ -725,11 +810,6 @@ template <class T>
 int launch_partitions_d(const AttnArgs& a, hipStream_t s) {
   if (a.head_dim == 64) return a.block_size == 16 ? launch_partitions_t<T, 64, 16>(a, s) : launch_partitions_t<T, 64, 32>(a, s);
   return a.block_size == 16 ? launch_partitions_t<T, 128, 16>(a, s) : launch_partitions_t<T, 128, 32>(a, s);
-}
-
-template <class T>
-int launch_merge_d(const AttnArgs& a, hipStream_t s) {
-  return a.head_dim == 64 ? launch_merge_t<T, 64>(a, s) : launch_merge_t<T, 128>(a, s);
 }
 
 }  // namespace
@@ -742,22 +822,18 @@ bool attn_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t
   return dtype == PKV_F16 || dtype == PKV_BF16;
 }
 
+int launch_attn_plan(const AttnArgs& a, void* stream) {
+  const Params P = make_params(a);
+  hipLaunchKernelGGL(attn_plan, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), P, a.tasks, a.counters);
+  return static_cast<int>(hipGetLastError());
+}
+
 int launch_attn_partitions(const AttnArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (a.dtype) {
     case PKV_F32: return launch_partitions_d<F32>(a, s);
     case PKV_F16: return launch_partitions_d<F16>(a, s);
     case PKV_BF16: return launch_partitions_d<BF16>(a, s);
-    default: return -1;
-  }
-}
-
-int launch_attn_merge(const AttnArgs& a, void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (a.dtype) {
-    case PKV_F32: return launch_merge_d<F32>(a, s);
-    case PKV_F16: return launch_merge_d<F16>(a, s);
-    case PKV_BF16: return launch_merge_d<BF16>(a, s);
     default: return -1;
   }
 }

@@ -44,6 +44,7 @@ struct AttnArgs {
   float* ws_ml;  // [num_seqs][num_q_heads][max_partitions][2]: running max (log2 units), sum
   int* tasks;    // [num_seqs * max_partitions]: (sequence, partition) items, longest first
   int* counters; // [64]: counters[0] = number of items
+  int* done;     // [num_seqs * num_q_heads]: finished partitions per (sequence, head group)
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
   int32_t max_blocks_per_seq, max_parts;
   float scale;
@@ -51,7 +52,7 @@ struct AttnArgs {
 
 // Byte offsets of the workspace regions (each 256-byte aligned) and the total size.
 struct WorkspaceLayout {
-  size_t o, ml, tasks, counters, total;
+  size_t o, ml, tasks, done, counters, total;
 };
 inline WorkspaceLayout workspace_layout(int64_t n, int64_t hq, int64_t d, int64_t parts) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -59,14 +60,15 @@ inline WorkspaceLayout workspace_layout(int64_t n, int64_t hq, int64_t d, int64_
   w.o = 0;
   w.ml = al(static_cast<size_t>(n * hq * parts * d) * sizeof(float));
   w.tasks = w.ml + al(static_cast<size_t>(n * hq * parts * 2) * sizeof(float));
-  w.counters = w.tasks + al(static_cast<size_t>(n * parts) * sizeof(int32_t));
+  w.done = w.tasks + al(static_cast<size_t>(n * parts) * sizeof(int32_t));
+  w.counters = w.done + al(static_cast<size_t>(n * hq) * sizeof(int32_t));
   w.total = w.counters + 256;
   return w;
 }
 
 // Returns -1 when no kernel exists for the shape/dtype/group size, else a hipError_t.
+int launch_attn_plan(const AttnArgs& a, void* stream);
 int launch_attn_partitions(const AttnArgs& a, void* stream);
-int launch_attn_merge(const AttnArgs& a, void* stream);
 // Whether a partition kernel exists for this configuration.
 bool attn_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
 

@@ -140,8 +140,8 @@ def test_two_runs_are_bitwise_identical_and_passes_compose():
     b = pkv.paged_attention_decode(q, st.k_pool, st.v_pool, st.tables, st.context_lens, w.scale)
     out = torch.empty_like(q)
     ws = pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_blocks_per_seq, w.block_size)
+    pkv.paged_attention_plan(q, st.k_pool, st.v_pool, st.tables, st.context_lens, ws)
     pkv.paged_attention_partitions(q, st.k_pool, st.v_pool, st.tables, st.context_lens, w.scale, out, ws)
-    pkv.paged_attention_merge(q, st.k_pool, st.v_pool, st.tables, st.context_lens, out, ws)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a.view(torch.int16), out.view(torch.int16))
