@@ -1,9 +1,10 @@
 """Benchmark of one paged decode step on one MI355X.
 
 A step is one pass of the whole hot path over one batch: the copy-on-write block
-copies of the step (if any), the KV write of the step's new tokens (slots from
-the host block manager), and paged attention (plan pass, then the partition pass
-whose last finisher per row does the log-sum-exp merge).  Inputs are seeded
+copies of the step (if any), then one launch that writes the step's new tokens
+into their slots (from the host block manager) and plans the attention, then the
+attention partition pass, whose last finisher per row does the log-sum-exp merge
+(a separate merge kernel for rows of more than 32 partitions).  Inputs are seeded
 synthetic data already resident in HBM.
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole step (attention's
@@ -186,8 +187,7 @@ def main():
     def step(e=None):
         if len(pairs):
             pkv.copy_blocks(kp, vp, pairs_d)
-        pkv.paged_kv_write(kp, vp, k_new, v_new, slots_d)
-        pkv.paged_attention_plan(q, kp, vp, tables, lens, ws)
+        pkv.decode_prepare(kp, vp, k_new, v_new, slots_d, q, tables, lens, ws)
         if e is not None:
             e[0].record(stream)
         pkv.paged_attention_partitions(q, kp, vp, tables, lens, w.scale, out, ws)
@@ -220,10 +220,11 @@ def main():
         return e0.elapsed_time(e1) / reps
 
     copy_ms = timed(lambda: pkv.copy_blocks(kp, vp, pairs_d)) if len(pairs) else 0.0
+    prep_ms = timed(lambda: pkv.decode_prepare(kp, vp, k_new, v_new, slots_d, q, tables, lens, ws))
     write_ms = timed(lambda: pkv.paged_kv_write(kp, vp, k_new, v_new, slots_d))
     plan_ms = timed(lambda: pkv.paged_attention_plan(q, kp, vp, tables, lens, ws))
-    log(f"step {ms_step:.4f} ms (partitions {part_ms:.4f}; alone: copy {copy_ms:.4f}, write {write_ms:.4f}, "
-        f"plan {plan_ms:.4f})")
+    log(f"step {ms_step:.4f} ms (partitions {part_ms:.4f}; alone: copy {copy_ms:.4f}, write+plan {prep_ms:.4f}, "
+        f"write {write_ms:.4f}, plan {plan_ms:.4f})")
     flushed = []
     if args.flush_reps > 0:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -264,7 +265,8 @@ def main():
         "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "attention_kv_gbs": round(ab["kv"] / ((plan_ms + part_ms) * 1e-3) / 1e9, 2),
         "kernel_ms": {"attn_partitions": round(part_ms, 5), "copy_blocks_alone": round(copy_ms, 5),
-                      "kv_write_alone": round(write_ms, 5), "attn_plan_alone": round(plan_ms, 5)},
+                      "write_and_plan_alone": round(prep_ms, 5), "kv_write_alone": round(write_ms, 5),
+                      "attn_plan_alone": round(plan_ms, 5)},
         "attn_partitions_ms_after_cache_flush": round(float(np.median(flushed)), 5) if flushed else None,
         "host_block_manager_step_us": round(host_bm_us, 1),
         "roofline": {"kernel": "attn_partition", "bound": "hbm", "achieved": round(achieved, 2),

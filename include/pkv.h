@@ -164,6 +164,21 @@ int32_t pkv_paged_attention_partitions(const pkv_pool_desc* pool, const void* k_
                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode-step preparation: the KV write of the step's new tokens (as pkv_paged_kv_write)
+ * and the plan pass of the step's attention (as pkv_paged_attention_plan) in a single
+ * launch.  A decode step is then [pkv_copy_blocks if the step has copy pairs],
+ * pkv_decode_prepare, pkv_paged_attention_partitions, with the same results as
+ * pkv_copy_blocks + pkv_paged_kv_write + pkv_paged_attention_decode.
+ * Arguments and errors are those of the two calls it replaces; num_tokens == 0 only
+ * plans, num_seqs == 0 only writes.
+ */
+int32_t pkv_decode_prepare(const pkv_pool_desc* pool, void* k_pool, void* v_pool,
+                           const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                           int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Host-side block manager: block tables, on-demand allocation, fork and
  * copy-on-write decisions.  Pages: agentalpha.top Q32 answer parts 2-3;
  * data.6616ai.com "PagedAttention：把虚拟内存搬进 KV Cache"; ohmygp.com "破局思路".

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "load", "library_path", "PoolDesc", "alloc_pools", "pool_desc", "paged_kv_write", "copy_blocks",
     "workspace_bytes", "alloc_workspace", "paged_attention_decode", "paged_attention_partitions",
-    "paged_attention_plan", "BlockManager", "PkvError", "PARTITION_TOKENS", "DTYPE_CODES",
+    "paged_attention_plan", "decode_prepare", "BlockManager", "PkvError", "PARTITION_TOKENS", "DTYPE_CODES",
 ]
 
 PARTITION_TOKENS = 512
@@ -71,6 +71,8 @@ def load():
         "pkv_paged_attention_partitions": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
                                             _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
         "pkv_paged_attention_plan": ([P(PoolDesc), _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_decode_prepare": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp,
+                                _c_vp, _c_sz, _c_vp], _c_i32),
         "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
         "pkv_bm_destroy": ([_c_vp], None),
         "pkv_bm_add_seq": ([_c_vp, _c_i32, _c_i32], _c_i32),
@@ -208,6 +210,22 @@ def paged_attention_plan(q, k_pool, v_pool, block_tables, context_lens, workspac
     d, N, Hq, W, _, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, q, workspace)
     _check(load().pkv_paged_attention_plan(ctypes.byref(d), N, Hq, W, _ptr(context_lens), _ptr(ws), ws.numel(),
                                            _stream(q.device)))
+
+
+def decode_prepare(k_pool, v_pool, k_new, v_new, slot_mapping, q, block_tables, context_lens, workspace) -> None:
+    """The step's KV write and the attention plan pass in one launch (see ``paged_kv_write``
+    and ``paged_attention_plan``); follow with ``paged_attention_partitions``."""
+    d = pool_desc(k_pool, v_pool)
+    T = k_new.shape[0]
+    for t in (k_new, v_new):
+        _require(tuple(t.shape) == (T, d.num_kv_heads, d.head_dim), "k_new/v_new must be [T, Hkv, D]")
+        _require(t.dtype == k_pool.dtype and t.is_contiguous() and t.device == k_pool.device, "k_new/v_new dtype/layout/device")
+    _require(slot_mapping.dtype == torch.int64 and tuple(slot_mapping.shape) == (T,) and slot_mapping.is_contiguous()
+             and slot_mapping.device == k_pool.device, "slot_mapping must be a contiguous int64 [T] device tensor")
+    _, N, Hq, W, _, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, q, workspace)
+    _check(load().pkv_decode_prepare(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                                     _ptr(slot_mapping), T, N, Hq, W, _ptr(context_lens), _ptr(ws), ws.numel(),
+                                     _stream(q.device)))
 
 
 def paged_attention_partitions(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace) -> None:

@@ -174,19 +174,52 @@ size_t pkv_pool_bytes(const pkv_pool_desc* pool) {
   return static_cast<size_t>(pool->num_blocks) * pool->num_kv_heads * pool->block_size * pool->head_dim * eb;
 }
 
+namespace {
+int32_t check_write(const char* who, const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                    const void* k_new, const void* v_new, const int64_t* slot_mapping, int32_t num_tokens) {
+  char buf[256];
+  int32_t st = pkv::check_pool(pool, who);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) {
+    std::snprintf(buf, sizeof(buf), "%s: negative num_tokens", who);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) {
+    std::snprintf(buf, sizeof(buf), "%s: null pointer argument", who);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (!pkv::aligned(k_pool, 16) || !pkv::aligned(v_pool, 16) || !pkv::aligned(k_new, 16) ||
+      !pkv::aligned(v_new, 16) || !pkv::aligned(slot_mapping, 8)) {
+    std::snprintf(buf, sizeof(buf), "%s: misaligned pointer", who);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  return PKV_OK;
+}
+}  // namespace
+
 int32_t pkv_paged_kv_write(const pkv_pool_desc* pool, void* k_pool, void* v_pool, const void* k_new,
                            const void* v_new, const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
-  int32_t st = pkv::check_pool(pool, "pkv_paged_kv_write");
-  if (st != PKV_OK) return st;
-  if (num_tokens < 0) return set_error(PKV_ERR_INVALID_ARG, "pkv_paged_kv_write: negative num_tokens");
-  if (num_tokens == 0) return PKV_OK;
-  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
-    return set_error(PKV_ERR_INVALID_ARG, "pkv_paged_kv_write: null pointer argument");
-  if (!pkv::aligned(k_pool, 16) || !pkv::aligned(v_pool, 16) || !pkv::aligned(k_new, 16) ||
-      !pkv::aligned(v_new, 16) || !pkv::aligned(slot_mapping, 8))
-    return set_error(PKV_ERR_INVALID_ARG, "pkv_paged_kv_write: misaligned pointer");
+  int32_t st = check_write("pkv_paged_kv_write", pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens);
+  if (st != PKV_OK || num_tokens == 0) return st;
   return pkv::launch_status(pkv::launch_kv_write(*pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream),
                             "pkv_paged_kv_write");
+}
+
+int32_t pkv_decode_prepare(const pkv_pool_desc* pool, void* k_pool, void* v_pool, const void* k_new,
+                           const void* v_new, const int64_t* slot_mapping, int32_t num_tokens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_write("pkv_decode_prepare", pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens);
+  if (st != PKV_OK) return st;
+  pkv::AttnCheck c = pkv::check_attention("pkv_decode_prepare", pool, nullptr, nullptr, nullptr, nullptr,
+                                          num_seqs, num_q_heads, nullptr, max_blocks_per_seq, context_lens, 1.0f,
+                                          workspace, workspace_bytes, false, false);
+  if (c.status != PKV_OK) return c.status;
+  if (num_seqs == 0) return pkv_paged_kv_write(pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream);
+  return pkv::launch_status(pkv::launch_decode_prepare(c.args, *pool, k_pool, v_pool, k_new, v_new, slot_mapping,
+                                                       num_tokens, stream),
+                            "pkv_decode_prepare");
 }
 
 int32_t pkv_copy_blocks(const pkv_pool_desc* pool, void* k_pool, void* v_pool, const int64_t* src_dst_pairs,

@@ -44,6 +44,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "kv_write_body.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -80,13 +81,21 @@ __device__ __forceinline__ int context_len(const Params& P, int b) { return min(
 // one item, which writes its zero output.  Only the order within a bucket depends
 // on timing, and no result depends on the order.
 // ---------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void attn_plan(Params P, int* __restrict__ tasks, int* __restrict__ counters) {
+// Sequences with more full partitions than this have their task entries written by
+// the whole workgroup instead of one thread.
+constexpr int kPlanSerialMax = 32;
+constexpr int kPlanCoopMax = 256;
+
+__device__ __forceinline__ void plan_body(const Params& P, int* __restrict__ tasks, int* __restrict__ counters) {
   const int N = P.N;
   constexpr int NB = kPT / 16;
   __shared__ int cnt[NB + 1];
   __shared__ int off[NB + 1];
+  __shared__ int n_coop;
+  __shared__ int coop_b[kPlanCoopMax], coop_s[kPlanCoopMax], coop_n[kPlanCoopMax];
   const int tid = threadIdx.x;
   if (tid <= NB) cnt[tid] = 0;
+  if (tid == 0) n_coop = 0;
   for (int i = tid; i < N * P.Hq; i += blockDim.x) P.done[i] = 0;
   __syncthreads();
   for (int b = tid; b < N; b += blockDim.x) {
@@ -112,10 +121,39 @@ __global__ __launch_bounds__(1024) void attn_plan(Params P, int* __restrict__ ta
     const int rem = L - full * kPT;
     if (full) {
       const int s = atomicAdd(&off[NB], full);
-      for (int q = 0; q < full; ++q) tasks[s + q] = b * P.Pmax + q;
+      const int k = full > kPlanSerialMax ? atomicAdd(&n_coop, 1) : kPlanCoopMax;
+      if (k < kPlanCoopMax) {
+        coop_b[k] = b;
+        coop_s[k] = s;
+        coop_n[k] = full;
+      } else {
+        for (int q = 0; q < full; ++q) tasks[s + q] = b * P.Pmax + q;
+      }
     }
     if (rem || L == 0) tasks[atomicAdd(&off[rem ? (rem + 15) >> 4 : 1], 1)] = b * P.Pmax + full;
   }
+  __syncthreads();
+  const int nc = min(n_coop, kPlanCoopMax);
+  for (int k = 0; k < nc; ++k) {
+    for (int q = tid; q < coop_n[k]; q += blockDim.x) tasks[coop_s[k] + q] = coop_b[k] * P.Pmax + q;
+  }
+}
+
+__global__ __launch_bounds__(1024) void attn_plan(Params P, int* __restrict__ tasks, int* __restrict__ counters) {
+  plan_body(P, tasks, counters);
+}
+
+// The step's KV write and the attention plan in one launch: workgroup 0 plans, the
+// others write (the two touch disjoint memory; the partition pass that follows in
+// stream order sees both).
+template <int EB>
+__global__ __launch_bounds__(256) void decode_prepare_kernel(Params P, WriteArgs wa, int* __restrict__ tasks,
+                                                             int* __restrict__ counters) {
+  if (blockIdx.x == 0) {
+    plan_body(P, tasks, counters);
+    return;
+  }
+  kv_write_one<EB>(wa, static_cast<int64_t>(blockIdx.x - 1) * blockDim.x + threadIdx.x);
 }
 
 // Device-scope (relaxed) stores and loads of the partition partials: coherent across
@@ -820,6 +858,36 @@ bool attn_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t
   if (group < 1) return false;
   if (dtype == PKV_F32) return group == 1 || group == 2 || group == 4;
   return dtype == PKV_F16 || dtype == PKV_BF16;
+}
+
+int launch_decode_prepare(const AttnArgs& a, const pkv_pool_desc& pool, void* k_pool, void* v_pool,
+                          const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
+                          void* stream) {
+  const int eb = elem_bytes(pool.dtype);
+  const int64_t total = static_cast<int64_t>(num_tokens) * pool.num_kv_heads * (pool.head_dim / (16 / eb));
+  if (total > kMaxWriteItems) {  // very large writes: two launches
+    const int rc = launch_attn_plan(a, stream);
+    return rc ? rc : launch_kv_write(pool, k_pool, v_pool, k_new, v_new, slots, num_tokens, stream);
+  }
+  const Params P = make_params(a);
+  WriteArgs wa;
+  wa.k_pool = static_cast<char*>(k_pool);
+  wa.v_pool = static_cast<char*>(v_pool);
+  wa.k_new = static_cast<const char*>(k_new);
+  wa.v_new = static_cast<const char*>(v_new);
+  wa.slots = slots;
+  wa.total = total;
+  wa.H = pool.num_kv_heads;
+  wa.D = pool.head_dim;
+  wa.B = pool.block_size;
+  const unsigned grid = 1 + static_cast<unsigned>((total + 255) / 256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (eb == 4) {
+    hipLaunchKernelGGL(decode_prepare_kernel<4>, dim3(grid), dim3(256), 0, s, P, wa, a.tasks, a.counters);
+  } else {
+    hipLaunchKernelGGL(decode_prepare_kernel<2>, dim3(grid), dim3(256), 0, s, P, wa, a.tasks, a.counters);
+  }
+  return static_cast<int>(hipGetLastError());
 }
 
 int launch_attn_plan(const AttnArgs& a, void* stream) {

@@ -68,6 +68,10 @@ inline WorkspaceLayout workspace_layout(int64_t n, int64_t hq, int64_t d, int64_
 
 // Returns -1 when no kernel exists for the shape/dtype/group size, else a hipError_t.
 int launch_attn_plan(const AttnArgs& a, void* stream);
+// The KV write of num_tokens tokens and the plan pass in one launch.
+int launch_decode_prepare(const AttnArgs& a, const pkv_pool_desc& pool, void* k_pool, void* v_pool,
+                          const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
+                          void* stream);
 int launch_attn_partitions(const AttnArgs& a, void* stream);
 // Whether a partition kernel exists for this configuration.
 bool attn_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);

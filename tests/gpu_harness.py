@@ -45,10 +45,14 @@ class GpuState:
     last_slots: np.ndarray
     last_pairs: np.ndarray
     copies: int
+    out: torch.Tensor = None  # attention output when the last step ran fused
 
 
-def replay_gpu(w, context, device="cuda", pad: int = 0, fill_bits=None) -> GpuState:
-    """Prefill, forks and decode steps through the library on ``device``."""
+def replay_gpu(w, context, device="cuda", pad: int = 0, fill_bits=None, fused_q=None) -> GpuState:
+    """Prefill, forks and decode steps through the library on ``device``.
+
+    With ``fused_q`` (query bits), the last step runs as the benchmark runs it: copy
+    pairs, then ``decode_prepare`` (KV write + plan) and ``paged_attention_partitions``."""
     fill_bits = synth.NAN_BITS[w.dtype] if fill_bits is None else fill_bits
     bm = pkv.BlockManager(w.num_blocks, w.block_size, w.free_order)
     kp, vp = pkv.alloc_pools(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, TORCH_DTYPE[w.dtype], device)
@@ -67,18 +71,30 @@ def replay_gpu(w, context, device="cuda", pad: int = 0, fill_bits=None) -> GpuSt
     slots = np.zeros(0, np.int64)
     pairs = np.zeros((0, 2), np.int64)
     copies = 0
+    out = None
     for i, seqs in enumerate(w.steps):
         slots, pairs = bm.step(seqs)
         copies += len(pairs)
         if len(pairs):
             pkv.copy_blocks(kp, vp, torch.from_numpy(pairs).to(device))
         k, v = w.step_kv(i)
-        pkv.paged_kv_write(kp, vp, to_device(k, w.dtype, device), to_device(v, w.dtype, device),
-                           torch.from_numpy(slots).to(device))
+        k, v = to_device(k, w.dtype, device), to_device(v, w.dtype, device)
+        slots_d = torch.from_numpy(slots).to(device)
+        if fused_q is not None and i == len(w.steps) - 1:
+            tables = torch.from_numpy(bm.block_tables(w.batch, w.max_blocks_per_seq, pad)).to(device)
+            lens = torch.from_numpy(np.asarray([bm.seq_len(int(s)) for s in w.batch], dtype=np.int32)).to(device)
+            q = to_device(fused_q, w.dtype, device)
+            out = torch.empty_like(q)
+            ws = pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_blocks_per_seq, w.block_size,
+                                     device)
+            pkv.decode_prepare(kp, vp, k, v, slots_d, q, tables, lens, ws)
+            pkv.paged_attention_partitions(q, kp, vp, tables, lens, w.scale, out, ws)
+        else:
+            pkv.paged_kv_write(kp, vp, k, v, slots_d)
     tables = torch.from_numpy(bm.block_tables(w.batch, w.max_blocks_per_seq, pad)).to(device)
     lens = torch.from_numpy(np.asarray([bm.seq_len(int(s)) for s in w.batch], dtype=np.int32)).to(device)
     torch.cuda.synchronize()
-    return GpuState(bm, kp, vp, tables, lens, slots, pairs, copies)
+    return GpuState(bm, kp, vp, tables, lens, slots, pairs, copies, out)
 
 
 def nan_block(w, bm) -> int:

@@ -24,11 +24,23 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run_case(w, rows=None, check_pools=True, q_scale=1.0):
+def _scaled_queries(w, q_scale):
+    q = w.queries()
+    if q_scale != 1.0:
+        qf = torch.from_numpy(q.view(np.int16 if w.dtype != "f32" else np.int32)).view(TORCH_DTYPE[w.dtype])
+        q = (qf.float() * q_scale).to(TORCH_DTYPE[w.dtype]).view(torch.int16 if w.dtype != "f32" else torch.int32)
+        q = q.numpy().view(np.uint16 if w.dtype != "f32" else np.uint32)
+    return q
+
+
+def _run_case(w, rows=None, check_pools=True, q_scale=1.0, fused=False):
+    """Replay on both sides and compare.  fused=True runs the last step as the
+    benchmark does (decode_prepare + partitions, padding entries zero)."""
     log(f"case {w.name}: N={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
-        f"B={w.block_size} dtype={w.dtype} NB={w.num_blocks} sum_len={int(w.context_lens.sum())}")
+        f"B={w.block_size} dtype={w.dtype} NB={w.num_blocks} sum_len={int(w.context_lens.sum())} fused={fused}")
     ctx = w.all_context_kv()
-    st = replay_gpu(w, ctx, DEV)
+    q = _scaled_queries(w, q_scale)
+    st = replay_gpu(w, ctx, DEV, fused_q=q if fused else None)
     pad = nan_block(w, st.bm)
     ora = oracle_replay(w, synth.NAN_BITS[w.dtype], pad=pad, context=ctx)
     # integer work: tables, lengths, slots, copy pairs are bit-exact
@@ -41,14 +53,12 @@ def _run_case(w, rows=None, check_pools=True, q_scale=1.0):
     if check_pools:
         assert (to_bits(st.k_pool, w.dtype) == ora.pool.k).all(), "K pool differs"
         assert (to_bits(st.v_pool, w.dtype) == ora.pool.v).all(), "V pool differs"
-    # padding entries point at a never-written (NaN) block
-    st.tables = torch.from_numpy(tables).to(DEV)
-    q = w.queries()
-    if q_scale != 1.0:
-        qf = torch.from_numpy(q.view(np.int16 if w.dtype != "f32" else np.int32)).view(TORCH_DTYPE[w.dtype])
-        q = (qf.float() * q_scale).to(TORCH_DTYPE[w.dtype]).view(torch.int16 if w.dtype != "f32" else torch.int32)
-        q = q.numpy().view(np.uint16 if w.dtype != "f32" else np.uint32)
-    out = run_attention(w, st, q, DEV)
+    if fused:
+        out = st.out
+    else:
+        # padding entries point at a never-written (NaN) block
+        st.tables = torch.from_numpy(tables).to(DEV)
+        out = run_attention(w, st, q, DEV)
     ref = oracle_attention(q, w.dtype, ora.pool, tables, ora.context_lens, w.scale, seqs=rows)
     err, rel = compare(w, out, ref, rows)
     log(f"case {w.name}: max abs err {err:.3e}, max rel L2 {rel:.3e}")
@@ -199,5 +209,21 @@ FULL = [
 
 @pytest.mark.parametrize("name,rows", FULL, ids=[f[0] for f in FULL])
 def test_full_size_workloads(name, rows):
+    """Full sizes, last step run as the benchmark runs it (decode_prepare + partitions)."""
     w = synth.by_name(name)
-    _run_case(w, rows=rows)
+    _run_case(w, rows=rows, fused=True)
+
+
+@pytest.mark.parametrize("name,make", SMALL[:6], ids=[s[0] for s in SMALL[:6]])
+def test_fused_prepare_matches_separate_calls(name, make):
+    """decode_prepare + partitions gives the same pool bytes and output bits as
+    paged_kv_write + paged_attention_decode."""
+    w = make()
+    ctx = w.all_context_kv()
+    q = w.queries()
+    a = replay_gpu(w, ctx, DEV, fused_q=q)
+    b = replay_gpu(w, ctx, DEV)
+    ob = run_attention(w, b, q, DEV)
+    assert torch.equal(a.k_pool.view(torch.uint8), b.k_pool.view(torch.uint8))
+    assert torch.equal(a.v_pool.view(torch.uint8), b.v_pool.view(torch.uint8))
+    assert torch.equal(a.out.view(torch.uint8), ob.view(torch.uint8))
