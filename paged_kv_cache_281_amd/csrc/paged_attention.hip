@@ -63,7 +63,7 @@ struct Params {
   float* ws_ml;
   const int* tables;
   const int* ctx;
-  const int* tasks;     // (sequence * Pmax + partition) items, longest first
+  const int2* tasks;    // {sequence * Pmax + partition, context length} items, longest first
   const int* counters;  // counters[0] = number of items
   int* done;            // [N * Hq]: partitions finished per (sequence, first head of a group)
   int N, Hq, Hkv, G, NHG, W, Pmax, Lmax;
@@ -86,13 +86,13 @@ __device__ __forceinline__ int context_len(const Params& P, int b) { return min(
 constexpr int kPlanSerialMax = 32;
 constexpr int kPlanCoopMax = 256;
 
-__device__ __forceinline__ void plan_body(const Params& P, int* __restrict__ tasks, int* __restrict__ counters) {
+__device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ tasks, int* __restrict__ counters) {
   const int N = P.N;
   constexpr int NB = kPT / 16;
   __shared__ int cnt[NB + 1];
   __shared__ int off[NB + 1];
   __shared__ int n_coop;
-  __shared__ int coop_b[kPlanCoopMax], coop_s[kPlanCoopMax], coop_n[kPlanCoopMax];
+  __shared__ int coop_b[kPlanCoopMax], coop_s[kPlanCoopMax], coop_n[kPlanCoopMax], coop_l[kPlanCoopMax];
   const int tid = threadIdx.x;
   if (tid <= NB) cnt[tid] = 0;
   if (tid == 0) n_coop = 0;
@@ -126,20 +126,21 @@ __device__ __forceinline__ void plan_body(const Params& P, int* __restrict__ tas
         coop_b[k] = b;
         coop_s[k] = s;
         coop_n[k] = full;
+        coop_l[k] = L;
       } else {
-        for (int q = 0; q < full; ++q) tasks[s + q] = b * P.Pmax + q;
+        for (int q = 0; q < full; ++q) tasks[s + q] = make_int2(b * P.Pmax + q, L);
       }
     }
-    if (rem || L == 0) tasks[atomicAdd(&off[rem ? (rem + 15) >> 4 : 1], 1)] = b * P.Pmax + full;
+    if (rem || L == 0) tasks[atomicAdd(&off[rem ? (rem + 15) >> 4 : 1], 1)] = make_int2(b * P.Pmax + full, L);
   }
   __syncthreads();
   const int nc = min(n_coop, kPlanCoopMax);
   for (int k = 0; k < nc; ++k) {
-    for (int q = tid; q < coop_n[k]; q += blockDim.x) tasks[coop_s[k] + q] = coop_b[k] * P.Pmax + q;
+    for (int q = tid; q < coop_n[k]; q += blockDim.x) tasks[coop_s[k] + q] = make_int2(coop_b[k] * P.Pmax + q, coop_l[k]);
   }
 }
 
-__global__ __launch_bounds__(1024) void attn_plan(Params P, int* __restrict__ tasks, int* __restrict__ counters) {
+__global__ __launch_bounds__(1024) void attn_plan(Params P, int2* __restrict__ tasks, int* __restrict__ counters) {
   plan_body(P, tasks, counters);
 }
 
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(1024) void attn_plan(Params P, int* __restrict__ ta
 // others write (the two touch disjoint memory; the partition pass that follows in
 // stream order sees both).
 template <int EB>
-__global__ __launch_bounds__(256) void decode_prepare_kernel(Params P, WriteArgs wa, int* __restrict__ tasks,
+__global__ __launch_bounds__(256) void decode_prepare_kernel(Params P, WriteArgs wa, int2* __restrict__ tasks,
                                                              int* __restrict__ counters) {
   if (blockIdx.x == 0) {
     plan_body(P, tasks, counters);
@@ -210,11 +211,11 @@ __device__ __forceinline__ void combine_and_store(const Params& P, const float (
 // Runs load/compute over this wave's units w, w+NW, w+2*NW, ... with three register
 // buffers: while unit i is computed, units i+1 and i+2 are in flight.  Loads in the
 // steady-state loop are unconditional, so each compute waits only for its own data.
+// The caller has already issued the loads of the first unit into A.
 template <int NW, class Buf, class Load, class Compute>
-__device__ __forceinline__ void pipeline3(int w, int nunits, Load&& load, Compute&& compute) {
+__device__ __forceinline__ void pipeline3(int w, int nunits, Buf& A, Load&& load, Compute&& compute) {
   const int n = nunits > w ? (nunits - w + NW - 1) / NW : 0;
-  Buf A, B, C;
-  if (n > 0) load(w, A);
+  Buf B, C;
   if (n > 1) load(w + NW, B);
   int i = 0;
   for (; i + 4 < n; i += 3) {
@@ -249,13 +250,13 @@ __device__ __forceinline__ void pipeline3(int w, int nunits, Load&& load, Comput
 }
 
 // Two-buffer variant: while unit i is computed, unit i+1 is in flight.  The
-// scheduling fences keep each prefetch issued before the compute it overlaps.
+// scheduling fences keep each prefetch issued before the compute it overlaps.  The
+// caller has already issued the loads of the first unit into A.
 #define PKV_FENCE() __builtin_amdgcn_sched_barrier(0)
 template <int NW, class Buf, class Load, class Compute>
-__device__ __forceinline__ void pipeline2(int w, int nunits, Load&& load, Compute&& compute) {
+__device__ __forceinline__ void pipeline2(int w, int nunits, Buf& A, Load&& load, Compute&& compute) {
   const int n = nunits > w ? (nunits - w + NW - 1) / NW : 0;
-  Buf A, B;
-  if (n > 0) load(w, A);
+  Buf B;
   int i = 0;
   for (; i + 2 < n; i += 2) {
     const int u = w + i * NW;
@@ -284,11 +285,11 @@ __device__ __forceinline__ void pipeline2(int w, int nunits, Load&& load, Comput
 #define PKV_STAGES 2
 #endif
 template <int NW, class Buf, class Load, class Compute>
-__device__ __forceinline__ void pipeline(int w, int nunits, Load&& load, Compute&& compute) {
+__device__ __forceinline__ void pipeline(int w, int nunits, Buf& first, Load&& load, Compute&& compute) {
   if constexpr (PKV_STAGES == 3) {
-    pipeline3<NW, Buf>(w, nunits, load, compute);
+    pipeline3<NW, Buf>(w, nunits, first, load, compute);
   } else {
-    pipeline2<NW, Buf>(w, nunits, load, compute);
+    pipeline2<NW, Buf>(w, nunits, first, load, compute);
   }
 }
 
@@ -440,7 +441,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int t = blockIdx.x / HY;
   const int hy = blockIdx.x - t * HY;
   if (t >= P.counters[0]) return;
-  const int item = P.tasks[t];
+  const int2 task = P.tasks[t];
+  const int item = task.x;
   if (item < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
   const int b = item / P.Pmax;
   const int p = item - b * P.Pmax;
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int hg = hy - kvh * P.NHG;
   const int hq0 = kvh * P.G + hg * 16;
   const int gcur = min(16, P.G - hg * 16);
-  const int L = context_len(P, b);
+  const int L = min(max(task.y, 0), P.Lmax);
   if (L <= 0) {
     if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
     return;
@@ -465,29 +467,21 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int nunits = (ntok + 15) >> 4;
   const int nblk = (ntok + B - 1) / B;
 
-  if (tid < nblk) s_tab[tid] = P.tables[static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP + tid];
-
+  // Preamble: issue every load first (the partition's table entries and the queries,
+  // then the first unit's block id and its K/V), write LDS afterwards; vmcnt counts
+  // in issue order, so the LDS writes wait only for the table and query loads.
+  const int* trow = P.tables + static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP;
+  // (unconditional loads from clamped, always-valid addresses keep the waits exact)
+  const int tab_val = __builtin_nontemporal_load(trow + min(tid, nblk - 1));
   const bool hv = m < gcur;
-#ifdef PKV_Q_IN_LDS
-  // query fragments live in LDS (lane-major, conflict-free) and are re-read per unit
-  __shared__ u32x4 s_q[KI][64];
-  if (w == 0) {
-    const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + (hv ? m : 0)) * D * EB;
-#pragma unroll
-    for (int ki = 0; ki < KI; ++ki)
-      s_q[ki][lane] = hv ? *reinterpret_cast<const u32x4*>(qrow + (4 * ki + r) * 16) : u32x4{0u, 0u, 0u, 0u};
-  }
-#else
   u32x4 qf[KI];
   {
     const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + (hv ? m : 0)) * D * EB;
 #pragma unroll
-    for (int ki = 0; ki < KI; ++ki) {
-      qf[ki] = hv ? *reinterpret_cast<const u32x4*>(qrow + (4 * ki + r) * 16) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int ki = 0; ki < KI; ++ki) qf[ki] = load_stream<u32x4>(qrow + (4 * ki + r) * 16);
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki) qf[ki] = hv ? qf[ki] : u32x4{0u, 0u, 0u, 0u};
   }
-#endif
-  __syncthreads();
 
   const char* kbase = P.kp + kvh * TILE;
   const char* vbase = P.vp + kvh * TILE;
@@ -495,10 +489,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int koff = (r * B + m) * 16;       // + ki * 4 * B * 16 + sub * 256
   const int voff = (m * B + 4 * r) * EB;   // + c * 16 * B * EB + sub * 16 * EB
 
-  auto load = [&](int u, Buf& f) {
-    const int bi = u / SUB;
-    const int sub = u - bi * SUB;
-    const int blk = __builtin_amdgcn_readfirstlane(s_tab[bi]);
+  auto load_blk = [&](int u, int blk, Buf& f) {
+    const int sub = u - (u / SUB) * SUB;
     const char* kt = kbase + blk * bstride + sub * 256;
     const char* vt = vbase + blk * bstride + sub * 16 * EB;
 #pragma unroll
@@ -506,6 +498,25 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
 #pragma unroll
     for (int c = 0; c < NC; ++c) f.v[c] = load_stream<u32x2>(vt + voff + c * 16 * B * EB);
   };
+  auto load = [&](int u, Buf& f) { load_blk(u, __builtin_amdgcn_readfirstlane(s_tab[u / SUB]), f); };
+  // the wave's first unit takes its block id straight from the table (a scalar load);
+  // a wave without units loads unit 0 (unused) so the load stays unconditional
+  Buf first;
+  {
+    const int u0 = w < nunits ? w : 0;
+    load_blk(u0, trow[u0 / SUB], first);
+  }
+  PKV_FENCE();
+  if (tid < nblk) s_tab[tid] = tab_val;
+#ifdef PKV_Q_IN_LDS
+  // query fragments live in LDS (lane-major, conflict-free) and are re-read per unit
+  __shared__ u32x4 s_q[KI][64];
+  if (w == 0) {
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki) s_q[ki][lane] = qf[ki];
+  }
+#endif
+  __syncthreads();
 
   float m_run = kNegInf;
   float l_part = 0.f;
@@ -558,7 +569,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     for (int c = 0; c < NC; ++c) o[c] = T::mfma_k16(f.v[c], pb, o[c]);
   };
 
-  pipeline<kWaves, Buf>(w, nunits, load, compute);
+  pipeline<kWaves, Buf>(w, nunits, first, load, compute);
 
   float l = sum_xor16(l_part);
   l = sum_xor32(l);
@@ -608,12 +619,13 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   const int t = blockIdx.x / P.Hkv;
   const int kvh = blockIdx.x - t * P.Hkv;
   if (t >= P.counters[0]) return;
-  const int item = P.tasks[t];
+  const int2 task = P.tasks[t];
+  const int item = task.x;
   if (item < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
   const int b = item / P.Pmax;
   const int p = item - b * P.Pmax;
   const int hq0 = kvh * G;
-  const int L = context_len(P, b);
+  const int L = min(max(task.y, 0), P.Lmax);
   if (L <= 0) {
     if (p == 0) zero_rows<T, D>(P, b, hq0, G);
     return;
@@ -630,7 +642,10 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   const int nunits = (ntok + 15) >> 4;
   const int nblk = (ntok + B - 1) / B;
 
-  if (tid < nblk) s_tab[tid] = P.tables[static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP + tid];
+  // Preamble: issue every load first (table entries, queries, then the first unit's
+  // block id and K/V), write LDS afterwards.
+  const int* trow = P.tables + static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP;
+  const int tab_val = __builtin_nontemporal_load(trow + min(tid, nblk - 1));  // unconditional: exact waits
 
   // queries: lane keeps chunks r + 4i of every head (fp32 pools: pre-scaled floats)
   u32x4 qw[G][KL];
@@ -638,16 +653,8 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   for (int g = 0; g < G; ++g) {
     const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + g) * D * EB;
 #pragma unroll
-    for (int i = 0; i < KL; ++i) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + (r + 4 * i) * 16);
-      if constexpr (EB == 4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(__uint_as_float(v[e]) * P.scale_log2);
-      }
-      qw[g][i] = v;
-    }
+    for (int i = 0; i < KL; ++i) qw[g][i] = load_stream<u32x4>(qrow + (r + 4 * i) * 16);
   }
-  __syncthreads();
 
   const char* kbase = P.kp + kvh * TILE;
   const char* vbase = P.vp + kvh * TILE;
@@ -655,10 +662,8 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   const int koff = (r * B + m) * 16;      // + i * 4 * B * 16 + sub * 256
   const int voff = (m * B + 4 * r) * EB;  // + c * 16 * B * EB + sub * 16 * EB
 
-  auto load = [&](int u, Buf& f) {
-    const int bi = u / SUB;
-    const int sub = u - bi * SUB;
-    const int blk = __builtin_amdgcn_readfirstlane(s_tab[bi]);
+  auto load_blk = [&](int u, int blk, Buf& f) {
+    const int sub = u - (u / SUB) * SUB;
     const char* kt = kbase + blk * bstride + sub * 256;
     const char* vt = vbase + blk * bstride + sub * 16 * EB;
 #pragma unroll
@@ -666,6 +671,27 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
 #pragma unroll
     for (int c = 0; c < NV; ++c) f.v[c] = load_stream<VVec>(vt + voff + c * 16 * B * EB);
   };
+  auto load = [&](int u, Buf& f) { load_blk(u, __builtin_amdgcn_readfirstlane(s_tab[u / SUB]), f); };
+  // the wave's first unit takes its block id straight from the table (a scalar load);
+  // a wave without units loads unit 0 (unused) so the load stays unconditional
+  Buf first;
+  {
+    const int u0 = w < nunits ? w : 0;
+    load_blk(u0, trow[u0 / SUB], first);
+  }
+  PKV_FENCE();
+  if (tid < nblk) s_tab[tid] = tab_val;
+  if constexpr (EB == 4) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qw[g][i][e] = __float_as_uint(__uint_as_float(qw[g][i][e]) * P.scale_log2);
+      }
+    }
+  }
+  __syncthreads();
 
   float m_run[G], l_part[G], o[G][NV];
 #pragma unroll
@@ -753,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
     }
   };
 
-  pipeline<kWaves, Buf>(w, nunits, load, compute);
+  pipeline<kWaves, Buf>(w, nunits, first, load, compute);
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -795,7 +821,7 @@ Params make_params(const AttnArgs& a) {
   P.ws_ml = a.ws_ml;
   P.tables = a.block_tables;
   P.ctx = a.context_lens;
-  P.tasks = a.tasks;
+  P.tasks = reinterpret_cast<const int2*>(a.tasks);
   P.counters = a.counters;
   P.done = a.done;
   P.N = a.num_seqs;
@@ -883,16 +909,19 @@ int launch_decode_prepare(const AttnArgs& a, const pkv_pool_desc& pool, void* k_
   const unsigned grid = 1 + static_cast<unsigned>((total + 255) / 256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (eb == 4) {
-    hipLaunchKernelGGL(decode_prepare_kernel<4>, dim3(grid), dim3(256), 0, s, P, wa, a.tasks, a.counters);
+    hipLaunchKernelGGL(decode_prepare_kernel<4>, dim3(grid), dim3(256), 0, s, P, wa, reinterpret_cast<int2*>(a.tasks),
+                       a.counters);
   } else {
-    hipLaunchKernelGGL(decode_prepare_kernel<2>, dim3(grid), dim3(256), 0, s, P, wa, a.tasks, a.counters);
+    hipLaunchKernelGGL(decode_prepare_kernel<2>, dim3(grid), dim3(256), 0, s, P, wa, reinterpret_cast<int2*>(a.tasks),
+                       a.counters);
   }
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_attn_plan(const AttnArgs& a, void* stream) {
   const Params P = make_params(a);
-  hipLaunchKernelGGL(attn_plan, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), P, a.tasks, a.counters);
+  hipLaunchKernelGGL(attn_plan, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), P,
+                     reinterpret_cast<int2*>(a.tasks), a.counters);
   return static_cast<int>(hipGetLastError());
 }
 

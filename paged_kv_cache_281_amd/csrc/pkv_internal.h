@@ -42,7 +42,7 @@ struct AttnArgs {
   const int32_t* context_lens;
   float* ws_o;   // [num_seqs][num_q_heads][max_partitions][head_dim]
   float* ws_ml;  // [num_seqs][num_q_heads][max_partitions][2]: running max (log2 units), sum
-  int* tasks;    // [num_seqs * max_partitions]: (sequence, partition) items, longest first
+  int* tasks;    // [num_seqs * max_partitions] x 2 ints: (item, context length), longest first
   int* counters; // [64]: counters[0] = number of items
   int* done;     // [num_seqs * num_q_heads]: finished partitions per (sequence, head group)
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
@@ -60,7 +60,7 @@ inline WorkspaceLayout workspace_layout(int64_t n, int64_t hq, int64_t d, int64_
   w.o = 0;
   w.ml = al(static_cast<size_t>(n * hq * parts * d) * sizeof(float));
   w.tasks = w.ml + al(static_cast<size_t>(n * hq * parts * 2) * sizeof(float));
-  w.done = w.tasks + al(static_cast<size_t>(n * parts) * sizeof(int32_t));
+  w.done = w.tasks + al(static_cast<size_t>(n * parts) * 2 * sizeof(int32_t));
   w.counters = w.done + al(static_cast<size_t>(n * hq) * sizeof(int32_t));
   w.total = w.counters + 256;
   return w;

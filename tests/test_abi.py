@@ -38,7 +38,7 @@ def test_workspace_and_pool_sizes(pkv_lib):
     n = lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 8192, 16)
     parts = 8192 * 16 // 512
     al = lambda x: (x + 255) // 256 * 256
-    assert n == al(8 * 32 * parts * 128 * 4) + al(8 * 32 * parts * 2 * 4) + al(8 * parts * 4) + al(8 * 32 * 4) + 256
+    assert n == al(8 * 32 * parts * 128 * 4) + al(8 * 32 * parts * 2 * 4) + al(8 * parts * 8) + al(8 * 32 * 4) + 256
     assert lib.pkv_paged_attention_workspace_bytes(-1, 32, 128, 8, 16) == 0
     d = pkv_lib.PoolDesc(65536, 16, 8, 128, 2)
     assert lib.pkv_pool_bytes(ctypes.byref(d)) == 2 * 2 ** 30
