@@ -590,6 +590,214 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
 }
 
 // ---------------------------------------------------------------------------------
+// MFMA partition kernel with 32-token units (bf16/fp16, 2..16 query heads): one unit
+// is one 32-token block, or two consecutive 16-token blocks.  The scores of a unit are
+// two 16x16x32 MFMA chains over D whose rows are the tokens tau_s(i) =
+// 8*(i/4) + 4*s + i%4 (s = 0, 1), so that lane (r, m) ends up holding the scores of
+// tokens 8r..8r+7; P.V is then one 16x16x32 MFMA per 16 d whose V^T fragment is 16
+// contiguous bytes of a V row (each V load instruction reads 1 KiB contiguously at
+// block 32, two 512-byte runs at block 16).
+// grid = (items * num_kv_heads * head_groups)
+// ---------------------------------------------------------------------------------
+template <class T, int D, int B, int GMAX>
+__global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partition_mfma32(Params P) {
+  constexpr int EB = T::kBytes;
+  static_assert(EB == 2, "MFMA path is for 16-bit pools");
+  constexpr int KI = D / 32;   // 16x16x32 steps over head_dim per 16-token sub-tile
+  constexpr int NC = D / 16;   // 16x16x32 P.V products per unit (16 d each)
+  constexpr int BPU = 32 / B;  // blocks per unit
+  constexpr int BPP = kPT / B;
+  constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
+  struct Buf {
+    u32x4 k[2][KI];
+    u32x4 v[NC];
+  };
+
+  __shared__ int s_tab[BPP];
+  __shared__ float s_m[kWaves][GMAX];
+  __shared__ float s_l[kWaves][GMAX];
+  __shared__ float s_o[kWaves][GMAX][D + 4];
+  __shared__ MergeSmem<D> s_merge;
+  __shared__ int s_last;
+  __shared__ u32x4 s_q[KI][64];
+
+  const int HY = P.Hkv * P.NHG;
+  const int t = blockIdx.x / HY;
+  const int hy = blockIdx.x - t * HY;
+  if (t >= P.counters[0]) return;
+  const int2 task = P.tasks[t];
+  const int item = task.x;
+  if (item < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
+  const int b = item / P.Pmax;
+  const int p = item - b * P.Pmax;
+  const int kvh = hy / P.NHG;
+  const int hg = hy - kvh * P.NHG;
+  const int hq0 = kvh * P.G + hg * 16;
+  const int gcur = min(16, P.G - hg * 16);
+  const int L = min(max(task.y, 0), P.Lmax);
+  if (L <= 0) {
+    if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
+    return;
+  }
+  const int np = (L + kPT - 1) / kPT;
+  if (p >= np) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane >> 4;
+  const int m = lane & 15;
+  const int ntok = min(kPT, L - p * kPT);
+  const int nunits = (ntok + 31) >> 5;
+  const int nblk = (ntok + B - 1) / B;
+
+  // preamble: all loads first (table entries, queries, first unit), LDS writes after
+  const int* trow = P.tables + static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP;
+  const int tab_val = __builtin_nontemporal_load(trow + min(tid, nblk - 1));
+  const bool hv = m < gcur;
+  u32x4 qf[KI];
+  {
+    const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + (hv ? m : 0)) * D * EB;
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki) qf[ki] = load_stream<u32x4>(qrow + (4 * ki + r) * 16);
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki) qf[ki] = hv ? qf[ki] : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const char* kbase = P.kp + kvh * TILE;
+  const char* vbase = P.vp + kvh * TILE;
+  const int64_t bstride = static_cast<int64_t>(P.Hkv) * TILE;
+  // lane geometry: K rows of sub-tile s are tokens tau_s(m); V lanes read tokens 8r..8r+7
+  const int tau0 = 8 * (m >> 2) + (m & 3);  // tau_s(m) = tau0 + 4 s, in 0..31
+  int koff[2];
+  int voff;
+  bool k_second;  // (block 16) this lane's K rows are in the unit's second block
+  bool v_second;
+  if constexpr (BPU == 2) {
+    k_second = m >= 8;
+    v_second = r >= 2;
+    koff[0] = (r * B + (tau0 & 15)) * 16;        // + ki * 4 * B * 16
+    koff[1] = (r * B + ((tau0 + 4) & 15)) * 16;
+    voff = (m * B + 8 * (r & 1)) * EB;           // + c * 16 * B * EB
+  } else {
+    k_second = false;
+    v_second = false;
+    koff[0] = (r * B + tau0) * 16;
+    koff[1] = (r * B + tau0 + 4) * 16;
+    voff = (m * B + 8 * r) * EB;
+  }
+
+  auto load_blk = [&](int blk0, int blk1, Buf& f) {
+    const char* k0 = kbase + blk0 * bstride;
+    const char* v0 = vbase + blk0 * bstride;
+    const char* kt = k0;
+    const char* vt = v0;
+    if constexpr (BPU == 2) {
+      const char* k1 = kbase + blk1 * bstride;
+      const char* v1 = vbase + blk1 * bstride;
+      kt = k_second ? k1 : k0;
+      vt = v_second ? v1 : v0;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int ki = 0; ki < KI; ++ki) f.k[s][ki] = load_stream<u32x4>(kt + koff[s] + ki * 4 * B * 16);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) f.v[c] = load_stream<u32x4>(vt + voff + c * 16 * B * EB);
+  };
+  auto load = [&](int u, Buf& f) {
+    const int blk0 = __builtin_amdgcn_readfirstlane(s_tab[u * BPU]);
+    const int blk1 = BPU == 2 ? __builtin_amdgcn_readfirstlane(s_tab[min(u * BPU + 1, nblk - 1)]) : blk0;
+    load_blk(blk0, blk1, f);
+  };
+  Buf first;
+  {
+    const int u0 = w < nunits ? w : 0;
+    const int blk0 = trow[u0 * BPU];
+    const int blk1 = BPU == 2 ? trow[min(u0 * BPU + 1, nblk - 1)] : blk0;
+    load_blk(blk0, blk1, first);
+  }
+  PKV_FENCE();
+  if (tid < nblk) s_tab[tid] = tab_val;
+  if (w == 0) {
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki) s_q[ki][lane] = qf[ki];
+  }
+  __syncthreads();
+
+  float m_run = kNegInf;
+  float l_part = 0.f;
+  f32x4 o[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int u, Buf& f) {
+    f32x4 acc[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ki = 0; ki < KI; ++ki) acc[s] = T::mfma_k32(f.k[s][ki], s_q[ki][lane], acc[s]);
+    }
+    float sc[8];  // tokens 8r + e of the unit, e = 4 s + j
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[4 * s + j] = acc[s][j] * P.scale_log2;
+    }
+    if (32 * u + 32 > ntok) {
+      const int t0 = 32 * u + 8 * r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc[e] = (t0 + e < ntok) ? sc[e] : kNegInf;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32 msk = (t0 + 2 * k < ntok ? 0x0000ffffu : 0u) | (t0 + 2 * k + 1 < ntok ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) f.v[c][k] &= msk;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
+    if (wave_any(mx > m_run + kRescaleLog2)) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - mn);
+      l_part *= alpha;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) o[c] *= alpha;
+      m_run = mn;
+    }
+    u32x4 pb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pb[k] = T::pack2(fast_exp2(sc[2 * k] - m_run), fast_exp2(sc[2 * k + 1] - m_run));
+    l_part += ((T::lo(pb[0]) + T::hi(pb[0])) + (T::lo(pb[1]) + T::hi(pb[1]))) +
+              ((T::lo(pb[2]) + T::hi(pb[2])) + (T::lo(pb[3]) + T::hi(pb[3])));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) o[c] = T::mfma_k32(f.v[c], pb, o[c]);
+  };
+
+  pipeline<kWaves, Buf>(w, nunits, first, load, compute);
+
+  float l = sum_xor16(l_part);
+  l = sum_xor32(l);
+  if (hv) {
+    if (r == 0) {
+      s_m[w][m] = m_run;
+      s_l[w][m] = l;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_o[w][m][16 * c + 4 * r + j] = o[c][j];
+    }
+  }
+  __syncthreads();
+  combine_and_store<T, D, GMAX>(P, s_m, s_l, s_o, b, hq0, gcur, p, np);
+  if (np > 1 && np <= kFuseMaxParts) finish_rows<T, D>(P, b, hq0, gcur, np, s_merge, s_last);
+}
+
+// ---------------------------------------------------------------------------------
 // Vector-ALU partition kernel: one query head per kv head (any pool type), or fp32
 // pools with G query heads per kv head.  grid = (num_kv_heads, max_partitions, num_seqs)
 // ---------------------------------------------------------------------------------
@@ -836,6 +1044,16 @@ Params make_params(const AttnArgs& a) {
   return P;
 }
 
+// Which MFMA kernel a block size uses: 32-token units or 16-token units.
+#ifndef PKV_UNIT32_B16
+#define PKV_UNIT32_B16 0
+#endif
+#ifndef PKV_UNIT32_B32
+#define PKV_UNIT32_B32 1
+#endif
+template <int B>
+constexpr bool kUnit32 = (B == 16) ? PKV_UNIT32_B16 != 0 : PKV_UNIT32_B32 != 0;
+
 template <class T, int D, int B>
 int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
   const Params P = make_params(a);
@@ -856,7 +1074,15 @@ int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
     }
   } else if constexpr (T::kBytes == 2) {
     const dim3 grid(static_cast<unsigned>(items * a.num_kv_heads * P.NHG));
-    if (P.G <= 4) {
+    if (kUnit32<B>) {
+      if (P.G <= 4) {
+        hipLaunchKernelGGL((attn_partition_mfma32<T, D, B, 4>), grid, block, 0, s, P);
+      } else if (P.G <= 8) {
+        hipLaunchKernelGGL((attn_partition_mfma32<T, D, B, 8>), grid, block, 0, s, P);
+      } else {
+        hipLaunchKernelGGL((attn_partition_mfma32<T, D, B, 16>), grid, block, 0, s, P);
+      }
+    } else if (P.G <= 4) {
       hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 4>), grid, block, 0, s, P);
     } else if (P.G <= 8) {
       hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 8>), grid, block, 0, s, P);

@@ -95,6 +95,9 @@ VARIANTS = [
     ("bf16_g2_d128_b16", "bf16", 8, 4, 128, 16, [1, 33, 520, 1600]),
     ("f16_g8_d64_b16", "f16", 16, 2, 64, 16, [2, 47, 512, 1537]),
     ("bf16_g16_d128_b32", "bf16", 32, 2, 128, 32, [5, 300, 999]),
+    ("f16_g4_d64_b32", "f16", 16, 4, 64, 32, [1, 31, 32, 33, 544, 1057]),
+    ("bf16_g8_d128_b32", "bf16", 16, 2, 128, 32, [2, 63, 65, 512, 1600]),
+    ("bf16_g5_d128_b16", "bf16", 10, 2, 128, 16, [1, 16, 17, 48, 530, 1111]),
     ("bf16_g32_d128_b16", "bf16", 32, 1, 128, 16, [9, 640, 1030]),
     ("bf16_g3_d128_b16", "bf16", 12, 4, 128, 16, [17, 200, 513]),
     ("f32_g2_d128_b16", "f32", 8, 4, 128, 16, [1, 100, 600]),
