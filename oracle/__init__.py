@@ -11,8 +11,9 @@ What it computes, and the passage each part follows:
   copy-on-write of refcounted blocks (agentalpha.top Q32 answer parts 2-3;
   data.6616ai.com "PagedAttention：把虚拟内存搬进 KV Cache"; ohmygp.com "破局思路").
 * ``kv_cache``       - the physical pool, the KV write into a slot, and the block copy.
-* ``attention``      - decode attention gathered through the block table, and the
-  partitioned form with a log-sum-exp merge.
+* ``attention``      - decode attention gathered through the block table, the
+  partitioned form with a log-sum-exp merge, and causal attention of a chunk of new
+  tokens (prefill / chunked prefill) over the same pool.
 * ``accounting``     - the memory-waste accounting of the ohmygp.com simulation.
 * ``replay``         - replays a ``synth`` workload through the parts above.
 

@@ -13,6 +13,14 @@ with g = h // (Hq / Hkv) for grouped-query heads (consecutive query heads share 
 KV head) and K/V[b, j] read from physical block ``table[b][j // B]`` at offset
 ``j % B``.  An empty context (L_b = 0) gives a zero output.
 
+``paged_attention_prefill`` is the multi-token form over the same pool: each
+sequence appends a chunk of C_b new tokens (their K/V already written to the pool,
+so the context length L_b includes them), and query token t of the chunk sits at
+position L_b - C_b + t and attends causally to positions 0 .. L_b - C_b + t.  This
+is the prefill / chunked-prefill step that FlashAttention-style blockwise loading
+serves over paged KV (agentalpha.top Q32 follow-up 3; data.6616ai.com "可能的追问");
+decode is its C_b = 1 case.
+
 ``partitioned_attention`` computes the same result in independent partitions of
 the context merged by log-sum-exp weights, the split-context form the pages tie
 to FlashAttention-style blockwise loading over paged KV (agentalpha.top Q32
@@ -68,6 +76,44 @@ def paged_attention_decode(q_bits: np.ndarray, q_dtype: str, pool: Pool, block_t
         for g in range(Hkv):
             heads = slice(g * G, (g + 1) * G)
             out[b, heads] = softmax_attention(q[b, heads], K[:, g, :], V[:, g, :], scale)
+    return out
+
+
+def paged_attention_prefill(q_bits: np.ndarray, q_dtype: str, pool: Pool, block_tables: np.ndarray,
+                            context_lens: np.ndarray, query_start: np.ndarray, scale: float) -> np.ndarray:
+    """Causal attention of each sequence's chunk of new tokens: float64 ``[T, Hq, D]``.
+
+    ``q`` holds the chunks back to back (``[T, Hq, D]``); sequence b owns rows
+    ``query_start[b] .. query_start[b+1]-1`` and its chunk is the last
+    C_b = query_start[b+1] - query_start[b] of its L_b context tokens (C_b <= L_b).
+    Row t of the chunk (position p = L_b - C_b + t) is softmax attention over the
+    context tokens j <= p.
+    """
+    q = widen(q_bits, q_dtype)
+    T, Hq, D = q.shape
+    Hkv = pool.num_kv_heads
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    qs = np.asarray(query_start, dtype=np.int64)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for b in range(len(qs) - 1):
+        C = int(qs[b + 1] - qs[b])
+        L = int(context_lens[b])
+        if C == 0:
+            continue
+        if C > L:
+            raise ValueError("a chunk cannot be longer than its context")
+        K, V = gather_context(pool, block_tables[b], L)
+        pos = L - C + np.arange(C)                         # position of each chunk token
+        visible = np.arange(L)[None, :] <= pos[:, None]    # [C, L] causal mask
+        for h in range(Hq):
+            g = h // G
+            s = scale * (q[qs[b]:qs[b + 1], h, :] @ K[:, g, :].T)   # [C, L]
+            s = np.where(visible, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)                                # masked entries give exp(-inf) = 0
+            out[qs[b]:qs[b + 1], h, :] = (p @ V[:, g, :]) / p.sum(axis=1, keepdims=True)
     return out
 
 
