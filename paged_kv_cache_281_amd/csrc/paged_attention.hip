@@ -249,38 +249,6 @@ __device__ __forceinline__ void pipeline3(int w, int nunits, Buf& A, Load&& load
   }
 }
 
-// Two-buffer variant: while unit i is computed, unit i+1 is in flight.  The
-// scheduling fences keep each prefetch issued before the compute it overlaps.  The
-// caller has already issued the loads of the first unit into A.
-#define PKV_FENCE() __builtin_amdgcn_sched_barrier(0)
-template <int NW, class Buf, class Load, class Compute>
-__device__ __forceinline__ void pipeline2(int w, int nunits, Buf& A, Load&& load, Compute&& compute) {
-  const int n = nunits > w ? (nunits - w + NW - 1) / NW : 0;
-  Buf B;
-  int i = 0;
-  for (; i + 2 < n; i += 2) {
-    const int u = w + i * NW;
-    load(u + NW, B);
-    PKV_FENCE();
-    compute(u, A);
-    PKV_FENCE();
-    load(u + 2 * NW, A);
-    PKV_FENCE();
-    compute(u + NW, B);
-    PKV_FENCE();
-  }
-  const int u = w + i * NW;
-  if (n - i == 2) {
-    load(u + NW, B);
-    PKV_FENCE();
-    compute(u, A);
-    PKV_FENCE();
-    compute(u + NW, B);
-  } else if (n - i == 1) {
-    compute(u, A);
-  }
-}
-
 #ifndef PKV_STAGES
 #define PKV_STAGES 2
 #endif
