@@ -142,6 +142,41 @@ int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Causal attention of chunks of new tokens over the paged pool (prefill and chunked
+ * prefill).  Pages: agentalpha.top Q32 follow-up 3 (FlashAttention loads K/V block by
+ * block; over paged storage that loading goes through the block table);
+ * data.6616ai.com "可能的追问" (FlashAttention fused with paged reads).  Sequence b
+ * appends a chunk of C_b = query_start[b+1] - query_start[b] tokens whose K/V are
+ * already written to the pool, so its context_lens[b] = L_b counts them.  Query row
+ * query_start[b] + t (t < C_b) sits at position p = L_b - C_b + t; for each query head
+ * h, with kv head g = h / (num_q_heads / H):
+ *     s_j = scale * dot(q[row][h], K[b, j, g])   for 0 <= j <= p
+ *     out[row][h] = sum_j softmax(s)_j * V[b, j, g]
+ * Decode is the C_b = 1 case.  bf16 and fp16 pools only (fp32: UNSUPPORTED).
+ *   q, out        device [num_tokens][num_q_heads][D], pool dtype, contiguous,
+ *                 16-byte aligned; sequence b's chunk is rows query_start[b] ..
+ *                 query_start[b+1]-1.
+ *   query_start   device int32 [num_seqs + 1], non-decreasing, query_start[0] = 0,
+ *                 query_start[num_seqs] = num_tokens.
+ *   num_tokens, max_query_len  host: the total rows and an upper bound on every C_b
+ *                 (it sizes the grid).
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; context_lens device
+ *                 int32 [num_seqs].
+ * Accumulation is fp32, the output is rounded to the pool dtype, and the reduction
+ * order depends only on logical positions.  No workspace; nothing is allocated.
+ * Device preconditions: C_b <= max_query_len; C_b <= context_lens[b] <=
+ * max_blocks_per_seq * B; table entries that are read are < num_blocks.  A sequence
+ * whose chunk breaks them (longer than its context, or outside q) gets no output rows
+ * written; rows past max_query_len are not written.  num_seqs == 0 or num_tokens == 0
+ * enqueues nothing.  Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
+ */
+int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                    void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                    const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, float scale, void* stream);
+
+/*
  * The two passes of pkv_paged_attention_decode, exposed separately (same arguments,
  * same results when called in this order on one stream with the same workspace and
  * context_lens) so that each pass can be timed on its own:

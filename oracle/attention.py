@@ -80,8 +80,11 @@ def paged_attention_decode(q_bits: np.ndarray, q_dtype: str, pool: Pool, block_t
 
 
 def paged_attention_prefill(q_bits: np.ndarray, q_dtype: str, pool: Pool, block_tables: np.ndarray,
-                            context_lens: np.ndarray, query_start: np.ndarray, scale: float) -> np.ndarray:
+                            context_lens: np.ndarray, query_start: np.ndarray, scale: float,
+                            seqs: Optional[Iterable[int]] = None) -> np.ndarray:
     """Causal attention of each sequence's chunk of new tokens: float64 ``[T, Hq, D]``.
+
+    Rows of sequences not listed in ``seqs`` (when given) stay zero.
 
     ``q`` holds the chunks back to back (``[T, Hq, D]``); sequence b owns rows
     ``query_start[b] .. query_start[b+1]-1`` and its chunk is the last
@@ -97,7 +100,7 @@ def paged_attention_prefill(q_bits: np.ndarray, q_dtype: str, pool: Pool, block_
     G = Hq // Hkv
     qs = np.asarray(query_start, dtype=np.int64)
     out = np.zeros((T, Hq, D), dtype=np.float64)
-    for b in range(len(qs) - 1):
+    for b in (range(len(qs) - 1) if seqs is None else seqs):
         C = int(qs[b + 1] - qs[b])
         L = int(context_lens[b])
         if C == 0:

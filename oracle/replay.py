@@ -56,3 +56,21 @@ def replay(w, fill_bits: int, pad: int = 0, context=None,
     return ReplayResult(bm, pool, tables.reshape(len(w.batch), w.max_blocks_per_seq), lens,
                         np.asarray(slots, dtype=np.int64),
                         np.asarray(pairs, dtype=np.int64).reshape(-1, 2), copies)
+
+
+def replay_prefill(w, fill_bits: int, context=None, pad: int = 0):
+    """Place a prefill workload: every sequence (ascending) is added with its whole
+    context and its K/V written at positions 0..L-1.  Returns (pool, block tables
+    int32 [N, W], context lengths int32 [N])."""
+    bm = BlockManager(w.num_blocks, w.block_size, w.free_order)
+    pool = Pool(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype, fill_bits)
+    if context is None:
+        context = w.all_context_kv()
+    for b in range(w.num_seqs):
+        L = int(w.context_lens[b])
+        bm.add_seq(b, L)
+        if L:
+            k, v = context[b]
+            paged_kv_write(pool, k, v, bm.slots(b, 0, L))
+    tables = np.asarray(bm.block_tables(range(w.num_seqs), w.max_blocks_per_seq, pad), dtype=np.int32)
+    return pool, tables.reshape(w.num_seqs, w.max_blocks_per_seq), np.asarray(w.context_lens, dtype=np.int32)

@@ -73,6 +73,8 @@ def load():
         "pkv_paged_attention_plan": ([P(PoolDesc), _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_sz, _c_vp], _c_i32),
         "pkv_decode_prepare": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp,
                                 _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_paged_attention_prefill": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
+                                         _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp], _c_i32),
         "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
         "pkv_bm_destroy": ([_c_vp], None),
         "pkv_bm_add_seq": ([_c_vp, _c_i32, _c_i32], _c_i32),
@@ -202,6 +204,39 @@ def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
     _check(load().pkv_paged_attention_decode(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq,
                                              _ptr(block_tables), W, _ptr(context_lens), float(scale), _ptr(ws),
                                              ws.numel(), _stream(q.device)))
+    return out
+
+
+def paged_attention_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+                            max_query_len: int, scale: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal attention of each sequence's chunk of new tokens over its paged context.
+
+    ``q`` is ``[T, Hq, D]`` with sequence b's chunk in rows ``query_start[b] ..
+    query_start[b+1]-1``; their K/V must already be in the pool (``context_lens``
+    counts them).  ``max_query_len`` (host int) bounds every chunk length.
+    """
+    d = pool_desc(k_pool, v_pool)
+    _require(q.dim() == 3 and q.shape[2] == d.head_dim and q.dtype == k_pool.dtype and q.is_contiguous()
+             and q.device == k_pool.device, "q must be a contiguous [T, Hq, D] device tensor of the pool dtype")
+    T, Hq, _ = q.shape
+    _require(query_start.dtype == torch.int32 and query_start.dim() == 1 and query_start.is_contiguous()
+             and query_start.device == k_pool.device, "query_start must be a contiguous int32 [N+1] device tensor")
+    N = query_start.shape[0] - 1
+    _require(N >= 0, "query_start needs N+1 entries")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == N
+             and block_tables.is_contiguous() and block_tables.device == k_pool.device,
+             "block_tables must be a contiguous int32 [N, W] device tensor")
+    _require(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (N,) and context_lens.is_contiguous()
+             and context_lens.device == k_pool.device, "context_lens must be a contiguous int32 [N] device tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous() and out.device == q.device,
+             "out must match q")
+    _check(load().pkv_paged_attention_prefill(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq,
+                                              _ptr(query_start), T, int(max_query_len), _ptr(block_tables),
+                                              block_tables.shape[1], _ptr(context_lens), float(scale),
+                                              _stream(q.device)))
     return out
 
 

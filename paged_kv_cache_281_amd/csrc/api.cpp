@@ -276,4 +276,65 @@ int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool
                                         max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes, stream);
 }
 
+int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                    void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                    const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, float scale, void* stream) {
+  const char* who = "pkv_paged_attention_prefill";
+  char buf[256];
+  int32_t st = pkv::check_pool(pool, who);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) {
+    std::snprintf(buf, sizeof(buf), "%s: num_seqs, num_tokens, max_query_len >= 0 and num_q_heads, "
+                  "max_blocks_per_seq > 0 required", who);
+    return pkv::set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (num_q_heads % pool->num_kv_heads != 0) {
+    std::snprintf(buf, sizeof(buf), "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who, num_q_heads,
+                  pool->num_kv_heads);
+    return pkv::set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (!pkv::prefill_supported(pool->dtype, pool->head_dim, pool->block_size)) {
+    std::snprintf(buf, sizeof(buf), "%s: no kernel for dtype %d, head_dim %d, block_size %d (bf16/fp16 only)", who,
+                  pool->dtype, pool->head_dim, pool->block_size);
+    return pkv::set_error(PKV_ERR_UNSUPPORTED, buf);
+  }
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
+  const int group = num_q_heads / pool->num_kv_heads;
+  const int64_t grid = pkv::prefill_tiles(max_query_len, group) * num_seqs * pool->num_kv_heads;
+  if (grid > 0x7fffffff || static_cast<int64_t>(num_tokens) * num_q_heads * pool->head_dim > (int64_t{1} << 40)) {
+    std::snprintf(buf, sizeof(buf), "%s: problem too large for one launch", who);
+    return pkv::set_error(PKV_ERR_UNSUPPORTED, buf);
+  }
+  if (!k_pool || !v_pool || !out || !q || !query_start || !block_tables || !context_lens) {
+    std::snprintf(buf, sizeof(buf), "%s: null pointer argument", who);
+    return pkv::set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (!pkv::aligned(k_pool, 16) || !pkv::aligned(v_pool, 16) || !pkv::aligned(q, 16) || !pkv::aligned(out, 16) ||
+      !pkv::aligned(query_start, 4) || !pkv::aligned(block_tables, 4) || !pkv::aligned(context_lens, 4)) {
+    std::snprintf(buf, sizeof(buf), "%s: misaligned pointer (pools, q, out need 16 bytes)", who);
+    return pkv::set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  pkv::PrefillArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.out = out;
+  a.q = q;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.max_query_len = max_query_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.block_size = pool->block_size;
+  a.dtype = pool->dtype;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale = scale;
+  return pkv::launch_status(pkv::launch_prefill(a, stream), who);
+}
+
 }  // extern "C"

@@ -76,4 +76,22 @@ int launch_attn_partitions(const AttnArgs& a, void* stream);
 // Whether a partition kernel exists for this configuration.
 bool attn_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
 
+struct PrefillArgs {
+  const void* k_pool;
+  const void* v_pool;
+  void* out;
+  const void* q;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;  // [num_seqs + 1]
+  int32_t num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
+  int32_t max_blocks_per_seq;
+  float scale;
+};
+// Workgroup tiles per (sequence, KV head) for chunks of up to max_query_len tokens.
+int64_t prefill_tiles(int64_t max_query_len, int64_t group);
+// Whether a prefill kernel exists for this configuration.
+bool prefill_supported(int32_t dtype, int32_t head_dim, int32_t block_size);
+int launch_prefill(const PrefillArgs& a, void* stream);
+
 }  // namespace pkv

@@ -34,7 +34,7 @@ DTYPES: Dict[str, Tuple[type, torch.dtype, int]] = {
 NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
 
 # seed-tuple tags for the different value streams of one workload
-_TAG_CTX_K, _TAG_CTX_V, _TAG_STEP_K, _TAG_STEP_V, _TAG_Q = 1, 2, 3, 4, 5
+_TAG_CTX_K, _TAG_CTX_V, _TAG_STEP_K, _TAG_STEP_V, _TAG_Q, _TAG_PF_Q = 1, 2, 3, 4, 5, 6
 
 
 def _gen_threads() -> int:
@@ -140,6 +140,114 @@ class Workload:
 
     def queries(self) -> np.ndarray:
         return normal_bits((self.seed, _TAG_Q), (self.num_seqs, self.num_q_heads, self.head_dim), self.dtype)
+
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    """One prefill / chunked-prefill batch over a paged pool.
+
+    Replayed by both sides in this order: for each sequence b (ascending) add it with
+    ``context_lens[b]`` tokens and write their K/V (positions 0..L-1) from
+    ``context_kv(b)``; the last ``chunk_lens[b]`` of them are the chunk.  Attention
+    then takes ``queries()`` (the chunks' tokens back to back, ``[T, Hq, D]``).
+    """
+
+    name: str
+    seed: int
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    scale: float
+    free_order: np.ndarray
+    context_lens: np.ndarray
+    chunk_lens: np.ndarray
+    notes: str = ""
+
+    @property
+    def num_seqs(self) -> int:
+        return int(len(self.context_lens))
+
+    @property
+    def elem_bytes(self) -> int:
+        return DTYPES[self.dtype][2]
+
+    def query_start(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.chunk_lens)]).astype(np.int32)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(np.sum(self.chunk_lens))
+
+    @property
+    def max_query_len(self) -> int:
+        return int(np.max(self.chunk_lens)) if len(self.chunk_lens) else 0
+
+    def flops(self) -> int:
+        """2 flops per multiply-add in q.K and in p.V: 4 * Hq * D per visible (row, key) pair."""
+        L = self.context_lens.astype(np.int64)
+        C = self.chunk_lens.astype(np.int64)
+        pairs = int(np.sum(C * (L - C) + C * (C + 1) // 2))
+        return 4 * self.num_q_heads * self.head_dim * pairs
+
+    def kv_bytes(self) -> int:
+        """K+V bytes of every context token once per KV head (each is read at least once)."""
+        return int(2 * int(self.context_lens.sum()) * self.num_kv_heads * self.head_dim * self.elem_bytes)
+
+    def context_kv(self, seq: int) -> Tuple[np.ndarray, np.ndarray]:
+        shape = (int(self.context_lens[seq]), self.num_kv_heads, self.head_dim)
+        return (normal_bits((self.seed, _TAG_CTX_K, seq), shape, self.dtype),
+                normal_bits((self.seed, _TAG_CTX_V, seq), shape, self.dtype))
+
+    def all_context_kv(self, threads: Optional[int] = None) -> Dict[int, Tuple[np.ndarray, np.ndarray]]:
+        threads = threads or _gen_threads()
+        with _cf.ThreadPoolExecutor(threads) as ex:
+            futs = [ex.submit(self.context_kv, b) for b in range(self.num_seqs)]
+            return {b: f.result() for b, f in enumerate(futs)}
+
+    def queries(self) -> np.ndarray:
+        return normal_bits((self.seed, _TAG_PF_Q), (self.num_tokens, self.num_q_heads, self.head_dim), self.dtype)
+
+
+def prefill_workload(name: str, seed: int, dtype: str, context_lens, chunk_lens, hq: int, hkv: int, d: int,
+                     block: int, slack: float = 1.1, notes: str = "") -> PrefillWorkload:
+    """A prefill batch with the given context and chunk lengths; the pool holds
+    ``slack`` times the blocks the batch needs, handed out in a seeded random order."""
+    L = np.asarray(context_lens, dtype=np.int64)
+    C = np.asarray(chunk_lens, dtype=np.int64)
+    if np.any(C > L) or np.any(C < 0):
+        raise ValueError("chunks must lie inside their contexts")
+    rng = np.random.default_rng([seed, 7])
+    need = int(sum(-(-int(x) // block) for x in L))
+    num_blocks = max(1, int(math.ceil(slack * need)))
+    width = int(max(1, max(-(-int(x) // block) for x in L)))
+    return PrefillWorkload(name=name, seed=seed, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                           block_size=block, num_blocks=num_blocks, max_blocks_per_seq=width,
+                           scale=1.0 / math.sqrt(d), free_order=rng.permutation(num_blocks).astype(np.int32),
+                           context_lens=L.astype(np.int32), chunk_lens=C.astype(np.int32), notes=notes)
+
+
+def prefill_bf16(seed: int = 1005, num_seqs: int = 64) -> PrefillWorkload:
+    """Whole-prompt prefill: 64 prompts with lengths from the interview post's request
+    mix (each prompt is its own chunk), 32 q / 8 kv heads, D=128, B=16, bf16."""
+    rng = np.random.default_rng(seed)
+    L = skewed_lengths(rng, num_seqs, 1)
+    return prefill_workload("prefill_bf16", seed, "bf16", L, L, 32, 8, 128, 16,
+                            notes="prompt lengths from the skewed request mix; chunk = whole prompt")
+
+
+def chunked_bf16(seed: int = 1006, num_seqs: int = 16, chunk: int = 512) -> PrefillWorkload:
+    """Chunked prefill: 16 sequences whose earlier tokens (the skewed mix scaled x2, up
+    to 8191) are already cached, each appending a chunk of 512 tokens; 32 q / 8 kv
+    heads, D=128, B=16, bf16."""
+    rng = np.random.default_rng(seed)
+    prefix = skewed_lengths(rng, num_seqs, 2)
+    C = np.full(num_seqs, chunk, dtype=np.int64)
+    return prefill_workload("chunked_bf16", seed, "bf16", prefix + C, C, 32, 8, 128, 16,
+                            notes="cached prefix from the x2 skewed mix, then a 512-token chunk")
 
 
 def _decode_workload(name: str, seed: int, dtype: str, lengths: np.ndarray, hq: int, hkv: int,
@@ -250,5 +358,13 @@ WORKLOADS = {
 }
 
 
-def by_name(name: str, **kw) -> Workload:
+PREFILL_WORKLOADS = {
+    "prefill_bf16": prefill_bf16,
+    "chunked_bf16": chunked_bf16,
+}
+
+
+def by_name(name: str, **kw):
+    if name in PREFILL_WORKLOADS:
+        return PREFILL_WORKLOADS[name](**kw)
     return WORKLOADS[name](**kw)

@@ -129,3 +129,45 @@ def compare(w, got: torch.Tensor, ref: np.ndarray, rows=None):
         assert not bad.any(), f"{bad.sum()} elements out of tolerance, max abs err {err.max()}"
         assert rel.max() < 1e-2, f"relative L2 error {rel.max()}"
     return float(err.max()), float(rel.max())
+
+
+@dataclasses.dataclass
+class PrefillState:
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    tables: torch.Tensor
+    context_lens: torch.Tensor
+    query_start: torch.Tensor
+
+
+def replay_prefill_gpu(w, context, device="cuda", fill_bits=None, free_order=None) -> PrefillState:
+    """Place a prefill workload through the library: every sequence is added with its
+    whole context and its K/V written with ``paged_kv_write``; unowned slots are NaN."""
+    fill_bits = synth.NAN_BITS[w.dtype] if fill_bits is None else fill_bits
+    order = w.free_order if free_order is None else free_order
+    bm = pkv.BlockManager(w.num_blocks, w.block_size, order)
+    kp, vp = pkv.alloc_pools(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, TORCH_DTYPE[w.dtype], device)
+    npi, ti = INT_VIEW[w.dtype]
+    fill = np.array([fill_bits], dtype=np.uint32 if w.dtype == "f32" else np.uint16).view(npi)[0]
+    kp.view(ti).fill_(int(fill))
+    vp.view(ti).fill_(int(fill))
+    for b in range(w.num_seqs):
+        L = int(w.context_lens[b])
+        bm.add_seq(b, L)
+        if L:
+            k, v = context[b]
+            slots = torch.from_numpy(bm.slots(b, 0, L)).to(device)
+            pkv.paged_kv_write(kp, vp, to_device(k, w.dtype, device), to_device(v, w.dtype, device), slots)
+    tables = torch.from_numpy(bm.block_tables(list(range(w.num_seqs)), w.max_blocks_per_seq, 0)).to(device)
+    lens = torch.from_numpy(np.asarray(w.context_lens, dtype=np.int32)).to(device)
+    qs = torch.from_numpy(w.query_start()).to(device)
+    torch.cuda.synchronize()
+    return PrefillState(kp, vp, tables, lens, qs)
+
+
+def run_prefill(w, st: PrefillState, q_bits: np.ndarray, device="cuda") -> torch.Tensor:
+    q = to_device(q_bits, w.dtype, device)
+    out = pkv.paged_attention_prefill(q, st.k_pool, st.v_pool, st.tables, st.context_lens, st.query_start,
+                                      w.max_query_len, w.scale)
+    torch.cuda.synchronize()
+    return out

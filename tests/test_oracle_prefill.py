@@ -166,3 +166,13 @@ def test_rejects_chunk_longer_than_context():
     K, V, pool, tables, qs, q = _case(2, [4], [4], 2, 1, 4, 4)
     with pytest.raises(ValueError):
         paged_attention_prefill(q, "f32", pool, tables, np.asarray([3]), qs, 1.0)
+
+
+def test_sequence_subset_matches_full_result():
+    lengths = [20, 33, 9]
+    chunks = [5, 33, 2]
+    K, V, pool, tables, qs, q = _case(31, lengths, chunks, 4, 2, 8, 8)
+    full = paged_attention_prefill(q, "f32", pool, tables, np.asarray(lengths), qs, 0.5)
+    part = paged_attention_prefill(q, "f32", pool, tables, np.asarray(lengths), qs, 0.5, seqs=[1])
+    np.testing.assert_array_equal(part[qs[1]:qs[2]], full[qs[1]:qs[2]])
+    assert not part[:qs[1]].any() and not part[qs[2]:].any()

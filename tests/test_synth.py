@@ -68,3 +68,19 @@ def test_replayed_pool_holds_each_sequence_context():
         assert (k[:L - 1] == ctx[b][0]).all() and (k[L - 1] == kstep[b]).all()
         v = r.pool.v_at(blocks, j % 16)
         assert (v[:L - 1] == ctx[b][1]).all() and (v[L - 1] == vstep[b]).all()
+
+
+def test_prefill_workloads_are_consistent():
+    import synth
+    for name in synth.PREFILL_WORKLOADS:
+        w = synth.by_name(name)
+        qs = w.query_start()
+        assert qs[0] == 0 and qs[-1] == w.num_tokens and np.all(np.diff(qs) == w.chunk_lens)
+        assert np.all(w.chunk_lens <= w.context_lens) and np.all(w.chunk_lens > 0)
+        need = sum(-(-int(L) // w.block_size) for L in w.context_lens)
+        assert w.num_blocks >= need and sorted(w.free_order.tolist()) == list(range(w.num_blocks))
+        assert w.max_blocks_per_seq * w.block_size >= w.context_lens.max()
+        # flops: 4 * Hq * D per visible (query row, key) pair, counted by brute force on a prefix of the batch
+        L, C = w.context_lens.astype(int), w.chunk_lens.astype(int)
+        pairs = sum(sum(L[b] - C[b] + t + 1 for t in range(C[b])) for b in range(w.num_seqs))
+        assert w.flops() == 4 * w.num_q_heads * w.head_dim * pairs
