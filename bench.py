@@ -11,6 +11,12 @@ Prints one JSON line.  ``value`` is KV GB/s over the whole step (attention's
 algorithmic K+V bytes / step time); ``roofline`` describes the dominant kernel
 (the attention partition pass) against MI355X's 8 TB/s HBM peak; ``cpu_baseline``
 times the fp64 oracle on a bounded sample of the same workload.
+
+With a prefill workload (``--workload prefill_bf16`` or ``chunked_bf16``) a step is
+the KV write of every sequence's chunk followed by the causal chunk attention (its
+plan pass and its attention pass);
+``value`` is attention TFLOP/s over the step and the roofline is the prefill kernel
+against the dense bf16 MFMA peak (2.5 PFLOP/s).
 """
 from __future__ import annotations
 
@@ -28,9 +34,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + decode tokens/sec, 1 GPU"
+PREFILL_METRIC = "paged prefill attention TFLOP/s (% of dense bf16 MFMA peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 PARTITION_TOKENS = 512
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_attention.hip")
+PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_prefill.hip")
 
 
 def log(msg):
@@ -55,16 +64,16 @@ def algorithmic_bytes(w, lens):
             "total": kv + q + out + partials + tables}
 
 
-def stored_traffic(workload):
-    """HBM bytes per launch of the partition kernel from a committed rocprofv3 PMC
-    summary, if its kernel source hash matches the current source; else None."""
-    path = os.path.join(ROOT, "profiles", f"attn_partition_{workload}_pmc.md")
+def stored_traffic(workload, kernel="attn_partition", src=KERNEL_SRC):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 PMC summary, if its
+    kernel source hash matches the current source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if not h or not t or h.group(1) != cur:
         return None
     return float(t.group(1))
@@ -99,6 +108,138 @@ def cpu_baseline(w, ctx, target_s):
             "tokens_per_s": done / el,
             "sample": f"KV write + attention of the first {done} of {w.num_seqs} sequences of the batch "
                       f"({kv_bytes / 1e9:.3f} GB of KV) in {el:.1f} s; fp64 NumPy, BLAS threads {threads}"}
+
+
+def cpu_baseline_prefill(w, ctx, target_s):
+    """The fp64 oracle (as it stands) on a bounded sample of a prefill batch: chunk
+    attention of one sequence at a time, shortest first, until ``target_s`` elapses."""
+    import synth
+    from oracle.attention import paged_attention_prefill as oracle_prefill
+    from oracle.replay import replay_prefill
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    pool, tables, lens = replay_prefill(w, synth.NAN_BITS[w.dtype], context=ctx)
+    q = w.queries()
+    qs = w.query_start()
+    L = np.asarray(w.context_lens, dtype=np.int64)
+    C = np.asarray(w.chunk_lens, dtype=np.int64)
+    done, flops = 0, 0
+    t0 = time.perf_counter()
+    for b in np.argsort(L, kind="stable"):
+        oracle_prefill(q, w.dtype, pool, tables, lens, qs, w.scale, seqs=[int(b)])
+        done += 1
+        flops += 4 * w.num_q_heads * w.head_dim * int(C[b] * (L[b] - C[b]) + C[b] * (C[b] + 1) // 2)
+        if time.perf_counter() - t0 > target_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"chunk attention of the {done} shortest of {w.num_seqs} sequences "
+                      f"({flops / 1e9:.2f} GFLOP) in {el:.1f} s; fp64 NumPy, BLAS threads {threads}"}
+
+
+def prefill_main(args, w, dev):
+    """One prefill step per iteration: the chunks' KV write, then the causal chunk attention."""
+    import torch
+    import paged_kv_cache_281_amd as pkv
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+    npi = np.int16
+    log(f"prefill workload {w.name}: N={w.num_seqs} tokens={w.num_tokens} max_chunk={w.max_query_len} "
+        f"context={int(w.context_lens.sum())} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
+        f"B={w.block_size} {w.dtype}")
+    ctx = w.all_context_kv()
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(npi)).to(dev).view(tdt[w.dtype])
+
+    bm = pkv.BlockManager(w.num_blocks, w.block_size, w.free_order)
+    kp, vp = pkv.alloc_pools(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, tdt[w.dtype], dev)
+    kp.view(torch.int16).fill_(0)
+    vp.view(torch.int16).fill_(0)
+    k_chunk, v_chunk, s_chunk = [], [], []
+    for b in range(w.num_seqs):
+        L, C = int(w.context_lens[b]), int(w.chunk_lens[b])
+        bm.add_seq(b, L)
+        k, v = ctx.pop(b)
+        slots = bm.slots(b, 0, L)
+        if L - C:  # the cached prefix is written once, before the timed steps
+            pkv.paged_kv_write(kp, vp, up(k[:L - C]), up(v[:L - C]), torch.from_numpy(slots[:L - C]).to(dev))
+        k_chunk.append(k[L - C:])
+        v_chunk.append(v[L - C:])
+        s_chunk.append(slots[L - C:])
+    k_new = up(np.concatenate(k_chunk))
+    v_new = up(np.concatenate(v_chunk))
+    slots_d = torch.from_numpy(np.concatenate(s_chunk)).to(dev)
+    tables = torch.from_numpy(bm.block_tables(list(range(w.num_seqs)), w.max_blocks_per_seq, 0)).to(dev)
+    lens = torch.from_numpy(np.asarray(w.context_lens, dtype=np.int32)).to(dev)
+    qs = torch.from_numpy(w.query_start()).to(dev)
+    q = up(w.queries())
+    out = torch.empty_like(q)
+    ws = pkv.alloc_prefill_workspace(w.num_seqs, w.num_tokens, w.num_q_heads, w.num_kv_heads, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(e=None):
+        pkv.paged_kv_write(kp, vp, k_new, v_new, slots_d)
+        if e is not None:
+            e[0].record(stream)
+        pkv.paged_attention_prefill(q, kp, vp, tables, lens, qs, w.max_query_len, w.scale, out, ws)
+        if e is not None:
+            e[1].record(stream)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        pkv.paged_kv_write(kp, vp, k_new, v_new, slots_d)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    write_ms = e0.elapsed_time(e1) / 10
+    log(f"step {ms_step:.4f} ms (prefill attention {attn_ms:.4f}, chunk KV write alone {write_ms:.4f})")
+    flops = w.flops()
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "query_tokens": w.num_tokens, "max_chunk": w.max_query_len,
+                   "context_tokens": int(w.context_lens.sum()), "flops": flops, "kv_bytes": w.kv_bytes()},
+        "tokens_per_s": round(w.num_tokens / (ms_step * 1e-3), 1),
+        "kernel_ms": {"attn_prefill": round(attn_ms, 5), "kv_write_alone": round(write_ms, 5)},
+        "roofline": {"kernel": "attn_prefill_mfma", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": stored_traffic(w.name, "attn_prefill", PREFILL_SRC), "algorithmic_flops": flops},
+    }
+    if not args.no_cpu_baseline:
+        del kp, vp
+        torch.cuda.empty_cache()
+        log("timing the oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline_prefill(w, w.all_context_kv(), args.cpu_seconds)
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -138,6 +279,9 @@ def main():
     ti = {"f32": (np.int32, torch.int32), "f16": (np.int16, torch.int16), "bf16": (np.int16, torch.int16)}
 
     w = synth.by_name(args.workload)
+    if args.workload in synth.PREFILL_WORKLOADS:
+        prefill_main(args, w, dev)
+        return
     log(f"workload {w.name}: N={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
         f"B={w.block_size} {w.dtype} tokens={int(w.context_lens.sum())}")
     t = time.perf_counter()

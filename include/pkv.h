@@ -162,19 +162,28 @@ int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool
  *                 (it sizes the grid).
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; context_lens device
  *                 int32 [num_seqs].
+ *   workspace     device, >= pkv_paged_attention_prefill_workspace_bytes(...),
+ *                 256-byte aligned; contents on entry do not matter.  It holds the
+ *                 (sequence, tile) task list a plan pass builds before the attention
+ *                 pass (longest first; no task for rows a chunk does not have).
  * Accumulation is fp32, the output is rounded to the pool dtype, and the reduction
- * order depends only on logical positions.  No workspace; nothing is allocated.
+ * order depends only on logical positions.  Nothing is allocated.
  * Device preconditions: C_b <= max_query_len; C_b <= context_lens[b] <=
- * max_blocks_per_seq * B; table entries that are read are < num_blocks.  A sequence
- * whose chunk breaks them (longer than its context, or outside q) gets no output rows
- * written; rows past max_query_len are not written.  num_seqs == 0 or num_tokens == 0
- * enqueues nothing.  Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
+ * max_blocks_per_seq * B; chunks do not overlap; table entries that are read are
+ * < num_blocks.  A sequence whose chunk breaks them (longer than its context, or
+ * outside q) gets no output rows written.  num_seqs == 0 or num_tokens == 0 enqueues
+ * nothing.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, LAUNCH.
  */
 int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
                                     void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
                                     const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                    const int32_t* context_lens, float scale, void* stream);
+                                    const int32_t* context_lens, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pkv_paged_attention_prefill needs for these sizes (0 on bad input). */
+size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                                   int32_t num_kv_heads);
 
 /*
  * The two passes of pkv_paged_attention_decode, exposed separately (same arguments,

@@ -74,7 +74,8 @@ def load():
         "pkv_decode_prepare": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp,
                                 _c_vp, _c_sz, _c_vp], _c_i32),
         "pkv_paged_attention_prefill": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
-                                         _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp], _c_i32),
+                                         _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_paged_attention_prefill_workspace_bytes": ([_c_i32, _c_i32, _c_i32, _c_i32], _c_sz),
         "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
         "pkv_bm_destroy": ([_c_vp], None),
         "pkv_bm_add_seq": ([_c_vp, _c_i32, _c_i32], _c_i32),
@@ -207,9 +208,20 @@ def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
     return out
 
 
+def prefill_workspace_bytes(num_seqs: int, num_tokens: int, num_q_heads: int, num_kv_heads: int) -> int:
+    return int(load().pkv_paged_attention_prefill_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads))
+
+
+def alloc_prefill_workspace(num_seqs: int, num_tokens: int, num_q_heads: int, num_kv_heads: int,
+                            device="cuda") -> torch.Tensor:
+    n = prefill_workspace_bytes(num_seqs, num_tokens, num_q_heads, num_kv_heads)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
 def paged_attention_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                             block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
-                            max_query_len: int, scale: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                            max_query_len: int, scale: float, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal attention of each sequence's chunk of new tokens over its paged context.
 
     ``q`` is ``[T, Hq, D]`` with sequence b's chunk in rows ``query_start[b] ..
@@ -233,10 +245,12 @@ def paged_attention_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
         out = torch.empty_like(q)
     _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous() and out.device == q.device,
              "out must match q")
+    if workspace is None:
+        workspace = alloc_prefill_workspace(N, T, Hq, d.num_kv_heads, q.device)
     _check(load().pkv_paged_attention_prefill(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq,
                                               _ptr(query_start), T, int(max_query_len), _ptr(block_tables),
                                               block_tables.shape[1], _ptr(context_lens), float(scale),
-                                              _stream(q.device)))
+                                              _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out
 
 

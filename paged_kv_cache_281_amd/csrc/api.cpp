@@ -276,11 +276,18 @@ int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool
                                         max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes, stream);
 }
 
+size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                                   int32_t num_kv_heads) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return 0;
+  return pkv::prefill_workspace_bytes(num_tokens, num_seqs, num_q_heads / num_kv_heads);
+}
+
 int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
                                     void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
                                     const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                    const int32_t* context_lens, float scale, void* stream) {
+                                    const int32_t* context_lens, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   const char* who = "pkv_paged_attention_prefill";
   char buf[256];
   int32_t st = pkv::check_pool(pool, who);
@@ -302,8 +309,8 @@ int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_poo
   }
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
   const int group = num_q_heads / pool->num_kv_heads;
-  const int64_t grid = pkv::prefill_tiles(max_query_len, group) * num_seqs * pool->num_kv_heads;
-  if (grid > 0x7fffffff || static_cast<int64_t>(num_tokens) * num_q_heads * pool->head_dim > (int64_t{1} << 40)) {
+  const int64_t grid = pkv::prefill_task_bound(num_tokens, num_seqs, group, 64) * pool->num_kv_heads;
+  if (grid > 0x7fffffff || static_cast<int64_t>(num_tokens) * num_q_heads > 0x7fffffff) {
     std::snprintf(buf, sizeof(buf), "%s: problem too large for one launch", who);
     return pkv::set_error(PKV_ERR_UNSUPPORTED, buf);
   }
@@ -316,7 +323,14 @@ int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_poo
     std::snprintf(buf, sizeof(buf), "%s: misaligned pointer (pools, q, out need 16 bytes)", who);
     return pkv::set_error(PKV_ERR_INVALID_ARG, buf);
   }
+  const size_t need = pkv::prefill_workspace_bytes(num_tokens, num_seqs, group);
+  if (workspace_bytes < need || !workspace || !pkv::aligned(workspace, 256)) {
+    std::snprintf(buf, sizeof(buf), "%s: workspace of %zu bytes (256-byte aligned) needed, got %zu", who, need,
+                  workspace_bytes);
+    return pkv::set_error(PKV_ERR_WORKSPACE, buf);
+  }
   pkv::PrefillArgs a;
+  a.workspace = workspace;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.out = out;

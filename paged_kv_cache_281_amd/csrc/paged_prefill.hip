@@ -11,24 +11,30 @@
 // position p = L_b - C_b + t and attends to positions 0..p.
 //
 // Work split.  The rows of the problem are (query token, query head) pairs of one KV
-// head, token-major: row = t * G + g.  A workgroup (4 waves) owns ROWS consecutive
-// rows of one (sequence, KV head); each wave owns RG groups of 16 rows and walks the
-// 16-token units of K/V from position 0 up to the last position its rows can see,
-// with two register buffers (the next unit's loads are in flight while the current
-// one is computed).  Waves are independent: no LDS, no barriers.
+// head, token-major: row = t * G + g.  A workgroup (4 waves) owns a tile of 64 * RG
+// consecutive rows of one (sequence, KV head), RG = 2 for chunks that fill whole
+// tiles and 1 for short ones.  A one-workgroup plan pass lists the (sequence, tile)
+// tasks that exist, those reading the most K/V first.
+// The workgroup walks 32-token units of K/V (one 32-token block or two 16-token
+// blocks) from position 0 up to the last position its rows can see.  All 256 threads
+// copy each unit from the pool into an LDS double buffer, issuing the next unit's
+// loads before the current one is computed, with one barrier per unit; each wave
+// reads the unit's fragments once and uses them for all of its RG groups of 16 rows.
 //
-// Products (16x16x32 and 16x16x16 bf16/fp16 MFMA, fp32 accumulate), per 16 rows:
+// Products (16x16x32 bf16/fp16 MFMA, fp32 accumulate), per 16 rows:
 //   S^T[token][row] = K[token][:] . Q[row][:]   (K fragment as A, Q^T as B)
 //   O^T[d][row]    += V^T[d][token] P^T[token][row]
-// The score accumulator's register layout (lane (r, m) holds tokens 4r..4r+3 of row m)
-// is the B operand of the P.V product as it stands, rounded to the pool type.  The
-// fragments are the decode kernel's: K chunk (4i + r) of token m, and V row (16c + m)
-// at tokens 4r..4r+3 of the transposed V tile.
+// The scores come from two chains whose A rows are the tokens
+// tau_s(i) = 8*(i/4) + 4*s + i%4 (s = 0, 1), so lane (r, m) holds the scores of
+// tokens 8r..8r+7 of row m: after the softmax, rounded to the pool type, they are the
+// B operand of the P.V product as they stand, and its A operand (V^T) is 16
+// contiguous bytes of a V row.
 //
 // Masking: a score is kept when its token is <= the row's position (a select, so a
-// NaN in a masked slot never propagates), and V elements of tokens past the context
-// are zeroed before they meet p = 0.  Every row sees token 0, so each row's running
-// max is finite after the first unit.
+// NaN in a masked slot never propagates; applied only on units that reach past a
+// wave's first position), and V elements of tokens past the context are zeroed before
+// they meet p = 0.  Every row sees token 0, so each row's running max is finite after
+// the first unit.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -41,11 +47,13 @@ constexpr int kPfWaves = 4;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr float kPfRescaleLog2 = 8.f;  // lazy rescale threshold (log2 units)
 
-#ifndef PKV_PREFILL_RG
-#define PKV_PREFILL_RG 2
+// Row groups (16 rows each) per wave: kRGBig when the chunks fill whole workgroup
+// tiles, 1 for short chunks (fewer idle rows).
+#ifndef PKV_PREFILL_RG_BIG
+#define PKV_PREFILL_RG_BIG 2
 #endif
-constexpr int kRG = PKV_PREFILL_RG;              // 16-row groups per wave
-constexpr int kTileRows = 16 * kRG * kPfWaves;   // rows per workgroup
+constexpr int kRGBig = PKV_PREFILL_RG_BIG;
+constexpr int kRGSmall = 1;
 
 struct PrefillParams {
   const char* q;
@@ -55,47 +63,139 @@ struct PrefillParams {
   const int* tables;
   const int* ctx;
   const int* qstart;
-  int N, T, Hq, Hkv, G, W, Lmax, ntiles;
+  int2* tasks;    // (sequence, tile) tasks, most units first (plan pass)
+  int* counters;  // counters[0] = number of tasks
+  int N, T, Hq, Hkv, G, W, Lmax, rows, cap;
   float scale_log2;
 };
 
+// Chunk geometry of sequence b, or false when its chunk is empty or breaks the
+// contract (longer than its context, or outside q).
+__device__ __forceinline__ bool chunk_of(const PrefillParams& P, int b, int& q0, int& C, int& L) {
+  q0 = P.qstart[b];
+  C = P.qstart[b + 1] - q0;
+  L = min(max(P.ctx[b], 0), P.Lmax);
+  return C > 0 && C <= L && q0 >= 0 && q0 <= P.T - C;
+}
+
+// 32-token units a tile of `rows` rows reads: up to its last row's position.
+__device__ __forceinline__ int tile_units(const PrefillParams& P, int C, int L, int tile) {
+  const int last = (L - C) + min(C * P.G - 1, (tile + 1) * P.rows - 1) / P.G;
+  return (last + 1 + 31) >> 5;
+}
+
+// ---------------------------------------------------------------------------------
+// Plan (one workgroup): lists every (sequence, tile) task, most units first, so the
+// long tiles start early and short ones fill in at the end; no task is listed for
+// rows a chunk does not have.  Tasks are bucketed by unit count (counts of
+// kPlanBuckets - 1 and more share the top bucket); the order within a bucket depends
+// on timing, and no result depends on the order.
+// ---------------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan(PrefillParams P) {
+  __shared__ int cnt[kPlanBuckets];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  for (int b = tid; b < P.N; b += kPlanThreads) {
+    int q0, C, L;
+    if (!chunk_of(P, b, q0, C, L)) continue;
+    const int ntile = (C * P.G + P.rows - 1) / P.rows;
+    for (int t = 0; t < ntile; ++t) atomicAdd(&cnt[kPlanBuckets - 1 - min(tile_units(P, C, L, t), kPlanBuckets - 1)], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the bucket counts (bucket 0 = most units)
+  int v = cnt[tid];
+  for (int d = 1; d < kPlanBuckets; d <<= 1) {
+    __syncthreads();
+    const int add = tid >= d ? cnt[tid - d] : 0;
+    __syncthreads();
+    cnt[tid] += add;
+  }
+  __syncthreads();
+  if (tid == kPlanBuckets - 1) P.counters[0] = min(cnt[tid], P.cap);
+  cnt[tid] -= v;  // exclusive offsets
+  __syncthreads();
+  for (int b = tid; b < P.N; b += kPlanThreads) {
+    int q0, C, L;
+    if (!chunk_of(P, b, q0, C, L)) continue;
+    const int ntile = (C * P.G + P.rows - 1) / P.rows;
+    for (int t = 0; t < ntile; ++t) {
+      const int slot = atomicAdd(&cnt[kPlanBuckets - 1 - min(tile_units(P, C, L, t), kPlanBuckets - 1)], 1);
+      if (slot < P.cap) P.tasks[slot] = make_int2(b, t);  // overlapping chunks could overflow the bound
+    }
+  }
+}
+
+// The 4 waves of a workgroup share each 32-token K/V unit.  All
+// 256 threads copy the next unit from the pool into an LDS double buffer (its global
+// loads are issued before the current unit is computed), one barrier per unit.  K is
+// stored as [chunk][half s][m] 16-byte pieces, where slot (s, m) holds token tau_s(m),
+// so the 16 lanes of a fragment read touch 256 contiguous bytes; V rows (32 tokens,
+// 64 bytes) are padded to 80 bytes so the 16 rows of a fragment read fall in distinct
+// banks.  Each wave reads its fragments for the unit once and uses them for all RG of
+// its 16-row groups.
+template <int D>
+struct PrefillSmem {
+  static constexpr int kChunks = D / 8;  // 16-byte K chunks per token
+  static constexpr int kVRow = 80;       // bytes per padded V row
+  static constexpr int kKBytes = kChunks * 32 * 16;
+  static constexpr int kBytes = kKBytes + D * kVRow;
+  char buf[2][kBytes];
+};
+
 template <class T, int D, int B, int RG>
-__global__ __launch_bounds__(kPfThreads) void attn_prefill_mfma(PrefillParams P) {
+__global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) {
   constexpr int EB = T::kBytes;
   static_assert(EB == 2, "MFMA path is for 16-bit pools");
-  constexpr int KI = D / 32;   // 16x16x32 steps over head_dim
-  constexpr int NC = D / 16;   // 16x16x16 products per unit (16 d each)
-  constexpr int SUB = B / 16;  // 16-token units per block
+  constexpr int KI = D / 32;
+  constexpr int NC = D / 16;
+  constexpr int BPU = 32 / B;
+  constexpr int ROWS = 16 * RG * kPfWaves;
+  constexpr int CH = PrefillSmem<D>::kChunks;
+  constexpr int VROW = PrefillSmem<D>::kVRow;
+  constexpr int KB = PrefillSmem<D>::kKBytes;
+  constexpr int KPIECES = CH * 32;   // 16-byte K pieces per unit
+  constexpr int VPIECES = D * 4;     // 16-byte V pieces per unit
+  constexpr int KPT = KPIECES / kPfThreads;  // per thread
+  constexpr int VPT = VPIECES / kPfThreads;
+  static_assert(KPIECES % kPfThreads == 0 && VPIECES % kPfThreads == 0, "pieces must divide evenly");
   constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
   typedef typename T::Bits Bits;
-  struct Buf {
-    u32x4 k[KI];
-    u32x2 v[NC];
-  };
+  __shared__ PrefillSmem<D> sm;
 
-  // Tiles holding the latest tokens (the most work) are launched first; KV heads
-  // vary fastest, so with 8 KV heads each XCD serves one head's K/V from its L2.
+  // task t = blockIdx / Hkv from the plan's list (longest first); KV heads vary
+  // fastest, so with 8 KV heads each XCD serves one head's K/V from its L2
   const int kvh = blockIdx.x % P.Hkv;
-  const int rest = blockIdx.x / P.Hkv;
-  const int b = rest % P.N;
-  const int tile = P.ntiles - 1 - rest / P.N;
-  const int q0 = P.qstart[b];
-  const int C = P.qstart[b + 1] - q0;
-  const int L = min(max(P.ctx[b], 0), P.Lmax);
-  // a chunk must lie inside q and inside its context; anything else writes nothing
-  if (C <= 0 || C > L || q0 < 0 || q0 > P.T - C) return;
+  const int t = blockIdx.x / P.Hkv;
+  // workgroup-uniform exits only (the unit loop has barriers)
+  if (t >= P.counters[0]) return;
+  const int2 task = P.tasks[t];
+  const int b = task.x;
+  const int tile = task.y;
+  if (b < 0 || b >= P.N || tile < 0) return;  // only a list left by the plan pass is valid
+  int q0, C, L;
+  if (!chunk_of(P, b, q0, C, L)) return;
   const int nrows = C * P.G;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wrow0 = tile * kTileRows + w * 16 * RG;
-  if (wrow0 >= nrows) return;  // no barriers in this kernel: an idle wave may leave
+  const int row0 = tile * ROWS;
+  if (row0 >= nrows) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;
   const int m = lane & 15;
   const int prefix = L - C;
-  const int t_last = min(nrows - 1, wrow0 + 16 * RG - 1) / P.G;
-  const int nunits = (prefix + t_last + 1 + 15) >> 4;  // units up to the last visible position
+  const int wg_last = prefix + min(nrows - 1, row0 + ROWS - 1) / P.G;
+  const int nunits = (wg_last + 1 + 31) >> 5;
+  const int nblk = (L + B - 1) / B;
+  const int wrow0 = row0 + w * 16 * RG;
+  const bool wave_rows = wrow0 < nrows;  // a wave past the chunk still copies and waits
+  const int wrow_c = wave_rows ? wrow0 : row0;
+  const int w_first = prefix + wrow_c / P.G;
+  const int w_last = prefix + min(nrows - 1, wrow_c + 16 * RG - 1) / P.G;
 
-  // this lane's row in each group (rows past the chunk compute on a valid row and are not stored)
   int pos[RG];
   int64_t orow[RG];
   bool store[RG];
@@ -104,7 +204,7 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_mfma(PrefillParams P)
   for (int k = 0; k < RG; ++k) {
     const int row = wrow0 + 16 * k + m;
     store[k] = row < nrows;
-    const int rr = store[k] ? row : wrow0;
+    const int rr = store[k] ? row : wrow_c;
     const int t = rr / P.G;
     const int g = rr - t * P.G;
     pos[k] = prefix + t;
@@ -114,84 +214,182 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_mfma(PrefillParams P)
     for (int ki = 0; ki < KI; ++ki) qf[k][ki] = *reinterpret_cast<const u32x4*>(qrow + (4 * ki + r) * 16);
   }
 
+  // this thread's pieces of every unit: K piece i = tid + 256 x -> chunk i / 32, slot i % 32
+  // (slot = 16 s + mm holds token tau_s(mm)); V piece i -> row i / 4, tokens 8 (i % 4) ..
   const int* trow = P.tables + static_cast<int64_t>(b) * P.W;
+  const int64_t bstride = static_cast<int64_t>(P.Hkv) * TILE;
   const char* kbase = P.kp + kvh * TILE;
   const char* vbase = P.vp + kvh * TILE;
-  const int64_t bstride = static_cast<int64_t>(P.Hkv) * TILE;
-  const int koff = (r * B + m) * 16;      // + ki * 4 * B * 16 + sub * 256
-  const int voff = (m * B + 4 * r) * EB;  // + c * 16 * B * EB + sub * 16 * EB
-
-  // K/V are re-read by every tile of the sequence: ordinary (cached) loads
-  auto load = [&](int u, Buf& f) {
-    const int e = u / SUB;
-    const int blk = trow[e];  // uniform: a scalar load
-    const int sub = u - e * SUB;
-    const char* kt = kbase + blk * bstride + sub * 256;
-    const char* vt = vbase + blk * bstride + sub * 16 * EB;
+  int kg_off[KPT], kl_off[KPT], vg_off[VPT], vl_off[VPT];
+  bool kg_hi[KPT], vg_hi[VPT];  // (16-token blocks) piece comes from the unit's second block
 #pragma unroll
-    for (int ki = 0; ki < KI; ++ki) f.k[ki] = *reinterpret_cast<const u32x4*>(kt + koff + ki * 4 * B * 16);
+  for (int x = 0; x < KPT; ++x) {
+    const int i = tid + kPfThreads * x;
+    const int c = i >> 5;
+    const int slot = i & 31;
+    const int ss = slot >> 4;
+    const int mm = slot & 15;
+    const int tok = 8 * (mm >> 2) + 4 * ss + (mm & 3);
+    kg_hi[x] = BPU == 2 && tok >= 16;
+    kg_off[x] = (c * B + (BPU == 2 ? (tok & 15) : tok)) * 16;
+    kl_off[x] = (c * 32 + slot) * 16;
+  }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) f.v[c] = *reinterpret_cast<const u32x2*>(vt + voff + c * 16 * B * EB);
+  for (int x = 0; x < VPT; ++x) {
+    const int i = tid + kPfThreads * x;
+    const int d = i >> 2;
+    const int qq = i & 3;
+    vg_hi[x] = BPU == 2 && qq >= 2;
+    vg_off[x] = (d * B + 8 * (BPU == 2 ? (qq & 1) : qq)) * EB;
+    vl_off[x] = KB + d * VROW + qq * 16;
+  }
+  struct Stage {
+    u32x4 k[KPT];
+    u32x4 v[VPT];
+  };
+  auto fetch = [&](int u, Stage& st) {
+    const int e0 = u * BPU;
+    const int blk0 = trow[e0];  // uniform: scalar loads
+    const int blk1 = BPU == 2 ? trow[min(e0 + 1, nblk - 1)] : blk0;  // absent second block: reuse the first
+    const char* k0 = kbase + blk0 * bstride;
+    const char* v0 = vbase + blk0 * bstride;
+    const char* k1 = kbase + blk1 * bstride;
+    const char* v1 = vbase + blk1 * bstride;
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) st.k[x] = *reinterpret_cast<const u32x4*>((kg_hi[x] ? k1 : k0) + kg_off[x]);
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) st.v[x] = *reinterpret_cast<const u32x4*>((vg_hi[x] ? v1 : v0) + vg_off[x]);
+  };
+  auto deposit = [&](int bi, const Stage& st) {
+    char* base = sm.buf[bi];
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) *reinterpret_cast<u32x4*>(base + kl_off[x]) = st.k[x];
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) *reinterpret_cast<u32x4*>(base + vl_off[x]) = st.v[x];
   };
 
-  float m_run[RG], l_part[RG];
+  float m_run[RG], l_run[RG];
   f32x4 o[RG][NC];
 #pragma unroll
   for (int k = 0; k < RG; ++k) {
     m_run[k] = kNegInf;
-    l_part[k] = 0.f;
+    l_run[k] = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) o[k][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const float cs = P.scale_log2;
 
-  auto compute = [&](int u, Buf& f) {
-    const int j0 = 16 * u + 4 * r;  // token of this lane's first score
-    if (16 * u + 16 > L) {          // tokens past the context: zero V
-      const u32 mlo = (j0 + 0 < L ? 0x0000ffffu : 0u) | (j0 + 1 < L ? 0xffff0000u : 0u);
-      const u32 mhi = (j0 + 2 < L ? 0x0000ffffu : 0u) | (j0 + 3 < L ? 0xffff0000u : 0u);
+  auto compute = [&](int u, int bi) {
+    const char* base = sm.buf[bi];
+    u32x4 kf[2][KI], vf[NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        f.v[c][0] &= mlo;
-        f.v[c][1] &= mhi;
-      }
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int ki = 0; ki < KI; ++ki)
+        kf[s2][ki] = *reinterpret_cast<const u32x4*>(base + ((4 * ki + r) * 32 + 16 * s2 + m) * 16);
     }
 #pragma unroll
-    for (int k = 0; k < RG; ++k) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c) vf[c] = *reinterpret_cast<const u32x4*>(base + KB + (16 * c + m) * VROW + r * 16);
+    const int j0 = 32 * u + 8 * r;
+    if (32 * u + 32 > L) {  // tokens past the context: zero V
 #pragma unroll
-      for (int ki = 0; ki < KI; ++ki) acc = T::mfma_k32(f.k[ki], qf[k][ki], acc);
-      float s[4];
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32 msk = (j0 + 2 * kk < L ? 0x0000ffffu : 0u) | (j0 + 2 * kk + 1 < L ? 0xffff0000u : 0u);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[j] = (j0 + j <= pos[k]) ? acc[j] * P.scale_log2 : kNegInf;
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = max_xor16(mx);
-      mx = max_xor32(mx);
-      if (wave_any(mx > m_run[k] + kPfRescaleLog2)) {
-        const float mn = fmaxf(m_run[k], mx);
-        const float alpha = fast_exp2(m_run[k] - mn);
-        l_part[k] *= alpha;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) o[k][c] *= alpha;
-        m_run[k] = mn;
+        for (int c = 0; c < NC; ++c) vf[c][kk] &= msk;
       }
-      const u32 p01 = T::pack2(fast_exp2(s[0] - m_run[k]), fast_exp2(s[1] - m_run[k]));
-      const u32 p23 = T::pack2(fast_exp2(s[2] - m_run[k]), fast_exp2(s[3] - m_run[k]));
-      l_part[k] += (T::lo(p01) + T::hi(p01)) + (T::lo(p23) + T::hi(p23));
-      const u32x2 pb = {p01, p23};
+    }
+    const bool diag = 32 * u + 31 > w_first;
+    // scores of every group: independent MFMA chains, interleaved
+    f32x4 acc[RG][2];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) o[k][c] = T::mfma_k16(f.v[c], pb, o[k][c]);
+    for (int k = 0; k < RG; ++k) {
+      acc[k][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ki = 0; ki < KI; ++ki) {
+#pragma unroll
+      for (int k = 0; k < RG; ++k) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) acc[k][s2] = T::mfma_k32(kf[s2][ki], qf[k][ki], acc[k][s2]);
+      }
+    }
+    float sc[RG][8];  // raw scores of tokens 8r + e, e = 4 s + j
+#pragma unroll
+    for (int k = 0; k < RG; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc[k][e] = acc[k][e >> 2][e & 3];
+    }
+    if (diag) {
+#pragma unroll
+      for (int k = 0; k < RG; ++k) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[k][e] = (j0 + e <= pos[k]) ? sc[k][e] : kNegInf;
+      }
+    }
+    float mx[RG];
+    bool grow = false;
+#pragma unroll
+    for (int k = 0; k < RG; ++k) {
+      float v = fmaxf(fmaxf(fmaxf(sc[k][0], sc[k][1]), fmaxf(sc[k][2], sc[k][3])),
+                      fmaxf(fmaxf(sc[k][4], sc[k][5]), fmaxf(sc[k][6], sc[k][7])));
+      v = max_xor16(v);
+      mx[k] = max_xor32(v) * cs;  // scale > 0: the max of the scaled scores
+      grow = grow || (mx[k] > m_run[k] + kPfRescaleLog2);
+    }
+    if (wave_any(grow)) {  // rare: some row's max rose by more than the threshold
+#pragma unroll
+      for (int k = 0; k < RG; ++k) {
+        if (wave_any(mx[k] > m_run[k] + kPfRescaleLog2)) {
+          const float mn = fmaxf(m_run[k], mx[k]);
+          const float alpha = fast_exp2(m_run[k] - mn);
+          l_run[k] *= alpha;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) o[k][c] *= alpha;
+          m_run[k] = mn;
+        }
+      }
+    }
+    u32x4 pb[RG];
+#pragma unroll
+    for (int k = 0; k < RG; ++k) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(sc[k][e], cs, -m_run[k]));
+      l_run[k] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) pb[k][kk] = T::pack2(p[2 * kk], p[2 * kk + 1]);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int k = 0; k < RG; ++k) o[k][c] = T::mfma_k32(vf[c], pb[k], o[k][c]);
     }
   };
 
-  Buf first;
-  load(0, first);
-  PKV_FENCE();
-  pipeline2<1, Buf>(0, nunits, first, load, compute);
+  // Unit u is computed from LDS buffer u % 2 while unit u + 1 waits in registers and
+  // unit u + 2 is being loaded: each unit's loads have two units of compute to land.
+  Stage s0, s1;
+  auto step = [&](int u, Stage& cur, Stage& nxt) {
+    // on entry `cur` is free and `nxt` holds unit u + 1 (if any)
+    if (u + 2 < nunits) fetch(u + 2, cur);
+    if (wave_rows && 32 * u <= w_last) compute(u, u & 1);  // units this wave's rows can see
+    if (u + 1 < nunits) deposit((u + 1) & 1, nxt);
+    __syncthreads();
+  };
+  fetch(0, s0);
+  if (nunits > 1) fetch(1, s1);
+  deposit(0, s0);
+  __syncthreads();
+  for (int u = 0; u < nunits; u += 2) {
+    step(u, s0, s1);
+    if (u + 1 < nunits) step(u + 1, s1, s0);
+  }
 
-  // lane (r, m) holds O^T[16c + 4r + j][row m]: four consecutive d per store
 #pragma unroll
   for (int k = 0; k < RG; ++k) {
-    float l = sum_xor16(l_part[k]);
+    float l = sum_xor16(l_run[k]);
     l = sum_xor32(l);
     const float inv = 1.f / l;
     if (store[k]) {
@@ -207,6 +405,18 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_mfma(PrefillParams P)
   }
 }
 
+template <class T, int D, int B, int RG>
+int launch_prefill_rg(const PrefillArgs& a, PrefillParams P, hipStream_t s) {
+  P.rows = 16 * RG * kPfWaves;
+  P.cap = static_cast<int>(prefill_task_bound(a.num_tokens, a.num_seqs, P.G, P.rows));
+  hipLaunchKernelGGL(prefill_plan, dim3(1), dim3(kPlanThreads), 0, s, P);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return static_cast<int>(e);
+  const int64_t grid = static_cast<int64_t>(P.cap) * P.Hkv;
+  hipLaunchKernelGGL((attn_prefill_lds<T, D, B, RG>), dim3(static_cast<unsigned>(grid)), dim3(kPfThreads), 0, s, P);
+  return static_cast<int>(hipGetLastError());
+}
+
 template <class T, int D, int B>
 int launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   PrefillParams P;
@@ -217,6 +427,8 @@ int launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   P.tables = a.block_tables;
   P.ctx = a.context_lens;
   P.qstart = a.query_start;
+  P.counters = static_cast<int*>(a.workspace);
+  P.tasks = reinterpret_cast<int2*>(static_cast<char*>(a.workspace) + kPrefillCounterBytes);
   P.N = a.num_seqs;
   P.T = a.num_tokens;
   P.Hq = a.num_q_heads;
@@ -224,12 +436,12 @@ int launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   P.G = a.num_q_heads / a.num_kv_heads;
   P.W = a.max_blocks_per_seq;
   P.Lmax = a.max_blocks_per_seq * a.block_size;
-  P.ntiles = static_cast<int>(prefill_tiles(a.max_query_len, P.G));
+  P.rows = 0;
+  P.cap = 0;
   P.scale_log2 = a.scale * kLog2e;
-  const int64_t grid = static_cast<int64_t>(P.ntiles) * P.N * P.Hkv;
-  hipLaunchKernelGGL((attn_prefill_mfma<T, D, B, kRG>), dim3(static_cast<unsigned>(grid)), dim3(kPfThreads), 0, s,
-                     P);
-  return static_cast<int>(hipGetLastError());
+  if (static_cast<int64_t>(a.max_query_len) * P.G >= 16 * kRGBig * kPfWaves)
+    return launch_prefill_rg<T, D, B, kRGBig>(a, P, s);
+  return launch_prefill_rg<T, D, B, kRGSmall>(a, P, s);
 }
 
 template <class T>
@@ -240,8 +452,14 @@ int launch_prefill_d(const PrefillArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int64_t prefill_tiles(int64_t max_query_len, int64_t group) {
-  return (max_query_len * group + kTileRows - 1) / kTileRows;
+int64_t prefill_task_bound(int64_t num_tokens, int64_t num_seqs, int64_t group, int64_t tile_rows) {
+  // sum_b ceil(C_b G / rows) <= T G / rows + N
+  return (num_tokens * group + tile_rows - 1) / tile_rows + num_seqs;
+}
+
+size_t prefill_workspace_bytes(int64_t num_tokens, int64_t num_seqs, int64_t group) {
+  return kPrefillCounterBytes +
+         static_cast<size_t>(prefill_task_bound(num_tokens, num_seqs, group, 16 * kRGSmall * kPfWaves)) * 8;
 }
 
 bool prefill_supported(int32_t dtype, int32_t head_dim, int32_t block_size) {

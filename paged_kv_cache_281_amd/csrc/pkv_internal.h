@@ -84,12 +84,17 @@ struct PrefillArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* query_start;  // [num_seqs + 1]
+  void* workspace;             // prefill_workspace_bytes(...) bytes, 256-byte aligned
   int32_t num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
   int32_t max_blocks_per_seq;
   float scale;
 };
-// Workgroup tiles per (sequence, KV head) for chunks of up to max_query_len tokens.
-int64_t prefill_tiles(int64_t max_query_len, int64_t group);
+// Prefill workspace: a 256-byte counter block, then the (sequence, tile) task list.
+constexpr size_t kPrefillCounterBytes = 256;
+// Upper bound on the (sequence, tile) tasks of a batch with tiles of tile_rows rows.
+int64_t prefill_task_bound(int64_t num_tokens, int64_t num_seqs, int64_t group, int64_t tile_rows);
+// Workspace bytes a prefill launch needs (for the smallest tile).
+size_t prefill_workspace_bytes(int64_t num_tokens, int64_t num_seqs, int64_t group);
 // Whether a prefill kernel exists for this configuration.
 bool prefill_supported(int32_t dtype, int32_t head_dim, int32_t block_size);
 int launch_prefill(const PrefillArgs& a, void* stream);

@@ -92,3 +92,35 @@ def test_block_manager_errors(pkv_lib):
     with pytest.raises(pkv_lib.PkvError):
         pkv_lib.BlockManager(4, 16, [0, 1, 1, 2])
     assert bm.refcount(99) == -1
+
+
+def test_prefill_host_side_errors(pkv_lib):
+    lib = pkv_lib.load()
+    P = pkv_lib.PoolDesc
+    fake = ctypes.c_void_p(0x1000)
+    d = ctypes.byref(P(64, 16, 8, 128, 2))
+    args = lambda **kw: dict(dict(k=fake, v=fake, out=fake, q=fake, n=2, hq=32, qs=fake, t=10, mq=8, tab=fake, w=4,
+                                  lens=fake, ws=fake, wsb=1 << 20), **kw)
+
+    def call(desc, **kw):
+        a = args(**kw)
+        return lib.pkv_paged_attention_prefill(desc, a["k"], a["v"], a["out"], a["q"], a["n"], a["hq"], a["qs"],
+                                               a["t"], a["mq"], a["tab"], a["w"], a["lens"], 0.1, a["ws"],
+                                               a["wsb"], None)
+
+    assert call(None) == 1 and b"null pool" in lib.pkv_last_error()
+    assert call(d, hq=12) == 1 and b"multiple" in lib.pkv_last_error()
+    # fp32 pools have no prefill kernel
+    assert call(ctypes.byref(P(64, 16, 8, 128, 0))) == 2 and b"bf16/fp16" in lib.pkv_last_error()
+    assert call(d, qs=None) == 1 and b"null pointer" in lib.pkv_last_error()
+    assert call(d, q=ctypes.c_void_p(0x1008)) == 1 and b"misaligned" in lib.pkv_last_error()
+    assert call(d, n=-1) == 1
+    # workspace: a 256-byte counter block, then 8 bytes per task of the bound
+    # ceil(T * G / 64) + N (T = 10 tokens, G = 4, N = 2 -> 3 tasks)
+    assert lib.pkv_paged_attention_prefill_workspace_bytes(2, 10, 32, 8) == 256 + 8 * 3
+    assert lib.pkv_paged_attention_prefill_workspace_bytes(2, 10, 12, 8) == 0
+    assert call(d, wsb=256 + 8 * 3 - 1) == 3 and b"workspace" in lib.pkv_last_error()
+    assert call(d, ws=ctypes.c_void_p(0x1010)) == 3
+    # nothing to do: no launch, no pointer checks
+    assert call(d, n=0, k=None, v=None, out=None, q=None, qs=None, tab=None, lens=None) == 0
+    assert call(d, t=0, k=None, v=None, out=None, q=None, qs=None, tab=None, lens=None) == 0
