@@ -25,8 +25,9 @@ int launch_kv_write(const pkv_pool_desc& pool, void* k_pool, void* v_pool, const
                     const void* v_new, const int64_t* slots, int32_t num_tokens, void* stream) {
   const int eb = elem_bytes(pool.dtype);
   const int X = 16 / eb;
-  const int64_t per_token = static_cast<int64_t>(pool.num_kv_heads) * (pool.head_dim / X);
-  const int64_t max_tokens = std::max<int64_t>(1, kMaxWriteItems / per_token);
+  const int64_t per_token = static_cast<int64_t>(pool.num_kv_heads) * (pool.head_dim / X);  // items per token
+  // tokens per launch: a multiple of X, so every launch starts a whole V item
+  const int64_t max_tokens = std::max<int64_t>(X, kMaxWriteItems / per_token / X * X);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t row_bytes = static_cast<int64_t>(pool.num_kv_heads) * pool.head_dim * eb;
   for (int64_t t0 = 0; t0 < num_tokens; t0 += max_tokens) {
@@ -37,7 +38,9 @@ int launch_kv_write(const pkv_pool_desc& pool, void* k_pool, void* v_pool, const
     a.k_new = static_cast<const char*>(k_new) + t0 * row_bytes;
     a.v_new = static_cast<const char*>(v_new) + t0 * row_bytes;
     a.slots = slots + t0;
-    a.total = nt * per_token;
+    a.tokens = nt;
+    a.total = eb == 4 ? kv_write_items<4>(nt, pool.num_kv_heads, pool.head_dim)
+                      : kv_write_items<2>(nt, pool.num_kv_heads, pool.head_dim);
     a.H = pool.num_kv_heads;
     a.D = pool.head_dim;
     a.B = pool.block_size;

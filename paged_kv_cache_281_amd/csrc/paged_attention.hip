@@ -1084,7 +1084,8 @@ int launch_decode_prepare(const AttnArgs& a, const pkv_pool_desc& pool, void* k_
                           const void* k_new, const void* v_new, const int64_t* slots, int32_t num_tokens,
                           void* stream) {
   const int eb = elem_bytes(pool.dtype);
-  const int64_t total = static_cast<int64_t>(num_tokens) * pool.num_kv_heads * (pool.head_dim / (16 / eb));
+  const int64_t total = eb == 4 ? kv_write_items<4>(num_tokens, pool.num_kv_heads, pool.head_dim)
+                                : kv_write_items<2>(num_tokens, pool.num_kv_heads, pool.head_dim);
   if (total > kMaxWriteItems) {  // very large writes: two launches
     const int rc = launch_attn_plan(a, stream);
     return rc ? rc : launch_kv_write(pool, k_pool, v_pool, k_new, v_new, slots, num_tokens, stream);
@@ -1096,6 +1097,7 @@ int launch_decode_prepare(const AttnArgs& a, const pkv_pool_desc& pool, void* k_
   wa.k_new = static_cast<const char*>(k_new);
   wa.v_new = static_cast<const char*>(v_new);
   wa.slots = slots;
+  wa.tokens = num_tokens;
   wa.total = total;
   wa.H = pool.num_kv_heads;
   wa.D = pool.head_dim;

@@ -104,3 +104,14 @@ def test_prefill_rejects_fp32_and_bad_arguments():
     with pytest.raises(pkv.PkvError) as e:
         pkv.paged_attention_prefill(q, kp, vp, tables, lens, qs, 3, 0.125)
     assert e.value.status == 2
+
+
+def test_prefill_pools_match_oracle():
+    """The placement writes (whole runs of blocks, one launch per sequence) leave the
+    pools bit-identical to the oracle's."""
+    w = _workload(CASES[4])
+    ctx = w.all_context_kv()
+    st = replay_prefill_gpu(w, ctx, DEV)
+    pool, _, _ = replay_prefill(w, synth.NAN_BITS[w.dtype], context=ctx)
+    assert (to_bits(st.k_pool, w.dtype) == pool.k).all()
+    assert (to_bits(st.v_pool, w.dtype) == pool.v).all()
