@@ -23,6 +23,14 @@ Readings where the pages leave the policy open (all stated in the design notes):
   block, the pair (old tail -> fresh) is emitted for copying, and the old tail
   loses one reference; the last remaining sharer writes in place;
 * a batch step visits sequences in the order given (ascending ids).
+
+Moving sequences between two managers (a device pool and a host pool) models the
+swap-out / swap-in of preemption (data.6616ai.com "PagedAttention 之外", scheduler
+and preemption; "可能的追问"): the moved sequences get fresh blocks in the
+destination, taken from its free list in the order their blocks are first met;
+a block shared by several moved sequences is copied once and stays shared; the
+source blocks are then released as by ``free_seq``.  The (source, destination)
+block pairs to copy are returned in that order.
 """
 from __future__ import annotations
 
@@ -134,3 +142,42 @@ class BlockManager:
                 raise ValueError("table wider than width")
             rows.append(t + [pad] * (width - len(t)))
         return rows
+
+
+def move_seqs(src: BlockManager, dst: BlockManager, seqs: Sequence[int]) -> List[Tuple[int, int]]:
+    """Move ``seqs`` (in order) from ``src`` to ``dst``; returns the block pairs to copy.
+
+    All or nothing: unknown or duplicate sequences, a sequence already in ``dst``,
+    or too few free blocks in ``dst`` raise before anything changes.
+    """
+    seqs = [int(s) for s in seqs]
+    if len(set(seqs)) != len(seqs):
+        raise ValueError("duplicate sequence")
+    for s in seqs:
+        if s not in src.tables:
+            raise KeyError(f"unknown sequence {s}")
+        if s in dst.tables:
+            raise ValueError(f"sequence {s} exists in the destination")
+    if src.block_size != dst.block_size:
+        raise ValueError("block sizes differ")
+    distinct = {b for s in seqs for b in src.tables[s]}
+    if len(distinct) > len(dst.free):
+        raise OutOfBlocks("destination has too few free blocks")
+    mapping: Dict[int, int] = {}
+    pairs: List[Tuple[int, int]] = []
+    for s in seqs:
+        table = []
+        for b in src.tables[s]:
+            if b in mapping:
+                c = mapping[b]
+                dst.refcount[c] += 1
+            else:
+                c = dst._take()
+                mapping[b] = c
+                pairs.append((b, c))
+            table.append(c)
+        dst.tables[s] = table
+        dst.lens[s] = src.lens[s]
+    for s in seqs:
+        src.free_seq(s)
+    return pairs

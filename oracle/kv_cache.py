@@ -73,3 +73,20 @@ def copy_blocks(pool: Pool, pairs) -> None:
     for src, dst in pairs:
         pool.k[int(dst)] = pool.k[int(src)]
         pool.v[int(dst)] = pool.v[int(src)]
+
+
+def swap_blocks(src: Pool, dst: Pool, pairs) -> None:
+    """Swap-out / swap-in: for each (s, d), block d of ``dst`` (K and V, every head
+    and slot) becomes a copy of block s of ``src``.  The two pools have the same
+    tile layout and may differ in block count (a device pool and a host pool).
+
+    Preemption under memory pressure moves a request's KV blocks to CPU memory and
+    back (data.6616ai.com "PagedAttention 之外", scheduler and preemption;
+    "可能的追问", KV swapped out to the CPU when the device is full).
+    """
+    if (src.num_kv_heads, src.head_dim, src.block_size, src.dtype) != \
+            (dst.num_kv_heads, dst.head_dim, dst.block_size, dst.dtype):
+        raise ValueError("pools must share the tile layout")
+    for s, d in pairs:
+        dst.k[int(d)] = src.k[int(s)]
+        dst.v[int(d)] = src.v[int(s)]
