@@ -99,6 +99,23 @@ int32_t pkv_paged_kv_write(const pkv_pool_desc* pool, void* k_pool, void* v_pool
 int32_t pkv_copy_blocks(const pkv_pool_desc* pool, void* k_pool, void* v_pool,
                         const int64_t* src_dst_pairs, int32_t num_pairs, void* stream);
 
+/*
+ * Swap copy: for each pair (s, d), block d of the destination pools (K and V, every
+ * head and slot) becomes a copy of block s of the source pools.  Pages:
+ * data.6616ai.com "PagedAttention 之外" (preemption swaps a request's KV to CPU memory)
+ * and "可能的追问" (swapped out when the device is full, resumed later).  The two
+ * pools share the tile layout `pool` describes (its num_blocks is not used); one of
+ * them is typically pinned host memory (hipHostMalloc / torch pin_memory), which
+ * the copy kernel reads or writes directly over the host link.
+ *   src_k, src_v, dst_k, dst_v  device or pinned host, 16-byte aligned.
+ *   src_dst_pairs  device or pinned host int64 [num_pairs][2].
+ * Device preconditions: block ids inside their pools; destinations distinct and the
+ * source and destination ranges do not overlap.  num_pairs == 0 enqueues nothing.
+ * Errors: INVALID_ARG, UNSUPPORTED, LAUNCH.
+ */
+int32_t pkv_swap_blocks(const pkv_pool_desc* pool, const void* src_k, const void* src_v, void* dst_k,
+                        void* dst_v, const int64_t* src_dst_pairs, int32_t num_pairs, void* stream);
+
 /* Context tokens per split-context partition of the attention pass. */
 #define PKV_PARTITION_TOKENS 512
 
@@ -263,6 +280,19 @@ int32_t pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t 
 /* Tables of `seqs` (host, n) as a host int32 [n][width] matrix padded with `pad`. */
 int32_t pkv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t width,
                             int32_t pad, int32_t* out);
+/* Swap-out / swap-in bookkeeping (data.6616ai.com "PagedAttention 之外", scheduler and
+ * preemption; "可能的追问": under memory pressure a request's KV goes to CPU memory and
+ * comes back later).  Moves `seqs` (host, n, in order) from manager `src` to `dst`
+ * (for example a device pool's manager and a pinned host pool's): each moved
+ * sequence gets fresh blocks of `dst`, taken from its free list in the order the
+ * source blocks are first met; a block shared by several moved sequences is copied
+ * once and stays shared; the source blocks are then released as by free_seq.
+ * pairs_out (host, [cap][2]) receives the (source block, destination block) pairs to
+ * copy with pkv_swap_blocks, *num_pairs their count.  All or nothing: unknown,
+ * duplicate or already-present sequences and a too-small cap are INVALID_ARG, too few
+ * free destination blocks OUT_OF_BLOCKS, and neither changes any state. */
+int32_t pkv_bm_move_seqs(pkv_bm* src, pkv_bm* dst, const int32_t* seqs, int32_t n, int64_t* pairs_out,
+                         int32_t cap, int32_t* num_pairs);
 /* Reference count of `block` (-1 if out of range), number of free blocks. */
 int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
 int32_t pkv_bm_num_free(const pkv_bm* bm);

@@ -76,6 +76,8 @@ def load():
         "pkv_paged_attention_prefill": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
                                          _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
         "pkv_paged_attention_prefill_workspace_bytes": ([_c_i32, _c_i32, _c_i32, _c_i32], _c_sz),
+        "pkv_swap_blocks": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp], _c_i32),
+        "pkv_bm_move_seqs": ([_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, P(_c_i32)], _c_i32),
         "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
         "pkv_bm_destroy": ([_c_vp], None),
         "pkv_bm_add_seq": ([_c_vp, _c_i32, _c_i32], _c_i32),
@@ -164,6 +166,37 @@ def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor)
              and pairs.device == k_pool.device, "pairs must be a contiguous int64 [P, 2] device tensor")
     _check(load().pkv_copy_blocks(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0],
                                   _stream(k_pool.device)))
+
+
+def alloc_host_pools(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype):
+    """K and V pools of the device layout in pinned host memory (the swap target)."""
+    ks, vs = pool_shapes(num_blocks, block_size, num_kv_heads, head_dim, dtype)
+    return (torch.empty(ks, dtype=dtype, pin_memory=True), torch.empty(vs, dtype=dtype, pin_memory=True))
+
+
+def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor, dst_v: torch.Tensor,
+                pairs: torch.Tensor) -> None:
+    """For each row (s, d) of the int64 ``[P, 2]`` tensor, block d of the destination
+    pools becomes a copy of block s of the source pools.  Pools are device tensors or
+    pinned host tensors of the same tile layout (block counts may differ); ``pairs``
+    is a device or pinned host tensor.  Runs on the current stream of the device
+    involved."""
+    for t in (src_k, src_v, dst_k, dst_v, pairs):
+        _require(t.is_cuda or t.is_pinned(), "swap operands must be device tensors or pinned host tensors")
+    _require(src_k.shape[1:] == dst_k.shape[1:] and src_v.shape[1:] == dst_v.shape[1:]
+             and src_k.dtype == dst_k.dtype, "source and destination pools must share the tile layout")
+    _require(src_k.dim() == 5 and src_v.dim() == 4 and src_k.shape[0] == src_v.shape[0]
+             and dst_k.shape[0] == dst_v.shape[0], "K pools must be 5-D and V pools 4-D")
+    _require(all(t.is_contiguous() for t in (src_k, src_v, dst_k, dst_v)), "pools must be contiguous")
+    _require(pairs.dtype == torch.int64 and pairs.dim() == 2 and pairs.shape[1] == 2 and pairs.is_contiguous(),
+             "pairs must be a contiguous int64 [P, 2] tensor")
+    dev = next((t.device for t in (src_k, dst_k, pairs) if t.is_cuda), None)
+    _require(dev is not None, "one operand must live on the device")
+    nb, h, dx, B, x = src_k.shape
+    _require(src_k.dtype in DTYPE_CODES and x * src_k.element_size() == 16, "unsupported pool layout")
+    d = PoolDesc(nb, B, h, dx * x, DTYPE_CODES[src_k.dtype])
+    _check(load().pkv_swap_blocks(ctypes.byref(d), _ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(pairs),
+                                  pairs.shape[0], _stream(dev)))
 
 
 def workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_blocks_per_seq: int, block_size: int) -> int:
@@ -327,6 +360,17 @@ class BlockManager:
 
     def free_seq(self, seq: int) -> None:
         _check(self._lib.pkv_bm_free_seq(self._h, seq))
+
+    def move_seqs(self, dst: "BlockManager", seqs: Sequence[int]) -> np.ndarray:
+        """Move ``seqs`` to manager ``dst``; returns the int64 ``[P, 2]`` (source block,
+        destination block) pairs to copy with ``swap_blocks``."""
+        s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        cap = max(1, self.num_blocks)
+        pairs = np.empty((cap, 2), dtype=np.int64)
+        n = _c_i32()
+        _check(self._lib.pkv_bm_move_seqs(self._h, dst._h, s.ctypes.data, len(s), pairs.ctypes.data, cap,
+                                          ctypes.byref(n)))
+        return pairs[:n.value].copy()
 
     def seq_len(self, seq: int) -> int:
         n = _c_i32()

@@ -235,6 +235,21 @@ int32_t pkv_copy_blocks(const pkv_pool_desc* pool, void* k_pool, void* v_pool, c
                             "pkv_copy_blocks");
 }
 
+int32_t pkv_swap_blocks(const pkv_pool_desc* pool, const void* src_k, const void* src_v, void* dst_k,
+                        void* dst_v, const int64_t* src_dst_pairs, int32_t num_pairs, void* stream) {
+  int32_t st = pkv::check_pool(pool, "pkv_swap_blocks");
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return set_error(PKV_ERR_INVALID_ARG, "pkv_swap_blocks: negative num_pairs");
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !src_dst_pairs)
+    return set_error(PKV_ERR_INVALID_ARG, "pkv_swap_blocks: null pointer argument");
+  if (!pkv::aligned(src_k, 16) || !pkv::aligned(src_v, 16) || !pkv::aligned(dst_k, 16) || !pkv::aligned(dst_v, 16) ||
+      !pkv::aligned(src_dst_pairs, 8))
+    return set_error(PKV_ERR_INVALID_ARG, "pkv_swap_blocks: misaligned pointer");
+  return pkv::launch_status(
+      pkv::launch_pool_copy(*pool, src_k, src_v, dst_k, dst_v, src_dst_pairs, num_pairs, stream), "pkv_swap_blocks");
+}
+
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                            int32_t max_blocks_per_seq, int32_t block_size) {
   if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;

@@ -167,6 +167,52 @@ int32_t pkv_bm_free_seq(pkv_bm* bm, int32_t seq) {
   return PKV_OK;
 }
 
+int32_t pkv_bm_move_seqs(pkv_bm* src, pkv_bm* dst, const int32_t* seqs, int32_t n, int64_t* pairs_out,
+                         int32_t cap, int32_t* num_pairs) {
+  if (!src || !dst || (n > 0 && !seqs) || !num_pairs) return bad("pkv_bm_move_seqs: null pointer");
+  if (src == dst) return bad("pkv_bm_move_seqs: source and destination are the same manager");
+  if (n < 0 || cap < 0) return bad("pkv_bm_move_seqs: negative count");
+  if (src->block_size != dst->block_size) return bad("pkv_bm_move_seqs: block sizes differ");
+  // validate everything first: the call is all or nothing
+  std::unordered_map<int32_t, int32_t> mapping;  // source block -> destination block
+  int64_t distinct = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq* s = find(src, seqs[i]);
+    if (!s) return bad("pkv_bm_move_seqs: unknown sequence");
+    if (find(dst, seqs[i])) return bad("pkv_bm_move_seqs: sequence exists in the destination");
+    for (int32_t j = 0; j < i; ++j)
+      if (seqs[j] == seqs[i]) return bad("pkv_bm_move_seqs: duplicate sequence");
+    for (int32_t b : s->table)
+      if (mapping.emplace(b, -1).second) ++distinct;
+  }
+  if (distinct > dst->count)
+    return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_move_seqs: destination has too few free blocks");
+  if (distinct > cap) return bad("pkv_bm_move_seqs: pairs_out capacity too small");
+  int32_t np = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq& s = src->seqs[seqs[i]];
+    pkv_bm::Seq d;
+    d.table.reserve(s.table.size());
+    for (int32_t b : s.table) {
+      int32_t& c = mapping[b];
+      if (c >= 0) {
+        ++dst->refcount[c];
+      } else {
+        c = dst->take();
+        pairs_out[2 * np] = b;
+        pairs_out[2 * np + 1] = c;
+        ++np;
+      }
+      d.table.push_back(c);
+    }
+    d.len = s.len;
+    dst->seqs.emplace(seqs[i], std::move(d));
+  }
+  for (int32_t i = 0; i < n; ++i) pkv_bm_free_seq(src, seqs[i]);
+  *num_pairs = np;
+  return PKV_OK;
+}
+
 int32_t pkv_bm_seq_len(const pkv_bm* bm, int32_t seq, int32_t* len) {
   if (!bm || !len) return bad("pkv_bm_seq_len: null pointer");
   const pkv_bm::Seq* s = find(bm, seq);

@@ -32,6 +32,9 @@ int launch_kv_write(const pkv_pool_desc& pool, void* k_pool, void* v_pool, const
                     const void* v_new, const int64_t* slots, int32_t num_tokens, void* stream);
 int launch_copy_blocks(const pkv_pool_desc& pool, void* k_pool, void* v_pool, const int64_t* pairs,
                        int32_t num_pairs, void* stream);
+// Whole-block copy from one pool pair to another of the same tile layout.
+int launch_pool_copy(const pkv_pool_desc& pool, const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                     const int64_t* pairs, int32_t num_pairs, void* stream);
 
 struct AttnArgs {
   const void* k_pool;

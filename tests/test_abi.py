@@ -124,3 +124,15 @@ def test_prefill_host_side_errors(pkv_lib):
     # nothing to do: no launch, no pointer checks
     assert call(d, n=0, k=None, v=None, out=None, q=None, qs=None, tab=None, lens=None) == 0
     assert call(d, t=0, k=None, v=None, out=None, q=None, qs=None, tab=None, lens=None) == 0
+
+
+def test_swap_host_side_errors(pkv_lib):
+    lib = pkv_lib.load()
+    d = ctypes.byref(pkv_lib.PoolDesc(64, 16, 8, 128, 2))
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.pkv_swap_blocks(d, fake, fake, fake, fake, fake, 0, None) == 0
+    assert lib.pkv_swap_blocks(d, fake, None, fake, fake, fake, 3, None) == 1
+    assert lib.pkv_swap_blocks(d, fake, fake, ctypes.c_void_p(0x1008), fake, fake, 3, None) == 1
+    assert b"misaligned" in lib.pkv_last_error()
+    assert lib.pkv_swap_blocks(d, fake, fake, fake, fake, fake, -1, None) == 1
+    assert lib.pkv_swap_blocks(None, fake, fake, fake, fake, fake, 1, None) == 1

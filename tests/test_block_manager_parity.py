@@ -96,3 +96,87 @@ def test_workload_tables_match_oracle(pkv_lib, name, kw):
     t2 = lib_bm.block_tables(w.batch, w.max_blocks_per_seq, 0)
     assert (t1 == t2).all()
     assert [lib_bm.seq_len(int(s)) for s in w.batch] == w.context_lens.tolist()
+
+
+@pytest.mark.parametrize("B", [4, 16])
+def test_moves_between_two_managers_match_oracle(pkv_lib, B):
+    """Random histories over a device manager and a host manager, with sequences
+    moved back and forth in groups (swap-out / swap-in), failing moves included."""
+    from oracle.block_manager import move_seqs
+    rng = np.random.default_rng(100 + B)
+    NG, NC = 120, 90
+    og, oc = rng.permutation(NG), rng.permutation(NC)
+    lg, lc = pkv_lib.BlockManager(NG, B, og), pkv_lib.BlockManager(NC, B, oc)
+    rg, rc = OracleBM(NG, B, og), OracleBM(NC, B, oc)
+    on_gpu, on_cpu, nxt = [], [], 0
+    for it in range(500):
+        op = rng.random()
+        if op < 0.2 or not on_gpu:
+            n = int(rng.integers(1, 4 * B))
+            if len(rg.free) >= -(-n // B):
+                rg.add_seq(nxt, n)
+                lg.add_seq(nxt, n)
+                on_gpu.append(nxt)
+            nxt += 1
+        elif op < 0.3:
+            p = int(rng.choice(on_gpu))
+            rg.fork(p, nxt)
+            lg.fork(p, nxt)
+            on_gpu.append(nxt)
+            nxt += 1
+        elif op < 0.45:
+            k = int(rng.integers(1, min(4, len(on_gpu)) + 1))
+            seqs = [int(x) for x in rng.choice(on_gpu, size=k, replace=False)]
+            try:
+                p1 = move_seqs(rg, rc, seqs)
+                ok = True
+            except OutOfBlocks:
+                ok = False
+            if ok:
+                p2 = lg.move_seqs(lc, seqs)
+                assert p2.tolist() == [list(p) for p in p1]
+                on_gpu = [s for s in on_gpu if s not in seqs]
+                on_cpu += seqs
+            else:
+                with pytest.raises(pkv_lib.PkvError) as e:
+                    lg.move_seqs(lc, seqs)
+                assert e.value.status == 5
+        elif op < 0.6 and on_cpu:
+            k = int(rng.integers(1, min(4, len(on_cpu)) + 1))
+            seqs = [int(x) for x in rng.choice(on_cpu, size=k, replace=False)]
+            try:
+                p1 = move_seqs(rc, rg, seqs)
+                ok = True
+            except OutOfBlocks:
+                ok = False
+            if ok:
+                p2 = lc.move_seqs(lg, seqs)
+                assert p2.tolist() == [list(p) for p in p1]
+                on_cpu = [s for s in on_cpu if s not in seqs]
+                on_gpu += seqs
+            else:
+                with pytest.raises(pkv_lib.PkvError) as e:
+                    lc.move_seqs(lg, seqs)
+                assert e.value.status == 5
+        elif op < 0.7 and len(on_gpu) > 1:
+            s = on_gpu.pop(int(rng.integers(len(on_gpu))))
+            rg.free_seq(s)
+            lg.free_seq(s)
+        else:
+            seqs = sorted(on_gpu)
+            if len(rg.free) < 2 * len(seqs):
+                continue
+            s1, p1 = rg.step(seqs)
+            s2, p2 = lg.step(seqs)
+            assert s2.tolist() == s1 and p2.tolist() == [list(p) for p in p1]
+        _same_state(lg, rg, on_gpu)
+        _same_state(lc, rc, on_cpu)
+    # invalid moves are rejected and change nothing
+    if on_gpu:
+        s = on_gpu[0]
+        free_before = lg.num_free()
+        with pytest.raises(pkv_lib.PkvError):
+            lg.move_seqs(lc, [s, s])
+        with pytest.raises(pkv_lib.PkvError):
+            lg.move_seqs(lc, [10 ** 6])
+        assert lg.num_free() == free_before
