@@ -17,6 +17,10 @@ the KV write of every sequence's chunk followed by the causal chunk attention (i
 plan pass and its attention pass);
 ``value`` is attention TFLOP/s over the step and the roofline is the prefill kernel
 against the dense bf16 MFMA peak (2.5 PFLOP/s).
+
+With ``--workload swap_bf16`` a step moves 64 sequences of the GQA batch to a host
+block manager, copies their blocks to pinned host memory, and brings them back; the
+roofline is the swap-out copy against PCIe 5.0 x16 (63 GB/s per direction).
 """
 from __future__ import annotations
 
@@ -35,6 +39,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV GB/s (% of HBM peak) + decode tokens/sec, 1 GPU"
 PREFILL_METRIC = "paged prefill attention TFLOP/s (% of dense bf16 MFMA peak), 1 GPU"
+SWAP_METRIC = "KV block swap GB/s between the device pool and pinned host memory, 1 GPU"
+PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PARTITION_TOKENS = 512
@@ -242,6 +248,119 @@ def prefill_main(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def swap_main(args, sw, dev):
+    """One step: move the chosen sequences to the host manager and copy their blocks out,
+    then move them back and copy in.  Pools hold arbitrary bytes (the copy moves bits)."""
+    import torch
+    import paged_kv_cache_281_amd as pkv
+    w = sw.base
+    tdt = torch.bfloat16
+    bm = pkv.BlockManager(w.num_blocks, w.block_size, w.free_order)
+    for seq, n in w.prefill:
+        bm.add_seq(seq, n)
+    kp, vp = pkv.alloc_pools(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, tdt, dev)
+    kp.view(torch.int16).random_()
+    vp.view(torch.int16).random_()
+    hk, hv = pkv.alloc_host_pools(sw.host_blocks, w.block_size, w.num_kv_heads, w.head_dim, tdt)
+    hbm = pkv.BlockManager(sw.host_blocks, w.block_size, np.arange(sw.host_blocks, dtype=np.int32))
+    block_bytes = 2 * w.num_kv_heads * w.block_size * w.head_dim * 2
+    stream = torch.cuda.current_stream(dev)
+    log(f"swap workload: {len(sw.moved)} of {w.num_seqs} sequences, host pool {sw.host_blocks} blocks")
+
+    host_us = []
+
+    def step(e=None):
+        t = time.perf_counter()
+        p_out = bm.move_seqs(hbm, sw.moved)
+        host_us.append((time.perf_counter() - t) * 1e6)
+        d_out = torch.from_numpy(p_out).to(dev, non_blocking=False)
+        if e is not None:
+            e[0].record(stream)
+        pkv.swap_blocks(kp, vp, hk, hv, d_out)
+        if e is not None:
+            e[1].record(stream)
+        p_in = hbm.move_seqs(bm, sw.moved)
+        d_in = torch.from_numpy(p_in).to(dev, non_blocking=False)
+        if e is not None:
+            e[2].record(stream)
+        pkv.swap_blocks(hk, hv, kp, vp, d_in)
+        if e is not None:
+            e[3].record(stream)
+        return len(p_out), len(p_in)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        n_out, n_in = step(ev[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    out_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    in_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    moved_bytes = n_out * block_bytes
+    gbs_out = moved_bytes / (out_ms * 1e-3) / 1e9
+    gbs_in = moved_bytes / (in_ms * 1e-3) / 1e9
+    # on-box ceiling: one contiguous DMA copy of the same bytes each way
+    flat = torch.empty(moved_bytes, dtype=torch.uint8, device=dev)
+    hflat = torch.empty(moved_bytes, dtype=torch.uint8, pin_memory=True)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    hflat.copy_(flat, non_blocking=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    hflat.copy_(flat, non_blocking=True)
+    e1.record(stream)
+    flat.copy_(hflat, non_blocking=True)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    dma_out = moved_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    dma_in = moved_bytes / (e1.elapsed_time(e2) * 1e-3) / 1e9
+    log(f"step {ms_step:.3f} ms: out {out_ms:.3f} ms ({gbs_out:.1f} GB/s), in {in_ms:.3f} ms ({gbs_in:.1f} GB/s); "
+        f"contiguous DMA {dma_out:.1f} / {dma_in:.1f} GB/s")
+    res = {
+        "metric": SWAP_METRIC,
+        "value": round(2 * moved_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": sw.name, "moved_sequences": len(sw.moved), "blocks_each_way": n_out,
+                   "bytes_each_way": moved_bytes, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size},
+        "kernel_ms": {"swap_out": round(out_ms, 5), "swap_in": round(in_ms, 5)},
+        "swap_out_gbs": round(gbs_out, 2),
+        "swap_in_gbs": round(gbs_in, 2),
+        "contiguous_dma_gbs": {"device_to_host": round(dma_out, 2), "host_to_device": round(dma_in, 2)},
+        "host_block_manager_move_us": round(float(np.median(host_us)), 1),
+        "roofline": {"kernel": "copy_blocks_kernel (swap out)", "bound": "pcie", "achieved": round(gbs_out, 2),
+                     "peak": PCIE_PEAK_GBS, "unit": "GB/s", "frac": round(gbs_out / PCIE_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": moved_bytes},
+    }
+    if not args.no_cpu_baseline:
+        from oracle.kv_cache import Pool, swap_blocks as oracle_swap
+        src = Pool(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, "bf16")
+        dst = Pool(sw.host_blocks, w.num_kv_heads, w.head_dim, w.block_size, "bf16")
+        pairs = bm.move_seqs(hbm, sw.moved)
+        t = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t < min(args.cpu_seconds, 5.0):
+            oracle_swap(src, dst, pairs)
+            reps += 1
+        el = time.perf_counter() - t
+        res["cpu_baseline"] = {"value": round(reps * moved_bytes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} oracle block copies of {len(pairs)} blocks in host memory "
+                                         f"(NumPy, one thread) in {el:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -279,6 +398,9 @@ def main():
     ti = {"f32": (np.int32, torch.int32), "f16": (np.int16, torch.int16), "bf16": (np.int16, torch.int16)}
 
     w = synth.by_name(args.workload)
+    if args.workload in synth.SWAP_WORKLOADS:
+        swap_main(args, w, dev)
+        return
     if args.workload in synth.PREFILL_WORKLOADS:
         prefill_main(args, w, dev)
         return

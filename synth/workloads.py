@@ -358,6 +358,29 @@ WORKLOADS = {
 }
 
 
+@dataclasses.dataclass
+class SwapWorkload:
+    """Preemption by swapping: the ``base`` decode workload's sequences are placed
+    (prefill operations only), then ``moved`` sequences go out to a host pool of
+    ``host_blocks`` blocks and come back (data.6616ai.com "PagedAttention 之外")."""
+
+    name: str
+    base: Workload
+    moved: List[int]
+    host_blocks: int
+
+
+def swap_bf16(num_moved: int = 64) -> SwapWorkload:
+    """The GQA batch (256 sequences, mix x2, 32/8 heads, D=128, B=16, bf16); its first
+    64 sequences are swapped out and back in."""
+    base = gqa_bf16()
+    moved = [int(s) for s in base.batch[:num_moved]]
+    need = sum(-(-int(base.context_lens[i]) // base.block_size) for i in range(num_moved))
+    return SwapWorkload("swap_bf16", base, moved, int(math.ceil(1.1 * need)))
+
+
+SWAP_WORKLOADS = {"swap_bf16": swap_bf16}
+
 PREFILL_WORKLOADS = {
     "prefill_bf16": prefill_bf16,
     "chunked_bf16": chunked_bf16,
@@ -365,6 +388,8 @@ PREFILL_WORKLOADS = {
 
 
 def by_name(name: str, **kw):
+    if name in SWAP_WORKLOADS:
+        return SWAP_WORKLOADS[name](**kw)
     if name in PREFILL_WORKLOADS:
         return PREFILL_WORKLOADS[name](**kw)
     return WORKLOADS[name](**kw)

@@ -84,3 +84,11 @@ def test_prefill_workloads_are_consistent():
         L, C = w.context_lens.astype(int), w.chunk_lens.astype(int)
         pairs = sum(sum(L[b] - C[b] + t + 1 for t in range(C[b])) for b in range(w.num_seqs))
         assert w.flops() == 4 * w.num_q_heads * w.head_dim * pairs
+
+
+def test_swap_workload_fits_its_host_pool():
+    import synth
+    sw = synth.by_name("swap_bf16")
+    w = sw.base
+    need = sum(-(-int(w.context_lens[i]) // w.block_size) for i in range(len(sw.moved)))
+    assert sw.host_blocks >= need and sw.moved == list(range(len(sw.moved)))
