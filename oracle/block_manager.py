@@ -55,6 +55,10 @@ class BlockManager:
         self.lens: Dict[int, int] = {}
 
     # -- allocation -----------------------------------------------------------
+    def _available(self) -> int:
+        """Blocks an allocation may take."""
+        return len(self.free)
+
     def _take(self) -> int:
         if not self.free:
             raise OutOfBlocks("no free block")
@@ -67,7 +71,7 @@ class BlockManager:
         if seq in self.tables:
             raise ValueError(f"sequence {seq} exists")
         nblk = -(-int(num_tokens) // self.block_size)
-        if nblk > len(self.free):
+        if nblk > self._available():
             raise OutOfBlocks("not enough free blocks")
         self.tables[seq] = [self._take() for _ in range(nblk)]
         self.lens[seq] = int(num_tokens)
@@ -119,8 +123,11 @@ class BlockManager:
         for blk in self.tables.pop(seq):
             self.refcount[blk] -= 1
             if self.refcount[blk] == 0:
-                self.free.append(blk)
+                self._release(blk)
         del self.lens[seq]
+
+    def _release(self, blk: int) -> None:
+        self.free.append(blk)
 
     # -- lookups --------------------------------------------------------------
     def slot_of(self, seq: int, pos: int) -> int:
@@ -161,7 +168,7 @@ def move_seqs(src: BlockManager, dst: BlockManager, seqs: Sequence[int]) -> List
     if src.block_size != dst.block_size:
         raise ValueError("block sizes differ")
     distinct = {b for s in seqs for b in src.tables[s]}
-    if len(distinct) > len(dst.free):
+    if len(distinct) > dst._available():
         raise OutOfBlocks("destination has too few free blocks")
     mapping: Dict[int, int] = {}
     pairs: List[Tuple[int, int]] = []
@@ -181,3 +188,102 @@ def move_seqs(src: BlockManager, dst: BlockManager, seqs: Sequence[int]) -> List
     for s in seqs:
         src.free_seq(s)
     return pairs
+
+
+# ---------------------------------------------------------------------------------
+# Prefix caching: data.6616ai.com "PagedAttention 之外" (the KV blocks of a prefix
+# shared across requests, such as a system prompt, are cached and reused, saving
+# prefill compute; vLLM's automatic prefix caching).  Readings (stated in the design
+# notes): each full block of a prompt is keyed by FNV-1a 64 over the key of the block
+# before it (0 for the first) followed by its token ids; a lookup also checks the
+# stored parent key and tokens.  A new prompt reuses the cached blocks of its longest
+# cached prefix of full blocks, never the block holding its last token (that token is
+# always computed).  Its other full blocks are registered when allocated (unless the
+# key is taken); its partial tail and blocks filled later by decoding are not cached.
+# A cached block whose count drops to zero stays addressable in an evictable list in
+# release order; allocation takes the free list first, then evicts the least
+# recently released cached block.
+# ---------------------------------------------------------------------------------
+FNV64_OFFSET = 0xCBF29CE484222325
+FNV64_PRIME = 0x100000001B3
+_MASK64 = (1 << 64) - 1
+
+
+def fnv1a64(data: bytes, h: int = FNV64_OFFSET) -> int:
+    """FNV-1a, 64-bit: for each byte, h ^= byte, then h *= prime (mod 2^64)."""
+    for byte in data:
+        h ^= byte
+        h = (h * FNV64_PRIME) & _MASK64
+    return h
+
+
+def block_key(parent_key: int, tokens: Sequence[int]) -> int:
+    data = int(parent_key).to_bytes(8, "little") + b"".join(
+        int(t).to_bytes(4, "little", signed=True) for t in tokens)
+    return fnv1a64(data)
+
+
+class PrefixCachingBlockManager(BlockManager):
+    def __init__(self, num_blocks: int, block_size: int, free_order: Sequence[int]):
+        super().__init__(num_blocks, block_size, free_order)
+        self.cached: Dict[int, int] = {}                      # key -> block
+        self.info: Dict[int, Tuple[int, int, Tuple[int, ...]]] = {}  # block -> (key, parent key, tokens)
+        self.evictable: "collections.OrderedDict[int, None]" = collections.OrderedDict()
+
+    def _available(self) -> int:
+        return len(self.free) + len(self.evictable)
+
+    def _take(self) -> int:
+        if self.free:
+            blk = self.free.popleft()
+        elif self.evictable:
+            blk, _ = self.evictable.popitem(last=False)
+            key = self.info.pop(blk)[0]
+            del self.cached[key]
+        else:
+            raise OutOfBlocks("no free block")
+        self.refcount[blk] = 1
+        return blk
+
+    def _release(self, blk: int) -> None:
+        if blk in self.info:
+            self.evictable[blk] = None
+        else:
+            self.free.append(blk)
+
+    def add_seq_tokens(self, seq: int, tokens: Sequence[int]) -> int:
+        """Register ``seq`` with prompt ``tokens``; returns the number of leading tokens
+        whose KV is already in the pool (a multiple of B)."""
+        if seq in self.tables:
+            raise ValueError(f"sequence {seq} exists")
+        B = self.block_size
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        nblk = -(-n // B)
+        lookup = max(n - 1, 0) // B      # full blocks entirely before the last token
+        keys, hits, parent = [], [], 0
+        for i in range(n // B):
+            toks = tuple(tokens[i * B:(i + 1) * B])
+            key = block_key(parent, toks)
+            keys.append((key, parent, toks))
+            blk = self.cached.get(key)
+            if i < lookup and len(hits) == i and blk is not None and self.info[blk][1:] == (parent, toks):
+                hits.append(blk)
+            parent = key
+        pinned_evictable = sum(1 for b in hits if self.refcount[b] == 0)
+        if nblk - len(hits) > self._available() - pinned_evictable:
+            raise OutOfBlocks("not enough free blocks")
+        for b in hits:
+            if self.refcount[b] == 0:
+                del self.evictable[b]
+            self.refcount[b] += 1
+        table = list(hits)
+        for i in range(len(hits), nblk):
+            blk = self._take()
+            if i < len(keys) and keys[i][0] not in self.cached:
+                self.cached[keys[i][0]] = blk
+                self.info[blk] = keys[i]
+            table.append(blk)
+        self.tables[seq] = table
+        self.lens[seq] = n
+        return len(hits) * B
