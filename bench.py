@@ -21,6 +21,9 @@ against the dense bf16 MFMA peak (2.5 PFLOP/s).
 With ``--workload swap_bf16`` a step moves 64 sequences of the GQA batch to a host
 block manager, copies their blocks to pinned host memory, and brings them back; the
 roofline is the swap-out copy against PCIe 5.0 x16 (63 GB/s per direction).
+With ``--workload prefix_bf16`` the same prefill batch (64 requests over 4 system
+prompts) is timed with the prefix cache (only uncached tokens written and attended
+from) and without it.
 """
 from __future__ import annotations
 
@@ -361,6 +364,97 @@ def swap_main(args, sw, dev):
     print(json.dumps(res), flush=True)
 
 
+def prefix_main(args, w, dev):
+    """Prefill of requests sharing system prompts, with the prefix cache (only uncached
+    tokens are written and attended from) and without it (whole prompts); same requests,
+    same queries per position."""
+    import torch
+    import paged_kv_cache_281_amd as pkv
+    tdt = torch.bfloat16
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
+
+    flops_row = 4 * w.num_q_heads * w.head_dim
+    lens = np.asarray([w.length(b) for b in range(w.num_seqs)], dtype=np.int64)
+    stream = torch.cuda.current_stream(dev)
+    res_runs = {}
+    for cache in (True, False):
+        t = time.perf_counter()
+        bm = pkv.BlockManager(w.num_blocks, w.block_size, w.free_order, prefix_cache=cache)
+        cached = np.asarray([bm.add_seq_tokens(b, w.tokens(b)) for b in range(w.num_seqs)], dtype=np.int64)
+        host_ms = (time.perf_counter() - t) * 1e3
+        kp, vp = pkv.alloc_pools(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, tdt, dev)
+        kp.view(torch.int16).fill_(0)
+        vp.view(torch.int16).fill_(0)
+        ks, vs, ss, qs_rows = [], [], [], []
+        for b in range(w.num_seqs):
+            k, v = w.kv(b)
+            c, L = int(cached[b]), int(lens[b])
+            ks.append(k[c:])
+            vs.append(v[c:])
+            ss.append(bm.slots(b, c, L - c))
+            qs_rows.append(w.queries(b)[c:])
+        k_new, v_new = up(np.concatenate(ks)), up(np.concatenate(vs))
+        slots = torch.from_numpy(np.concatenate(ss)).to(dev)
+        q = up(np.concatenate(qs_rows))
+        chunks = lens - cached
+        qstart = torch.from_numpy(np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)).to(dev)
+        tables = torch.from_numpy(bm.block_tables(list(range(w.num_seqs)), w.max_blocks_per_seq, 0)).to(dev)
+        lens_d = torch.from_numpy(lens.astype(np.int32)).to(dev)
+        out = torch.empty_like(q)
+        ws = pkv.alloc_prefill_workspace(w.num_seqs, q.shape[0], w.num_q_heads, w.num_kv_heads, dev)
+        mq = int(chunks.max())
+        torch.cuda.synchronize()
+
+        def step(e=None):
+            pkv.paged_kv_write(kp, vp, k_new, v_new, slots)
+            if e is not None:
+                e[0].record(stream)
+            pkv.paged_attention_prefill(q, kp, vp, tables, lens_d, qstart, mq, w.scale, out, ws)
+            if e is not None:
+                e[1].record(stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(ev[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        attn = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        flops = flops_row * int(np.sum(chunks * (lens - chunks) + chunks * (chunks + 1) // 2))
+        res_runs["cached" if cache else "uncached"] = {
+            "ms_per_step": round(ms, 5), "attn_ms": round(attn, 5), "computed_tokens": int(chunks.sum()),
+            "cached_tokens": int(cached.sum()), "flops": flops, "attn_tflops": round(flops / (attn * 1e-3) / 1e12, 2),
+            "host_block_manager_ms": round(host_ms, 2)}
+        log(f"{'with' if cache else 'without'} prefix cache: step {ms:.4f} ms, attention {attn:.4f} ms, "
+            f"{int(chunks.sum())} of {int(lens.sum())} prompt tokens computed")
+        del kp, vp
+        torch.cuda.empty_cache()
+    c, u = res_runs["cached"], res_runs["uncached"]
+    total = int(lens.sum())
+    res = {
+        "metric": "prompt tokens/s of a prefill batch sharing system prompts, with prefix caching, 1 GPU",
+        "value": round(total / (c["ms_per_step"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": c["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.num_seqs, "system_prompts": len(w.system_lens),
+                   "prompt_tokens": total, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size},
+        "with_cache": c, "without_cache": u,
+        "speedup": round(u["ms_per_step"] / c["ms_per_step"], 3),
+        "roofline": {"kernel": "attn_prefill_lds (cached run)", "bound": "mfma", "achieved": c["attn_tflops"],
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(c["attn_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops": c["flops"]},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -398,6 +492,9 @@ def main():
     ti = {"f32": (np.int32, torch.int32), "f16": (np.int16, torch.int16), "bf16": (np.int16, torch.int16)}
 
     w = synth.by_name(args.workload)
+    if args.workload in synth.PREFIX_WORKLOADS:
+        prefix_main(args, w, dev)
+        return
     if args.workload in synth.SWAP_WORKLOADS:
         swap_main(args, w, dev)
         return

@@ -293,9 +293,36 @@ int32_t pkv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, in
  * free destination blocks OUT_OF_BLOCKS, and neither changes any state. */
 int32_t pkv_bm_move_seqs(pkv_bm* src, pkv_bm* dst, const int32_t* seqs, int32_t n, int64_t* pairs_out,
                          int32_t cap, int32_t* num_pairs);
-/* Reference count of `block` (-1 if out of range), number of free blocks. */
+/* Reference count of `block` (-1 if out of range); blocks an allocation may take
+ * (free, plus released cached blocks when prefix caching is on). */
 int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block);
 int32_t pkv_bm_num_free(const pkv_bm* bm);
+
+/*
+ * Prefix caching.  Pages: data.6616ai.com "PagedAttention 之外" (the KV blocks of a
+ * prefix shared across requests, such as a system prompt, can be cached and reused,
+ * saving prefill compute in multi-turn and few-shot use).  Policy:
+ *  - every full block of a prompt is keyed by FNV-1a 64 over the key of the block
+ *    before it (0 for the first; 8 bytes little-endian) followed by its token ids
+ *    (4 bytes each, little-endian); a lookup also compares the stored parent key and
+ *    tokens;
+ *  - add_seq_tokens reuses the cached blocks of the prompt's longest cached prefix of
+ *    full blocks, never the block holding its last token, and returns in
+ *    *cached_tokens how many leading tokens already have their K/V in the pool (the
+ *    caller writes and computes only the rest); its other full blocks are registered
+ *    as they are allocated (unless the key is taken); partial tails and blocks filled
+ *    by decoding are not cached;
+ *  - a cached block whose count drops to zero stays addressable in an evictable list
+ *    in release order; allocation takes the free list first, then evicts the least
+ *    recently released cached block.
+ * set_prefix_cache switches it on or off for a manager without sequences or cached
+ * blocks (INVALID_ARG otherwise).  Without it, add_seq_tokens is add_seq with
+ * *cached_tokens = 0.  OUT_OF_BLOCKS leaves the state unchanged.
+ */
+int32_t pkv_bm_set_prefix_cache(pkv_bm* bm, int32_t enable);
+int32_t pkv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, int32_t n, int32_t* cached_tokens);
+/* Number of blocks registered in the prefix cache (in use or evictable). */
+int32_t pkv_bm_num_cached(const pkv_bm* bm);
 
 #ifdef __cplusplus
 }

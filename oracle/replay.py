@@ -74,3 +74,29 @@ def replay_prefill(w, fill_bits: int, context=None, pad: int = 0):
             paged_kv_write(pool, k, v, bm.slots(b, 0, L))
     tables = np.asarray(bm.block_tables(range(w.num_seqs), w.max_blocks_per_seq, pad), dtype=np.int32)
     return pool, tables.reshape(w.num_seqs, w.max_blocks_per_seq), np.asarray(w.context_lens, dtype=np.int32)
+
+
+def replay_prefix(w, fill_bits: int, cache: bool = True):
+    """Place a prefix-sharing workload request by request.  With ``cache`` each request
+    reuses the cached blocks of its prompt prefix and only its remaining tokens' K/V are
+    written; without it every token is written.  Returns (pool, block tables int32
+    [N, W], context lengths int32 [N], cached token count per request)."""
+    from .block_manager import PrefixCachingBlockManager
+    bm = (PrefixCachingBlockManager if cache else BlockManager)(w.num_blocks, w.block_size, w.free_order)
+    pool = Pool(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype, fill_bits)
+    cached = []
+    for b in range(w.num_seqs):
+        toks = w.tokens(b)
+        L = len(toks)
+        if cache:
+            c = bm.add_seq_tokens(b, toks)
+        else:
+            bm.add_seq(b, L)
+            c = 0
+        k, v = w.kv(b)
+        if L > c:
+            paged_kv_write(pool, k[c:], v[c:], bm.slots(b, c, L - c))
+        cached.append(c)
+    tables = np.asarray(bm.block_tables(range(w.num_seqs), w.max_blocks_per_seq, 0), dtype=np.int32)
+    lens = np.asarray([w.length(b) for b in range(w.num_seqs)], dtype=np.int32)
+    return pool, tables.reshape(w.num_seqs, w.max_blocks_per_seq), lens, np.asarray(cached, dtype=np.int32)

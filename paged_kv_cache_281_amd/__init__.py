@@ -79,6 +79,9 @@ def load():
         "pkv_swap_blocks": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp], _c_i32),
         "pkv_bm_move_seqs": ([_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, P(_c_i32)], _c_i32),
         "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
+        "pkv_bm_set_prefix_cache": ([_c_vp, _c_i32], _c_i32),
+        "pkv_bm_add_seq_tokens": ([_c_vp, _c_i32, _c_vp, _c_i32, P(_c_i32)], _c_i32),
+        "pkv_bm_num_cached": ([_c_vp], _c_i32),
         "pkv_bm_destroy": ([_c_vp], None),
         "pkv_bm_add_seq": ([_c_vp, _c_i32, _c_i32], _c_i32),
         "pkv_bm_fork": ([_c_vp, _c_i32, _c_i32], _c_i32),
@@ -322,7 +325,7 @@ def paged_attention_partitions(q, k_pool, v_pool, block_tables, context_lens, sc
 class BlockManager:
     """Host-side block manager of libpkv (tables, on-demand allocation, fork, copy-on-write)."""
 
-    def __init__(self, num_blocks: int, block_size: int, free_order: Sequence[int]):
+    def __init__(self, num_blocks: int, block_size: int, free_order: Sequence[int], prefix_cache: bool = False):
         self._lib = load()
         order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
         _require(order.shape == (num_blocks,), "free_order must hold num_blocks entries")
@@ -330,6 +333,19 @@ class BlockManager:
         _check(self._lib.pkv_bm_create(num_blocks, block_size, order.ctypes.data, ctypes.byref(h)))
         self._h = h
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        if prefix_cache:
+            _check(self._lib.pkv_bm_set_prefix_cache(self._h, 1))
+
+    def add_seq_tokens(self, seq: int, tokens: Sequence[int]) -> int:
+        """Add ``seq`` with prompt ``tokens``; returns how many leading tokens already
+        have their K/V in the pool (prefix cache hits)."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        c = _c_i32()
+        _check(self._lib.pkv_bm_add_seq_tokens(self._h, seq, t.ctypes.data, len(t), ctypes.byref(c)))
+        return c.value
+
+    def num_cached(self) -> int:
+        return int(self._lib.pkv_bm_num_cached(self._h))
 
     def __del__(self):
         h = getattr(self, "_h", None)

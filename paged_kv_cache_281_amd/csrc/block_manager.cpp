@@ -10,9 +10,20 @@
 //
 // The free list is a ring buffer over all block ids: allocation pops from the
 // front, release pushes to the back.  Tables are per-sequence vectors.
+//
+// Prefix caching (optional; data.6616ai.com "PagedAttention 之外": the KV blocks of
+// a prefix shared across requests, such as a system prompt, are cached and reused):
+// every full block of a prompt is keyed by FNV-1a 64 over the key of the block
+// before it (0 for the first) and its token ids; a new prompt reuses the cached
+// blocks of its longest cached prefix of full blocks, never the block holding its
+// last token.  Its other full blocks are registered when allocated (unless the key
+// is taken); partial tails and blocks filled by decoding are not cached.  A cached
+// block whose count drops to zero joins an evictable list in release order;
+// allocation takes the free list first, then evicts the least recently released.
 #include <cstdint>
 #include <cstring>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pkv.h"
@@ -31,16 +42,55 @@ struct pkv_bm {
   };
   std::unordered_map<int32_t, Seq> seqs;
 
+  // prefix cache
+  bool prefix_cache = false;
+  std::unordered_map<uint64_t, int32_t> cached;  // key -> block
+  std::vector<char> has_key;                      // per block: registered in `cached`
+  std::vector<uint64_t> key, parent_key;
+  std::vector<std::vector<int32_t>> key_tokens;
+  std::vector<int32_t> ev_prev, ev_next;          // evictable list (release order)
+  int32_t ev_head = -1, ev_tail = -1;
+  int64_t ev_count = 0;
+
+  int64_t available() const { return count + ev_count; }
+
+  void ev_push(int32_t b) {
+    ev_prev[b] = ev_tail;
+    ev_next[b] = -1;
+    if (ev_tail >= 0) ev_next[ev_tail] = b; else ev_head = b;
+    ev_tail = b;
+    ++ev_count;
+  }
+  void ev_remove(int32_t b) {
+    if (ev_prev[b] >= 0) ev_next[ev_prev[b]] = ev_next[b]; else ev_head = ev_next[b];
+    if (ev_next[b] >= 0) ev_prev[ev_next[b]] = ev_prev[b]; else ev_tail = ev_prev[b];
+    --ev_count;
+  }
+
+  // callers check available() first
   int32_t take() {
-    int32_t b = ring[head];
-    head = (head + 1) % num_blocks;
-    --count;
+    int32_t b;
+    if (count > 0) {
+      b = ring[head];
+      head = (head + 1) % num_blocks;
+      --count;
+    } else {
+      b = ev_head;
+      ev_remove(b);
+      cached.erase(key[b]);
+      has_key[b] = 0;
+      key_tokens[b].clear();
+    }
     refcount[b] = 1;
     return b;
   }
   void give_back(int32_t b) {
     ring[(head + count) % num_blocks] = b;
     ++count;
+  }
+  // a block whose count reached zero
+  void release(int32_t b) {
+    if (prefix_cache && has_key[b]) ev_push(b); else give_back(b);
   }
 };
 
@@ -58,6 +108,29 @@ const pkv_bm::Seq* find(const pkv_bm* bm, int32_t seq) {
 }
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// FNV-1a, 64-bit: for each byte, h ^= byte, then h *= 1099511628211 (mod 2^64).
+uint64_t fnv1a64_bytes(const unsigned char* p, size_t n, uint64_t h) {
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 1099511628211ULL;
+  }
+  return h;
+}
+
+// Key of a full block: FNV-1a 64 over the parent key (8 bytes, little-endian) and the
+// block's token ids (4 bytes each, little-endian two's complement).
+uint64_t block_key(uint64_t parent, const int32_t* tokens, int32_t n) {
+  unsigned char buf[8];
+  for (int i = 0; i < 8; ++i) buf[i] = static_cast<unsigned char>(parent >> (8 * i));
+  uint64_t h = fnv1a64_bytes(buf, 8, 14695981039346656037ULL);
+  for (int32_t t = 0; t < n; ++t) {
+    const uint32_t u = static_cast<uint32_t>(tokens[t]);
+    for (int i = 0; i < 4; ++i) buf[i] = static_cast<unsigned char>(u >> (8 * i));
+    h = fnv1a64_bytes(buf, 4, h);
+  }
+  return h;
+}
 
 }  // namespace
 
@@ -90,7 +163,8 @@ int32_t pkv_bm_add_seq(pkv_bm* bm, int32_t seq, int32_t num_tokens) {
   if (seq < 0 || num_tokens < 0) return bad("pkv_bm_add_seq: negative sequence id or token count");
   if (find(bm, seq)) return bad("pkv_bm_add_seq: sequence already exists");
   int64_t need = div_up(num_tokens, bm->block_size);
-  if (need > bm->count) return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_add_seq: not enough free blocks");
+  if (need > bm->available())
+    return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_add_seq: not enough free blocks");
   pkv_bm::Seq s;
   s.table.reserve(need);
   for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->take());
@@ -120,12 +194,12 @@ int32_t pkv_bm_append_slot(pkv_bm* bm, int32_t seq, int64_t* slot, int32_t* cow_
   *cow_src = -1;
   *cow_dst = -1;
   if (pos % B == 0) {
-    if (bm->count == 0) return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_append_slot: no free block");
+    if (bm->available() == 0) return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_append_slot: no free block");
     s->table.push_back(bm->take());
   } else {
     int32_t tail = s->table.back();
     if (bm->refcount[tail] > 1) {
-      if (bm->count == 0) return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_append_slot: no free block");
+      if (bm->available() == 0) return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_append_slot: no free block");
       int32_t fresh = bm->take();
       --bm->refcount[tail];
       s->table.back() = fresh;
@@ -161,7 +235,7 @@ int32_t pkv_bm_free_seq(pkv_bm* bm, int32_t seq) {
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return bad("pkv_bm_free_seq: unknown sequence");
   for (int32_t b : it->second.table) {
-    if (--bm->refcount[b] == 0) bm->give_back(b);
+    if (--bm->refcount[b] == 0) bm->release(b);
   }
   bm->seqs.erase(it);
   return PKV_OK;
@@ -185,7 +259,7 @@ int32_t pkv_bm_move_seqs(pkv_bm* src, pkv_bm* dst, const int32_t* seqs, int32_t 
     for (int32_t b : s->table)
       if (mapping.emplace(b, -1).second) ++distinct;
   }
-  if (distinct > dst->count)
+  if (distinct > dst->available())
     return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_move_seqs: destination has too few free blocks");
   if (distinct > cap) return bad("pkv_bm_move_seqs: pairs_out capacity too small");
   int32_t np = 0;
@@ -269,6 +343,85 @@ int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block) {
   return bm->refcount[block];
 }
 
-int32_t pkv_bm_num_free(const pkv_bm* bm) { return bm ? static_cast<int32_t>(bm->count) : -1; }
+int32_t pkv_bm_num_free(const pkv_bm* bm) { return bm ? static_cast<int32_t>(bm->available()) : -1; }
+
+int32_t pkv_bm_num_cached(const pkv_bm* bm) { return bm ? static_cast<int32_t>(bm->cached.size()) : -1; }
+
+int32_t pkv_bm_set_prefix_cache(pkv_bm* bm, int32_t enable) {
+  if (!bm) return bad("pkv_bm_set_prefix_cache: null manager");
+  if (!bm->seqs.empty() || !bm->cached.empty())
+    return bad("pkv_bm_set_prefix_cache: only a manager without sequences or cached blocks can switch");
+  bm->prefix_cache = enable != 0;
+  const size_t n = static_cast<size_t>(bm->num_blocks);
+  bm->has_key.assign(n, 0);
+  bm->key.assign(n, 0);
+  bm->parent_key.assign(n, 0);
+  bm->key_tokens.assign(n, {});
+  bm->ev_prev.assign(n, -1);
+  bm->ev_next.assign(n, -1);
+  bm->ev_head = bm->ev_tail = -1;
+  bm->ev_count = 0;
+  return PKV_OK;
+}
+
+int32_t pkv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, int32_t n, int32_t* cached_tokens) {
+  if (!bm || (n > 0 && !tokens) || !cached_tokens) return bad("pkv_bm_add_seq_tokens: null pointer");
+  if (seq < 0 || n < 0) return bad("pkv_bm_add_seq_tokens: negative sequence id or token count");
+  if (find(bm, seq)) return bad("pkv_bm_add_seq_tokens: sequence already exists");
+  if (!bm->prefix_cache) {
+    const int32_t st = pkv_bm_add_seq(bm, seq, n);
+    if (st == PKV_OK) *cached_tokens = 0;
+    return st;
+  }
+  const int32_t B = bm->block_size;
+  const int64_t nblk = div_up(n, B);
+  const int32_t nfull = n / B;
+  const int32_t lookup = (n > 0 ? n - 1 : 0) / B;  // full blocks entirely before the last token
+  std::vector<uint64_t> keys(nfull), parents(nfull);
+  std::vector<int32_t> hits;
+  uint64_t parent = 0;
+  for (int32_t i = 0; i < nfull; ++i) {
+    const int32_t* t = tokens + static_cast<int64_t>(i) * B;
+    const uint64_t k = block_key(parent, t, B);
+    keys[i] = k;
+    parents[i] = parent;
+    if (i < lookup && static_cast<int32_t>(hits.size()) == i) {
+      auto it = bm->cached.find(k);
+      if (it != bm->cached.end()) {
+        const int32_t b = it->second;
+        if (bm->parent_key[b] == parent && std::memcmp(bm->key_tokens[b].data(), t, sizeof(int32_t) * B) == 0)
+          hits.push_back(b);
+      }
+    }
+    parent = k;
+  }
+  int64_t pinned_evictable = 0;
+  for (int32_t b : hits)
+    if (bm->refcount[b] == 0) ++pinned_evictable;
+  if (nblk - static_cast<int64_t>(hits.size()) > bm->available() - pinned_evictable)
+    return pkv::set_error(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_add_seq_tokens: not enough free blocks");
+  for (int32_t b : hits) {
+    if (bm->refcount[b] == 0) bm->ev_remove(b);
+    ++bm->refcount[b];
+  }
+  pkv_bm::Seq s;
+  s.table = hits;
+  s.table.reserve(nblk);
+  for (int64_t i = static_cast<int64_t>(hits.size()); i < nblk; ++i) {
+    const int32_t b = bm->take();
+    if (i < nfull && bm->cached.find(keys[i]) == bm->cached.end()) {
+      bm->cached.emplace(keys[i], b);
+      bm->has_key[b] = 1;
+      bm->key[b] = keys[i];
+      bm->parent_key[b] = parents[i];
+      bm->key_tokens[b].assign(tokens + i * B, tokens + (i + 1) * B);
+    }
+    s.table.push_back(b);
+  }
+  s.len = n;
+  bm->seqs.emplace(seq, std::move(s));
+  *cached_tokens = static_cast<int32_t>(hits.size()) * B;
+  return PKV_OK;
+}
 
 }  // extern "C"

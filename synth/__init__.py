@@ -10,5 +10,5 @@ from .workloads import (  # noqa: F401
     DTYPES, NAN_BITS, Workload, normal_bits, skewed_lengths,
     tiny_fp32, mha_bf16, gqa_bf16, cow_fp16, long_bf16, by_name, WORKLOADS,
     PrefillWorkload, prefill_workload, prefill_bf16, chunked_bf16, PREFILL_WORKLOADS,
-    SwapWorkload, swap_bf16, SWAP_WORKLOADS,
+    SwapWorkload, swap_bf16, SWAP_WORKLOADS, PrefixWorkload, prefix_bf16, PREFIX_WORKLOADS,
 )

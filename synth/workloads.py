@@ -35,6 +35,7 @@ NAN_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0}
 
 # seed-tuple tags for the different value streams of one workload
 _TAG_CTX_K, _TAG_CTX_V, _TAG_STEP_K, _TAG_STEP_V, _TAG_Q, _TAG_PF_Q = 1, 2, 3, 4, 5, 6
+_TAG_SYS_TOK, _TAG_SFX_TOK, _TAG_SYS_K, _TAG_SYS_V, _TAG_SFX_K, _TAG_SFX_V, _TAG_REQ_Q = 7, 8, 9, 10, 11, 12, 13
 
 
 def _gen_threads() -> int:
@@ -381,6 +382,80 @@ def swap_bf16(num_moved: int = 64) -> SwapWorkload:
 
 SWAP_WORKLOADS = {"swap_bf16": swap_bf16}
 
+
+@dataclasses.dataclass
+class PrefixWorkload:
+    """Requests that share system prompts (data.6616ai.com "PagedAttention 之外",
+    prefix caching).  Request b is system prompt ``system_of[b]`` followed by its own
+    suffix.  Token ids and K/V of a system prompt are drawn once per prompt, so equal
+    prefixes hold equal K/V (as K/V at a position depend only on the tokens up to it);
+    suffix values and every query row are drawn per request."""
+
+    name: str
+    seed: int
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    scale: float
+    free_order: np.ndarray
+    system_lens: List[int]
+    system_of: List[int]
+    suffix_lens: List[int]
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.system_of)
+
+    @property
+    def elem_bytes(self) -> int:
+        return DTYPES[self.dtype][2]
+
+    def length(self, b: int) -> int:
+        return self.system_lens[self.system_of[b]] + self.suffix_lens[b]
+
+    def tokens(self, b: int) -> np.ndarray:
+        s = self.system_of[b]
+        sys_tok = np.random.default_rng([self.seed, _TAG_SYS_TOK, s]).integers(0, 32000, self.system_lens[s])
+        sfx_tok = np.random.default_rng([self.seed, _TAG_SFX_TOK, b]).integers(0, 32000, self.suffix_lens[b])
+        return np.concatenate([sys_tok, sfx_tok]).astype(np.int32)
+
+    def kv(self, b: int) -> Tuple[np.ndarray, np.ndarray]:
+        s = self.system_of[b]
+        hs = (self.system_lens[s], self.num_kv_heads, self.head_dim)
+        hx = (self.suffix_lens[b], self.num_kv_heads, self.head_dim)
+        k = np.concatenate([normal_bits((self.seed, _TAG_SYS_K, s), hs, self.dtype),
+                            normal_bits((self.seed, _TAG_SFX_K, b), hx, self.dtype)])
+        v = np.concatenate([normal_bits((self.seed, _TAG_SYS_V, s), hs, self.dtype),
+                            normal_bits((self.seed, _TAG_SFX_V, b), hx, self.dtype)])
+        return k, v
+
+    def queries(self, b: int) -> np.ndarray:
+        """Query rows of every position of request b ``[L_b, Hq, D]``."""
+        return normal_bits((self.seed, _TAG_REQ_Q, b), (self.length(b), self.num_q_heads, self.head_dim), self.dtype)
+
+
+def prefix_bf16(seed: int = 1007, num_requests: int = 64, num_systems: int = 4) -> PrefixWorkload:
+    """64 requests over 4 system prompts of U{512..2047} tokens; user suffixes from the
+    interview post's request mix; 32 q / 8 kv heads, D=128, B=16, bf16."""
+    rng = np.random.default_rng(seed)
+    system_lens = rng.integers(512, 2048, size=num_systems).tolist()
+    system_of = rng.integers(0, num_systems, size=num_requests).tolist()
+    suffix_lens = skewed_lengths(rng, num_requests, 1).tolist()
+    B = 16
+    L = [system_lens[s] + x for s, x in zip(system_of, suffix_lens)]
+    need = sum(-(-x // B) for x in L)
+    nb = int(math.ceil(1.1 * need))
+    return PrefixWorkload("prefix_bf16", seed, "bf16", 32, 8, 128, B, nb, max(-(-x // B) for x in L),
+                          1.0 / math.sqrt(128), rng.permutation(nb).astype(np.int32), system_lens, system_of,
+                          suffix_lens)
+
+
+PREFIX_WORKLOADS = {"prefix_bf16": prefix_bf16}
+
 PREFILL_WORKLOADS = {
     "prefill_bf16": prefill_bf16,
     "chunked_bf16": chunked_bf16,
@@ -388,6 +463,8 @@ PREFILL_WORKLOADS = {
 
 
 def by_name(name: str, **kw):
+    if name in PREFIX_WORKLOADS:
+        return PREFIX_WORKLOADS[name](**kw)
     if name in SWAP_WORKLOADS:
         return SWAP_WORKLOADS[name](**kw)
     if name in PREFILL_WORKLOADS:

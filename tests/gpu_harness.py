@@ -171,3 +171,38 @@ def run_prefill(w, st: PrefillState, q_bits: np.ndarray, device="cuda") -> torch
                                       w.max_query_len, w.scale)
     torch.cuda.synchronize()
     return out
+
+
+def replay_prefix_gpu(w, device="cuda", cache=True, fill_bits=None):
+    """Place a prefix-sharing workload through the library (prefix-caching block manager
+    when ``cache``); returns (PrefillState, cached token count per request)."""
+    fill_bits = synth.NAN_BITS[w.dtype] if fill_bits is None else fill_bits
+    bm = pkv.BlockManager(w.num_blocks, w.block_size, w.free_order, prefix_cache=cache)
+    kp, vp = pkv.alloc_pools(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, TORCH_DTYPE[w.dtype], device)
+    npi, ti = INT_VIEW[w.dtype]
+    fill = np.array([fill_bits], dtype=np.uint16).view(npi)[0]
+    kp.view(ti).fill_(int(fill))
+    vp.view(ti).fill_(int(fill))
+    cached = []
+    for b in range(w.num_seqs):
+        toks = w.tokens(b)
+        L = len(toks)
+        c = bm.add_seq_tokens(b, toks)
+        k, v = w.kv(b)
+        if L > c:
+            slots = torch.from_numpy(bm.slots(b, c, L - c)).to(device)
+            pkv.paged_kv_write(kp, vp, to_device(k[c:], w.dtype, device), to_device(v[c:], w.dtype, device), slots)
+        cached.append(c)
+    cached = np.asarray(cached, dtype=np.int32)
+    lens = np.asarray([w.length(b) for b in range(w.num_seqs)], dtype=np.int32)
+    chunks = lens - cached
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    tables = torch.from_numpy(bm.block_tables(list(range(w.num_seqs)), w.max_blocks_per_seq, 0)).to(device)
+    st = PrefillState(kp, vp, tables, torch.from_numpy(lens).to(device), torch.from_numpy(qs).to(device))
+    torch.cuda.synchronize()
+    return st, cached, bm
+
+
+def prefix_queries(w, cached) -> np.ndarray:
+    """Query rows of the uncached positions of every request, back to back."""
+    return np.concatenate([w.queries(b)[int(cached[b]):] for b in range(w.num_seqs)])

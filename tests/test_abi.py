@@ -136,3 +136,13 @@ def test_swap_host_side_errors(pkv_lib):
     assert b"misaligned" in lib.pkv_last_error()
     assert lib.pkv_swap_blocks(d, fake, fake, fake, fake, fake, -1, None) == 1
     assert lib.pkv_swap_blocks(None, fake, fake, fake, fake, fake, 1, None) == 1
+
+
+def test_prefix_cache_switch_and_plain_fallback(pkv_lib):
+    bm = pkv_lib.BlockManager(8, 4, list(range(8)))
+    assert bm.add_seq_tokens(0, [1, 2, 3, 4, 5]) == 0  # cache off: plain add
+    assert pkv_lib.load().pkv_bm_set_prefix_cache(bm._h, 1) == 1  # a manager with sequences cannot switch
+    bm.free_seq(0)
+    assert pkv_lib.load().pkv_bm_set_prefix_cache(bm._h, 1) == 0
+    assert bm.add_seq_tokens(1, [1, 2, 3, 4, 5]) == 0
+    assert bm.add_seq_tokens(2, [1, 2, 3, 4, 5]) == 4 and bm.num_cached() == 1

@@ -180,3 +180,67 @@ def test_moves_between_two_managers_match_oracle(pkv_lib, B):
         with pytest.raises(pkv_lib.PkvError):
             lg.move_seqs(lc, [10 ** 6])
         assert lg.num_free() == free_before
+
+
+@pytest.mark.parametrize("B", [4, 16])
+def test_prefix_cache_matches_oracle(pkv_lib, B):
+    """Random request streams over a small pool: prompts share system prefixes, some
+    repeat exactly, sequences decode, fork and leave; evictions happen under pressure.
+    Tables, counts, cached-block counts and every cached-token answer must match."""
+    from oracle.block_manager import PrefixCachingBlockManager
+    rng = np.random.default_rng(7 + B)
+    NB = 60
+    order = rng.permutation(NB)
+    lib_bm = pkv_lib.BlockManager(NB, B, order, prefix_cache=True)
+    ora = PrefixCachingBlockManager(NB, B, order)
+    systems = [rng.integers(0, 1000, size=int(rng.integers(B, 5 * B))).tolist() for _ in range(4)]
+    seen = []
+    live, nxt, hits = [], 0, 0
+    for it in range(700):
+        op = rng.random()
+        if op < 0.35 or not live:
+            if seen and rng.random() < 0.2:
+                prompt = list(seen[int(rng.integers(len(seen)))])
+            else:
+                prompt = systems[int(rng.integers(4))] + rng.integers(0, 1000, size=int(rng.integers(0, 2 * B))).tolist()
+            if not prompt:
+                continue
+            try:
+                c1 = ora.add_seq_tokens(nxt, prompt)
+                ok = True
+            except OutOfBlocks:
+                ok = False
+            if ok:
+                c2 = lib_bm.add_seq_tokens(nxt, prompt)
+                assert c2 == c1
+                hits += c1 > 0
+                live.append(nxt)
+                seen.append(prompt)
+            else:
+                with pytest.raises(pkv_lib.PkvError) as e:
+                    lib_bm.add_seq_tokens(nxt, prompt)
+                assert e.value.status == 5
+            nxt += 1
+        elif op < 0.45:
+            p = int(rng.choice(live))
+            ora.fork(p, nxt)
+            lib_bm.fork(p, nxt)
+            live.append(nxt)
+            nxt += 1
+        elif op < 0.75 and live:
+            s = live.pop(int(rng.integers(len(live))))
+            ora.free_seq(s)
+            lib_bm.free_seq(s)
+        else:
+            seqs = sorted(live)
+            if ora._available() < 2 * len(seqs):
+                continue
+            s1, p1 = ora.step(seqs)
+            s2, p2 = lib_bm.step(seqs)
+            assert s2.tolist() == s1 and p2.tolist() == [list(p) for p in p1]
+        for s in live:
+            assert lib_bm.block_table(s) == ora.block_table(s)
+        assert [lib_bm.refcount(b) for b in range(NB)] == ora.refcount
+        assert lib_bm.num_free() == ora._available()
+        assert lib_bm.num_cached() == len(ora.cached)
+    assert hits > 20  # the stream did exercise reuse
