@@ -5,7 +5,9 @@ copies of the step (if any), then one launch that writes the step's new tokens
 into their slots (from the host block manager) and plans the attention, then the
 attention partition pass, whose last finisher per row does the log-sum-exp merge
 (a separate merge kernel for rows of more than 32 partitions).  Inputs are seeded
-synthetic data already resident in HBM.
+synthetic data already resident in HBM.  The step's launches are captured once as
+a HIP graph and the timed steps are graph replays (``--eager`` times stream
+launches instead; both are reported).
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole step (attention's
 algorithmic K+V bytes / step time); ``roofline`` describes the dominant kernel
@@ -465,6 +467,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="extra partition-pass timings, each after a 512 MiB cache flush")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the decode step as stream launches instead of replays of its HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -557,7 +561,7 @@ def main():
         if e is not None:
             e[1].record(stream)
 
-    # timed region: exactly `steps` steps; events bracket the partition kernel in each
+    # timed region (eager): exactly `steps` steps; events bracket the partition kernel in each
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for _ in range(args.warmup):
         step()
@@ -567,7 +571,32 @@ def main():
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    eager_ms = wall * 1e3 / args.steps
+    ms_step = eager_ms
+    graph_ms = None
+    if not args.eager:
+        # The decode step has a fixed shape, so it is captured once as a HIP graph and
+        # replayed: one launch per step instead of three (data.6616ai.com
+        # "PagedAttention 之外": graph capture removes the per-launch CPU cost of decode).
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        ms_step = graph_ms
+        log(f"graph replay: {graph_ms:.4f} ms per step (stream launches {eager_ms:.4f} ms)")
     part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
 
     # outside the timed region: the other passes on their own, then the partition
@@ -632,6 +661,8 @@ def main():
                       "attn_plan_alone": round(plan_ms, 5)},
         "attn_partitions_ms_after_cache_flush": round(float(np.median(flushed)), 5) if flushed else None,
         "host_block_manager_step_us": round(host_bm_us, 1),
+        "step_launch": "eager" if graph_ms is None else "hip_graph",
+        "eager_ms_per_step": round(eager_ms, 5),
         "roofline": {"kernel": "attn_partition", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": ab},
