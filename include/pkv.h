@@ -1,5 +1,6 @@
 /*
- * pkv.h -- paged KV cache for decode on AMD Instinct MI355X (gfx950): C ABI.
+ * pkv.h -- paged KV cache on AMD Instinct MI355X (gfx950): C ABI (decode attention,
+ * KV write, copy-on-write, prefill / chunked prefill, swap, prefix caching).
  *
  * The method (pages: agentalpha.top "Q32：vLLM PagedAttention 原理", data.6616ai.com
  * "vLLM" article, ohmygp.com "batch-008-day-02-interview-1"): the KV cache is cut
@@ -18,7 +19,11 @@
  *  - A call returns a pkv_status.  On failure nothing is enqueued and
  *    pkv_last_error() returns a message for the calling thread.
  *  - Preconditions marked "device" are not checked on the host (that would need a
- *    device->host sync); violating them is undefined behaviour.
+ *    device->host sync); violating them is undefined behaviour.  A debug build of
+ *    the library (PKV_DEBUG=1, libpkv_debug.so) checks them: each call waits for
+ *    `stream`, copies the slots, block tables, context lengths, copy pairs or chunk
+ *    offsets it is about to use to the host, and returns INVALID_ARG on a violation
+ *    before enqueuing anything (so every debug call is synchronous).
  *
  * KV pool layout (the pages do not fix one).  Let X = 16 / element_bytes (8 for
  * bf16/fp16, 4 for fp32), H = num_kv_heads, D = head_dim, B = block_size.

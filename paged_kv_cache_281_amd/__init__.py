@@ -56,7 +56,20 @@ def load():
     path = library_path()
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m paged_kv_cache_281_amd.build`")
-    lib = ctypes.CDLL(path)
+    _LIB = _bind(ctypes.CDLL(path))
+    return _LIB
+
+
+def load_debug():
+    """The debug build (libpkv_debug.so, PKV_DEBUG=1): same C ABI, with every device
+    precondition checked on the host before launch.  Raises if it has not been built."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv_debug.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m paged_kv_cache_281_amd.build --debug`")
+    return _bind(ctypes.CDLL(path))
+
+
+def _bind(lib):
     P = ctypes.POINTER
     sig = {
         "pkv_version": ([], ctypes.c_char_p),
@@ -99,7 +112,6 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
-    _LIB = lib
     return lib
 
 

@@ -1,10 +1,14 @@
 // C ABI of libpkv: argument validation, workspace sizing and dispatch to the
-// gfx950 kernels.  No entry point allocates device memory or synchronises.
+// gfx950 kernels.  No entry point allocates device memory or synchronises, except in
+// a debug build (PKV_DEBUG=1), whose entry points wait for the stream to check the
+// device arrays they are given.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "pkv.h"
 #include "pkv_internal.h"
@@ -145,6 +149,105 @@ int32_t set_error(int32_t status, const char* msg) {
   return status;
 }
 
+// ---------------------------------------------------------------------------------
+// Precondition checks of a debug build (PKV_DEBUG=1).  A release build trusts the
+// device arrays it is given (block ids, slots, lengths, copy pairs, chunk offsets);
+// a debug build waits for the caller's stream, copies the arrays the call is about
+// to use to the host and rejects violations with INVALID_ARG before any launch, so
+// every debug call is synchronous.
+// ---------------------------------------------------------------------------------
+#ifndef PKV_DEBUG
+#define PKV_DEBUG 0
+#endif
+constexpr bool kDebugChecks = PKV_DEBUG != 0;
+
+template <class T>
+bool fetch_host(const T* p, int64_t n, void* stream, std::vector<T>& out) {
+  out.assign(static_cast<size_t>(n), T{});
+  if (n == 0) return true;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return false;
+  return hipMemcpy(out.data(), p, static_cast<size_t>(n) * sizeof(T), hipMemcpyDefault) == hipSuccess;
+}
+
+int32_t debug_fail(const char* who, const char* what) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s: debug check failed: %s", who, what);
+  return set_error(PKV_ERR_INVALID_ARG, buf);
+}
+
+// slots < num_blocks * B; non-negative slots distinct
+int32_t debug_check_slots(const char* who, const pkv_pool_desc& pool, const int64_t* slots, int32_t n,
+                          void* stream) {
+  std::vector<int64_t> h;
+  if (!fetch_host(slots, n, stream, h)) return debug_fail(who, "cannot read slot_mapping");
+  const int64_t limit = static_cast<int64_t>(pool.num_blocks) * pool.block_size;
+  std::vector<int64_t> seen;
+  for (int64_t x : h) {
+    if (x >= limit) return debug_fail(who, "slot past the pool");
+    if (x >= 0) seen.push_back(x);
+  }
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return debug_fail(who, "duplicate slot");
+  return PKV_OK;
+}
+
+// 0 <= context_lens[b] <= W * B; table entries that are read lie in the pool
+int32_t debug_check_tables(const char* who, const pkv_pool_desc& pool, const int32_t* tables, int32_t W,
+                           const int32_t* lens, int32_t n, void* stream) {
+  std::vector<int32_t> hl, ht;
+  if (!fetch_host(lens, n, stream, hl)) return debug_fail(who, "cannot read context_lens");
+  if (tables && !fetch_host(tables, static_cast<int64_t>(n) * W, stream, ht))
+    return debug_fail(who, "cannot read block_tables");
+  for (int32_t b = 0; b < n; ++b) {
+    if (hl[b] < 0 || static_cast<int64_t>(hl[b]) > static_cast<int64_t>(W) * pool.block_size)
+      return debug_fail(who, "context length outside 0 .. max_blocks_per_seq * block_size");
+    if (!tables) continue;
+    const int32_t used = (hl[b] + pool.block_size - 1) / pool.block_size;
+    for (int32_t j = 0; j < used; ++j) {
+      const int32_t blk = ht[static_cast<size_t>(b) * W + j];
+      if (blk < 0 || blk >= pool.num_blocks) return debug_fail(who, "block table entry outside the pool");
+    }
+  }
+  return PKV_OK;
+}
+
+// copy pairs: ids in the pool, destinations distinct and never a source
+int32_t debug_check_pairs(const char* who, const pkv_pool_desc& pool, const int64_t* pairs, int32_t n,
+                          void* stream) {
+  std::vector<int64_t> h;
+  if (!fetch_host(pairs, 2 * static_cast<int64_t>(n), stream, h)) return debug_fail(who, "cannot read pairs");
+  std::vector<int64_t> src, dst;
+  for (int32_t i = 0; i < n; ++i) {
+    if (h[2 * i] < 0 || h[2 * i] >= pool.num_blocks || h[2 * i + 1] < 0 || h[2 * i + 1] >= pool.num_blocks)
+      return debug_fail(who, "block id outside the pool");
+    src.push_back(h[2 * i]);
+    dst.push_back(h[2 * i + 1]);
+  }
+  std::sort(src.begin(), src.end());
+  std::sort(dst.begin(), dst.end());
+  if (std::adjacent_find(dst.begin(), dst.end()) != dst.end()) return debug_fail(who, "duplicate destination");
+  for (int64_t d : dst)
+    if (std::binary_search(src.begin(), src.end(), d)) return debug_fail(who, "a destination is also a source");
+  return PKV_OK;
+}
+
+// chunk offsets: query_start[0] = 0, non-decreasing, query_start[N] = T, every chunk
+// at most max_query_len and at most its context
+int32_t debug_check_chunks(const char* who, const int32_t* qstart, const int32_t* lens, int32_t n, int32_t T,
+                           int32_t max_query_len, void* stream) {
+  std::vector<int32_t> hq, hl;
+  if (!fetch_host(qstart, static_cast<int64_t>(n) + 1, stream, hq) || !fetch_host(lens, n, stream, hl))
+    return debug_fail(who, "cannot read query_start / context_lens");
+  if (hq[0] != 0 || hq[n] != T) return debug_fail(who, "query_start must run from 0 to num_tokens");
+  for (int32_t b = 0; b < n; ++b) {
+    const int32_t C = hq[b + 1] - hq[b];
+    if (C < 0) return debug_fail(who, "query_start decreases");
+    if (C > max_query_len) return debug_fail(who, "a chunk is longer than max_query_len");
+    if (C > hl[b]) return debug_fail(who, "a chunk is longer than its context");
+  }
+  return PKV_OK;
+}
+
 }  // namespace pkv
 
 using pkv::set_error;
@@ -202,6 +305,9 @@ int32_t pkv_paged_kv_write(const pkv_pool_desc* pool, void* k_pool, void* v_pool
                            const void* v_new, const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
   int32_t st = check_write("pkv_paged_kv_write", pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens);
   if (st != PKV_OK || num_tokens == 0) return st;
+  if (pkv::kDebugChecks && (st = pkv::debug_check_slots("pkv_paged_kv_write", *pool, slot_mapping, num_tokens,
+                                                        stream)) != PKV_OK)
+    return st;
   return pkv::launch_status(pkv::launch_kv_write(*pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream),
                             "pkv_paged_kv_write");
 }
@@ -217,6 +323,12 @@ int32_t pkv_decode_prepare(const pkv_pool_desc* pool, void* k_pool, void* v_pool
                                           workspace, workspace_bytes, false, false);
   if (c.status != PKV_OK) return c.status;
   if (num_seqs == 0) return pkv_paged_kv_write(pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream);
+  if (pkv::kDebugChecks) {
+    if ((st = pkv::debug_check_slots("pkv_decode_prepare", *pool, slot_mapping, num_tokens, stream)) != PKV_OK ||
+        (st = pkv::debug_check_tables("pkv_decode_prepare", *pool, nullptr, max_blocks_per_seq, context_lens,
+                                      num_seqs, stream)) != PKV_OK)
+      return st;
+  }
   return pkv::launch_status(pkv::launch_decode_prepare(c.args, *pool, k_pool, v_pool, k_new, v_new, slot_mapping,
                                                        num_tokens, stream),
                             "pkv_decode_prepare");
@@ -231,6 +343,10 @@ int32_t pkv_copy_blocks(const pkv_pool_desc* pool, void* k_pool, void* v_pool, c
   if (!k_pool || !v_pool || !src_dst_pairs) return set_error(PKV_ERR_INVALID_ARG, "pkv_copy_blocks: null pointer argument");
   if (!pkv::aligned(k_pool, 16) || !pkv::aligned(v_pool, 16) || !pkv::aligned(src_dst_pairs, 8))
     return set_error(PKV_ERR_INVALID_ARG, "pkv_copy_blocks: misaligned pointer");
+  if (pkv::kDebugChecks) {
+    const int32_t dst = pkv::debug_check_pairs("pkv_copy_blocks", *pool, src_dst_pairs, num_pairs, stream);
+    if (dst != PKV_OK) return dst;
+  }
   return pkv::launch_status(pkv::launch_copy_blocks(*pool, k_pool, v_pool, src_dst_pairs, num_pairs, stream),
                             "pkv_copy_blocks");
 }
@@ -266,6 +382,11 @@ int32_t pkv_paged_attention_partitions(const pkv_pool_desc* pool, const void* k_
                                           workspace, workspace_bytes, true);
   if (c.status != PKV_OK) return c.status;
   if (num_seqs == 0) return PKV_OK;
+  if (pkv::kDebugChecks) {
+    const int32_t st = pkv::debug_check_tables("pkv_paged_attention_partitions", *pool, block_tables,
+                                               max_blocks_per_seq, context_lens, num_seqs, stream);
+    if (st != PKV_OK) return st;
+  }
   return pkv::launch_status(pkv::launch_attn_partitions(c.args, stream), "pkv_paged_attention_partitions");
 }
 
@@ -277,6 +398,11 @@ int32_t pkv_paged_attention_plan(const pkv_pool_desc* pool, int32_t num_seqs, in
                                           workspace, workspace_bytes, false, false);
   if (c.status != PKV_OK) return c.status;
   if (num_seqs == 0) return PKV_OK;
+  if (pkv::kDebugChecks) {
+    const int32_t st = pkv::debug_check_tables("pkv_paged_attention_plan", *pool, nullptr, max_blocks_per_seq,
+                                               context_lens, num_seqs, stream);
+    if (st != PKV_OK) return st;
+  }
   return pkv::launch_status(pkv::launch_attn_plan(c.args, stream), "pkv_paged_attention_plan");
 }
 
@@ -343,6 +469,12 @@ int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_poo
     std::snprintf(buf, sizeof(buf), "%s: workspace of %zu bytes (256-byte aligned) needed, got %zu", who, need,
                   workspace_bytes);
     return pkv::set_error(PKV_ERR_WORKSPACE, buf);
+  }
+  if (pkv::kDebugChecks) {
+    int32_t dst = pkv::debug_check_chunks(who, query_start, context_lens, num_seqs, num_tokens, max_query_len, stream);
+    if (dst == PKV_OK)
+      dst = pkv::debug_check_tables(who, *pool, block_tables, max_blocks_per_seq, context_lens, num_seqs, stream);
+    if (dst != PKV_OK) return dst;
   }
   pkv::PrefillArgs a;
   a.workspace = workspace;
