@@ -57,8 +57,10 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w, lens):
-    """Bytes the attention partition pass must move, by item (see the design notes)."""
+def algorithmic_bytes(w, lens, table_format="int32"):
+    """Bytes the attention partition pass must move, by item (see the design notes).
+    Table entries are 4 bytes (2 for 16-bit tables); two-level tables add one 4-byte
+    directory entry per partition."""
     e = w.elem_bytes
     H, D, B, Hq = w.num_kv_heads, w.head_dim, w.block_size, w.num_q_heads
     G = Hq // H
@@ -70,7 +72,10 @@ def algorithmic_bytes(w, lens):
     single = parts <= 1
     out = int(single.sum() * Hq * D * e)
     partials = int(2 * parts[~single].sum() * Hq * (D + 2) * 4)  # written, then read by the merge
-    tables = int(groups * (-(-lens // B)).sum() * 4 + len(lens) * 4)
+    eb = 2 if table_format == "int16" else 4
+    tables = int(groups * (-(-lens // B)).sum() * eb + len(lens) * 4)
+    if table_format == "two_level":
+        tables += int(groups * parts.sum() * 4)
     return {"kv": kv, "q": q, "out": out, "partials": partials, "tables": tables,
             "total": kv + q + out + partials + tables}
 
@@ -469,6 +474,8 @@ def main():
                     help="extra partition-pass timings, each after a 512 MiB cache flush")
     ap.add_argument("--eager", action="store_true",
                     help="time the decode step as stream launches instead of replays of its HIP graph")
+    ap.add_argument("--tables", choices=["int32", "int16", "two_level"], default="int32",
+                    help="block-table format of the decode step (flat int32, flat 16-bit, or two-level)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -540,12 +547,22 @@ def main():
     k_new, v_new = (up(x) for x in w.step_kv(len(w.steps) - 1))
     slots_d = torch.from_numpy(slots).to(dev)
     pairs_d = torch.from_numpy(pairs).to(dev)
-    tables = torch.from_numpy(bm.block_tables(w.batch, w.max_blocks_per_seq, 0)).to(dev)
+    width = w.max_blocks_per_seq
+    if args.tables == "two_level":
+        E = PARTITION_TOKENS // w.block_size
+        ld, lv = bm.block_tables_2l(w.batch, -(-width // E), 0)
+        tables = pkv.TwoLevelTables(torch.from_numpy(ld).to(dev), torch.from_numpy(lv).to(dev))
+        table_bytes = int(ld.nbytes + lv.nbytes)
+        width = ld.shape[1] * E
+    else:
+        tab = bm.block_tables16 if args.tables == "int16" else bm.block_tables
+        tables = torch.from_numpy(tab(w.batch, width, 0)).to(dev)
+        table_bytes = int(tables.numel() * tables.element_size())
     lens_np = np.asarray([bm.seq_len(int(s)) for s in w.batch], dtype=np.int32)
     lens = torch.from_numpy(lens_np).to(dev)
     q = up(w.queries())
     out = torch.empty_like(q)
-    ws = pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_blocks_per_seq, w.block_size, dev)
+    ws = pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, width, w.block_size, dev)
     torch.cuda.synchronize()
     log(f"set-up done; step has {len(pairs)} copy pairs, {len(slots)} new tokens")
 
@@ -631,10 +648,10 @@ def main():
             flushed.append(e0.elapsed_time(e1))
         del scratch
 
-    ab = algorithmic_bytes(w, lens_np)
+    ab = algorithmic_bytes(w, lens_np, args.tables)
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
     achieved = ab["total"] / (part_ms * 1e-3) / 1e9
-    traffic = stored_traffic(args.workload)
+    traffic = stored_traffic(args.workload) if args.tables == "int32" else None
     res = {
         "metric": METRIC,
         "value": round(kv_gbs, 2),
@@ -652,7 +669,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "context_tokens": int(lens_np.sum()), "max_context": int(lens_np.max()),
                    "partition_tokens": PARTITION_TOKENS, "copy_pairs": int(len(pairs)),
-                   "kv_bytes": ab["kv"]},
+                   "kv_bytes": ab["kv"], "tables": args.tables, "table_bytes": table_bytes},
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "attention_kv_gbs": round(ab["kv"] / ((plan_ms + part_ms) * 1e-3) / 1e9, 2),

@@ -203,6 +203,65 @@ int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_poo
                                     const int32_t* context_lens, float scale, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/*
+ * 16-bit block tables: the same calls with uint16 table entries, for pools of at most
+ * 65536 blocks (agentalpha.top Q32 follow-up 1: a block table can use 16-bit indices
+ * while there are fewer than 65536 blocks, halving its memory).  Tables are otherwise
+ * identical; a pool with more blocks is UNSUPPORTED.  Results are bit-identical to the
+ * int32-table calls on the same data.
+ */
+int32_t pkv_paged_attention_decode_t16(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
+                                       const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                       const uint16_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, float scale, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+int32_t pkv_paged_attention_partitions_t16(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                           void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                           const uint16_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, float scale, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+int32_t pkv_paged_attention_prefill_t16(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                        void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                        const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
+                                        const uint16_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, float scale, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
+ * Two-level block tables (agentalpha.top Q32 follow-up 1: a hierarchical table, in the
+ * manner of multi-level page tables, keeps mostly empty tables small).  A sequence's
+ * entries are cut into leaves of E = PKV_PARTITION_TOKENS / block_size int32 block ids
+ * (one attention partition's entries: 32 at block size 16, 16 at 32):
+ *   leaves    device int32 [num_leaves][E];
+ *   leaf_dir  device int32 [num_seqs][dir_width]: the leaf that holds entries
+ *             j*E .. j*E+E-1 of sequence b is leaf_dir[b][j].
+ * Entry j of sequence b is leaves[leaf_dir[b][j / E]][j % E].  Each call equals the
+ * flat-table call with max_blocks_per_seq = dir_width * E on the table those lookups
+ * give, bit for bit.  Only the directory entries and leaf entries of a sequence's
+ * first ceil(L / B) blocks are read; directory entries read must lie in
+ * 0 .. num_leaves - 1 (a device precondition, checked by the debug library).  A batch
+ * whose longest table sets the width of every row stores dir_width int32 per
+ * sequence plus the leaves it uses, instead of dir_width * E per sequence.
+ * Errors: as the flat calls; INVALID_ARG also when dir_width <= 0, num_leaves < 0,
+ * dir_width * E exceeds INT32_MAX, or leaf_dir is null or misaligned.
+ */
+int32_t pkv_paged_attention_decode_2l(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
+                                      const void* q, int32_t num_seqs, int32_t num_q_heads, const int32_t* leaf_dir,
+                                      int32_t dir_width, const int32_t* leaves, int32_t num_leaves,
+                                      const int32_t* context_lens, float scale, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+int32_t pkv_paged_attention_partitions_2l(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                          void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                          const int32_t* leaf_dir, int32_t dir_width, const int32_t* leaves,
+                                          int32_t num_leaves, const int32_t* context_lens, float scale,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+int32_t pkv_paged_attention_prefill_2l(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                       void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                       const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
+                                       const int32_t* leaf_dir, int32_t dir_width, const int32_t* leaves,
+                                       int32_t num_leaves, const int32_t* context_lens, float scale,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes pkv_paged_attention_prefill needs for these sizes (0 on bad input). */
 size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                                    int32_t num_kv_heads);
@@ -285,6 +344,20 @@ int32_t pkv_bm_block_table(const pkv_bm* bm, int32_t seq, int32_t* out, int32_t 
 /* Tables of `seqs` (host, n) as a host int32 [n][width] matrix padded with `pad`. */
 int32_t pkv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t width,
                             int32_t pad, int32_t* out);
+/* The same as a host uint16 matrix (INVALID_ARG if a block id or `pad` exceeds 65535). */
+int32_t pkv_bm_block_tables16(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t width,
+                              int32_t pad, uint16_t* out);
+/* Two-level tables of `seqs` (host, n) for the _2l calls: each table cut into leaves of
+ * PKV_PARTITION_TOKENS / block_size entries, numbered by sequence (in `seqs` order) and
+ * then position; dir_out (host int32 [n][dir_width]) receives the leaf of every run,
+ * leaves_out (host int32 [leaf_cap][entries]) the leaves, the last leaf of a sequence
+ * padded with `pad`.  One more leaf, last, holds only `pad` and is named by the
+ * directory entries past a sequence's leaves.  *num_leaves = the leaves written
+ * (sum over seqs of ceil(blocks / entries), plus 1 when n > 0); with leaves_out null
+ * only *num_leaves is set.  INVALID_ARG when a table needs more than dir_width leaves
+ * or the leaves exceed leaf_cap. */
+int32_t pkv_bm_block_tables_2l(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t dir_width, int32_t pad,
+                               int32_t* dir_out, int32_t* leaves_out, int32_t leaf_cap, int32_t* num_leaves);
 /* Swap-out / swap-in bookkeeping (data.6616ai.com "PagedAttention 之外", scheduler and
  * preemption; "可能的追问": under memory pressure a request's KV goes to CPU memory and
  * comes back later).  Moves `seqs` (host, n, in order) from manager `src` to `dst`

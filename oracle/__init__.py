@@ -15,10 +15,12 @@ What it computes, and the passage each part follows:
   partitioned form with a log-sum-exp merge, and causal attention of a chunk of new
   tokens (prefill / chunked prefill) over the same pool.
 * ``accounting``     - the memory-waste accounting of the ohmygp.com simulation.
+* ``tables``         - flat, 16-bit and two-level block tables and their memory
+  (agentalpha.top Q32 follow-up 1).
 * ``replay``         - replays a ``synth`` workload through the parts above.
 
 Every function here is pinned by a ``-m "not gpu"`` test against something other
 than itself (worked examples from the pages, closed forms, library routines,
 brute force on tiny inputs); no function is "parity unpinned".
 """
-from . import accounting, attention, block_manager, kv_cache, numerics, replay  # noqa: F401
+from . import accounting, attention, block_manager, kv_cache, numerics, replay, tables  # noqa: F401

@@ -14,15 +14,17 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import List, Optional, Sequence, Tuple
+from typing import List, NamedTuple, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
 
 __all__ = [
-    "load", "library_path", "PoolDesc", "alloc_pools", "pool_desc", "paged_kv_write", "copy_blocks",
-    "workspace_bytes", "alloc_workspace", "paged_attention_decode", "paged_attention_partitions",
-    "paged_attention_plan", "decode_prepare", "BlockManager", "PkvError", "PARTITION_TOKENS", "DTYPE_CODES",
+    "load", "load_debug", "library_path", "PoolDesc", "pool_shapes", "alloc_pools", "alloc_host_pools", "pool_desc",
+    "paged_kv_write", "copy_blocks", "swap_blocks", "workspace_bytes", "alloc_workspace", "TwoLevelTables",
+    "paged_attention_decode", "paged_attention_partitions", "paged_attention_plan", "decode_prepare",
+    "prefill_workspace_bytes", "alloc_prefill_workspace", "paged_attention_prefill", "BlockManager", "PkvError",
+    "PARTITION_TOKENS", "DTYPE_CODES",
 ]
 
 PARTITION_TOKENS = 512
@@ -91,6 +93,21 @@ def _bind(lib):
         "pkv_paged_attention_prefill_workspace_bytes": ([_c_i32, _c_i32, _c_i32, _c_i32], _c_sz),
         "pkv_swap_blocks": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp], _c_i32),
         "pkv_bm_move_seqs": ([_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_i32, P(_c_i32)], _c_i32),
+        "pkv_paged_attention_decode_t16": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
+                                            _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_paged_attention_partitions_t16": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
+                                                _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_paged_attention_prefill_t16": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
+                                             _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_bm_block_tables16": ([_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp], _c_i32),
+        "pkv_paged_attention_decode_2l": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
+                                           _c_vp, _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_paged_attention_partitions_2l": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
+                                               _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_paged_attention_prefill_2l": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
+                                            _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp],
+                                           _c_i32),
+        "pkv_bm_block_tables_2l": ([_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_i32, P(_c_i32)], _c_i32),
         "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
         "pkv_bm_set_prefix_cache": ([_c_vp, _c_i32], _c_i32),
         "pkv_bm_add_seq_tokens": ([_c_vp, _c_i32, _c_vp, _c_i32, P(_c_i32)], _c_i32),
@@ -225,17 +242,40 @@ def alloc_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_blocks_p
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
+class TwoLevelTables(NamedTuple):
+    """Two-level block tables: row b of ``leaf_dir`` (int32 ``[N, dir_width]``) names,
+    for every run of ``PARTITION_TOKENS // block_size`` entries of sequence b's table,
+    the row of ``leaves`` (int32 ``[num_leaves, PARTITION_TOKENS // block_size]``) that
+    holds them.  Accepted wherever the attention calls take ``block_tables``."""
+    leaf_dir: torch.Tensor
+    leaves: torch.Tensor
+
+
+def _tables(block_tables, N: int, d: PoolDesc, device):
+    """(entry point suffix, the table arguments of the C call, flat width W)."""
+    if isinstance(block_tables, TwoLevelTables):
+        ld, lv = block_tables
+        E = PARTITION_TOKENS // d.block_size
+        _require(ld.dtype == torch.int32 and ld.dim() == 2 and ld.shape[0] == N and ld.is_contiguous()
+                 and ld.device == device, "leaf_dir must be a contiguous int32 [N, dir_width] device tensor")
+        _require(lv.dtype == torch.int32 and lv.dim() == 2 and lv.shape[1] == E and lv.is_contiguous()
+                 and lv.device == device, f"leaves must be a contiguous int32 [num_leaves, {E}] device tensor")
+        return "_2l", (_ptr(ld), ld.shape[1], _ptr(lv), lv.shape[0]), ld.shape[1] * E
+    _require(block_tables.dtype in (torch.int32, torch.int16) and block_tables.dim() == 2
+             and block_tables.shape[0] == N and block_tables.is_contiguous() and block_tables.device == device,
+             "block_tables must be a contiguous int32 (or 16-bit) [N, W] device tensor, or TwoLevelTables")
+    suffix = "_t16" if block_tables.dtype == torch.int16 else ""
+    return suffix, (_ptr(block_tables), block_tables.shape[1]), block_tables.shape[1]
+
+
 def _attn_args(q, k_pool, v_pool, block_tables, context_lens, out, workspace):
     d = pool_desc(k_pool, v_pool)
     _require(q.dim() == 3 and q.shape[2] == d.head_dim and q.dtype == k_pool.dtype and q.is_contiguous()
              and q.device == k_pool.device, "q must be a contiguous [N, Hq, D] device tensor of the pool dtype")
     N, Hq, _ = q.shape
-    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == N
-             and block_tables.is_contiguous() and block_tables.device == k_pool.device,
-             "block_tables must be a contiguous int32 [N, W] device tensor")
+    _, _, W = _tables(block_tables, N, d, k_pool.device)
     _require(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (N,) and context_lens.is_contiguous()
              and context_lens.device == k_pool.device, "context_lens must be a contiguous int32 [N] device tensor")
-    W = block_tables.shape[1]
     if out is None:
         out = torch.empty_like(q)
     _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous() and out.device == q.device,
@@ -250,9 +290,10 @@ def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """softmax(scale * q K^T) V per sequence and query head, K/V read through the block tables."""
     d, N, Hq, W, out, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, out, workspace)
-    _check(load().pkv_paged_attention_decode(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq,
-                                             _ptr(block_tables), W, _ptr(context_lens), float(scale), _ptr(ws),
-                                             ws.numel(), _stream(q.device)))
+    suffix, targs, _ = _tables(block_tables, N, d, k_pool.device)
+    fn = getattr(load(), "pkv_paged_attention_decode" + suffix)
+    _check(fn(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq, *targs, _ptr(context_lens),
+              float(scale), _ptr(ws), ws.numel(), _stream(q.device)))
     return out
 
 
@@ -284,9 +325,7 @@ def paged_attention_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
              and query_start.device == k_pool.device, "query_start must be a contiguous int32 [N+1] device tensor")
     N = query_start.shape[0] - 1
     _require(N >= 0, "query_start needs N+1 entries")
-    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == N
-             and block_tables.is_contiguous() and block_tables.device == k_pool.device,
-             "block_tables must be a contiguous int32 [N, W] device tensor")
+    suffix, targs, _ = _tables(block_tables, N, d, k_pool.device)
     _require(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (N,) and context_lens.is_contiguous()
              and context_lens.device == k_pool.device, "context_lens must be a contiguous int32 [N] device tensor")
     if out is None:
@@ -295,10 +334,10 @@ def paged_attention_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
              "out must match q")
     if workspace is None:
         workspace = alloc_prefill_workspace(N, T, Hq, d.num_kv_heads, q.device)
-    _check(load().pkv_paged_attention_prefill(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq,
-                                              _ptr(query_start), T, int(max_query_len), _ptr(block_tables),
-                                              block_tables.shape[1], _ptr(context_lens), float(scale),
-                                              _ptr(workspace), workspace.numel(), _stream(q.device)))
+    fn = getattr(load(), "pkv_paged_attention_prefill" + suffix)
+    _check(fn(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq, _ptr(query_start), T,
+              int(max_query_len), *targs, _ptr(context_lens), float(scale), _ptr(workspace), workspace.numel(),
+              _stream(q.device)))
     return out
 
 
@@ -328,9 +367,10 @@ def decode_prepare(k_pool, v_pool, k_new, v_new, slot_mapping, q, block_tables, 
 def paged_attention_partitions(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace) -> None:
     """Second pass of ``paged_attention_decode`` (partitions, with the merge of split rows)."""
     d, N, Hq, W, out, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, out, workspace)
-    _check(load().pkv_paged_attention_partitions(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N,
-                                                 Hq, _ptr(block_tables), W, _ptr(context_lens), float(scale),
-                                                 _ptr(ws), ws.numel(), _stream(q.device)))
+    suffix, targs, _ = _tables(block_tables, N, d, k_pool.device)
+    fn = getattr(load(), "pkv_paged_attention_partitions" + suffix)
+    _check(fn(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq, *targs, _ptr(context_lens),
+              float(scale), _ptr(ws), ws.numel(), _stream(q.device)))
 
 
 # ---- host block manager ----------------------------------------------------------------
@@ -416,6 +456,27 @@ class BlockManager:
         out = np.empty(cap, dtype=np.int32)
         _check(self._lib.pkv_bm_block_table(self._h, seq, out.ctypes.data, cap, ctypes.byref(n)))
         return out[:n.value].tolist()
+
+    def block_tables16(self, seqs: Sequence[int], width: int, pad: int) -> np.ndarray:
+        """Tables as 16-bit entries (``int16`` storage of the unsigned ids), for the
+        ``_t16`` attention calls on pools of at most 65536 blocks."""
+        s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        out = np.empty((len(s), width), dtype=np.uint16)
+        _check(self._lib.pkv_bm_block_tables16(self._h, s.ctypes.data, len(s), width, pad, out.ctypes.data))
+        return out.view(np.int16)
+
+    def block_tables_2l(self, seqs: Sequence[int], dir_width: int, pad: int) -> Tuple[np.ndarray, np.ndarray]:
+        """Two-level tables (host arrays ``leaf_dir`` [n, dir_width], ``leaves``
+        [num_leaves, PARTITION_TOKENS // block_size]) for ``TwoLevelTables``."""
+        s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        ld = np.empty((len(s), dir_width), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_bm_block_tables_2l(self._h, s.ctypes.data, len(s), dir_width, pad, ld.ctypes.data,
+                                                None, 0, ctypes.byref(n)))
+        lv = np.empty((n.value, PARTITION_TOKENS // self.block_size), dtype=np.int32)
+        _check(self._lib.pkv_bm_block_tables_2l(self._h, s.ctypes.data, len(s), dir_width, pad, ld.ctypes.data,
+                                                lv.ctypes.data, n.value, ctypes.byref(n)))
+        return ld, lv
 
     def block_tables(self, seqs: Sequence[int], width: int, pad: int) -> np.ndarray:
         s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))

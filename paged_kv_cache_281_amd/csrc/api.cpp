@@ -64,9 +64,9 @@ size_t workspace_bytes_for(int64_t n, int64_t hq, int64_t d, int64_t parts) {
 
 AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
                           void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
-                          const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          const void* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                           float scale, const void* workspace, size_t workspace_bytes, bool need_pools,
-                          bool need_out = true) {
+                          bool need_out = true, int table_bytes = 4) {
   AttnCheck c{PKV_OK, {}};
   char buf[256];
   if ((c.status = check_pool(pool, who)) != PKV_OK) return c;
@@ -103,7 +103,7 @@ AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void
     }
     if ((need_out && !aligned(out, 16)) ||
         (need_pools && (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(q, 16))) ||
-        !aligned(block_tables, 4) || !aligned(context_lens, 4)) {
+        !aligned(block_tables, table_bytes) || !aligned(context_lens, 4)) {
       std::snprintf(buf, sizeof(buf), "%s: misaligned pointer (pools, q, out need 16 bytes)", who);
       c.status = set_error(PKV_ERR_INVALID_ARG, buf);
       return c;
@@ -122,6 +122,7 @@ AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void
   a.out = out;
   a.q = q;
   a.block_tables = block_tables;
+  a.table_bytes = table_bytes;
   a.context_lens = context_lens;
   const WorkspaceLayout L = workspace_layout(num_seqs, num_q_heads, pool->head_dim, parts);
   char* ws = static_cast<char*>(const_cast<void*>(workspace));
@@ -192,9 +193,11 @@ int32_t debug_check_slots(const char* who, const pkv_pool_desc& pool, const int6
 }
 
 // 0 <= context_lens[b] <= W * B; table entries that are read lie in the pool
-int32_t debug_check_tables(const char* who, const pkv_pool_desc& pool, const int32_t* tables, int32_t W,
+template <class Tab = int32_t>
+int32_t debug_check_tables(const char* who, const pkv_pool_desc& pool, const Tab* tables, int32_t W,
                            const int32_t* lens, int32_t n, void* stream) {
-  std::vector<int32_t> hl, ht;
+  std::vector<int32_t> hl;
+  std::vector<Tab> ht;
   if (!fetch_host(lens, n, stream, hl)) return debug_fail(who, "cannot read context_lens");
   if (tables && !fetch_host(tables, static_cast<int64_t>(n) * W, stream, ht))
     return debug_fail(who, "cannot read block_tables");
@@ -204,7 +207,32 @@ int32_t debug_check_tables(const char* who, const pkv_pool_desc& pool, const int
     if (!tables) continue;
     const int32_t used = (hl[b] + pool.block_size - 1) / pool.block_size;
     for (int32_t j = 0; j < used; ++j) {
-      const int32_t blk = ht[static_cast<size_t>(b) * W + j];
+      const int64_t blk = static_cast<int64_t>(ht[static_cast<size_t>(b) * W + j]);
+      if (blk < 0 || blk >= pool.num_blocks) return debug_fail(who, "block table entry outside the pool");
+    }
+  }
+  return PKV_OK;
+}
+
+// two-level tables: the directory entries that are read name leaves 0 .. num_leaves - 1,
+// and the leaf entries that are read lie in the pool
+int32_t debug_check_tables_2l(const char* who, const pkv_pool_desc& pool, const int32_t* dir,
+                              const int32_t* leaves, int32_t num_leaves, int32_t W, const int32_t* lens,
+                              int32_t n, void* stream) {
+  const int32_t E = PKV_PARTITION_TOKENS / pool.block_size;
+  const int32_t Wd = W / E;
+  std::vector<int32_t> hl, hd, hv;
+  if (!fetch_host(lens, n, stream, hl)) return debug_fail(who, "cannot read context_lens");
+  if (!fetch_host(dir, static_cast<int64_t>(n) * Wd, stream, hd)) return debug_fail(who, "cannot read leaf_dir");
+  if (!fetch_host(leaves, static_cast<int64_t>(num_leaves) * E, stream, hv)) return debug_fail(who, "cannot read leaves");
+  for (int32_t b = 0; b < n; ++b) {
+    if (hl[b] < 0 || static_cast<int64_t>(hl[b]) > static_cast<int64_t>(W) * pool.block_size)
+      return debug_fail(who, "context length outside 0 .. dir_width * leaf entries * block_size");
+    const int32_t used = (hl[b] + pool.block_size - 1) / pool.block_size;
+    for (int32_t j = 0; j < used; ++j) {
+      const int32_t leaf = hd[static_cast<size_t>(b) * Wd + j / E];
+      if (leaf < 0 || leaf >= num_leaves) return debug_fail(who, "leaf directory entry outside the leaves");
+      const int32_t blk = hv[static_cast<size_t>(leaf) * E + j % E];
       if (blk < 0 || blk >= pool.num_blocks) return debug_fail(who, "block table entry outside the pool");
     }
   }
@@ -325,7 +353,7 @@ int32_t pkv_decode_prepare(const pkv_pool_desc* pool, void* k_pool, void* v_pool
   if (num_seqs == 0) return pkv_paged_kv_write(pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream);
   if (pkv::kDebugChecks) {
     if ((st = pkv::debug_check_slots("pkv_decode_prepare", *pool, slot_mapping, num_tokens, stream)) != PKV_OK ||
-        (st = pkv::debug_check_tables("pkv_decode_prepare", *pool, nullptr, max_blocks_per_seq, context_lens,
+        (st = pkv::debug_check_tables<int32_t>("pkv_decode_prepare", *pool, nullptr, max_blocks_per_seq, context_lens,
                                       num_seqs, stream)) != PKV_OK)
       return st;
   }
@@ -372,22 +400,115 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
   return pkv::workspace_bytes_for(num_seqs, num_q_heads, head_dim, pkv::max_partitions(max_blocks_per_seq, block_size));
 }
 
+}  // extern "C"
+
+namespace pkv {
+namespace {
+
+// 16-bit tables address at most 65536 blocks.
+int32_t check_t16(const pkv_pool_desc* pool, const char* who) {
+  if (pool && pool->num_blocks > 65536) {
+    char buf[256];
+    std::snprintf(buf, sizeof(buf), "%s: 16-bit block tables address at most 65536 blocks, the pool has %d", who,
+                  pool->num_blocks);
+    return set_error(PKV_ERR_UNSUPPORTED, buf);
+  }
+  return PKV_OK;
+}
+
+// A two-level table as the calls take it (null dir: a flat table).
+struct LeafRef {
+  const int32_t* dir = nullptr;
+  int32_t num_leaves = 0;
+};
+
+// Entries per leaf of a two-level table, and the flat width it stands for.
+int32_t two_level_width(const char* who, const pkv_pool_desc* pool, int32_t num_seqs, const int32_t* dir,
+                        int32_t dir_width, int32_t num_leaves, int32_t* W) {
+  int32_t st = check_pool(pool, who);
+  if (st != PKV_OK) return st;
+  const int32_t E = PKV_PARTITION_TOKENS / pool->block_size;
+  char buf[256];
+  if (dir_width <= 0 || num_leaves < 0 || dir_width > 0x7fffffff / E) {
+    std::snprintf(buf, sizeof(buf), "%s: dir_width in 1 .. %d and num_leaves >= 0 required", who, 0x7fffffff / E);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (num_seqs > 0 && !dir) {
+    std::snprintf(buf, sizeof(buf), "%s: null pointer argument", who);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (!aligned(dir, 4)) {
+    std::snprintf(buf, sizeof(buf), "%s: misaligned leaf_dir", who);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  *W = dir_width * E;
+  return PKV_OK;
+}
+
+template <class Tab>
+int32_t partitions_impl(const char* who, const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
+                        const void* q, int32_t num_seqs, int32_t num_q_heads, const Tab* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream, LeafRef two = {}, bool with_plan = false) {
+  // every argument is checked before the first launch (the plan pass included)
+  AttnCheck c = check_attention(who, pool, k_pool, v_pool, out, q, num_seqs, num_q_heads, block_tables,
+                                max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes, true, true,
+                                static_cast<int>(sizeof(Tab)));
+  if (c.status != PKV_OK) return c.status;
+  if (num_seqs == 0) return PKV_OK;
+  if (kDebugChecks) {
+    const int32_t st =
+        two.dir ? debug_check_tables_2l(who, *pool, two.dir, reinterpret_cast<const int32_t*>(block_tables),
+                                        two.num_leaves, max_blocks_per_seq, context_lens, num_seqs, stream)
+                : debug_check_tables(who, *pool, block_tables, max_blocks_per_seq, context_lens, num_seqs, stream);
+    if (st != PKV_OK) return st;
+  }
+  c.args.table_dir = two.dir;
+  if (with_plan) {
+    const int rc = launch_attn_plan(c.args, stream);
+    if (rc != 0) return launch_status(rc, who);
+  }
+  return launch_status(launch_attn_partitions(c.args, stream), who);
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" {
+
 int32_t pkv_paged_attention_partitions(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
                                        const void* q, int32_t num_seqs, int32_t num_q_heads,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* context_lens, float scale, void* workspace,
                                        size_t workspace_bytes, void* stream) {
-  pkv::AttnCheck c = pkv::check_attention("pkv_paged_attention_partitions", pool, k_pool, v_pool, out, q, num_seqs,
-                                          num_q_heads, block_tables, max_blocks_per_seq, context_lens, scale,
-                                          workspace, workspace_bytes, true);
-  if (c.status != PKV_OK) return c.status;
-  if (num_seqs == 0) return PKV_OK;
-  if (pkv::kDebugChecks) {
-    const int32_t st = pkv::debug_check_tables("pkv_paged_attention_partitions", *pool, block_tables,
-                                               max_blocks_per_seq, context_lens, num_seqs, stream);
-    if (st != PKV_OK) return st;
-  }
-  return pkv::launch_status(pkv::launch_attn_partitions(c.args, stream), "pkv_paged_attention_partitions");
+  return pkv::partitions_impl("pkv_paged_attention_partitions", pool, k_pool, v_pool, out, q, num_seqs, num_q_heads,
+                              block_tables, max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes,
+                              stream);
+}
+
+int32_t pkv_paged_attention_partitions_t16(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                           void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                           const uint16_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, float scale, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  const int32_t st = pkv::check_t16(pool, "pkv_paged_attention_partitions_t16");
+  if (st != PKV_OK) return st;
+  return pkv::partitions_impl("pkv_paged_attention_partitions_t16", pool, k_pool, v_pool, out, q, num_seqs,
+                              num_q_heads, block_tables, max_blocks_per_seq, context_lens, scale, workspace,
+                              workspace_bytes, stream);
+}
+
+int32_t pkv_paged_attention_partitions_2l(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                          void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                          const int32_t* leaf_dir, int32_t dir_width, const int32_t* leaves,
+                                          int32_t num_leaves, const int32_t* context_lens, float scale,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "pkv_paged_attention_partitions_2l";
+  int32_t W = 0;
+  const int32_t st = pkv::two_level_width(who, pool, num_seqs, leaf_dir, dir_width, num_leaves, &W);
+  if (st != PKV_OK) return st;
+  return pkv::partitions_impl(who, pool, k_pool, v_pool, out, q, num_seqs, num_q_heads, leaves, W, context_lens,
+                              scale, workspace, workspace_bytes, stream, pkv::LeafRef{leaf_dir, num_leaves});
 }
 
 int32_t pkv_paged_attention_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_q_heads,
@@ -399,7 +520,7 @@ int32_t pkv_paged_attention_plan(const pkv_pool_desc* pool, int32_t num_seqs, in
   if (c.status != PKV_OK) return c.status;
   if (num_seqs == 0) return PKV_OK;
   if (pkv::kDebugChecks) {
-    const int32_t st = pkv::debug_check_tables("pkv_paged_attention_plan", *pool, nullptr, max_blocks_per_seq,
+    const int32_t st = pkv::debug_check_tables<int32_t>("pkv_paged_attention_plan", *pool, nullptr, max_blocks_per_seq,
                                                context_lens, num_seqs, stream);
     if (st != PKV_OK) return st;
   }
@@ -410,11 +531,34 @@ int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool
                                    const void* q, int32_t num_seqs, int32_t num_q_heads, const int32_t* block_tables,
                                    int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  int32_t st = pkv_paged_attention_plan(pool, num_seqs, num_q_heads, max_blocks_per_seq, context_lens, workspace,
-                                        workspace_bytes, stream);
-  if (st != PKV_OK || num_seqs == 0) return st;
-  return pkv_paged_attention_partitions(pool, k_pool, v_pool, out, q, num_seqs, num_q_heads, block_tables,
-                                        max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes, stream);
+  return pkv::partitions_impl("pkv_paged_attention_decode", pool, k_pool, v_pool, out, q, num_seqs, num_q_heads,
+                              block_tables, max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes,
+                              stream, {}, true);
+}
+
+int32_t pkv_paged_attention_decode_t16(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
+                                       const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                       const uint16_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, float scale, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const int32_t st = pkv::check_t16(pool, "pkv_paged_attention_decode_t16");
+  if (st != PKV_OK) return st;
+  return pkv::partitions_impl("pkv_paged_attention_decode_t16", pool, k_pool, v_pool, out, q, num_seqs, num_q_heads,
+                              block_tables, max_blocks_per_seq, context_lens, scale, workspace, workspace_bytes,
+                              stream, {}, true);
+}
+
+int32_t pkv_paged_attention_decode_2l(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
+                                      const void* q, int32_t num_seqs, int32_t num_q_heads, const int32_t* leaf_dir,
+                                      int32_t dir_width, const int32_t* leaves, int32_t num_leaves,
+                                      const int32_t* context_lens, float scale, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const char* who = "pkv_paged_attention_decode_2l";
+  int32_t W = 0;
+  const int32_t st = pkv::two_level_width(who, pool, num_seqs, leaf_dir, dir_width, num_leaves, &W);
+  if (st != PKV_OK) return st;
+  return pkv::partitions_impl(who, pool, k_pool, v_pool, out, q, num_seqs, num_q_heads, leaves, W, context_lens,
+                              scale, workspace, workspace_bytes, stream, pkv::LeafRef{leaf_dir, num_leaves}, true);
 }
 
 size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
@@ -423,66 +567,75 @@ size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num
   return pkv::prefill_workspace_bytes(num_tokens, num_seqs, num_q_heads / num_kv_heads);
 }
 
-int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
-                                    void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
-                                    const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
-                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                    const int32_t* context_lens, float scale, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
-  const char* who = "pkv_paged_attention_prefill";
+}  // extern "C"
+
+namespace pkv {
+namespace {
+
+template <class Tab>
+int32_t prefill_impl(const char* who, const pkv_pool_desc* pool, const void* k_pool, const void* v_pool, void* out,
+                     const void* q, int32_t num_seqs, int32_t num_q_heads, const int32_t* query_start,
+                     int32_t num_tokens, int32_t max_query_len, const Tab* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, float scale, void* workspace, size_t workspace_bytes,
+                     void* stream, LeafRef two = {}) {
   char buf[256];
-  int32_t st = pkv::check_pool(pool, who);
+  int32_t st = check_pool(pool, who);
   if (st != PKV_OK) return st;
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) {
     std::snprintf(buf, sizeof(buf), "%s: num_seqs, num_tokens, max_query_len >= 0 and num_q_heads, "
                   "max_blocks_per_seq > 0 required", who);
-    return pkv::set_error(PKV_ERR_INVALID_ARG, buf);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
   }
   if (num_q_heads % pool->num_kv_heads != 0) {
     std::snprintf(buf, sizeof(buf), "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who, num_q_heads,
                   pool->num_kv_heads);
-    return pkv::set_error(PKV_ERR_INVALID_ARG, buf);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
   }
-  if (!pkv::prefill_supported(pool->dtype, pool->head_dim, pool->block_size)) {
+  if (!prefill_supported(pool->dtype, pool->head_dim, pool->block_size)) {
     std::snprintf(buf, sizeof(buf), "%s: no kernel for dtype %d, head_dim %d, block_size %d (bf16/fp16 only)", who,
                   pool->dtype, pool->head_dim, pool->block_size);
-    return pkv::set_error(PKV_ERR_UNSUPPORTED, buf);
+    return set_error(PKV_ERR_UNSUPPORTED, buf);
   }
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
   const int group = num_q_heads / pool->num_kv_heads;
-  const int64_t grid = pkv::prefill_task_bound(num_tokens, num_seqs, group, 64) * pool->num_kv_heads;
+  const int64_t grid = prefill_task_bound(num_tokens, num_seqs, group, 64) * pool->num_kv_heads;
   if (grid > 0x7fffffff || static_cast<int64_t>(num_tokens) * num_q_heads > 0x7fffffff) {
     std::snprintf(buf, sizeof(buf), "%s: problem too large for one launch", who);
-    return pkv::set_error(PKV_ERR_UNSUPPORTED, buf);
+    return set_error(PKV_ERR_UNSUPPORTED, buf);
   }
   if (!k_pool || !v_pool || !out || !q || !query_start || !block_tables || !context_lens) {
     std::snprintf(buf, sizeof(buf), "%s: null pointer argument", who);
-    return pkv::set_error(PKV_ERR_INVALID_ARG, buf);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
   }
-  if (!pkv::aligned(k_pool, 16) || !pkv::aligned(v_pool, 16) || !pkv::aligned(q, 16) || !pkv::aligned(out, 16) ||
-      !pkv::aligned(query_start, 4) || !pkv::aligned(block_tables, 4) || !pkv::aligned(context_lens, 4)) {
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(q, 16) || !aligned(out, 16) ||
+      !aligned(query_start, 4) || !aligned(block_tables, sizeof(Tab)) || !aligned(context_lens, 4)) {
     std::snprintf(buf, sizeof(buf), "%s: misaligned pointer (pools, q, out need 16 bytes)", who);
-    return pkv::set_error(PKV_ERR_INVALID_ARG, buf);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
   }
-  const size_t need = pkv::prefill_workspace_bytes(num_tokens, num_seqs, group);
-  if (workspace_bytes < need || !workspace || !pkv::aligned(workspace, 256)) {
+  const size_t need = prefill_workspace_bytes(num_tokens, num_seqs, group);
+  if (workspace_bytes < need || !workspace || !aligned(workspace, 256)) {
     std::snprintf(buf, sizeof(buf), "%s: workspace of %zu bytes (256-byte aligned) needed, got %zu", who, need,
                   workspace_bytes);
-    return pkv::set_error(PKV_ERR_WORKSPACE, buf);
+    return set_error(PKV_ERR_WORKSPACE, buf);
   }
-  if (pkv::kDebugChecks) {
-    int32_t dst = pkv::debug_check_chunks(who, query_start, context_lens, num_seqs, num_tokens, max_query_len, stream);
+  if (kDebugChecks) {
+    int32_t dst = debug_check_chunks(who, query_start, context_lens, num_seqs, num_tokens, max_query_len, stream);
     if (dst == PKV_OK)
-      dst = pkv::debug_check_tables(who, *pool, block_tables, max_blocks_per_seq, context_lens, num_seqs, stream);
+      dst = two.dir ? debug_check_tables_2l(who, *pool, two.dir, reinterpret_cast<const int32_t*>(block_tables),
+                                            two.num_leaves, max_blocks_per_seq, context_lens, num_seqs, stream)
+                    : debug_check_tables(who, *pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                         stream);
     if (dst != PKV_OK) return dst;
   }
-  pkv::PrefillArgs a;
+  PrefillArgs a;
   a.workspace = workspace;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.out = out;
   a.q = q;
   a.block_tables = block_tables;
+  a.table_bytes = static_cast<int32_t>(sizeof(Tab));
+  a.table_dir = two.dir;
   a.context_lens = context_lens;
   a.query_start = query_start;
   a.num_seqs = num_seqs;
@@ -495,7 +648,51 @@ int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_poo
   a.dtype = pool->dtype;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.scale = scale;
-  return pkv::launch_status(pkv::launch_prefill(a, stream), who);
+  return launch_status(launch_prefill(a, stream), who);
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" {
+
+int32_t pkv_paged_attention_prefill(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                    void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                    const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return pkv::prefill_impl("pkv_paged_attention_prefill", pool, k_pool, v_pool, out, q, num_seqs, num_q_heads,
+                           query_start, num_tokens, max_query_len, block_tables, max_blocks_per_seq, context_lens,
+                           scale, workspace, workspace_bytes, stream);
+}
+
+int32_t pkv_paged_attention_prefill_t16(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                        void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                        const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
+                                        const uint16_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, float scale, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  const int32_t st = pkv::check_t16(pool, "pkv_paged_attention_prefill_t16");
+  if (st != PKV_OK) return st;
+  return pkv::prefill_impl("pkv_paged_attention_prefill_t16", pool, k_pool, v_pool, out, q, num_seqs, num_q_heads,
+                           query_start, num_tokens, max_query_len, block_tables, max_blocks_per_seq, context_lens,
+                           scale, workspace, workspace_bytes, stream);
+}
+
+int32_t pkv_paged_attention_prefill_2l(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                       void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                       const int32_t* query_start, int32_t num_tokens, int32_t max_query_len,
+                                       const int32_t* leaf_dir, int32_t dir_width, const int32_t* leaves,
+                                       int32_t num_leaves, const int32_t* context_lens, float scale,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "pkv_paged_attention_prefill_2l";
+  int32_t W = 0;
+  const int32_t st = pkv::two_level_width(who, pool, num_seqs, leaf_dir, dir_width, num_leaves, &W);
+  if (st != PKV_OK) return st;
+  return pkv::prefill_impl(who, pool, k_pool, v_pool, out, q, num_seqs, num_q_heads, query_start, num_tokens,
+                           max_query_len, leaves, W, context_lens, scale, workspace, workspace_bytes, stream,
+                           pkv::LeafRef{leaf_dir, num_leaves});
 }
 
 }  // extern "C"

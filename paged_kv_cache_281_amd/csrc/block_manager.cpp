@@ -338,6 +338,70 @@ int32_t pkv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, in
   return PKV_OK;
 }
 
+int32_t pkv_bm_block_tables16(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t width, int32_t pad,
+                              uint16_t* out) {
+  if (!bm || (n > 0 && (!seqs || !out))) return bad("pkv_bm_block_tables16: null pointer");
+  if (n < 0 || width < 0) return bad("pkv_bm_block_tables16: negative size");
+  if (pad < 0 || pad > 65535) return bad("pkv_bm_block_tables16: pad does not fit 16 bits");
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq* s = find(bm, seqs[i]);
+    if (!s) return bad("pkv_bm_block_tables16: unknown sequence");
+    if (static_cast<int64_t>(s->table.size()) > width) return bad("pkv_bm_block_tables16: table wider than width");
+    for (int32_t b : s->table)
+      if (b > 65535) return bad("pkv_bm_block_tables16: block id does not fit 16 bits");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq* s = find(bm, seqs[i]);
+    uint16_t* row = out + static_cast<int64_t>(i) * width;
+    const int32_t k = static_cast<int32_t>(s->table.size());
+    for (int32_t j = 0; j < k; ++j) row[j] = static_cast<uint16_t>(s->table[j]);
+    for (int32_t j = k; j < width; ++j) row[j] = static_cast<uint16_t>(pad);
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_bm_block_tables_2l(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t dir_width, int32_t pad,
+                               int32_t* dir_out, int32_t* leaves_out, int32_t leaf_cap, int32_t* num_leaves) {
+  if (!bm || !num_leaves || (n > 0 && (!seqs || !dir_out))) return bad("pkv_bm_block_tables_2l: null pointer");
+  if (n < 0 || dir_width <= 0 || leaf_cap < 0) return bad("pkv_bm_block_tables_2l: bad size");
+  if (PKV_PARTITION_TOKENS % bm->block_size != 0)
+    return bad("pkv_bm_block_tables_2l: the block size does not divide a partition");
+  const int64_t E = PKV_PARTITION_TOKENS / bm->block_size;
+  int64_t total = n > 0 ? 1 : 0;  // the shared padding leaf
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq* s = find(bm, seqs[i]);
+    if (!s) return bad("pkv_bm_block_tables_2l: unknown sequence");
+    const int64_t k = (static_cast<int64_t>(s->table.size()) + E - 1) / E;
+    if (k > dir_width) return bad("pkv_bm_block_tables_2l: table needs more than dir_width leaves");
+    total += k;
+  }
+  if (total > 0x7fffffff) return bad("pkv_bm_block_tables_2l: too many leaves");
+  *num_leaves = static_cast<int32_t>(total);
+  if (!leaves_out) return PKV_OK;  // count only
+  if (total > leaf_cap) return bad("pkv_bm_block_tables_2l: leaves do not fit leaf_cap");
+  if (n == 0) return PKV_OK;
+  const int32_t pad_leaf = static_cast<int32_t>(total - 1);
+  int32_t next = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq* s = find(bm, seqs[i]);
+    const int64_t nb = static_cast<int64_t>(s->table.size());
+    int32_t* drow = dir_out + static_cast<int64_t>(i) * dir_width;
+    for (int64_t j = 0; j < dir_width; ++j) {
+      if (j * E >= nb) {
+        drow[j] = pad_leaf;
+        continue;
+      }
+      drow[j] = next;
+      int32_t* leaf = leaves_out + static_cast<int64_t>(next) * E;
+      for (int64_t e = 0; e < E; ++e) leaf[e] = j * E + e < nb ? s->table[j * E + e] : pad;
+      ++next;
+    }
+  }
+  int32_t* leaf = leaves_out + static_cast<int64_t>(pad_leaf) * E;
+  for (int64_t e = 0; e < E; ++e) leaf[e] = pad;
+  return PKV_OK;
+}
+
 int32_t pkv_bm_refcount(const pkv_bm* bm, int32_t block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
   return bm->refcount[block];

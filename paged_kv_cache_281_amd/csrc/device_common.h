@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
 
 namespace pkv {
 
@@ -162,6 +163,27 @@ __device__ __forceinline__ void pipeline2(int w, int nunits, Buf& A, Load&& load
     compute(u + NW, B);
   } else if (n - i == 1) {
     compute(u, A);
+  }
+}
+
+// Block tables.  Flat (Tab = int or uint16_t): entry j of sequence b is
+// tables[b * W + j].  Two-level (Tab = TwoLevel): the sequence's row of the directory,
+// dir[b * (W / LEAF) ..], names for every run of LEAF entries the leaf that holds them,
+// and leaf l is the int32 entries tables[l * LEAF .. l * LEAF + LEAF).  table_row
+// returns the address of entry e of sequence b; entries up to the end of e's leaf (or
+// row) follow it.  Two-level lookups cost one more (scalar) load.
+struct TwoLevel {};
+template <class Tab> struct TabEntry { typedef Tab type; };
+template <> struct TabEntry<TwoLevel> { typedef int type; };
+
+template <class Tab, int LEAF>
+__device__ __forceinline__ const typename TabEntry<Tab>::type* table_row(const void* tables, const int* dir, int b,
+                                                                         int W, int e) {
+  if constexpr (std::is_same<Tab, TwoLevel>::value) {
+    const int leaf = dir[static_cast<int64_t>(b) * (W / LEAF) + e / LEAF];
+    return static_cast<const int*>(tables) + static_cast<int64_t>(leaf) * LEAF + e % LEAF;
+  } else {
+    return static_cast<const Tab*>(tables) + static_cast<int64_t>(b) * W + e;
   }
 }
 

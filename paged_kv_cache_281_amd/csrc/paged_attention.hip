@@ -61,7 +61,8 @@ struct Params {
   char* out;
   float* ws_o;
   float* ws_ml;
-  const int* tables;
+  const void* tables;   // int32 or uint16 entries, or two-level leaves (the kernels' Tab parameter)
+  const int* dir;       // two-level tables: the leaf directory
   const int* ctx;
   const int2* tasks;    // {sequence * Pmax + partition, context length} items, longest first
   const int* counters;  // counters[0] = number of items
@@ -381,10 +382,10 @@ __device__ __forceinline__ void finish_rows(const Params& P, int b, int hq0, int
 // MFMA partition kernel: bf16/fp16 pools, 2..16 query heads per workgroup.
 // grid = (num_kv_heads * head_groups, max_partitions, num_seqs)
 // ---------------------------------------------------------------------------------
-template <class T, int D, int B, int GMAX>
 #ifndef PKV_MFMA_WAVES_PER_EU
 #define PKV_MFMA_WAVES_PER_EU 1
 #endif
+template <class T, int D, int B, int GMAX, class Tab>
 __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partition_mfma(Params P) {
   constexpr int EB = T::kBytes;
   static_assert(EB == 2, "MFMA path is for 16-bit pools");
@@ -438,9 +439,9 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   // Preamble: issue every load first (the partition's table entries and the queries,
   // then the first unit's block id and its K/V), write LDS afterwards; vmcnt counts
   // in issue order, so the LDS writes wait only for the table and query loads.
-  const int* trow = P.tables + static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP;
+  const auto* trow = table_row<Tab, BPP>(P.tables, P.dir, b, P.W, p * BPP);
   // (unconditional loads from clamped, always-valid addresses keep the waits exact)
-  const int tab_val = __builtin_nontemporal_load(trow + min(tid, nblk - 1));
+  const int tab_val = static_cast<int>(__builtin_nontemporal_load(trow + min(tid, nblk - 1)));
   const bool hv = m < gcur;
   u32x4 qf[KI];
   {
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    load_blk(u0, trow[u0 / SUB], first);
+    load_blk(u0, static_cast<int>(trow[u0 / SUB]), first);
   }
   PKV_FENCE();
   if (tid < nblk) s_tab[tid] = tab_val;
@@ -567,7 +568,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
 // block 32, two 512-byte runs at block 16).
 // grid = (items * num_kv_heads * head_groups)
 // ---------------------------------------------------------------------------------
-template <class T, int D, int B, int GMAX>
+template <class T, int D, int B, int GMAX, class Tab>
 __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partition_mfma32(Params P) {
   constexpr int EB = T::kBytes;
   static_assert(EB == 2, "MFMA path is for 16-bit pools");
@@ -620,8 +621,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int nblk = (ntok + B - 1) / B;
 
   // preamble: all loads first (table entries, queries, first unit), LDS writes after
-  const int* trow = P.tables + static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP;
-  const int tab_val = __builtin_nontemporal_load(trow + min(tid, nblk - 1));
+  const auto* trow = table_row<Tab, BPP>(P.tables, P.dir, b, P.W, p * BPP);
+  const int tab_val = static_cast<int>(__builtin_nontemporal_load(trow + min(tid, nblk - 1)));
   const bool hv = m < gcur;
   u32x4 qf[KI];
   {
@@ -682,8 +683,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    const int blk0 = trow[u0 * BPU];
-    const int blk1 = BPU == 2 ? trow[min(u0 * BPU + 1, nblk - 1)] : blk0;
+    const int blk0 = static_cast<int>(trow[u0 * BPU]);
+    const int blk1 = BPU == 2 ? static_cast<int>(trow[min(u0 * BPU + 1, nblk - 1)]) : blk0;
     load_blk(blk0, blk1, first);
   }
   PKV_FENCE();
@@ -769,7 +770,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
 // Vector-ALU partition kernel: one query head per kv head (any pool type), or fp32
 // pools with G query heads per kv head.  grid = (num_kv_heads, max_partitions, num_seqs)
 // ---------------------------------------------------------------------------------
-template <class T, int D, int B, int G>
+template <class T, int D, int B, int G, class Tab>
 __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   constexpr int EB = T::kBytes;
   constexpr int X = 16 / EB;
@@ -820,8 +821,8 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
 
   // Preamble: issue every load first (table entries, queries, then the first unit's
   // block id and K/V), write LDS afterwards.
-  const int* trow = P.tables + static_cast<int64_t>(b) * P.W + static_cast<int64_t>(p) * BPP;
-  const int tab_val = __builtin_nontemporal_load(trow + min(tid, nblk - 1));  // unconditional: exact waits
+  const auto* trow = table_row<Tab, BPP>(P.tables, P.dir, b, P.W, p * BPP);
+  const int tab_val = static_cast<int>(__builtin_nontemporal_load(trow + min(tid, nblk - 1)));  // unconditional: exact waits
 
   // queries: lane keeps chunks r + 4i of every head (fp32 pools: pre-scaled floats)
   u32x4 qw[G][KL];
@@ -853,7 +854,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    load_blk(u0, trow[u0 / SUB], first);
+    load_blk(u0, static_cast<int>(trow[u0 / SUB]), first);
   }
   PKV_FENCE();
   if (tid < nblk) s_tab[tid] = tab_val;
@@ -996,6 +997,7 @@ Params make_params(const AttnArgs& a) {
   P.ws_o = a.ws_o;
   P.ws_ml = a.ws_ml;
   P.tables = a.block_tables;
+  P.dir = a.table_dir;
   P.ctx = a.context_lens;
   P.tasks = reinterpret_cast<const int2*>(a.tasks);
   P.counters = a.counters;
@@ -1022,7 +1024,7 @@ Params make_params(const AttnArgs& a) {
 template <int B>
 constexpr bool kUnit32 = (B == 16) ? PKV_UNIT32_B16 != 0 : PKV_UNIT32_B32 != 0;
 
-template <class T, int D, int B>
+template <class T, int D, int B, class Tab>
 int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
   const Params P = make_params(a);
   const dim3 block(kThreads);
@@ -1031,12 +1033,12 @@ int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
   if (valu) {
     const dim3 grid(static_cast<unsigned>(items * a.num_kv_heads));
     switch (P.G) {
-      case 1: hipLaunchKernelGGL((attn_partition_valu<T, D, B, 1>), grid, block, 0, s, P); break;
+      case 1: hipLaunchKernelGGL((attn_partition_valu<T, D, B, 1, Tab>), grid, block, 0, s, P); break;
       case 2:
-        if constexpr (T::kBytes == 4) { hipLaunchKernelGGL((attn_partition_valu<T, D, B, 2>), grid, block, 0, s, P); break; }
+        if constexpr (T::kBytes == 4) { hipLaunchKernelGGL((attn_partition_valu<T, D, B, 2, Tab>), grid, block, 0, s, P); break; }
         return -1;
       case 4:
-        if constexpr (T::kBytes == 4) { hipLaunchKernelGGL((attn_partition_valu<T, D, B, 4>), grid, block, 0, s, P); break; }
+        if constexpr (T::kBytes == 4) { hipLaunchKernelGGL((attn_partition_valu<T, D, B, 4, Tab>), grid, block, 0, s, P); break; }
         return -1;
       default: return -1;
     }
@@ -1044,18 +1046,18 @@ int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(items * a.num_kv_heads * P.NHG));
     if (kUnit32<B>) {
       if (P.G <= 4) {
-        hipLaunchKernelGGL((attn_partition_mfma32<T, D, B, 4>), grid, block, 0, s, P);
+        hipLaunchKernelGGL((attn_partition_mfma32<T, D, B, 4, Tab>), grid, block, 0, s, P);
       } else if (P.G <= 8) {
-        hipLaunchKernelGGL((attn_partition_mfma32<T, D, B, 8>), grid, block, 0, s, P);
+        hipLaunchKernelGGL((attn_partition_mfma32<T, D, B, 8, Tab>), grid, block, 0, s, P);
       } else {
-        hipLaunchKernelGGL((attn_partition_mfma32<T, D, B, 16>), grid, block, 0, s, P);
+        hipLaunchKernelGGL((attn_partition_mfma32<T, D, B, 16, Tab>), grid, block, 0, s, P);
       }
     } else if (P.G <= 4) {
-      hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 4>), grid, block, 0, s, P);
+      hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 4, Tab>), grid, block, 0, s, P);
     } else if (P.G <= 8) {
-      hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 8>), grid, block, 0, s, P);
+      hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 8, Tab>), grid, block, 0, s, P);
     } else {
-      hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 16>), grid, block, 0, s, P);
+      hipLaunchKernelGGL((attn_partition_mfma<T, D, B, 16, Tab>), grid, block, 0, s, P);
     }
   }
   const hipError_t e = hipGetLastError();
@@ -1064,10 +1066,17 @@ int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
   return static_cast<int>(hipGetLastError());
 }
 
+template <class T, class Tab>
+int launch_partitions_tab(const AttnArgs& a, hipStream_t s) {
+  if (a.head_dim == 64)
+    return a.block_size == 16 ? launch_partitions_t<T, 64, 16, Tab>(a, s) : launch_partitions_t<T, 64, 32, Tab>(a, s);
+  return a.block_size == 16 ? launch_partitions_t<T, 128, 16, Tab>(a, s) : launch_partitions_t<T, 128, 32, Tab>(a, s);
+}
+
 template <class T>
 int launch_partitions_d(const AttnArgs& a, hipStream_t s) {
-  if (a.head_dim == 64) return a.block_size == 16 ? launch_partitions_t<T, 64, 16>(a, s) : launch_partitions_t<T, 64, 32>(a, s);
-  return a.block_size == 16 ? launch_partitions_t<T, 128, 16>(a, s) : launch_partitions_t<T, 128, 32>(a, s);
+  if (a.table_dir) return launch_partitions_tab<T, TwoLevel>(a, s);
+  return a.table_bytes == 2 ? launch_partitions_tab<T, uint16_t>(a, s) : launch_partitions_tab<T, int>(a, s);
 }
 
 }  // namespace

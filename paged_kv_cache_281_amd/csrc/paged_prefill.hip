@@ -60,7 +60,8 @@ struct PrefillParams {
   const char* kp;
   const char* vp;
   char* out;
-  const int* tables;
+  const void* tables;  // int32 or uint16 entries, or two-level leaves (the kernel's Tab parameter)
+  const int* dir;      // two-level tables: the leaf directory
   const int* ctx;
   const int* qstart;
   int2* tasks;    // (sequence, tile) tasks, most units first (plan pass)
@@ -146,7 +147,7 @@ struct PrefillSmem {
   char buf[2][kBytes];
 };
 
-template <class T, int D, int B, int RG>
+template <class T, int D, int B, int RG, class Tab>
 __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) {
   constexpr int EB = T::kBytes;
   static_assert(EB == 2, "MFMA path is for 16-bit pools");
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
 
   // this thread's pieces of every unit: K piece i = tid + 256 x -> chunk i / 32, slot i % 32
   // (slot = 16 s + mm holds token tau_s(mm)); V piece i -> row i / 4, tokens 8 (i % 4) ..
-  const int* trow = P.tables + static_cast<int64_t>(b) * P.W;
+  constexpr int LEAF = PKV_PARTITION_TOKENS / B;  // two-level leaf: 512 tokens' entries
   const int64_t bstride = static_cast<int64_t>(P.Hkv) * TILE;
   const char* kbase = P.kp + kvh * TILE;
   const char* vbase = P.vp + kvh * TILE;
@@ -248,9 +249,10 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     u32x4 v[VPT];
   };
   auto fetch = [&](int u, Stage& st) {
-    const int e0 = u * BPU;
-    const int blk0 = trow[e0];  // uniform: scalar loads
-    const int blk1 = BPU == 2 ? trow[min(e0 + 1, nblk - 1)] : blk0;  // absent second block: reuse the first
+    const int e0 = u * BPU;  // a unit's entries lie in one leaf (LEAF is a multiple of BPU)
+    const auto* trow = table_row<Tab, LEAF>(P.tables, P.dir, b, P.W, e0);
+    const int blk0 = static_cast<int>(trow[0]);  // uniform: scalar loads
+    const int blk1 = BPU == 2 ? static_cast<int>(trow[e0 + 1 < nblk ? 1 : 0]) : blk0;  // absent second block: reuse the first
     const char* k0 = kbase + blk0 * bstride;
     const char* v0 = vbase + blk0 * bstride;
     const char* k1 = kbase + blk1 * bstride;
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
   }
 }
 
-template <class T, int D, int B, int RG>
+template <class T, int D, int B, int RG, class Tab>
 int launch_prefill_rg(const PrefillArgs& a, PrefillParams P, hipStream_t s) {
   P.rows = 16 * RG * kPfWaves;
   P.cap = static_cast<int>(prefill_task_bound(a.num_tokens, a.num_seqs, P.G, P.rows));
@@ -413,11 +415,12 @@ int launch_prefill_rg(const PrefillArgs& a, PrefillParams P, hipStream_t s) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return static_cast<int>(e);
   const int64_t grid = static_cast<int64_t>(P.cap) * P.Hkv;
-  hipLaunchKernelGGL((attn_prefill_lds<T, D, B, RG>), dim3(static_cast<unsigned>(grid)), dim3(kPfThreads), 0, s, P);
+  hipLaunchKernelGGL((attn_prefill_lds<T, D, B, RG, Tab>), dim3(static_cast<unsigned>(grid)), dim3(kPfThreads), 0, s,
+                     P);
   return static_cast<int>(hipGetLastError());
 }
 
-template <class T, int D, int B>
+template <class T, int D, int B, class Tab>
 int launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   PrefillParams P;
   P.q = static_cast<const char*>(a.q);
@@ -425,6 +428,7 @@ int launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   P.vp = static_cast<const char*>(a.v_pool);
   P.out = static_cast<char*>(a.out);
   P.tables = a.block_tables;
+  P.dir = a.table_dir;
   P.ctx = a.context_lens;
   P.qstart = a.query_start;
   P.counters = static_cast<int*>(a.workspace);
@@ -440,14 +444,21 @@ int launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
   P.cap = 0;
   P.scale_log2 = a.scale * kLog2e;
   if (static_cast<int64_t>(a.max_query_len) * P.G >= 16 * kRGBig * kPfWaves)
-    return launch_prefill_rg<T, D, B, kRGBig>(a, P, s);
-  return launch_prefill_rg<T, D, B, kRGSmall>(a, P, s);
+    return launch_prefill_rg<T, D, B, kRGBig, Tab>(a, P, s);
+  return launch_prefill_rg<T, D, B, kRGSmall, Tab>(a, P, s);
+}
+
+template <class T, class Tab>
+int launch_prefill_tab(const PrefillArgs& a, hipStream_t s) {
+  if (a.head_dim == 64)
+    return a.block_size == 16 ? launch_prefill_t<T, 64, 16, Tab>(a, s) : launch_prefill_t<T, 64, 32, Tab>(a, s);
+  return a.block_size == 16 ? launch_prefill_t<T, 128, 16, Tab>(a, s) : launch_prefill_t<T, 128, 32, Tab>(a, s);
 }
 
 template <class T>
 int launch_prefill_d(const PrefillArgs& a, hipStream_t s) {
-  if (a.head_dim == 64) return a.block_size == 16 ? launch_prefill_t<T, 64, 16>(a, s) : launch_prefill_t<T, 64, 32>(a, s);
-  return a.block_size == 16 ? launch_prefill_t<T, 128, 16>(a, s) : launch_prefill_t<T, 128, 32>(a, s);
+  if (a.table_dir) return launch_prefill_tab<T, TwoLevel>(a, s);
+  return a.table_bytes == 2 ? launch_prefill_tab<T, uint16_t>(a, s) : launch_prefill_tab<T, int>(a, s);
 }
 
 }  // namespace

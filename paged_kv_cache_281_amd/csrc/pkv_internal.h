@@ -41,7 +41,8 @@ struct AttnArgs {
   const void* v_pool;
   void* out;
   const void* q;
-  const int32_t* block_tables;
+  const void* block_tables;  // int32, or uint16 when table_bytes == 2; two-level: the leaves
+  const int32_t* table_dir = nullptr;  // two-level tables: leaf directory [N][W / leaf entries], else null
   const int32_t* context_lens;
   float* ws_o;   // [num_seqs][num_q_heads][max_partitions][head_dim]
   float* ws_ml;  // [num_seqs][num_q_heads][max_partitions][2]: running max (log2 units), sum
@@ -50,6 +51,7 @@ struct AttnArgs {
   int* done;     // [num_seqs * num_q_heads]: finished partitions per (sequence, head group)
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
   int32_t max_blocks_per_seq, max_parts;
+  int32_t table_bytes;  // 4 (int32 entries) or 2 (uint16 entries)
   float scale;
 };
 
@@ -84,12 +86,14 @@ struct PrefillArgs {
   const void* v_pool;
   void* out;
   const void* q;
-  const int32_t* block_tables;
+  const void* block_tables;  // int32, or uint16 when table_bytes == 2; two-level: the leaves
+  const int32_t* table_dir = nullptr;  // two-level tables: leaf directory [N][W / leaf entries], else null
   const int32_t* context_lens;
   const int32_t* query_start;  // [num_seqs + 1]
   void* workspace;             // prefill_workspace_bytes(...) bytes, 256-byte aligned
   int32_t num_seqs, num_tokens, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
   int32_t max_blocks_per_seq;
+  int32_t table_bytes;
   float scale;
 };
 // Prefill workspace: a 256-byte counter block, then the (sequence, tile) task list.

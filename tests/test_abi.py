@@ -75,6 +75,71 @@ def test_host_side_argument_errors(pkv_lib):
                                         fake, 1.0, fake, 1 << 24, None)
     assert st == 2
     assert lib.pkv_paged_attention_decode(d, None, None, None, None, 0, 32, None, 4, None, 1.0, None, 0, None) == 0
+    # 16-bit tables address at most 65536 blocks
+    big = ctypes.byref(P(65537, 16, 8, 128, 2))
+    for fn in (lib.pkv_paged_attention_decode_t16, lib.pkv_paged_attention_partitions_t16):
+        st = fn(big, fake, fake, fake, fake, 4, 32, fake, 4, fake, 1.0, fake, 1 << 24, None)
+        assert st == 2 and b"65536" in lib.pkv_last_error()
+    st = lib.pkv_paged_attention_prefill_t16(big, fake, fake, fake, fake, 2, 32, fake, 10, 8, fake, 4, fake, 0.1,
+                                             fake, 1 << 20, None)
+    assert st == 2 and b"65536" in lib.pkv_last_error()
+    # at 65536 blocks the 16-bit calls check their arguments like the int32 ones
+    full = ctypes.byref(P(65536, 16, 8, 128, 2))
+    st = lib.pkv_paged_attention_decode_t16(full, fake, fake, fake, fake, 4, 12, fake, 4, fake, 1.0, fake, 1 << 24, None)
+    assert st == 1 and b"multiple" in lib.pkv_last_error()
+    st = lib.pkv_paged_attention_partitions_t16(full, fake, fake, fake, fake, 4, 32, ctypes.c_void_p(0x1001), 4, fake,
+                                                1.0, fake, 1 << 24, None)
+    assert st == 1 and b"misaligned" in lib.pkv_last_error()
+
+
+def test_two_level_host_side_errors(pkv_lib):
+    lib = pkv_lib.load()
+    P = pkv_lib.PoolDesc
+    fake = ctypes.c_void_p(0x1000)
+    d = ctypes.byref(P(64, 16, 8, 128, 2))
+
+    def dec(dir_=fake, dw=4, leaves=fake, nl=8, n=4, ws=1 << 24):
+        return lib.pkv_paged_attention_decode_2l(d, fake, fake, fake, fake, n, 32, dir_, dw, leaves, nl, fake, 1.0,
+                                                 fake, ws, None)
+
+    assert dec(dw=0) == 1 and b"dir_width" in lib.pkv_last_error()
+    assert dec(nl=-1) == 1
+    assert dec(dw=(1 << 31) // 32) == 1  # dir_width * 32 entries overflows int32
+    assert dec(dir_=None) == 1 and b"null" in lib.pkv_last_error()
+    assert dec(dir_=ctypes.c_void_p(0x1002)) == 1 and b"misaligned" in lib.pkv_last_error()
+    assert dec(leaves=None) == 1 and b"null" in lib.pkv_last_error()
+    assert dec(leaves=ctypes.c_void_p(0x1002)) == 1 and b"misaligned" in lib.pkv_last_error()
+    # the flat width is dir_width * 32 entries: the workspace is sized for 4 * 32 blocks
+    need = lib.pkv_paged_attention_workspace_bytes(4, 32, 128, 4 * 32, 16)
+    assert dec(ws=need - 1) == 3
+    assert dec(n=0, dir_=None, leaves=None) == 0
+    st = lib.pkv_paged_attention_partitions_2l(d, fake, fake, fake, fake, 4, 32, fake, 0, fake, 8, fake, 1.0, fake,
+                                               1 << 24, None)
+    assert st == 1
+    st = lib.pkv_paged_attention_prefill_2l(d, fake, fake, fake, fake, 2, 32, fake, 10, 8, None, 4, fake, 8, fake,
+                                            0.1, fake, 1 << 20, None)
+    assert st == 1 and b"null" in lib.pkv_last_error()
+    st = lib.pkv_paged_attention_prefill_2l(None, fake, fake, fake, fake, 2, 32, fake, 10, 8, fake, 4, fake, 8, fake,
+                                            0.1, fake, 1 << 20, None)
+    assert st == 1 and b"null pool" in lib.pkv_last_error()
+    # the block manager's two-level tables
+    bm = pkv_lib.BlockManager(64, 16, list(range(64)))
+    bm.add_seq(0, 33 * 16)  # 33 blocks: two 32-entry leaves
+    with pytest.raises(pkv_lib.PkvError):
+        bm.block_tables_2l([0], 1, 0)
+    d2, lv = bm.block_tables_2l([0], 3, 63)
+    assert d2.tolist() == [[0, 1, 2]] and lv.shape == (3, 32)
+    assert lv[1].tolist() == [32] + [63] * 31 and lv[2].tolist() == [63] * 32
+    n = ctypes.c_int32(0)
+    assert lib.pkv_bm_block_tables_2l(bm._h, (ctypes.c_int32 * 1)(0), 1, 3, 0, (ctypes.c_int32 * 3)(), None, 0,
+                                      ctypes.byref(n)) == 0 and n.value == 3
+    out = (ctypes.c_int32 * 64)()
+    assert lib.pkv_bm_block_tables_2l(bm._h, (ctypes.c_int32 * 1)(0), 1, 3, 0, (ctypes.c_int32 * 3)(), out, 2,
+                                      ctypes.byref(n)) == 1 and b"leaf_cap" in lib.pkv_last_error()
+    odd = pkv_lib.BlockManager(8, 24, list(range(8)))
+    odd.add_seq(0, 5)
+    with pytest.raises(pkv_lib.PkvError):
+        odd.block_tables_2l([0], 1, 0)
 
 
 def test_block_manager_errors(pkv_lib):

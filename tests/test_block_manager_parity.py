@@ -3,6 +3,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import tables as oracle_tables
 from oracle.block_manager import BlockManager as OracleBM, OutOfBlocks
 
 
@@ -70,6 +71,13 @@ def test_random_operations_match_oracle(pkv_lib, B):
     for s in live:
         L = ora.lens[s]
         assert lib_bm.slots(s, 0, L).tolist() == ora.slots(s, 0, L)
+    # two-level tables of the final state, in a shuffled sequence order
+    E = 512 // B
+    seqs = [int(x) for x in rng.permutation(live)]
+    width = max(-(-len(ora.block_table(x)) // E) for x in seqs) + 1
+    d, lv = lib_bm.block_tables_2l(seqs, width, 7)
+    od, olv = oracle_tables.two_level([ora.block_table(x) for x in seqs], B, width, 7)
+    assert np.array_equal(d, od) and np.array_equal(lv, olv)
 
 
 @pytest.mark.parametrize("name,kw", [("tiny_fp32", {}), ("mha_bf16", {}), ("gqa_bf16", {}),
@@ -244,3 +252,28 @@ def test_prefix_cache_matches_oracle(pkv_lib, B):
         assert lib_bm.num_free() == ora._available()
         assert lib_bm.num_cached() == len(ora.cached)
     assert hits > 20  # the stream did exercise reuse
+
+
+def test_block_tables16_match_int32_tables(pkv_lib):
+    """16-bit tables hold the int32 tables' ids as unsigned 16-bit values, including ids
+    above 32767, and the same padding; ids or padding that do not fit are rejected."""
+    NB = 65536
+    order = list(range(NB - 1, -1, -1))  # the first blocks handed out have ids >= 32768
+    bm = pkv_lib.BlockManager(NB, 16, order)
+    bm.add_seq(0, 40)
+    bm.add_seq(1, 0)
+    bm.add_seq(2, 17)
+    t32 = bm.block_tables([2, 0, 1], 4, 9)
+    t16 = bm.block_tables16([2, 0, 1], 4, 9)
+    assert t16.dtype == np.int16 and t16.shape == (3, 4)
+    assert np.array_equal(t16.view(np.uint16).astype(np.int32), t32)
+    assert t32.max() == NB - 1 and t16.view(np.uint16).max() == NB - 1
+    with pytest.raises(pkv_lib.PkvError):
+        bm.block_tables16([0], 4, 65536)
+    with pytest.raises(pkv_lib.PkvError):
+        bm.block_tables16([0], 2, 0)  # three blocks do not fit a width of two
+    big = pkv_lib.BlockManager(NB + 1, 16, list(range(NB, -1, -1)))
+    big.add_seq(0, 16)
+    assert big.block_table(0) == [NB]
+    with pytest.raises(pkv_lib.PkvError):
+        big.block_tables16([0], 1, 0)

@@ -68,6 +68,24 @@ def test_debug_attention_checks(dlib):
     assert b"outside the pool" in dlib.pkv_last_error()
     assert call(tables, torch.tensor([65, 20], dtype=torch.int32, device=DEV)) == 1  # past W * B
     assert b"context length" in dlib.pkv_last_error()
+    # two-level tables: one 32-entry leaf per sequence
+    leaves = torch.full((2, 32), 99, dtype=torch.int32, device=DEV)
+    leaves[0, :4] = torch.tensor([0, 1, 2, 3])
+    leaves[1, :2] = torch.tensor([4, 5])
+
+    def call2(ldir, lens):
+        return dlib.pkv_paged_attention_decode_2l(d, _p(kp), _p(vp), _p(out), _p(q), N, Hq, _p(ldir), 1, _p(leaves),
+                                                  2, _p(lens), 0.1, _p(ws), ws.numel(), _stream())
+
+    ldir = torch.tensor([[0], [1]], dtype=torch.int32, device=DEV)
+    assert call2(ldir, torch.tensor([64, 20], dtype=torch.int32, device=DEV)) == 0
+    assert call2(torch.tensor([[0], [2]], dtype=torch.int32, device=DEV),
+                 torch.tensor([64, 20], dtype=torch.int32, device=DEV)) == 1  # leaf 2 of 2
+    assert b"leaf directory" in dlib.pkv_last_error()
+    assert call2(ldir, torch.tensor([64, 40], dtype=torch.int32, device=DEV)) == 1  # entry 2 of leaf 1 = 99
+    assert b"outside the pool" in dlib.pkv_last_error()
+    assert call2(ldir, torch.tensor([513, 20], dtype=torch.int32, device=DEV)) == 1  # past 32 entries * B
+    assert b"context length" in dlib.pkv_last_error()
     # prefill: chunk offsets
     T = 10
     qp = torch.zeros(T, Hq, D, dtype=torch.bfloat16, device=DEV)
