@@ -26,6 +26,10 @@ roofline is the swap-out copy against PCIe 5.0 x16 (63 GB/s per direction).
 With ``--workload prefix_bf16`` the same prefill batch (64 requests over 4 system
 prompts) is timed with the prefix cache (only uncached tokens written and attended
 from) and without it.
+With ``--workload lenclass_bf16`` the GQA batch is held three ways: all in one block-16
+pool, all in one block-32 pool, and by length class (sequences under 1024 tokens in a
+block-16 pool, the others in a block-32 pool, one decode step over both).  ``value`` is
+the per-class step's K+V GB/s; every configuration's step time and memory are reported.
 """
 from __future__ import annotations
 
@@ -462,6 +466,183 @@ def prefix_main(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def lenclass_main(args, lw, dev):
+    """Decode step of one batch under three block-size choices (see the module docstring)."""
+    import torch
+    import paged_kv_cache_281_amd as pkv
+    base = lw.base
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[base.dtype]
+    log(f"length-class workload: {base.num_seqs} sequences, threshold {lw.threshold}: "
+        f"{lw.short.num_seqs} in block 16, {lw.long.num_seqs} in block 32")
+    t = time.perf_counter()
+    ctx = base.all_context_kv()
+    log(f"generated context values in {time.perf_counter() - t:.1f} s")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdt)
+
+    def setup(w):
+        p = {"w": w}
+        bm = pkv.BlockManager(w.num_blocks, w.block_size, w.free_order)
+        kp, vp = pkv.alloc_pools(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, tdt, dev)
+        kp.view(torch.int16).fill_(0)
+        vp.view(torch.int16).fill_(0)
+        for seq, n in w.prefill:
+            bm.add_seq(seq, n)
+            if n:
+                k, v = ctx[seq]
+                pkv.paged_kv_write(kp, vp, up(k[:n]), up(v[:n]), torch.from_numpy(bm.slots(seq, 0, n)).to(dev))
+        slots, pairs = bm.step(w.steps[-1])
+        assert len(pairs) == 0
+        k_new, v_new = (up(x) for x in w.step_kv(0))
+        lens_np = np.asarray([bm.seq_len(int(s)) for s in w.batch], dtype=np.int32)
+        used_blocks = w.num_blocks - bm.num_free()
+        p.update(bm=bm, kp=kp, vp=vp, k_new=k_new, v_new=v_new, slots=torch.from_numpy(slots).to(dev),
+                 tables=torch.from_numpy(bm.block_tables(w.batch, w.max_blocks_per_seq, 0)).to(dev),
+                 lens_np=lens_np, lens=torch.from_numpy(lens_np).to(dev), q=up(w.queries()),
+                 ws=pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_blocks_per_seq,
+                                        w.block_size, dev),
+                 blocks=used_blocks, slots_alloc=used_blocks * w.block_size)
+        p["out"] = torch.empty_like(p["q"])
+        return p
+
+    stream = torch.cuda.current_stream(dev)
+    results = {}
+    for name, parts_w in (("all_b16", [base]), ("all_b32", [lw.all32]), ("by_class", [lw.short, lw.long])):
+        parts = [setup(w) for w in parts_w]
+        torch.cuda.synchronize()
+
+        def step(ev=None):
+            for i, p in enumerate(parts):
+                w = p["w"]
+                pkv.decode_prepare(p["kp"], p["vp"], p["k_new"], p["v_new"], p["slots"], p["q"], p["tables"],
+                                   p["lens"], p["ws"])
+                if ev is not None:
+                    ev[i][0].record(stream)
+                pkv.paged_attention_partitions(p["q"], p["kp"], p["vp"], p["tables"], p["lens"], w.scale, p["out"],
+                                               p["ws"])
+                if ev is not None:
+                    ev[i][1].record(stream)
+
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in parts] for _ in range(args.steps)]
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        part_ms = [float(np.mean([e[i][0].elapsed_time(e[i][1]) for e in evs])) for i in range(len(parts))]
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        conc_ms = None
+        if len(parts) > 1:
+            # the pools are independent: one graph branch per pool (fork / join on
+            # streams of default priority), so the two partition passes can overlap;
+            # reported beside the one-branch step, which is the step timed
+            branches = [torch.cuda.Stream(device=dev) for _ in parts]
+
+            def step_branches():
+                cur = torch.cuda.current_stream(dev)
+                for b in branches:
+                    b.wait_stream(cur)
+                for p, b in zip(parts, branches):
+                    with torch.cuda.stream(b):
+                        pkv.decode_prepare(p["kp"], p["vp"], p["k_new"], p["v_new"], p["slots"], p["q"],
+                                           p["tables"], p["lens"], p["ws"])
+                        pkv.paged_attention_partitions(p["q"], p["kp"], p["vp"], p["tables"], p["lens"],
+                                                       p["w"].scale, p["out"], p["ws"])
+                for b in branches:
+                    cur.wait_stream(b)
+
+            g2 = torch.cuda.CUDAGraph()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                step_branches()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g2):
+                step_branches()
+            for _ in range(args.warmup):
+                g2.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                g2.replay()
+            torch.cuda.synchronize()
+            conc_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+            log(f"{name}: pools as parallel graph branches {conc_ms:.4f} ms (one branch {graph_ms:.4f})")
+        abs_ = [algorithmic_bytes(p["w"], p["lens_np"]) for p in parts]
+        kv = sum(a["kv"] for a in abs_)
+        used = sum(int(p["lens_np"].sum()) for p in parts)
+        alloc = sum(p["slots_alloc"] for p in parts)
+        per_slot = 2 * base.num_kv_heads * base.head_dim * base.elem_bytes
+        results[name] = {
+            "block_sizes": [p["w"].block_size for p in parts], "sequences": [p["w"].num_seqs for p in parts],
+            "ms_per_step": round(graph_ms, 5), "eager_ms_per_step": round(eager_ms, 5),
+            "parallel_branches_ms_per_step": None if conc_ms is None else round(conc_ms, 5),
+            "partition_kernel_ms": [round(x, 5) for x in part_ms],
+            "kv_gbs": round(kv / (graph_ms * 1e-3) / 1e9, 2),
+            "partition_kernel_gbs": round(sum(a["total"] for a in abs_) / (sum(part_ms) * 1e-3) / 1e9, 2),
+            "tokens": used, "allocated_slots": alloc, "wasted_slots": alloc - used,
+            "kv_bytes_allocated": alloc * per_slot, "table_entries": sum(p["blocks"] for p in parts),
+            "kv_bytes": kv, "algorithmic_bytes": sum(a["total"] for a in abs_),
+        }
+        log(f"{name}: step {graph_ms:.4f} ms (eager {eager_ms:.4f}), partition kernels {part_ms}, "
+            f"waste {alloc - used} slots, {results[name]['table_entries']} table entries")
+        del parts, g
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    r = results["by_class"]
+    achieved = r["algorithmic_bytes"] / (sum(r["partition_kernel_ms"]) * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": r["kv_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": base.dtype,
+        "data": "synthetic",
+        "config": {"workload": lw.name, "threshold": lw.threshold, "num_seqs": base.num_seqs,
+                   "num_q_heads": base.num_q_heads, "num_kv_heads": base.num_kv_heads, "head_dim": base.head_dim,
+                   "block_sizes": "16 below the threshold, 32 from it", "context_tokens": r["tokens"],
+                   "kv_bytes": r["kv_bytes"]},
+        "pct_hbm_peak": round(100.0 * r["kv_gbs"] / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(base.num_seqs / (r["ms_per_step"] * 1e-3), 1),
+        "step_launch": "hip_graph",
+        "configurations": results,
+        "roofline": {"kernel": "attn_partition (block-16 and block-32 launches)", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": r["algorithmic_bytes"]},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(base, ctx, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,6 +684,9 @@ def main():
     ti = {"f32": (np.int32, torch.int32), "f16": (np.int16, torch.int16), "bf16": (np.int16, torch.int16)}
 
     w = synth.by_name(args.workload)
+    if args.workload in synth.LENCLASS_WORKLOADS:
+        lenclass_main(args, w, dev)
+        return
     if args.workload in synth.PREFIX_WORKLOADS:
         prefix_main(args, w, dev)
         return

@@ -11,4 +11,5 @@ from .workloads import (  # noqa: F401
     tiny_fp32, mha_bf16, gqa_bf16, cow_fp16, long_bf16, by_name, WORKLOADS,
     PrefillWorkload, prefill_workload, prefill_bf16, chunked_bf16, PREFILL_WORKLOADS,
     SwapWorkload, swap_bf16, SWAP_WORKLOADS, PrefixWorkload, prefix_bf16, PREFIX_WORKLOADS,
+    restrict, LengthClassWorkload, lenclass_bf16, LENCLASS_WORKLOADS,
 )

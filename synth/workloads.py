@@ -359,6 +359,60 @@ WORKLOADS = {
 }
 
 
+def restrict(base: Workload, name: str, seqs: Sequence[int], block: int, slack: float = 1.1) -> Workload:
+    """``base`` (a one-step decode batch) restricted to ``seqs`` and held in blocks of
+    ``block`` tokens, in a pool of ``slack`` times the blocks it needs placed by a seeded
+    permutation.  Sequence ids and context values are those of ``base``; the step's new
+    tokens and the queries are drawn for the restricted batch."""
+    seqs = sorted(int(x) for x in seqs)
+    pos = {int(s): i for i, s in enumerate(base.batch)}
+    lengths = np.asarray([int(base.context_lens[pos[s]]) for s in seqs], dtype=np.int64)
+    need = int(sum(-(-int(L) // block) for L in lengths))
+    num_blocks = max(1, int(math.ceil(slack * need)))
+    width = int(max([1] + [-(-int(L) // block) for L in lengths]))
+    rng = np.random.default_rng([base.seed, block, len(seqs)])
+    return Workload(
+        name=name, seed=base.seed, dtype=base.dtype, num_q_heads=base.num_q_heads,
+        num_kv_heads=base.num_kv_heads, head_dim=base.head_dim, block_size=block, num_blocks=num_blocks,
+        max_blocks_per_seq=width, scale=base.scale, free_order=rng.permutation(num_blocks).astype(np.int32),
+        prefill=[(s, int(L) - 1) for s, L in zip(seqs, lengths)], forks=[], steps=[seqs],
+        batch=np.asarray(seqs, dtype=np.int32), context_lens=lengths.astype(np.int32),
+        notes=f"{base.name} restricted to {len(seqs)} sequences, block {block}")
+
+
+@dataclasses.dataclass
+class LengthClassWorkload:
+    """One decode batch under a per-length-class block size (agentalpha.top Q32, the
+    résumé note after follow-up 2: short sequences in 16-token blocks, long ones in
+    32-token blocks).  ``short`` and ``long`` split ``base`` at ``threshold`` tokens
+    into a block-16 and a block-32 workload with pools of their own; ``all16`` (=
+    ``base``) and ``all32`` hold the whole batch in one pool of either block size."""
+
+    name: str
+    threshold: int
+    base: Workload
+    short: Workload
+    long: Workload
+    all32: Workload
+
+
+def lenclass_bf16(threshold: int = 1024, num_seqs: int = 256, max_len: Optional[int] = None) -> LengthClassWorkload:
+    """The GQA batch (256 sequences, mix x2, 32/8 heads, D=128, bf16) split at 1024
+    tokens: the mix's short range (70%) in block 16, the rest in block 32."""
+    base = gqa_bf16(num_seqs=num_seqs, max_len=max_len)
+    L = base.context_lens
+    short = [int(s) for s, x in zip(base.batch, L) if int(x) < threshold]
+    long_ = [int(s) for s, x in zip(base.batch, L) if int(x) >= threshold]
+    return LengthClassWorkload(
+        "lenclass_bf16", threshold, base,
+        restrict(base, "lenclass_bf16_short_b16", short, 16),
+        restrict(base, "lenclass_bf16_long_b32", long_, 32),
+        restrict(base, "lenclass_bf16_all_b32", list(base.batch), 32))
+
+
+LENCLASS_WORKLOADS = {"lenclass_bf16": lenclass_bf16}
+
+
 @dataclasses.dataclass
 class SwapWorkload:
     """Preemption by swapping: the ``base`` decode workload's sequences are placed
@@ -463,6 +517,8 @@ PREFILL_WORKLOADS = {
 
 
 def by_name(name: str, **kw):
+    if name in LENCLASS_WORKLOADS:
+        return LENCLASS_WORKLOADS[name](**kw)
     if name in PREFIX_WORKLOADS:
         return PREFIX_WORKLOADS[name](**kw)
     if name in SWAP_WORKLOADS:

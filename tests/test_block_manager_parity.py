@@ -4,6 +4,7 @@ import pytest
 
 import synth
 from oracle import tables as oracle_tables
+from oracle.accounting import class_block_size, paged_footprint
 from oracle.block_manager import BlockManager as OracleBM, OutOfBlocks
 
 
@@ -277,3 +278,23 @@ def test_block_tables16_match_int32_tables(pkv_lib):
     assert big.block_table(0) == [NB]
     with pytest.raises(pkv_lib.PkvError):
         big.block_tables16([0], 1, 0)
+
+
+def test_length_class_pools_match_the_accounting(pkv_lib):
+    """The library's managers allocate, for each block-size choice of the length-class
+    batch, exactly the slots and table entries the oracle's accounting counts."""
+    lw = synth.lenclass_bf16()
+    lens = [int(x) for x in lw.base.context_lens]
+    choices = {"all_b16": ([lw.base], [16] * len(lens)), "all_b32": ([lw.all32], [32] * len(lens)),
+               "by_class": ([lw.short, lw.long], [class_block_size(x, lw.threshold) for x in lens])}
+    for name, (parts, Bs) in choices.items():
+        alloc = entries = 0
+        for w in parts:
+            bm = pkv_lib.BlockManager(w.num_blocks, w.block_size, w.free_order)
+            for s, n in w.prefill:
+                bm.add_seq(s, n)
+            bm.step(w.steps[-1])
+            used = w.num_blocks - bm.num_free()
+            alloc += used * w.block_size
+            entries += used
+        assert (alloc, entries) == paged_footprint(lens, Bs)[::2], name
