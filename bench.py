@@ -52,7 +52,8 @@ SWAP_METRIC = "KV block swap GB/s between the device pool and pinned host memory
 PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-PARTITION_TOKENS = 512
+PARTITION_TOKENS = 1024  # the library's decode partition
+LEAF_TOKENS = 512  # the library's two-level leaf
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_attention.hip")
 PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_prefill.hip")
 
@@ -649,6 +650,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_bf16")
+    ap.add_argument("--num-seqs", type=int, default=None,
+                    help="override the workload's number of sequences (decode workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-reps", type=int, default=10,
@@ -683,7 +686,7 @@ def main():
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
     ti = {"f32": (np.int32, torch.int32), "f16": (np.int16, torch.int16), "bf16": (np.int16, torch.int16)}
 
-    w = synth.by_name(args.workload)
+    w = synth.by_name(args.workload, **({"num_seqs": args.num_seqs} if args.num_seqs else {}))
     if args.workload in synth.LENCLASS_WORKLOADS:
         lenclass_main(args, w, dev)
         return
@@ -733,7 +736,7 @@ def main():
     pairs_d = torch.from_numpy(pairs).to(dev)
     width = w.max_blocks_per_seq
     if args.tables == "two_level":
-        E = PARTITION_TOKENS // w.block_size
+        E = LEAF_TOKENS // w.block_size
         ld, lv = bm.block_tables_2l(w.batch, -(-width // E), 0)
         tables = pkv.TwoLevelTables(torch.from_numpy(ld).to(dev), torch.from_numpy(lv).to(dev))
         table_bytes = int(ld.nbytes + lv.nbytes)

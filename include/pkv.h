@@ -122,7 +122,9 @@ int32_t pkv_swap_blocks(const pkv_pool_desc* pool, const void* src_k, const void
                         void* dst_v, const int64_t* src_dst_pairs, int32_t num_pairs, void* stream);
 
 /* Context tokens per split-context partition of the attention pass. */
-#define PKV_PARTITION_TOKENS 512
+#define PKV_PARTITION_TOKENS 1024
+/* Context tokens whose block ids one leaf of a two-level block table holds. */
+#define PKV_LEAF_TOKENS 512
 
 /* Workspace bytes pkv_paged_attention_decode needs for these sizes (0 on bad input):
  * fp32 partial results of every (sequence, query head, partition), the task list and
@@ -230,8 +232,8 @@ int32_t pkv_paged_attention_prefill_t16(const pkv_pool_desc* pool, const void* k
 /*
  * Two-level block tables (agentalpha.top Q32 follow-up 1: a hierarchical table, in the
  * manner of multi-level page tables, keeps mostly empty tables small).  A sequence's
- * entries are cut into leaves of E = PKV_PARTITION_TOKENS / block_size int32 block ids
- * (one attention partition's entries: 32 at block size 16, 16 at 32):
+ * entries are cut into leaves of E = PKV_LEAF_TOKENS / block_size int32 block ids
+ * (512 tokens' entries: 32 at block size 16, 16 at 32):
  *   leaves    device int32 [num_leaves][E];
  *   leaf_dir  device int32 [num_seqs][dir_width]: the leaf that holds entries
  *             j*E .. j*E+E-1 of sequence b is leaf_dir[b][j].
@@ -348,7 +350,7 @@ int32_t pkv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, in
 int32_t pkv_bm_block_tables16(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t width,
                               int32_t pad, uint16_t* out);
 /* Two-level tables of `seqs` (host, n) for the _2l calls: each table cut into leaves of
- * PKV_PARTITION_TOKENS / block_size entries, numbered by sequence (in `seqs` order) and
+ * PKV_LEAF_TOKENS / block_size entries, numbered by sequence (in `seqs` order) and
  * then position; dir_out (host int32 [n][dir_width]) receives the leaf of every run,
  * leaves_out (host int32 [leaf_cap][entries]) the leaves, the last leaf of a sequence
  * padded with `pad`.  One more leaf, last, holds only `pad` and is named by the

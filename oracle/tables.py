@@ -15,7 +15,7 @@ library):
 * flat: row b of a [N][W] matrix holds entries 0 .. W-1 of sequence b, padded past
   its table; entries are 4-byte ints, or 2-byte unsigned ints below 65536 blocks.
 * two-level: a sequence's entries are cut into leaves of E = 512 / B ids (the
-  entries of one 512-token attention partition); row b of a [N][dir_width]
+  entries of 512 tokens); row b of a [N][dir_width]
   directory names the leaf that holds each run of E entries of sequence b.  Leaves
   are numbered by sequence (in the given order) and then by position; a sequence's
   last leaf is padded with ``pad``; one final leaf holds only ``pad`` and every
@@ -30,7 +30,7 @@ from typing import List, Sequence, Tuple
 
 import numpy as np
 
-PARTITION_TOKENS = 512  # context tokens per attention partition, and per leaf
+LEAF_TOKENS = 512  # context tokens whose block ids one leaf holds
 
 
 def table_entries(context_len: int, block_size: int) -> int:
@@ -49,8 +49,8 @@ def flat_table_bytes(num_seqs: int, width: int, entry_bytes: int) -> int:
 
 
 def leaf_entries(block_size: int) -> int:
-    """Entries per two-level leaf: the blocks of one attention partition."""
-    return PARTITION_TOKENS // int(block_size)
+    """Entries per two-level leaf: the blocks of 512 tokens."""
+    return LEAF_TOKENS // int(block_size)
 
 
 def two_level(tables: Sequence[Sequence[int]], block_size: int, dir_width: int,

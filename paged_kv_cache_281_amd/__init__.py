@@ -24,10 +24,11 @@ __all__ = [
     "paged_kv_write", "copy_blocks", "swap_blocks", "workspace_bytes", "alloc_workspace", "TwoLevelTables",
     "paged_attention_decode", "paged_attention_partitions", "paged_attention_plan", "decode_prepare",
     "prefill_workspace_bytes", "alloc_prefill_workspace", "paged_attention_prefill", "BlockManager", "PkvError",
-    "PARTITION_TOKENS", "DTYPE_CODES",
+    "PARTITION_TOKENS", "LEAF_TOKENS", "DTYPE_CODES",
 ]
 
-PARTITION_TOKENS = 512
+PARTITION_TOKENS = 1024  # decode split-context partition (PKV_PARTITION_TOKENS)
+LEAF_TOKENS = 512  # tokens whose block ids one two-level leaf holds (PKV_LEAF_TOKENS)
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _c_i32, _c_i64, _c_vp, _c_sz, _c_f = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
 
@@ -244,8 +245,8 @@ def alloc_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_blocks_p
 
 class TwoLevelTables(NamedTuple):
     """Two-level block tables: row b of ``leaf_dir`` (int32 ``[N, dir_width]``) names,
-    for every run of ``PARTITION_TOKENS // block_size`` entries of sequence b's table,
-    the row of ``leaves`` (int32 ``[num_leaves, PARTITION_TOKENS // block_size]``) that
+    for every run of ``LEAF_TOKENS // block_size`` entries of sequence b's table,
+    the row of ``leaves`` (int32 ``[num_leaves, LEAF_TOKENS // block_size]``) that
     holds them.  Accepted wherever the attention calls take ``block_tables``."""
     leaf_dir: torch.Tensor
     leaves: torch.Tensor
@@ -255,7 +256,7 @@ def _tables(block_tables, N: int, d: PoolDesc, device):
     """(entry point suffix, the table arguments of the C call, flat width W)."""
     if isinstance(block_tables, TwoLevelTables):
         ld, lv = block_tables
-        E = PARTITION_TOKENS // d.block_size
+        E = LEAF_TOKENS // d.block_size
         _require(ld.dtype == torch.int32 and ld.dim() == 2 and ld.shape[0] == N and ld.is_contiguous()
                  and ld.device == device, "leaf_dir must be a contiguous int32 [N, dir_width] device tensor")
         _require(lv.dtype == torch.int32 and lv.dim() == 2 and lv.shape[1] == E and lv.is_contiguous()
@@ -467,13 +468,13 @@ class BlockManager:
 
     def block_tables_2l(self, seqs: Sequence[int], dir_width: int, pad: int) -> Tuple[np.ndarray, np.ndarray]:
         """Two-level tables (host arrays ``leaf_dir`` [n, dir_width], ``leaves``
-        [num_leaves, PARTITION_TOKENS // block_size]) for ``TwoLevelTables``."""
+        [num_leaves, LEAF_TOKENS // block_size]) for ``TwoLevelTables``."""
         s = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
         ld = np.empty((len(s), dir_width), dtype=np.int32)
         n = ctypes.c_int32(0)
         _check(self._lib.pkv_bm_block_tables_2l(self._h, s.ctypes.data, len(s), dir_width, pad, ld.ctypes.data,
                                                 None, 0, ctypes.byref(n)))
-        lv = np.empty((n.value, PARTITION_TOKENS // self.block_size), dtype=np.int32)
+        lv = np.empty((n.value, LEAF_TOKENS // self.block_size), dtype=np.int32)
         _check(self._lib.pkv_bm_block_tables_2l(self._h, s.ctypes.data, len(s), dir_width, pad, ld.ctypes.data,
                                                 lv.ctypes.data, n.value, ctypes.byref(n)))
         return ld, lv

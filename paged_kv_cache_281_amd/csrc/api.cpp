@@ -219,7 +219,7 @@ int32_t debug_check_tables(const char* who, const pkv_pool_desc& pool, const Tab
 int32_t debug_check_tables_2l(const char* who, const pkv_pool_desc& pool, const int32_t* dir,
                               const int32_t* leaves, int32_t num_leaves, int32_t W, const int32_t* lens,
                               int32_t n, void* stream) {
-  const int32_t E = PKV_PARTITION_TOKENS / pool.block_size;
+  const int32_t E = PKV_LEAF_TOKENS / pool.block_size;
   const int32_t Wd = W / E;
   std::vector<int32_t> hl, hd, hv;
   if (!fetch_host(lens, n, stream, hl)) return debug_fail(who, "cannot read context_lens");
@@ -427,7 +427,7 @@ int32_t two_level_width(const char* who, const pkv_pool_desc* pool, int32_t num_
                         int32_t dir_width, int32_t num_leaves, int32_t* W) {
   int32_t st = check_pool(pool, who);
   if (st != PKV_OK) return st;
-  const int32_t E = PKV_PARTITION_TOKENS / pool->block_size;
+  const int32_t E = PKV_LEAF_TOKENS / pool->block_size;
   char buf[256];
   if (dir_width <= 0 || num_leaves < 0 || dir_width > 0x7fffffff / E) {
     std::snprintf(buf, sizeof(buf), "%s: dir_width in 1 .. %d and num_leaves >= 0 required", who, 0x7fffffff / E);

@@ -364,9 +364,9 @@ int32_t pkv_bm_block_tables_2l(const pkv_bm* bm, const int32_t* seqs, int32_t n,
                                int32_t* dir_out, int32_t* leaves_out, int32_t leaf_cap, int32_t* num_leaves) {
   if (!bm || !num_leaves || (n > 0 && (!seqs || !dir_out))) return bad("pkv_bm_block_tables_2l: null pointer");
   if (n < 0 || dir_width <= 0 || leaf_cap < 0) return bad("pkv_bm_block_tables_2l: bad size");
-  if (PKV_PARTITION_TOKENS % bm->block_size != 0)
-    return bad("pkv_bm_block_tables_2l: the block size does not divide a partition");
-  const int64_t E = PKV_PARTITION_TOKENS / bm->block_size;
+  if (PKV_LEAF_TOKENS % bm->block_size != 0)
+    return bad("pkv_bm_block_tables_2l: the block size does not divide a leaf");
+  const int64_t E = PKV_LEAF_TOKENS / bm->block_size;
   int64_t total = n > 0 ? 1 : 0;  // the shared padding leaf
   for (int32_t i = 0; i < n; ++i) {
     const pkv_bm::Seq* s = find(bm, seqs[i]);

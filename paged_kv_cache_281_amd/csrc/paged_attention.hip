@@ -51,6 +51,8 @@ namespace pkv {
 namespace {
 
 constexpr int kPT = PKV_PARTITION_TOKENS;
+template <int B>
+constexpr int kLeaf = PKV_LEAF_TOKENS / B;  // entries per two-level leaf
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
@@ -439,9 +441,10 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   // Preamble: issue every load first (the partition's table entries and the queries,
   // then the first unit's block id and its K/V), write LDS afterwards; vmcnt counts
   // in issue order, so the LDS writes wait only for the table and query loads.
-  const auto* trow = table_row<Tab, BPP>(P.tables, P.dir, b, P.W, p * BPP);
-  // (unconditional loads from clamped, always-valid addresses keep the waits exact)
-  const int tab_val = static_cast<int>(__builtin_nontemporal_load(trow + min(tid, nblk - 1)));
+  // (unconditional loads from clamped, always-valid addresses keep the waits exact; a
+  // partition may span several two-level leaves, so each lane looks its entry up)
+  const int tab_val = static_cast<int>(__builtin_nontemporal_load(
+      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + min(tid, nblk - 1))));
   const bool hv = m < gcur;
   u32x4 qf[KI];
   {
@@ -473,7 +476,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    load_blk(u0, static_cast<int>(trow[u0 / SUB]), first);
+    load_blk(u0, static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + u0 / SUB)), first);
   }
   PKV_FENCE();
   if (tid < nblk) s_tab[tid] = tab_val;
@@ -621,8 +624,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int nblk = (ntok + B - 1) / B;
 
   // preamble: all loads first (table entries, queries, first unit), LDS writes after
-  const auto* trow = table_row<Tab, BPP>(P.tables, P.dir, b, P.W, p * BPP);
-  const int tab_val = static_cast<int>(__builtin_nontemporal_load(trow + min(tid, nblk - 1)));
+  const int tab_val = static_cast<int>(__builtin_nontemporal_load(
+      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + min(tid, nblk - 1))));
   const bool hv = m < gcur;
   u32x4 qf[KI];
   {
@@ -683,8 +686,10 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    const int blk0 = static_cast<int>(trow[u0 * BPU]);
-    const int blk1 = BPU == 2 ? static_cast<int>(trow[min(u0 * BPU + 1, nblk - 1)]) : blk0;
+    // (the unit's entries lie in one leaf: leaves hold an even number of entries)
+    const auto* e0 = table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + u0 * BPU);
+    const int blk0 = static_cast<int>(e0[0]);
+    const int blk1 = BPU == 2 ? static_cast<int>(e0[u0 * BPU + 1 < nblk ? 1 : 0]) : blk0;
     load_blk(blk0, blk1, first);
   }
   PKV_FENCE();
@@ -821,8 +826,9 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
 
   // Preamble: issue every load first (table entries, queries, then the first unit's
   // block id and K/V), write LDS afterwards.
-  const auto* trow = table_row<Tab, BPP>(P.tables, P.dir, b, P.W, p * BPP);
-  const int tab_val = static_cast<int>(__builtin_nontemporal_load(trow + min(tid, nblk - 1)));  // unconditional: exact waits
+  // (unconditional: exact waits)
+  const int tab_val = static_cast<int>(__builtin_nontemporal_load(
+      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + min(tid, nblk - 1))));
 
   // queries: lane keeps chunks r + 4i of every head (fp32 pools: pre-scaled floats)
   u32x4 qw[G][KL];
@@ -854,7 +860,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    load_blk(u0, static_cast<int>(trow[u0 / SUB]), first);
+    load_blk(u0, static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + u0 / SUB)), first);
   }
   PKV_FENCE();
   if (tid < nblk) s_tab[tid] = tab_val;

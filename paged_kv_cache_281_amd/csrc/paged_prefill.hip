@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
 
   // this thread's pieces of every unit: K piece i = tid + 256 x -> chunk i / 32, slot i % 32
   // (slot = 16 s + mm holds token tau_s(mm)); V piece i -> row i / 4, tokens 8 (i % 4) ..
-  constexpr int LEAF = PKV_PARTITION_TOKENS / B;  // two-level leaf: 512 tokens' entries
+  constexpr int LEAF = PKV_LEAF_TOKENS / B;  // two-level leaf entries
   const int64_t bstride = static_cast<int64_t>(P.Hkv) * TILE;
   const char* kbase = P.kp + kvh * TILE;
   const char* vbase = P.vp + kvh * TILE;

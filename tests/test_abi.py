@@ -32,11 +32,11 @@ def test_status_strings_and_version(pkv_lib):
 
 def test_workspace_and_pool_sizes(pkv_lib):
     lib = pkv_lib.load()
-    # partial outputs (8 sequences x 32 heads x 256 partitions x 128 floats), (max, sum)
+    # partial outputs (8 sequences x 32 heads x 128 partitions x 128 floats), (max, sum)
     # pairs, the (sequence, partition) task list, per-row counters and a counter block,
     # each 256-byte aligned
     n = lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 8192, 16)
-    parts = 8192 * 16 // 512
+    parts = 8192 * 16 // 1024
     al = lambda x: (x + 255) // 256 * 256
     assert n == al(8 * 32 * parts * 128 * 4) + al(8 * 32 * parts * 2 * 4) + al(8 * parts * 8) + al(8 * 32 * 4) + 256
     assert lib.pkv_paged_attention_workspace_bytes(-1, 32, 128, 8, 16) == 0

@@ -24,7 +24,7 @@ DECODE = [
     ("mha_bf16", lambda: synth.mha_bf16(num_seqs=6, max_len=1500)),
     ("gqa_bf16", lambda: synth.gqa_bf16(num_seqs=10, max_len=2100)),
     ("cow_fp16_p1020", lambda: synth.cow_fp16(1020, num_prompts=2, max_suffix=40)),
-    ("long_bf16_b16", lambda: synth.long_bf16(16, num_seqs=2, context=40 * 512)),
+    ("long_bf16_b16", lambda: synth.long_bf16(16, num_seqs=2, context=40 * 1024)),  # the separate merge
     ("long_bf16_b32", lambda: synth.long_bf16(32, num_seqs=2, context=2100)),
 ]
 
@@ -110,7 +110,7 @@ def test_prefill_t16_matches_int32_tables(case):
 
 
 def _two_level(bm, seqs, width_blocks, block_size, pad, device):
-    E = pkv.PARTITION_TOKENS // block_size
+    E = pkv.LEAF_TOKENS // block_size
     dw = -(-width_blocks // E)
     ld, lv = bm.block_tables_2l(seqs, dw, pad)
     return ld, lv, pkv.TwoLevelTables(torch.from_numpy(ld).to(device), torch.from_numpy(lv).to(device))
@@ -136,7 +136,7 @@ def test_decode_two_level_matches_flat_tables(name, make):
     q = to_device(w.queries(), w.dtype, DEV)
     flat = pkv.paged_attention_decode(q, st.k_pool, st.v_pool, st.tables, st.context_lens, w.scale)
     two = pkv.paged_attention_decode(q, st.k_pool, st.v_pool, tl, st.context_lens, w.scale)
-    E = pkv.PARTITION_TOKENS // w.block_size
+    E = pkv.LEAF_TOKENS // w.block_size
     ws = pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, ld.shape[1] * E, w.block_size, DEV)
     pkv.paged_attention_plan(q, st.k_pool, st.v_pool, tl, st.context_lens, ws)
     two_p = torch.empty_like(q)
@@ -157,7 +157,7 @@ def test_prefill_two_level_matches_flat_tables(case):
     ctx = w.all_context_kv()
     st = replay_prefill_gpu(w, ctx, DEV)
     # the two-level form of the flat rows, from the oracle's construction
-    E = pkv.PARTITION_TOKENS // w.block_size
+    E = pkv.LEAF_TOKENS // w.block_size
     tabs = _used(st.tables.cpu().numpy(), np.asarray(w.context_lens), w.block_size)
     ld, lv = oracle_two_level(tabs, w.block_size, -(-w.max_blocks_per_seq // E), 0)
     tl = pkv.TwoLevelTables(torch.from_numpy(ld).to(DEV), torch.from_numpy(lv).to(DEV))

@@ -23,7 +23,7 @@ def test_graph_replays_match_eager_step(name):
     elif name == "cow":
         w = synth.cow_fp16(1020, num_prompts=3, max_suffix=20)
     else:
-        w = synth.long_bf16(16, num_seqs=2, context=40 * 512)  # 40 partitions: the separate merge kernel
+        w = synth.long_bf16(16, num_seqs=2, context=40 * 1024)  # 40 partitions: the separate merge kernel
     log(f"graph replay {name}: {w.num_seqs} sequences")
     ctx = w.all_context_kv()
     st = replay_gpu(w, ctx, DEV)

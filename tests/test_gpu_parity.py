@@ -90,19 +90,19 @@ def _custom(name, dtype, hq, hkv, d, block, lengths, seed):
 
 VARIANTS = [
     # name, dtype, Hq, Hkv, D, B, lengths
-    ("bf16_g1_d64_b32", "bf16", 4, 4, 64, 32, [1, 15, 16, 17, 511, 512, 513, 1100]),
+    ("bf16_g1_d64_b32", "bf16", 4, 4, 64, 32, [1, 15, 16, 17, 511, 512, 513, 1023, 1024, 1025, 2100]),
     ("f16_g1_d128_b16", "f16", 4, 4, 128, 16, [3, 64, 700, 1025]),
     ("bf16_g2_d128_b16", "bf16", 8, 4, 128, 16, [1, 33, 520, 1600]),
-    ("f16_g8_d64_b16", "f16", 16, 2, 64, 16, [2, 47, 512, 1537]),
+    ("f16_g8_d64_b16", "f16", 16, 2, 64, 16, [2, 47, 512, 1024, 1537, 2049]),
     ("bf16_g16_d128_b32", "bf16", 32, 2, 128, 32, [5, 300, 999]),
     ("f16_g4_d64_b32", "f16", 16, 4, 64, 32, [1, 31, 32, 33, 544, 1057]),
-    ("bf16_g8_d128_b32", "bf16", 16, 2, 128, 32, [2, 63, 65, 512, 1600]),
+    ("bf16_g8_d128_b32", "bf16", 16, 2, 128, 32, [2, 63, 65, 512, 1023, 1025, 3100]),
     ("bf16_g5_d128_b16", "bf16", 10, 2, 128, 16, [1, 16, 17, 48, 530, 1111]),
     ("bf16_g32_d128_b16", "bf16", 32, 1, 128, 16, [9, 640, 1030]),
     ("bf16_g3_d128_b16", "bf16", 12, 4, 128, 16, [17, 200, 513]),
     ("f32_g2_d128_b16", "f32", 8, 4, 128, 16, [1, 100, 600]),
     ("f32_g4_d64_b32", "f32", 8, 2, 64, 32, [31, 32, 33, 1000]),
-    ("f32_g1_d128_b32", "f32", 2, 2, 128, 32, [7, 512, 2049]),
+    ("f32_g1_d128_b32", "f32", 2, 2, 128, 32, [7, 512, 1024, 2049]),
 ]
 
 
