@@ -62,10 +62,25 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w, lens, table_format="int32"):
+def unique_tokens(tables, lens, block_size):
+    """Distinct (block, offset) slots the batch reads: a block shared by several
+    sequences counts once, with the most slots any of them reads."""
+    used = {}
+    for row, L in zip(tables, lens):
+        L = int(L)
+        for j in range(-(-L // block_size)):
+            n = min(block_size, L - j * block_size)
+            b = int(row[j])
+            used[b] = max(used.get(b, 0), n)
+    return sum(used.values())
+
+
+def algorithmic_bytes(w, lens, table_format="int32", unique=None):
     """Bytes the attention partition pass must move, by item (see the design notes).
     Table entries are 4 bytes (2 for 16-bit tables); two-level tables add one 4-byte
-    directory entry per partition."""
+    directory entry per leaf read.  K+V count every context token of every sequence
+    (``kv``); with ``unique`` (distinct slots read) the total counts shared blocks
+    once, the bytes that must come from HBM."""
     e = w.elem_bytes
     H, D, B, Hq = w.num_kv_heads, w.head_dim, w.block_size, w.num_q_heads
     G = Hq // H
@@ -80,9 +95,11 @@ def algorithmic_bytes(w, lens, table_format="int32"):
     eb = 2 if table_format == "int16" else 4
     tables = int(groups * (-(-lens // B)).sum() * eb + len(lens) * 4)
     if table_format == "two_level":
-        tables += int(groups * parts.sum() * 4)
-    return {"kv": kv, "q": q, "out": out, "partials": partials, "tables": tables,
-            "total": kv + q + out + partials + tables}
+        leaf = LEAF_TOKENS // B
+        tables += int(groups * (-(-(-(-lens // B)) // leaf)).sum() * 4)
+    kv_hbm = kv if unique is None else int(2 * unique * H * D * e)
+    return {"kv": kv, "kv_unique": kv_hbm, "q": q, "out": out, "partials": partials, "tables": tables,
+            "total": kv_hbm + q + out + partials + tables}
 
 
 def stored_traffic(workload, kernel="attn_partition", src=KERNEL_SRC):
@@ -835,7 +852,8 @@ def main():
             flushed.append(e0.elapsed_time(e1))
         del scratch
 
-    ab = algorithmic_bytes(w, lens_np, args.tables)
+    uniq = unique_tokens(bm.block_tables(w.batch, w.max_blocks_per_seq, 0), lens_np, w.block_size)
+    ab = algorithmic_bytes(w, lens_np, args.tables, uniq)
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
     achieved = ab["total"] / (part_ms * 1e-3) / 1e9
     traffic = stored_traffic(args.workload) if args.tables == "int32" else None
