@@ -58,6 +58,18 @@ KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_attenti
 PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_prefill.hip")
 
 
+def spread(ms):
+    """median, p10 and p90 of a list of kernel times (ms)."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "n": int(a.size)}
+
+
+def host_cpus():
+    """Host CPUs as the oracle saw them: the machine's count and this process's affinity."""
+    return {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -142,7 +154,7 @@ def cpu_baseline(w, ctx, target_s):
         if time.perf_counter() - t0 > target_s:
             break
     el = time.perf_counter() - t0
-    return {"value": kv_bytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": kv_bytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle", **host_cpus(),
             "tokens_per_s": done / el,
             "sample": f"KV write + attention of the first {done} of {w.num_seqs} sequences of the batch "
                       f"({kv_bytes / 1e9:.3f} GB of KV) in {el:.1f} s; fp64 NumPy, BLAS threads {threads}"}
@@ -173,7 +185,7 @@ def cpu_baseline_prefill(w, ctx, target_s):
         if time.perf_counter() - t0 > target_s:
             break
     el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle", **host_cpus(),
             "sample": f"chunk attention of the {done} shortest of {w.num_seqs} sequences "
                       f"({flops / 1e9:.2f} GFLOP) in {el:.1f} s; fp64 NumPy, BLAS threads {threads}"}
 
@@ -237,7 +249,8 @@ def prefill_main(args, w, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_all = [e[0].elapsed_time(e[1]) for e in ev]
+    attn_ms = float(np.mean(attn_all))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(10):
@@ -267,6 +280,7 @@ def prefill_main(args, w, dev):
                    "context_tokens": int(w.context_lens.sum()), "flops": flops, "kv_bytes": w.kv_bytes()},
         "tokens_per_s": round(w.num_tokens / (ms_step * 1e-3), 1),
         "kernel_ms": {"attn_prefill": round(attn_ms, 5), "kv_write_alone": round(write_ms, 5)},
+        "attn_prefill_ms_spread": spread(attn_all),
         "roofline": {"kernel": "attn_prefill_mfma", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -387,7 +401,7 @@ def swap_main(args, sw, dev):
             reps += 1
         el = time.perf_counter() - t
         res["cpu_baseline"] = {"value": round(reps * moved_bytes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
-                               "kind": "oracle",
+                               "kind": "oracle", **host_cpus(),
                                "sample": f"{reps} oracle block copies of {len(pairs)} blocks in host memory "
                                          f"(NumPy, one thread) in {el:.1f} s"}
     print(json.dumps(res), flush=True)
@@ -818,7 +832,8 @@ def main():
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         ms_step = graph_ms
         log(f"graph replay: {graph_ms:.4f} ms per step (stream launches {eager_ms:.4f} ms)")
-    part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    part_all = [e[0].elapsed_time(e[1]) for e in ev]
+    part_ms = float(np.mean(part_all))
 
     # outside the timed region: the other passes on their own, then the partition
     # pass after flushing L2 / MALL with a 512 MiB write
@@ -882,6 +897,8 @@ def main():
                       "write_and_plan_alone": round(prep_ms, 5), "kv_write_alone": round(write_ms, 5),
                       "attn_plan_alone": round(plan_ms, 5)},
         "attn_partitions_ms_after_cache_flush": round(float(np.median(flushed)), 5) if flushed else None,
+        "attn_partitions_ms_spread": spread(part_all),
+        "attn_partitions_ms_after_cache_flush_spread": spread(flushed) if flushed else None,
         "host_block_manager_step_us": round(host_bm_us, 1),
         "step_launch": "eager" if graph_ms is None else "hip_graph",
         "eager_ms_per_step": round(eager_ms, 5),

@@ -32,3 +32,10 @@ def test_algorithmic_bytes_items():
     assert bench.algorithmic_bytes(w, lens, "two_level")["tables"] == H * blocks * 4 + 4 * 4 + H * leaves * 4
     u = bench.algorithmic_bytes(w, lens, unique=100)
     assert u["kv_unique"] == 2 * 100 * H * D * e and u["total"] == ab["total"] - ab["kv"] + u["kv_unique"]
+
+
+def test_spread_and_host_cpus():
+    s = bench.spread([1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0, 8.0, 9.0, 10.0, 11.0])
+    assert s == {"median": 6.0, "p10": 2.0, "p90": 10.0, "n": 11}
+    h = bench.host_cpus()
+    assert h["cpu_count"] >= h["affinity"] >= 1
