@@ -109,13 +109,20 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
     if (rem || L == 0) atomicAdd(&cnt[rem ? (rem + 15) >> 4 : 1], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int k = NB; k >= 1; --k) {
-      off[k] = acc;
-      acc += cnt[k];
+  // exclusive offsets of the buckets, longest first (bucket NB, then NB - 1, ...): one
+  // wave scans them with lane shuffles, lane i holding bucket NB - i
+  static_assert(NB <= 64, "one wave scans the buckets");
+  if (tid < 64) {
+    const int k = NB - tid;
+    const int c = k >= 1 ? cnt[k] : 0;
+    int v = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(v, d, 64);
+      v += tid >= d ? t : 0;
     }
-    counters[0] = acc;
+    if (k >= 1) off[k] = v - c;
+    if (tid == 63) counters[0] = v;
   }
   __syncthreads();
   for (int b = tid; b < N; b += blockDim.x) {
@@ -150,8 +157,13 @@ __global__ __launch_bounds__(1024) void attn_plan(Params P, int2* __restrict__ t
 // The step's KV write and the attention plan in one launch: workgroup 0 plans, the
 // others write (the two touch disjoint memory; the partition pass that follows in
 // stream order sees both).
+#ifndef PKV_PREP_THREADS
+#define PKV_PREP_THREADS 256
+#endif
+constexpr int kPrepThreads = PKV_PREP_THREADS;
+
 template <int EB>
-__global__ __launch_bounds__(256) void decode_prepare_kernel(Params P, WriteArgs wa, int2* __restrict__ tasks,
+__global__ __launch_bounds__(kPrepThreads) void decode_prepare_kernel(Params P, WriteArgs wa, int2* __restrict__ tasks,
                                                              int* __restrict__ counters) {
   if (blockIdx.x == 0) {
     plan_body(P, tasks, counters);
@@ -1117,13 +1129,13 @@ int launch_decode_prepare(const AttnArgs& a, const pkv_pool_desc& pool, void* k_
   wa.H = pool.num_kv_heads;
   wa.D = pool.head_dim;
   wa.B = pool.block_size;
-  const unsigned grid = 1 + static_cast<unsigned>((total + 255) / 256);
+  const unsigned grid = 1 + static_cast<unsigned>((total + kPrepThreads - 1) / kPrepThreads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (eb == 4) {
-    hipLaunchKernelGGL(decode_prepare_kernel<4>, dim3(grid), dim3(256), 0, s, P, wa, reinterpret_cast<int2*>(a.tasks),
+    hipLaunchKernelGGL(decode_prepare_kernel<4>, dim3(grid), dim3(kPrepThreads), 0, s, P, wa, reinterpret_cast<int2*>(a.tasks),
                        a.counters);
   } else {
-    hipLaunchKernelGGL(decode_prepare_kernel<2>, dim3(grid), dim3(256), 0, s, P, wa, reinterpret_cast<int2*>(a.tasks),
+    hipLaunchKernelGGL(decode_prepare_kernel<2>, dim3(grid), dim3(kPrepThreads), 0, s, P, wa, reinterpret_cast<int2*>(a.tasks),
                        a.counters);
   }
   return static_cast<int>(hipGetLastError());
