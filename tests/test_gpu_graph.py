@@ -1,7 +1,7 @@
 """The decode step (KV write + plan + partition pass, and copy-on-write copies when the
 step has pairs) captured as a HIP graph and replayed: every replay, with eager library
 work and synchronisations between replays, gives the bits of the eager step, and the
-eager result matches the oracle."""
+eager result matches the oracle (int32, 16-bit and two-level tables)."""
 import numpy as np
 import pytest
 import torch
@@ -16,24 +16,33 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.mark.parametrize("name", ["gqa", "cow", "long"])
-def test_graph_replays_match_eager_step(name):
+@pytest.mark.parametrize("name,tables", [("gqa", "int32"), ("cow", "int32"), ("long", "int32"), ("gqa", "int16"),
+                                         ("long", "two_level")])
+def test_graph_replays_match_eager_step(name, tables):
     if name == "gqa":
         w = synth.gqa_bf16(num_seqs=8, max_len=1500)
     elif name == "cow":
         w = synth.cow_fp16(1020, num_prompts=3, max_suffix=20)
     else:
         w = synth.long_bf16(16, num_seqs=2, context=40 * 1024)  # 40 partitions: the separate merge kernel
-    log(f"graph replay {name}: {w.num_seqs} sequences")
+    log(f"graph replay {name}, {tables} tables: {w.num_seqs} sequences")
     ctx = w.all_context_kv()
     st = replay_gpu(w, ctx, DEV)
+    width = w.max_blocks_per_seq
+    if tables == "int16":
+        st.tables = torch.from_numpy(st.bm.block_tables16(w.batch, width, 0)).to(DEV)
+    elif tables == "two_level":
+        E = pkv.LEAF_TOKENS // w.block_size
+        ld, lv = st.bm.block_tables_2l(w.batch, -(-width // E), 0)
+        st.tables = pkv.TwoLevelTables(torch.from_numpy(ld).to(DEV), torch.from_numpy(lv).to(DEV))
+        width = ld.shape[1] * E
     # rebuild the last step's inputs: undo nothing, just re-run it (writes are idempotent)
     slots = torch.from_numpy(st.last_slots).to(DEV)
     pairs = torch.from_numpy(st.last_pairs).to(DEV)
     k, v = (to_device(x, w.dtype, DEV) for x in w.step_kv(len(w.steps) - 1))
     q = to_device(w.queries(), w.dtype, DEV)
     out = torch.empty_like(q)
-    ws = pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_blocks_per_seq, w.block_size, DEV)
+    ws = pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, width, w.block_size, DEV)
 
     def step():
         if len(st.last_pairs):
