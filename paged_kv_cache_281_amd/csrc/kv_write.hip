@@ -28,8 +28,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
 // so that neighbouring workgroups read neighbouring bytes of the token rows.  When the group's
 // slots are one whole block in order (prefill chunks fill whole blocks), the block's K
 // tile [D/X][B][X] and V tile [D][B] are built in LDS from coalesced reads of the token
-// rows and stored as contiguous 16-byte pieces.  Otherwise each token goes to its own
-// slot (K as 16-byte pieces, V element by element; slot -1 is skipped).
+// rows and stored as contiguous 16-byte pieces.  Otherwise each token goes from LDS to
+// its own slot (K as 16-byte pieces, V element by element; slot -1 is skipped).
 #ifndef PKV_KV_WRITE_THREADS
 #define PKV_KV_WRITE_THREADS 256
 #endif
@@ -60,13 +60,14 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_tiles_kernel(const cha
   const int64_t si = lane < n ? slots[t0 + lane] : s0 + lane;
   const bool whole = n == B && s0 >= 0 && s0 % B == 0 &&
                      __builtin_amdgcn_ballot_w64(lane < B && si != s0 + lane) == 0;
-  if (whole) {
-    // every load first, then LDS: piece j = (token j / CH, chunk j % CH)
+  // the group's token rows into LDS, every load first: piece j = (token j / CH, chunk
+  // j % CH); tokens past the end read the last token again (never stored)
+  {
     u32x4 kr[NP], vr[NP];
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
       const int j = min(tid + NT * x, B * CH - 1);
-      const int i = j / CH, c = j - (j / CH) * CH;
+      const int i = min(j / CH, n - 1), c = j - (j / CH) * CH;
       kr[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ksrc + i * row + c * 16));
       vr[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vsrc + i * row + c * 16));
     }
@@ -77,7 +78,9 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_tiles_kernel(const cha
       sk[c][i] = kr[x];
       *reinterpret_cast<u32x4*>(&sv[i][c * X]) = vr[x];
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  if (whole) {
     const int64_t tile = (s0 / B * H + h) * static_cast<int64_t>(D) * B * EB;  // bytes
     for (int j = tid; j < B * CH; j += NT) {  // K tile out: piece j = (chunk j / B, token j % B)
       const int c = j / B, i = j - (j / B) * B;
@@ -98,19 +101,21 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_tiles_kernel(const cha
     }
     return;
   }
-  for (int j = tid; j < n * CH; j += NT) {  // K: one 16-byte piece per (token, chunk)
-    const int i = j / CH, c = j - (j / CH) * CH;
+  // Otherwise token by token, tokens varying fastest: runs of consecutive slots (a
+  // chunk that starts inside a block) still give contiguous stores.
+  for (int j = tid; j < n * CH; j += NT) {  // K: one 16-byte piece per (chunk j / n, token j % n)
+    const int c = j / n, i = j - (j / n) * n;
     const int64_t s = slots[t0 + i];
     if (s < 0) continue;
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ksrc + i * row + c * 16));
-    *reinterpret_cast<u32x4*>(k_pool + ((s / B * H + h) * static_cast<int64_t>(D) * B + (c * B + s % B) * X) * EB) = v;
+    *reinterpret_cast<u32x4*>(k_pool + ((s / B * H + h) * static_cast<int64_t>(D) * B + (c * B + s % B) * X) * EB) =
+        sk[c][i];
   }
-  for (int j = tid; j < n * D; j += NT) {  // V: one element per (token, d)
-    const int i = j / D, d = j - (j / D) * D;
+  for (int j = tid; j < n * D; j += NT) {  // V: one element per (row j / n, token j % n)
+    const int d = j / n, i = j - (j / n) * n;
     const int64_t s = slots[t0 + i];
     if (s < 0) continue;
-    const E v = *reinterpret_cast<const E*>(vsrc + i * row + d * EB);
-    reinterpret_cast<E*>(v_pool)[(s / B * H + h) * static_cast<int64_t>(D) * B + static_cast<int64_t>(d) * B + s % B] = v;
+    reinterpret_cast<E*>(v_pool)[(s / B * H + h) * static_cast<int64_t>(D) * B + static_cast<int64_t>(d) * B + s % B] =
+        sv[i][d];
   }
 }
 
