@@ -1,9 +1,9 @@
 """GPU parity of paged_kv_write with mixed slot patterns against the oracle write.
 
-Runs of consecutive, aligned slots take the 16-byte V store; everything else (runs
-that start off a multiple of the vector width, runs cut by a block boundary, gaps,
-padding slots, a token count that is not a multiple of the width) takes one element
-per token.  Both must leave the pools bit-identical to the oracle's.
+Groups of B tokens whose slots are one whole block in order are stored as whole
+tiles; everything else (runs that start inside a block, runs crossing a block
+boundary, a shuffled block, gaps, padding slots, a short last group) goes token by
+token.  Both must leave the pools bit-identical to the oracle's.
 """
 import numpy as np
 import pytest
@@ -32,13 +32,14 @@ def _slots(rng, nb, B):
     return s
 
 
-@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f16", 32), ("f32", 16)])
-def test_kv_write_mixed_slots(dtype, B):
+@pytest.mark.parametrize("dtype,B,D", [("bf16", 16, 64), ("f16", 32, 64), ("f32", 16, 64), ("bf16", 16, 128),
+                                       ("bf16", 32, 128), ("f16", 16, 128), ("f32", 32, 128), ("f32", 32, 64)])
+def test_kv_write_mixed_slots(dtype, B, D):
     rng = np.random.default_rng(4)
-    nb, H, D = 20, 3, 64
+    nb, H = 20, 3
     slots = _slots(rng, nb, B)
     T = len(slots)
-    log(f"kv write {dtype} B={B}: {T} tokens")
+    log(f"kv write {dtype} B={B} D={D}: {T} tokens")
     k = synth.normal_bits((77, 1), (T, H, D), dtype)
     v = synth.normal_bits((77, 2), (T, H, D), dtype)
     kp, vp = pkv.alloc_pools(nb, B, H, D, TORCH_DTYPE[dtype], DEV)
