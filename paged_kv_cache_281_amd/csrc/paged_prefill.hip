@@ -94,19 +94,51 @@ __device__ __forceinline__ int tile_units(const PrefillParams& P, int C, int L, 
 // ---------------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = 1024;
+static_assert(kPlanBuckets == kPlanThreads, "one bucket per plan thread");
+
+// Calls f(b, t, C, L) for every (sequence b, tile t) the chunks have.  Sequences are
+// taken kPlanThreads at a time; their tiles are spread over all threads (a block-wide
+// scan of the tile counts, then a binary search per tile), so a long chunk's many
+// tiles do not fall on one thread.
+template <class F>
+__device__ __forceinline__ void plan_tiles(const PrefillParams& P, int* s_end, int* s_c, int* s_l, F&& f) {
+  const int tid = threadIdx.x;
+  for (int b0 = 0; b0 < P.N; b0 += kPlanThreads) {
+    int q0, C = 0, L = 0, nt = 0;
+    if (b0 + tid < P.N && chunk_of(P, b0 + tid, q0, C, L)) nt = (C * P.G + P.rows - 1) / P.rows;
+    s_c[tid] = C;
+    s_l[tid] = L;
+    s_end[tid] = nt;
+    for (int d = 1; d < kPlanThreads; d <<= 1) {  // inclusive scan: s_end[i] = tiles of sequences b0 .. b0 + i
+      __syncthreads();
+      const int add = tid >= d ? s_end[tid - d] : 0;
+      __syncthreads();
+      s_end[tid] += add;
+    }
+    __syncthreads();
+    const int total = s_end[kPlanThreads - 1];
+    for (int g = tid; g < total; g += kPlanThreads) {
+      int lo = 0, hi = kPlanThreads - 1;  // first sequence whose range ends past g
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_end[mid] > g) hi = mid; else lo = mid + 1;
+      }
+      f(b0 + lo, g - (lo ? s_end[lo - 1] : 0), s_c[lo], s_l[lo]);
+    }
+    __syncthreads();  // s_end, s_c, s_l are reused by the next batch
+  }
+}
 
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan(PrefillParams P) {
   __shared__ int cnt[kPlanBuckets];
+  __shared__ int s_end[kPlanThreads], s_c[kPlanThreads], s_l[kPlanThreads];
   const int tid = threadIdx.x;
   cnt[tid] = 0;
   __syncthreads();
-  for (int b = tid; b < P.N; b += kPlanThreads) {
-    int q0, C, L;
-    if (!chunk_of(P, b, q0, C, L)) continue;
-    const int ntile = (C * P.G + P.rows - 1) / P.rows;
-    for (int t = 0; t < ntile; ++t) atomicAdd(&cnt[kPlanBuckets - 1 - min(tile_units(P, C, L, t), kPlanBuckets - 1)], 1);
-  }
-  __syncthreads();
+  auto bucket = [&](int t, int C, int L) {
+    return kPlanBuckets - 1 - min(tile_units(P, C, L, t), kPlanBuckets - 1);
+  };
+  plan_tiles(P, s_end, s_c, s_l, [&](int b, int t, int C, int L) { atomicAdd(&cnt[bucket(t, C, L)], 1); });
   // exclusive scan of the bucket counts (bucket 0 = most units)
   int v = cnt[tid];
   for (int d = 1; d < kPlanBuckets; d <<= 1) {
@@ -119,15 +151,10 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan(PrefillParams P) {
   if (tid == kPlanBuckets - 1) P.counters[0] = min(cnt[tid], P.cap);
   cnt[tid] -= v;  // exclusive offsets
   __syncthreads();
-  for (int b = tid; b < P.N; b += kPlanThreads) {
-    int q0, C, L;
-    if (!chunk_of(P, b, q0, C, L)) continue;
-    const int ntile = (C * P.G + P.rows - 1) / P.rows;
-    for (int t = 0; t < ntile; ++t) {
-      const int slot = atomicAdd(&cnt[kPlanBuckets - 1 - min(tile_units(P, C, L, t), kPlanBuckets - 1)], 1);
-      if (slot < P.cap) P.tasks[slot] = make_int2(b, t);  // overlapping chunks could overflow the bound
-    }
-  }
+  plan_tiles(P, s_end, s_c, s_l, [&](int b, int t, int C, int L) {
+    const int slot = atomicAdd(&cnt[bucket(t, C, L)], 1);
+    if (slot < P.cap) P.tasks[slot] = make_int2(b, t);  // overlapping chunks could overflow the bound
+  });
 }
 
 // The 4 waves of a workgroup share each 32-token K/V unit.  All
