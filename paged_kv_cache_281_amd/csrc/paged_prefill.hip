@@ -402,7 +402,9 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
   Stage s0, s1;
   auto step = [&](int u, Stage& cur, Stage& nxt) {
     // on entry `cur` is free and `nxt` holds unit u + 1 (if any)
-    if (u + 2 < nunits) fetch(u + 2, cur);
+    // unconditional (the last unit again near the end): a load issued on only some
+    // paths would make the deposit below wait for every outstanding load
+    fetch(min(u + 2, nunits - 1), cur);
     if (wave_rows && 32 * u <= w_last) compute(u, u & 1);  // units this wave's rows can see
     if (u + 1 < nunits) deposit((u + 1) & 1, nxt);
     __syncthreads();
