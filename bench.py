@@ -52,7 +52,7 @@ SWAP_METRIC = "KV block swap GB/s between the device pool and pinned host memory
 PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-PARTITION_TOKENS = 1024  # the library's decode partition
+PARTITION_TOKENS = 1024  # the library's shorter decode partition (the plan may pick 2048)
 LEAF_TOKENS = 512  # the library's two-level leaf
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_attention.hip")
 PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_prefill.hip")
@@ -87,7 +87,7 @@ def unique_tokens(tables, lens, block_size):
     return sum(used.values())
 
 
-def algorithmic_bytes(w, lens, table_format="int32", unique=None):
+def algorithmic_bytes(w, lens, table_format="int32", unique=None, partition_tokens=PARTITION_TOKENS):
     """Bytes the attention partition pass must move, by item (see the design notes).
     Table entries are 4 bytes (2 for 16-bit tables); two-level tables add one 4-byte
     directory entry per leaf read.  K+V count every context token of every sequence
@@ -100,7 +100,7 @@ def algorithmic_bytes(w, lens, table_format="int32", unique=None):
     lens = np.asarray(lens, dtype=np.int64)
     kv = int(2 * lens.sum() * H * D * e)
     q = int(len(lens) * Hq * D * e)
-    parts = -(-lens // PARTITION_TOKENS)
+    parts = -(-lens // partition_tokens)
     single = parts <= 1
     out = int(single.sum() * Hq * D * e)
     partials = int(2 * parts[~single].sum() * Hq * (D + 2) * 4)  # written, then read by the merge
@@ -112,6 +112,12 @@ def algorithmic_bytes(w, lens, table_format="int32", unique=None):
     kv_hbm = kv if unique is None else int(2 * unique * H * D * e)
     return {"kv": kv, "kv_unique": kv_hbm, "q": q, "out": out, "partials": partials, "tables": tables,
             "total": kv_hbm + q + out + partials + tables}
+
+
+def partition_tokens_of(w, lens):
+    """The decode partition size the library's plan pass picks for this batch."""
+    import paged_kv_cache_281_amd as pkv
+    return pkv.decode_partition_tokens(lens, w.num_q_heads, w.num_kv_heads)
 
 
 def stored_traffic(workload, kernel="attn_partition", src=KERNEL_SRC):
@@ -620,7 +626,8 @@ def lenclass_main(args, lw, dev):
             torch.cuda.synchronize()
             conc_ms = (time.perf_counter() - t0) * 1e3 / args.steps
             log(f"{name}: pools as parallel graph branches {conc_ms:.4f} ms (one branch {graph_ms:.4f})")
-        abs_ = [algorithmic_bytes(p["w"], p["lens_np"]) for p in parts]
+        abs_ = [algorithmic_bytes(p["w"], p["lens_np"], partition_tokens=partition_tokens_of(p["w"], p["lens_np"]))
+                for p in parts]
         kv = sum(a["kv"] for a in abs_)
         used = sum(int(p["lens_np"].sum()) for p in parts)
         alloc = sum(p["slots_alloc"] for p in parts)
@@ -691,6 +698,8 @@ def main():
                     help="time the decode step as stream launches instead of replays of its HIP graph")
     ap.add_argument("--tables", choices=["int32", "int16", "two_level"], default="int32",
                     help="block-table format of the decode step (flat int32, flat 16-bit, or two-level)")
+    ap.add_argument("--partition-tokens", type=int, choices=[0, 1024, 2048], default=0,
+                    help="fix the decode partition size (0: the plan pass chooses per batch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -714,6 +723,7 @@ def main():
     import paged_kv_cache_281_amd as pkv
     import synth
     pkv.load()
+    pkv.set_decode_partition_tokens(args.partition_tokens)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
     ti = {"f32": (np.int32, torch.int32), "f16": (np.int16, torch.int16), "bf16": (np.int16, torch.int16)}
 
@@ -868,7 +878,8 @@ def main():
         del scratch
 
     uniq = unique_tokens(bm.block_tables(w.batch, w.max_blocks_per_seq, 0), lens_np, w.block_size)
-    ab = algorithmic_bytes(w, lens_np, args.tables, uniq)
+    pt = partition_tokens_of(w, lens_np)
+    ab = algorithmic_bytes(w, lens_np, args.tables, uniq, pt)
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
     achieved = ab["total"] / (part_ms * 1e-3) / 1e9
     traffic = stored_traffic(args.workload) if args.tables == "int32" else None
@@ -888,7 +899,7 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "context_tokens": int(lens_np.sum()), "max_context": int(lens_np.max()),
-                   "partition_tokens": PARTITION_TOKENS, "copy_pairs": int(len(pairs)),
+                   "partition_tokens": pt, "copy_pairs": int(len(pairs)),
                    "kv_bytes": ab["kv"], "tables": args.tables, "table_bytes": table_bytes},
         "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),

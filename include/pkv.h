@@ -121,8 +121,11 @@ int32_t pkv_copy_blocks(const pkv_pool_desc* pool, void* k_pool, void* v_pool,
 int32_t pkv_swap_blocks(const pkv_pool_desc* pool, const void* src_k, const void* src_v, void* dst_k,
                         void* dst_v, const int64_t* src_dst_pairs, int32_t num_pairs, void* stream);
 
-/* Context tokens per split-context partition of the attention pass. */
+/* Context tokens per split-context partition of the attention pass: the plan pass picks
+ * PKV_PARTITION_TOKENS or PKV_PARTITION_TOKENS_MAX for each launch (see
+ * pkv_decode_partition_tokens); workspaces are sized for the smaller one. */
 #define PKV_PARTITION_TOKENS 1024
+#define PKV_PARTITION_TOKENS_MAX 2048
 /* Context tokens whose block ids one leaf of a two-level block table holds. */
 #define PKV_LEAF_TOKENS 512
 
@@ -142,8 +145,10 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  *     s_j = scale * dot(q[b][h], K[b, j, g])   for 0 <= j < context_lens[b]
  *     out[b][h] = sum_j softmax(s)_j * V[b, j, g]
  * where token j of sequence b sits in block block_tables[b][j / B] at offset j % B.
- * Long contexts are split into PKV_PARTITION_TOKENS-token partitions whose partial
- * results are merged with log-sum-exp weights (in `workspace`).  Context lengths above
+ * Long contexts are split into partitions of PKV_PARTITION_TOKENS or
+ * PKV_PARTITION_TOKENS_MAX tokens (chosen per call from the context lengths, as
+ * pkv_decode_partition_tokens states) whose partial results are merged with
+ * log-sum-exp weights (in `workspace`).  Context lengths above
  * max_blocks_per_seq * B break the contract; they are clamped to it (no access goes
  * past the table row).
  *   q, out        device [num_seqs][num_q_heads][D], pool dtype, contiguous, 16-byte aligned.
@@ -272,8 +277,13 @@ size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num
  * The two passes of pkv_paged_attention_decode, exposed separately (same arguments,
  * same results when called in this order on one stream with the same workspace and
  * context_lens) so that each pass can be timed on its own:
- *  - plan: lists the (sequence, partition) items in the workspace, longest first, and
- *    clears the per-row completion counters;
+ *  - plan: picks the partition size, lists the (sequence, partition) items in the
+ *    workspace, longest first, and clears the per-row completion counters.  `tables`
+ *    (a host struct; NULL allowed) lets it read the first block id of each sequence:
+ *    a sequence whose first block equals the previous sequence's (a forked or cached
+ *    prefix) has its last partition listed next to that sequence's, so the workgroups
+ *    that read the shared blocks run together.  It changes the order only, never a
+ *    result;
  *  - partitions: one workgroup per item and kv-head group; writes the final output of
  *    sequences that fit one partition and partial results of the others; the
  *    workgroup that completes the last partition of a row merges that row's partials
@@ -281,9 +291,18 @@ size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num
  * A partitions pass without a preceding plan pass on that workspace gives undefined
  * output values (but stays within the buffers).  Errors as pkv_paged_attention_decode.
  */
+typedef struct {
+  const void* entries;      /* flat tables: device rows [num_seqs][max_blocks_per_seq] of
+                               entry_bytes each; two-level tables: the device int32 leaves */
+  const int32_t* leaf_dir;  /* two-level tables: the device leaf directory
+                               [num_seqs][max_blocks_per_seq / (PKV_LEAF_TOKENS / B)]; NULL if flat */
+  int32_t entry_bytes;      /* 4 (int32) or 2 (16-bit) for flat tables, 4 for two-level */
+  int32_t reserved;         /* 0 */
+} pkv_table_ref;
 int32_t pkv_paged_attention_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t max_blocks_per_seq, const int32_t* context_lens, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 const pkv_table_ref* tables, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 int32_t pkv_paged_attention_partitions(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
                                        void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -297,13 +316,39 @@ int32_t pkv_paged_attention_partitions(const pkv_pool_desc* pool, const void* k_
  * pkv_decode_prepare, pkv_paged_attention_partitions, with the same results as
  * pkv_copy_blocks + pkv_paged_kv_write + pkv_paged_attention_decode.
  * Arguments and errors are those of the two calls it replaces; num_tokens == 0 only
- * plans, num_seqs == 0 only writes.
+ * plans, num_seqs == 0 only writes.  `tables` is as for pkv_paged_attention_plan.
  */
 int32_t pkv_decode_prepare(const pkv_pool_desc* pool, void* k_pool, void* v_pool,
                            const void* k_new, const void* v_new, const int64_t* slot_mapping,
                            int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           const pkv_table_ref* tables, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * The partition size (in tokens) the plan pass picks for a decode call with these
+ * context lengths (host copy) on the current device.  Fewer, longer partitions save
+ * each workgroup's fixed start and end (table entries, queries and first K/V unit;
+ * combine, partial stores, merge), but a batch too small to keep the chip busy ends
+ * when its longest items do.  The plan takes PKV_PARTITION_TOKENS_MAX when some
+ * context exceeds PKV_PARTITION_TOKENS and
+ *     3 * sum_b(context_lens[b]) * workgroups_per_item >= 2 * min(max_b context_lens[b], PKV_PARTITION_TOKENS_MAX) * slots
+ * (the token work per resident workgroup slot reaches two thirds of the longest item),
+ * with workgroups_per_item = H * ceil(G / 16) and slots = 3 resident workgroups per
+ * compute unit (768 on MI355X); else PKV_PARTITION_TOKENS.  A value set with
+ * pkv_set_decode_partition_tokens takes precedence.  Host-only and synchronous; no
+ * device is needed (without one, 256 compute units are assumed).
+ * Errors: INVALID_ARG (null pointers, num_seqs < 0, heads not positive or not a multiple).
+ */
+int32_t pkv_decode_partition_tokens(const int32_t* context_lens_host, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t* tokens);
+/*
+ * Fixes the decode partition size of every later plan pass in the process:
+ * PKV_PARTITION_TOKENS or PKV_PARTITION_TOKENS_MAX, or 0 for the per-call choice above
+ * (the default).  For tuning and tests; results are the same either way up to fp32
+ * rounding of the merge.  Errors: INVALID_ARG (any other value).
+ */
+int32_t pkv_set_decode_partition_tokens(int32_t tokens);
 
 /*
  * Host-side block manager: block tables, on-demand allocation, fork and

@@ -24,10 +24,12 @@ __all__ = [
     "paged_kv_write", "copy_blocks", "swap_blocks", "workspace_bytes", "alloc_workspace", "TwoLevelTables",
     "paged_attention_decode", "paged_attention_partitions", "paged_attention_plan", "decode_prepare",
     "prefill_workspace_bytes", "alloc_prefill_workspace", "paged_attention_prefill", "BlockManager", "PkvError",
-    "PARTITION_TOKENS", "LEAF_TOKENS", "DTYPE_CODES",
+    "PARTITION_TOKENS", "PARTITION_TOKENS_MAX", "LEAF_TOKENS", "DTYPE_CODES", "decode_partition_tokens", "TableRef",
+    "set_decode_partition_tokens",
 ]
 
-PARTITION_TOKENS = 1024  # decode split-context partition (PKV_PARTITION_TOKENS)
+PARTITION_TOKENS = 1024  # decode split-context partition (PKV_PARTITION_TOKENS; the workspace unit)
+PARTITION_TOKENS_MAX = 2048  # the longer partition the plan may choose (PKV_PARTITION_TOKENS_MAX)
 LEAF_TOKENS = 512  # tokens whose block ids one two-level leaf holds (PKV_LEAF_TOKENS)
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _c_i32, _c_i64, _c_vp, _c_sz, _c_f = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
@@ -44,6 +46,11 @@ class PkvError(RuntimeError):
 class PoolDesc(ctypes.Structure):
     _fields_ = [("num_blocks", _c_i32), ("block_size", _c_i32), ("num_kv_heads", _c_i32),
                 ("head_dim", _c_i32), ("dtype", _c_i32)]
+
+
+class TableRef(ctypes.Structure):
+    """pkv_table_ref: where the plan pass reads each sequence's first block id."""
+    _fields_ = [("entries", _c_vp), ("leaf_dir", _c_vp), ("entry_bytes", _c_i32), ("reserved", _c_i32)]
 
 
 def library_path() -> str:
@@ -86,9 +93,12 @@ def _bind(lib):
                                         _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
         "pkv_paged_attention_partitions": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
                                             _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
-        "pkv_paged_attention_plan": ([P(PoolDesc), _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_paged_attention_plan": ([P(PoolDesc), _c_i32, _c_i32, _c_i32, _c_vp, P(TableRef), _c_vp, _c_sz, _c_vp],
+                                     _c_i32),
         "pkv_decode_prepare": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp,
-                                _c_vp, _c_sz, _c_vp], _c_i32),
+                                P(TableRef), _c_vp, _c_sz, _c_vp], _c_i32),
+        "pkv_decode_partition_tokens": ([_c_vp, _c_i32, _c_i32, _c_i32, P(_c_i32)], _c_i32),
+        "pkv_set_decode_partition_tokens": ([_c_i32], _c_i32),
         "pkv_paged_attention_prefill": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
                                          _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
         "pkv_paged_attention_prefill_workspace_bytes": ([_c_i32, _c_i32, _c_i32, _c_i32], _c_sz),
@@ -342,11 +352,35 @@ def paged_attention_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
     return out
 
 
+def _table_ref(block_tables) -> TableRef:
+    """The plan's view of the tables (first block id of each sequence)."""
+    if isinstance(block_tables, TwoLevelTables):
+        ld, lv = block_tables
+        return TableRef(_ptr(lv), _ptr(ld), 4, 0)
+    return TableRef(_ptr(block_tables), None, block_tables.element_size(), 0)
+
+
 def paged_attention_plan(q, k_pool, v_pool, block_tables, context_lens, workspace) -> None:
-    """First pass of ``paged_attention_decode``: the (sequence, partition) task list."""
+    """First pass of ``paged_attention_decode``: the partition size and the (sequence,
+    partition) task list."""
     d, N, Hq, W, _, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, q, workspace)
-    _check(load().pkv_paged_attention_plan(ctypes.byref(d), N, Hq, W, _ptr(context_lens), _ptr(ws), ws.numel(),
-                                           _stream(q.device)))
+    tr = _table_ref(block_tables)
+    _check(load().pkv_paged_attention_plan(ctypes.byref(d), N, Hq, W, _ptr(context_lens), ctypes.byref(tr), _ptr(ws),
+                                           ws.numel(), _stream(q.device)))
+
+
+def decode_partition_tokens(context_lens, num_q_heads: int, num_kv_heads: int) -> int:
+    """The partition size the plan pass picks for these context lengths (host values)."""
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    out = _c_i32()
+    _check(load().pkv_decode_partition_tokens(lens.ctypes.data if lens.size else None, lens.size, int(num_q_heads),
+                                              int(num_kv_heads), ctypes.byref(out)))
+    return out.value
+
+
+def set_decode_partition_tokens(tokens: int) -> None:
+    """Fix the decode partition size of later calls (1024 or 2048), or 0 for the plan's choice."""
+    _check(load().pkv_set_decode_partition_tokens(int(tokens)))
 
 
 def decode_prepare(k_pool, v_pool, k_new, v_new, slot_mapping, q, block_tables, context_lens, workspace) -> None:
@@ -360,9 +394,10 @@ def decode_prepare(k_pool, v_pool, k_new, v_new, slot_mapping, q, block_tables, 
     _require(slot_mapping.dtype == torch.int64 and tuple(slot_mapping.shape) == (T,) and slot_mapping.is_contiguous()
              and slot_mapping.device == k_pool.device, "slot_mapping must be a contiguous int64 [T] device tensor")
     _, N, Hq, W, _, ws = _attn_args(q, k_pool, v_pool, block_tables, context_lens, q, workspace)
+    tr = _table_ref(block_tables)
     _check(load().pkv_decode_prepare(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
-                                     _ptr(slot_mapping), T, N, Hq, W, _ptr(context_lens), _ptr(ws), ws.numel(),
-                                     _stream(q.device)))
+                                     _ptr(slot_mapping), T, N, Hq, W, _ptr(context_lens), ctypes.byref(tr), _ptr(ws),
+                                     ws.numel(), _stream(q.device)))
 
 
 def paged_attention_partitions(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace) -> None:

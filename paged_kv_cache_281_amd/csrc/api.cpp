@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 #include <string>
@@ -140,7 +141,36 @@ AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_parts = static_cast<int32_t>(parts);
   a.scale = scale;
+  a.slots = resident_slots();
+  a.force_log2 = forced_partition_log2();
   return c;
+}
+
+// The block tables a plan pass is given (optional): which sequences share a first block.
+int32_t apply_table_ref(const char* who, const pkv_pool_desc& pool, const pkv_table_ref* t, int32_t num_seqs,
+                        int32_t max_blocks_per_seq, AttnArgs& a) {
+  if (!t || num_seqs == 0) return PKV_OK;
+  char buf[256];
+  const int32_t E = PKV_LEAF_TOKENS / pool.block_size;
+  const bool two = t->leaf_dir != nullptr;
+  if (!t->entries || (t->entry_bytes != 4 && t->entry_bytes != 2) || (two && t->entry_bytes != 4) ||
+      (two && max_blocks_per_seq % E != 0) || t->reserved != 0) {
+    std::snprintf(buf, sizeof(buf), "%s: bad table reference (entries, entry_bytes 2 or 4, two-level: 4 and "
+                  "max_blocks_per_seq a multiple of %d, reserved 0)", who, E);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (!aligned(t->entries, t->entry_bytes) || !aligned(t->leaf_dir, 4)) {
+    std::snprintf(buf, sizeof(buf), "%s: misaligned table reference", who);
+    return set_error(PKV_ERR_INVALID_ARG, buf);
+  }
+  if (t->entry_bytes == 2 && pool.num_blocks > 65536) {
+    std::snprintf(buf, sizeof(buf), "%s: 16-bit block tables address at most 65536 blocks", who);
+    return set_error(PKV_ERR_UNSUPPORTED, buf);
+  }
+  a.block_tables = t->entries;
+  a.table_bytes = t->entry_bytes;
+  a.table_dir = t->leaf_dir;
+  return PKV_OK;
 }
 
 }  // namespace
@@ -148,6 +178,38 @@ AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void
 int32_t set_error(int32_t status, const char* msg) {
   g_last_error = msg ? msg : "";
   return status;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_slots[kMaxDevices];
+std::atomic<int32_t> g_force_log2{0};
+}  // namespace
+
+int32_t resident_slots() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 256 * kSlotsPerCU;
+  }
+  int32_t v = g_slots[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+    }
+    v = cus * kSlotsPerCU;
+    g_slots[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+int32_t forced_partition_log2() { return g_force_log2.load(std::memory_order_relaxed); }
+
+int32_t set_forced_partition_log2(int32_t lg) {
+  g_force_log2.store(lg, std::memory_order_relaxed);
+  return PKV_OK;
 }
 
 // ---------------------------------------------------------------------------------
@@ -343,13 +405,15 @@ int32_t pkv_paged_kv_write(const pkv_pool_desc* pool, void* k_pool, void* v_pool
 int32_t pkv_decode_prepare(const pkv_pool_desc* pool, void* k_pool, void* v_pool, const void* k_new,
                            const void* v_new, const int64_t* slot_mapping, int32_t num_tokens, int32_t num_seqs,
                            int32_t num_q_heads, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           const pkv_table_ref* tables, void* workspace, size_t workspace_bytes, void* stream) {
   int32_t st = check_write("pkv_decode_prepare", pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens);
   if (st != PKV_OK) return st;
   pkv::AttnCheck c = pkv::check_attention("pkv_decode_prepare", pool, nullptr, nullptr, nullptr, nullptr,
                                           num_seqs, num_q_heads, nullptr, max_blocks_per_seq, context_lens, 1.0f,
                                           workspace, workspace_bytes, false, false);
   if (c.status != PKV_OK) return c.status;
+  if ((st = pkv::apply_table_ref("pkv_decode_prepare", *pool, tables, num_seqs, max_blocks_per_seq, c.args)) != PKV_OK)
+    return st;
   if (num_seqs == 0) return pkv_paged_kv_write(pool, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream);
   if (pkv::kDebugChecks) {
     if ((st = pkv::debug_check_slots("pkv_decode_prepare", *pool, slot_mapping, num_tokens, stream)) != PKV_OK ||
@@ -392,6 +456,31 @@ int32_t pkv_swap_blocks(const pkv_pool_desc* pool, const void* src_k, const void
     return set_error(PKV_ERR_INVALID_ARG, "pkv_swap_blocks: misaligned pointer");
   return pkv::launch_status(
       pkv::launch_pool_copy(*pool, src_k, src_v, dst_k, dst_v, src_dst_pairs, num_pairs, stream), "pkv_swap_blocks");
+}
+
+int32_t pkv_decode_partition_tokens(const int32_t* context_lens_host, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t* tokens) {
+  if (!tokens || num_seqs < 0 || (num_seqs > 0 && !context_lens_host) || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return pkv::set_error(PKV_ERR_INVALID_ARG, "pkv_decode_partition_tokens: bad arguments");
+  unsigned long long total = 0;
+  int lmax = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int L = std::max(context_lens_host[b], 0);
+    total += static_cast<unsigned long long>(L);
+    lmax = std::max(lmax, L);
+  }
+  const int G = num_q_heads / num_kv_heads;
+  const int hy = num_kv_heads * ((G + 15) / 16);
+  *tokens = 1 << pkv::choose_partition_log2(total, lmax, hy, pkv::resident_slots(), pkv::forced_partition_log2());
+  return PKV_OK;
+}
+
+int32_t pkv_set_decode_partition_tokens(int32_t tokens) {
+  if (tokens == 0) return pkv::set_forced_partition_log2(0);
+  if (tokens == PKV_PARTITION_TOKENS) return pkv::set_forced_partition_log2(pkv::kLgPartMin);
+  if (tokens == PKV_PARTITION_TOKENS_MAX) return pkv::set_forced_partition_log2(pkv::kLgPartMax);
+  return pkv::set_error(PKV_ERR_INVALID_ARG, "pkv_set_decode_partition_tokens: 0, 1024 or 2048 expected");
 }
 
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -512,12 +601,16 @@ int32_t pkv_paged_attention_partitions_2l(const pkv_pool_desc* pool, const void*
 }
 
 int32_t pkv_paged_attention_plan(const pkv_pool_desc* pool, int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t max_blocks_per_seq, const int32_t* context_lens, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 const pkv_table_ref* tables, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   pkv::AttnCheck c = pkv::check_attention("pkv_paged_attention_plan", pool, nullptr, nullptr, nullptr, nullptr,
                                           num_seqs, num_q_heads, nullptr, max_blocks_per_seq, context_lens, 1.0f,
                                           workspace, workspace_bytes, false, false);
   if (c.status != PKV_OK) return c.status;
+  const int32_t tst =
+      pkv::apply_table_ref("pkv_paged_attention_plan", *pool, tables, num_seqs, max_blocks_per_seq, c.args);
+  if (tst != PKV_OK) return tst;
   if (num_seqs == 0) return PKV_OK;
   if (pkv::kDebugChecks) {
     const int32_t st = pkv::debug_check_tables<int32_t>("pkv_paged_attention_plan", *pool, nullptr, max_blocks_per_seq,

@@ -9,7 +9,7 @@
 // "先搞清敌人" (decode is bound by memory, not compute).
 //
 // Work split.  A workgroup (4 waves) owns one (sequence, kv head [, group of up to
-// 16 query heads], partition of PKV_PARTITION_TOKENS context tokens).  It stages
+// 16 query heads], partition of 1024 or 2048 context tokens, chosen per launch).  It stages
 // the partition's block-table entries in LDS, then each wave walks every 4th
 // 16-token unit of the partition with a register double buffer (the next unit's K
 // and V loads are in flight while the current unit is computed), keeping an online
@@ -50,7 +50,7 @@
 namespace pkv {
 namespace {
 
-constexpr int kPT = PKV_PARTITION_TOKENS;
+constexpr int kPTMax = PKV_PARTITION_TOKENS_MAX;  // largest partition (LDS table staging)
 template <int B>
 constexpr int kLeaf = PKV_LEAF_TOKENS / B;  // entries per two-level leaf
 constexpr int kWaves = 4;
@@ -67,10 +67,14 @@ struct Params {
   const int* dir;       // two-level tables: the leaf directory
   const int* ctx;
   const int2* tasks;    // {sequence * Pmax + partition, context length} items, longest first
-  const int* counters;  // counters[0] = number of items
+  const int* counters;  // counters[0] = number of items, counters[1] = log2 of the partition size
   int* done;            // [N * Hq]: partitions finished per (sequence, first head of a group)
   int N, Hq, Hkv, G, NHG, W, Pmax, Lmax;
   float scale_log2;
+  int tab_bytes;   // 4 or 2 (flat tables)
+  int leaf_e;      // entries per two-level leaf
+  int slots;       // resident partition workgroups (plan's size choice)
+  int force_log2;  // 0, or the partition size fixed by the caller (log2)
 };
 
 // Context length of sequence b, clamped to what its table can address (longer
@@ -78,43 +82,163 @@ struct Params {
 __device__ __forceinline__ int context_len(const Params& P, int b) { return min(max(P.ctx[b], 0), P.Lmax); }
 
 // ---------------------------------------------------------------------------------
-// Plan kernel (one workgroup): lists every (sequence, partition) item, longest first
-// so that the short tail partitions of a skewed batch run last.  Items are bucketed
-// by their number of 16-token units (full partitions first); an empty sequence gets
-// one item, which writes its zero output.  Only the order within a bucket depends
-// on timing, and no result depends on the order.
+// Plan kernel (one workgroup).  It picks this launch's partition size, then lists every
+// (sequence, partition) item, longest first so that the short tail partitions of a
+// skewed batch run last.
+//
+// Size: 2048 tokens unless the batch is too small to hide its longest 2048-token item
+// (choose_partition_log2): fewer, longer partitions save each workgroup's fixed start
+// and end, but a batch that cannot fill the chip ends when its longest item does.
+//
+// Order: items are bucketed into 64 classes by their number of tokens (classes of
+// PT/64 tokens; full partitions first, an empty sequence gets one item in class 1,
+// which writes its zero output).  A sequence whose first physical block is the
+// previous sequence's (a forked or cached prefix: parallel samples, beams, a shared
+// prompt) joins that sequence's group, within aligned runs of 16 sequences; the tail
+// items of a group are listed next to each other under the group's largest class, so
+// the workgroups that read the shared blocks run together and find them in L2.  Only
+// the order within a class depends on timing, and no result depends on the order.
 // ---------------------------------------------------------------------------------
 // Sequences with more full partitions than this have their task entries written by
 // the whole workgroup instead of one thread.
 constexpr int kPlanSerialMax = 32;
 constexpr int kPlanCoopMax = 256;
+constexpr int kPlanClasses = 64;
+constexpr int kGroupRun = 16;  // a group never crosses an aligned run of this many sequences
+
+// First block id of sequence b's table row.
+__device__ __forceinline__ int first_block(const Params& P, int b) {
+  if (P.dir) {
+    const int leaf = P.dir[static_cast<int64_t>(b) * (P.W / P.leaf_e)];
+    return static_cast<const int*>(P.tables)[static_cast<int64_t>(leaf) * P.leaf_e];
+  }
+  if (P.tab_bytes == 2) return static_cast<const uint16_t*>(P.tables)[static_cast<int64_t>(b) * P.W];
+  return static_cast<const int*>(P.tables)[static_cast<int64_t>(b) * P.W];
+}
+
+// Sequence b as the plan sees it.  Every lane of the workgroup calls this with
+// consecutive b (b = base + threadIdx.x, base a multiple of the workgroup size), so the
+// 16 lanes of each aligned run hold 16 consecutive sequences.
+struct PlanSeq {
+  int L;          // context length; -1 past the batch
+  bool head;      // first sequence of its group
+  bool last;      // last sequence of its group
+  int last_lane;  // lane of its group's last sequence
+};
+
+__device__ __forceinline__ PlanSeq plan_seq(const Params& P, int b) {
+  const int lane = threadIdx.x & 63;
+  PlanSeq s;
+  s.L = b < P.N ? context_len(P, b) : -1;
+  const int fb = (s.L > 0 && P.tables) ? first_block(P, b) : -1;
+  const int prev_L = __shfl_up(s.L, 1, kGroupRun);
+  const int prev_fb = __shfl_up(fb, 1, kGroupRun);
+  const bool follows = (lane & (kGroupRun - 1)) != 0 && fb >= 0 && prev_L > 0 && prev_fb == fb;
+  s.head = !follows;
+  const bool next_follows = __shfl_down(static_cast<int>(follows), 1, kGroupRun) != 0;
+  s.last = (lane & (kGroupRun - 1)) == kGroupRun - 1 || !next_follows;
+  // the first group end at or after this lane (lane 15 of a run always ends one)
+  int v = s.last ? lane : 64;
+#pragma unroll
+  for (int d = 1; d < kGroupRun; d <<= 1) v = min(v, __shfl_down(v, d, kGroupRun));
+  s.last_lane = v;
+  return s;
+}
+
+// A sequence's items at partition size 2^lg: `full` whole partitions and, in `cls`
+// (1..64; 0 = none), its tail item.
+__device__ __forceinline__ void tail_class(int L, int lg, int& full, int& cls) {
+  if (L < 0) {
+    full = 0;
+    cls = 0;
+    return;
+  }
+  full = L >> lg;
+  const int rem = L - (full << lg);
+  const int sh = lg - 6;  // classes of 2^lg / 64 tokens
+  cls = rem ? (rem + (1 << sh) - 1) >> sh : (L == 0 ? 1 : 0);
+}
+
+// Inclusive scan over the lane's group, from its head up to the lane: the largest class
+// and the number of tail items.
+__device__ __forceinline__ void group_scan(bool head, int& cls, int& cnt) {
+  int h = head;
+#pragma unroll
+  for (int d = 1; d < kGroupRun; d <<= 1) {
+    const int c2 = __shfl_up(cls, d, kGroupRun);
+    const int n2 = __shfl_up(cnt, d, kGroupRun);
+    const int h2 = __shfl_up(h, d, kGroupRun);
+    if (!h) {
+      cls = max(cls, c2);
+      cnt += n2;
+    }
+    h |= h2;
+  }
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
+  const unsigned lo = static_cast<unsigned>(__shfl_xor(static_cast<int>(static_cast<unsigned>(v)), mask, 64));
+  const unsigned hi = static_cast<unsigned>(__shfl_xor(static_cast<int>(static_cast<unsigned>(v >> 32)), mask, 64));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
 
 __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ tasks, int* __restrict__ counters) {
   const int N = P.N;
-  constexpr int NB = kPT / 16;
-  __shared__ int cnt[NB + 1];
+  constexpr int NB = kPlanClasses;
+  __shared__ int cnt[2][NB + 1];
   __shared__ int off[NB + 1];
-  __shared__ int n_coop;
+  __shared__ int n_coop, s_lmax;
+  __shared__ unsigned long long s_tokens;
   __shared__ int coop_b[kPlanCoopMax], coop_s[kPlanCoopMax], coop_n[kPlanCoopMax], coop_l[kPlanCoopMax];
   const int tid = threadIdx.x;
-  if (tid <= NB) cnt[tid] = 0;
-  if (tid == 0) n_coop = 0;
+  const int lane = tid & 63;
+  if (tid <= NB) {
+    cnt[0][tid] = 0;
+    cnt[1][tid] = 0;
+  }
+  if (tid == 0) {
+    n_coop = 0;
+    s_lmax = 0;
+    s_tokens = 0;
+  }
   for (int i = tid; i < N * P.Hq; i += blockDim.x) P.done[i] = 0;
   __syncthreads();
-  for (int b = tid; b < N; b += blockDim.x) {
-    const int L = context_len(P, b);
-    const int full = L / kPT;
-    const int rem = L - full * kPT;
-    if (full) atomicAdd(&cnt[NB], full);
-    if (rem || L == 0) atomicAdd(&cnt[rem ? (rem + 15) >> 4 : 1], 1);
+  // pass 1: item counts per class at both partition sizes, total and longest length
+  // (uniform trip count: every lane takes part in the shuffles)
+  unsigned long long tokens = 0;
+  int lmax = 0;
+  for (int b0 = 0; b0 < N; b0 += blockDim.x) {
+    const PlanSeq s = plan_seq(P, b0 + tid);
+    tokens += static_cast<unsigned long long>(max(s.L, 0));
+    lmax = max(lmax, s.L);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      int full, cls;
+      tail_class(s.L, kLgPartMin + c, full, cls);
+      int n = cls > 0;
+      group_scan(s.head, cls, n);
+      if (full) atomicAdd(&cnt[c][NB], full);
+      if (s.last && n) atomicAdd(&cnt[c][cls], n);
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    tokens += shfl_xor_u64(tokens, d);
+    lmax = max(lmax, __shfl_xor(lmax, d, 64));
+  }
+  if (lane == 0) {
+    atomicAdd(&s_tokens, tokens);
+    atomicMax(&s_lmax, lmax);
   }
   __syncthreads();
-  // exclusive offsets of the buckets, longest first (bucket NB, then NB - 1, ...): one
-  // wave scans them with lane shuffles, lane i holding bucket NB - i
-  static_assert(NB <= 64, "one wave scans the buckets");
+  const int lg = choose_partition_log2(s_tokens, s_lmax, P.Hkv * P.NHG, P.slots, P.force_log2);
+  const int* ccnt = cnt[lg - kLgPartMin];
+  // exclusive offsets of the classes, longest first (class NB, then NB - 1, ...): one
+  // wave scans them with lane shuffles, lane i holding class NB - i
+  static_assert(NB <= 64, "one wave scans the classes");
   if (tid < 64) {
     const int k = NB - tid;
-    const int c = k >= 1 ? cnt[k] : 0;
+    const int c = k >= 1 ? ccnt[k] : 0;
     int v = c;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -122,26 +246,39 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
       v += tid >= d ? t : 0;
     }
     if (k >= 1) off[k] = v - c;
-    if (tid == 63) counters[0] = v;
+    if (tid == 63) {
+      counters[0] = v;
+      counters[1] = lg;
+    }
   }
   __syncthreads();
-  for (int b = tid; b < N; b += blockDim.x) {
-    const int L = context_len(P, b);
-    const int full = L / kPT;
-    const int rem = L - full * kPT;
+  // pass 2: write the items
+  for (int b0 = 0; b0 < N; b0 += blockDim.x) {
+    const int b = b0 + tid;
+    const PlanSeq s = plan_seq(P, b);
+    const int L = s.L;
+    int full, cls;
+    tail_class(L, lg, full, cls);
+    const bool own = cls > 0;
+    int n = own;
+    group_scan(s.head, cls, n);
     if (full) {
-      const int s = atomicAdd(&off[NB], full);
+      const int st = atomicAdd(&off[NB], full);
       const int k = full > kPlanSerialMax ? atomicAdd(&n_coop, 1) : kPlanCoopMax;
       if (k < kPlanCoopMax) {
         coop_b[k] = b;
-        coop_s[k] = s;
+        coop_s[k] = st;
         coop_n[k] = full;
         coop_l[k] = L;
       } else {
-        for (int q = 0; q < full; ++q) tasks[s + q] = make_int2(b * P.Pmax + q, L);
+        for (int q = 0; q < full; ++q) tasks[st + q] = make_int2(b * P.Pmax + q, L);
       }
     }
-    if (rem || L == 0) tasks[atomicAdd(&off[rem ? (rem + 15) >> 4 : 1], 1)] = make_int2(b * P.Pmax + full, L);
+    // the group's last sequence reserves its tail items' places; n - 1 is this
+    // sequence's place among them
+    int base = (s.last && n) ? atomicAdd(&off[cls], n) : 0;
+    base = __shfl(base, s.last_lane, 64);
+    if (own) tasks[base + n - 1] = make_int2(b * P.Pmax + full, L);
   }
   __syncthreads();
   const int nc = min(n_coop, kPlanCoopMax);
@@ -406,14 +543,14 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   constexpr int KI = D / 32;   // 16x16x32 steps over head_dim
   constexpr int NC = D / 16;   // 16x16x16 products per unit (16 d each)
   constexpr int SUB = B / 16;  // 16-token units per block
-  constexpr int BPP = kPT / B;
+  constexpr int BPP_MAX = kPTMax / B;  // table entries of the largest partition
   constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
   struct Buf {
     u32x4 k[KI];
     u32x2 v[NC];
   };
 
-  __shared__ int s_tab[BPP];
+  __shared__ int s_tab[BPP_MAX];
   __shared__ float s_m[kWaves][GMAX];
   __shared__ float s_l[kWaves][GMAX];
   __shared__ float s_o[kWaves][GMAX][D + 4];
@@ -438,7 +575,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
     return;
   }
-  const int np = (L + kPT - 1) / kPT;
+  const int lg = min(max(P.counters[1], kLgPartMin), kLgPartMax);  // this launch's partition size
+  const int np = (L + (1 << lg) - 1) >> lg;
   if (p >= np) return;
 
   const int tid = threadIdx.x;
@@ -446,7 +584,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;
   const int m = lane & 15;
-  const int ntok = min(kPT, L - p * kPT);
+  const int ntok = min(1 << lg, L - (p << lg));
+  const int pe = (p << lg) / B;  // the partition's first table entry
   const int nunits = (ntok + 15) >> 4;
   const int nblk = (ntok + B - 1) / B;
 
@@ -456,7 +595,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   // (unconditional loads from clamped, always-valid addresses keep the waits exact; a
   // partition may span several two-level leaves, so each lane looks its entry up)
   const int tab_val = static_cast<int>(__builtin_nontemporal_load(
-      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + min(tid, nblk - 1))));
+      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + min(tid, nblk - 1))));
   const bool hv = m < gcur;
   u32x4 qf[KI];
   {
@@ -488,7 +627,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    load_blk(u0, static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + u0 / SUB)), first);
+    load_blk(u0, static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + u0 / SUB)), first);
   }
   PKV_FENCE();
   if (tid < nblk) s_tab[tid] = tab_val;
@@ -590,14 +729,14 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   constexpr int KI = D / 32;   // 16x16x32 steps over head_dim per 16-token sub-tile
   constexpr int NC = D / 16;   // 16x16x32 P.V products per unit (16 d each)
   constexpr int BPU = 32 / B;  // blocks per unit
-  constexpr int BPP = kPT / B;
+  constexpr int BPP_MAX = kPTMax / B;  // table entries of the largest partition
   constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
   struct Buf {
     u32x4 k[2][KI];
     u32x4 v[NC];
   };
 
-  __shared__ int s_tab[BPP];
+  __shared__ int s_tab[BPP_MAX];
   __shared__ float s_m[kWaves][GMAX];
   __shared__ float s_l[kWaves][GMAX];
   __shared__ float s_o[kWaves][GMAX][D + 4];
@@ -623,7 +762,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
     return;
   }
-  const int np = (L + kPT - 1) / kPT;
+  const int lg = min(max(P.counters[1], kLgPartMin), kLgPartMax);  // this launch's partition size
+  const int np = (L + (1 << lg) - 1) >> lg;
   if (p >= np) return;
 
   const int tid = threadIdx.x;
@@ -631,13 +771,14 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;
   const int m = lane & 15;
-  const int ntok = min(kPT, L - p * kPT);
+  const int ntok = min(1 << lg, L - (p << lg));
+  const int pe = (p << lg) / B;  // the partition's first table entry
   const int nunits = (ntok + 31) >> 5;
   const int nblk = (ntok + B - 1) / B;
 
   // preamble: all loads first (table entries, queries, first unit), LDS writes after
   const int tab_val = static_cast<int>(__builtin_nontemporal_load(
-      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + min(tid, nblk - 1))));
+      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + min(tid, nblk - 1))));
   const bool hv = m < gcur;
   u32x4 qf[KI];
   {
@@ -699,7 +840,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   {
     const int u0 = w < nunits ? w : 0;
     // (the unit's entries lie in one leaf: leaves hold an even number of entries)
-    const auto* e0 = table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + u0 * BPU);
+    const auto* e0 = table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + u0 * BPU);
     const int blk0 = static_cast<int>(e0[0]);
     const int blk1 = BPU == 2 ? static_cast<int>(e0[u0 * BPU + 1 < nblk ? 1 : 0]) : blk0;
     load_blk(blk0, blk1, first);
@@ -795,7 +936,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   constexpr int KL = NCH / 4;  // K chunks per lane per unit: r, r+4, r+8, ...
   constexpr int NV = D / 16;   // V rows per lane per unit: m, m+16, ...
   constexpr int SUB = B / 16;
-  constexpr int BPP = kPT / B;
+  constexpr int BPP_MAX = kPTMax / B;  // table entries of the largest partition
   constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
   typedef typename std::conditional<EB == 2, u32x2, u32x4>::type VVec;  // 4 tokens of one V row
   struct Buf {
@@ -803,7 +944,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
     VVec v[NV];
   };
 
-  __shared__ int s_tab[BPP];
+  __shared__ int s_tab[BPP_MAX];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ float s_o[kWaves][G][D + 4];
@@ -824,7 +965,8 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
     if (p == 0) zero_rows<T, D>(P, b, hq0, G);
     return;
   }
-  const int np = (L + kPT - 1) / kPT;
+  const int lg = min(max(P.counters[1], kLgPartMin), kLgPartMax);  // this launch's partition size
+  const int np = (L + (1 << lg) - 1) >> lg;
   if (p >= np) return;
 
   const int tid = threadIdx.x;
@@ -832,7 +974,8 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;
   const int m = lane & 15;
-  const int ntok = min(kPT, L - p * kPT);
+  const int ntok = min(1 << lg, L - (p << lg));
+  const int pe = (p << lg) / B;  // the partition's first table entry
   const int nunits = (ntok + 15) >> 4;
   const int nblk = (ntok + B - 1) / B;
 
@@ -840,7 +983,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   // block id and K/V), write LDS afterwards.
   // (unconditional: exact waits)
   const int tab_val = static_cast<int>(__builtin_nontemporal_load(
-      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + min(tid, nblk - 1))));
+      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + min(tid, nblk - 1))));
 
   // queries: lane keeps chunks r + 4i of every head (fp32 pools: pre-scaled floats)
   u32x4 qw[G][KL];
@@ -872,7 +1015,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    load_blk(u0, static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, p * BPP + u0 / SUB)), first);
+    load_blk(u0, static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + u0 / SUB)), first);
   }
   PKV_FENCE();
   if (tid < nblk) s_tab[tid] = tab_val;
@@ -1001,7 +1144,8 @@ __global__ __launch_bounds__(kThreads) void attn_merge_long(Params P) {
   __shared__ MergeSmem<D> s_merge;
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int np = (context_len(P, b) + kPT - 1) / kPT;
+  const int lg = min(max(P.counters[1], kLgPartMin), kLgPartMax);
+  const int np = (context_len(P, b) + (1 << lg) - 1) >> lg;
   if (np <= kFuseMaxParts) return;
   merge_row<T, D, false>(P, static_cast<int64_t>(b) * P.Hq + hq, np, s_merge);
 }
@@ -1029,6 +1173,10 @@ Params make_params(const AttnArgs& a) {
   P.Pmax = a.max_parts;
   P.Lmax = a.max_blocks_per_seq * a.block_size;
   P.scale_log2 = a.scale * kLog2e;
+  P.tab_bytes = a.table_bytes;
+  P.leaf_e = PKV_LEAF_TOKENS / a.block_size;
+  P.slots = a.slots;
+  P.force_log2 = a.force_log2;
   return P;
 }
 

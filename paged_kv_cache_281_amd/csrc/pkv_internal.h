@@ -4,6 +4,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include <hip/hip_runtime.h>
+
 #include "pkv.h"
 
 namespace pkv {
@@ -53,7 +55,39 @@ struct AttnArgs {
   int32_t max_blocks_per_seq, max_parts;
   int32_t table_bytes;  // 4 (int32 entries) or 2 (uint16 entries)
   float scale;
+  int32_t slots = 768;     // resident partition workgroups on the device (plan's size choice)
+  int32_t force_log2 = 0;  // 0, or the log2 of a partition size fixed by the caller
 };
+
+// Decode partition sizes (log2 of tokens) the plan pass chooses between.
+constexpr int kLgPartMin = 10;  // PKV_PARTITION_TOKENS: the workspace is sized for it
+constexpr int kLgPartMax = 11;  // PKV_PARTITION_TOKENS_MAX
+static_assert((1 << kLgPartMin) == PKV_PARTITION_TOKENS && (1 << kLgPartMax) == PKV_PARTITION_TOKENS_MAX,
+              "partition sizes");
+constexpr int kSlotsPerCU = 3;  // partition workgroups resident per compute unit
+
+// The plan's partition size for a batch of `tokens` context tokens in total, the longest
+// `lmax`, with `hy` workgroups per (sequence, partition) item: the larger size once the
+// batch's token work per resident workgroup slot reaches two thirds of its longest item
+// (capped at the larger size), else the smaller one.  Measured on MI355X: batches below
+// that ratio (GQA batches of 32 to 96 sequences) ran 1-19% faster with the smaller size,
+// batches at or above it (a 64-sequence MHA batch, a 256-sequence GQA batch, 256 forked
+// samples, one or eight 128K-token sequences) 1-5% faster with the larger one.
+__host__ __device__ inline int choose_partition_log2(unsigned long long tokens, int lmax, int hy, int slots,
+                                                     int force_log2) {
+  if (force_log2) return force_log2;
+  if (lmax <= (1 << kLgPartMin)) return kLgPartMin;
+  const unsigned long long longest = lmax < (1 << kLgPartMax) ? lmax : (1 << kLgPartMax);
+  return 3ull * tokens * static_cast<unsigned long long>(hy) >= 2ull * longest * static_cast<unsigned long long>(slots)
+             ? kLgPartMax
+             : kLgPartMin;
+}
+
+// Resident partition workgroups on the current device (cached per device).
+int32_t resident_slots();
+// The partition size fixed by pkv_set_decode_partition_tokens (log2), or 0.
+int32_t forced_partition_log2();
+int32_t set_forced_partition_log2(int32_t log2_tokens);
 
 // Byte offsets of the workspace regions (each 256-byte aligned) and the total size.
 struct WorkspaceLayout {

@@ -211,3 +211,65 @@ def test_prefix_cache_switch_and_plain_fallback(pkv_lib):
     assert pkv_lib.load().pkv_bm_set_prefix_cache(bm._h, 1) == 0
     assert bm.add_seq_tokens(1, [1, 2, 3, 4, 5]) == 0
     assert bm.add_seq_tokens(2, [1, 2, 3, 4, 5]) == 4 and bm.num_cached() == 1
+
+
+def test_decode_partition_size_rule(pkv_lib):
+    """The plan's partition size: 2048 when some context exceeds 1024 tokens and the token
+    work per workgroup slot reaches two thirds of the longest item (768 slots without a
+    device: 256 compute units x 3)."""
+    import synth
+    pt = pkv_lib.decode_partition_tokens
+    assert pt([], 32, 8) == 1024
+    assert pt([1024] * 4096, 32, 8) == 1024            # no context needs a second 1024 partition
+    assert pt(synth.gqa_bf16().context_lens, 32, 8) == 2048
+    assert pt(synth.gqa_bf16(num_seqs=32).context_lens, 32, 8) == 1024
+    assert pt(synth.mha_bf16().context_lens, 32, 32) == 2048
+    assert pt(synth.long_bf16(16, num_seqs=1).context_lens, 32, 8) == 2048
+    assert pt(synth.cow_fp16(1020).context_lens, 32, 8) == 2048
+    assert pt(synth.gqa_bf16(num_seqs=96).context_lens, 32, 8) == 1024
+    # the boundary: 3 * tokens * workgroups per item against 2 * longest * slots
+    assert pt([2048] + [0] * 15, 32, 8) == 1024            # 3 * 2048 * 8 < 2 * 2048 * 768
+    assert pt([2048] * 64, 32, 8) == 2048                  # 3 * 131072 * 8 == 2 * 2048 * 768
+    assert pt([2048] * 63, 32, 8) == 1024
+    assert pt([3000] * 64, 32, 8) == 2048                  # the longest item is capped at 2048 tokens
+    assert pt([3000] + [500] * 256, 32, 8) == 1024         # 131000 tokens: 3 * 131000 * 8 < 2 * 2048 * 768
+    assert pt([3000] + [500] * 257, 32, 8) == 2048         # 131500 tokens
+    assert pt([2048] * 64, 64, 2) == 1024                  # 32 query heads per kv head: 4 workgroups per item
+    assert pt([2048] * 128, 64, 2) == 2048
+    lib = pkv_lib.load()
+    out = ctypes.c_int32()
+    assert lib.pkv_decode_partition_tokens(None, 3, 32, 8, ctypes.byref(out)) == 1
+    assert lib.pkv_decode_partition_tokens(None, 0, 30, 8, ctypes.byref(out)) == 1
+    try:
+        pkv_lib.set_decode_partition_tokens(2048)
+        assert pt([100], 32, 8) == 2048
+        pkv_lib.set_decode_partition_tokens(1024)
+        assert pt(synth.gqa_bf16().context_lens, 32, 8) == 1024
+        assert lib.pkv_set_decode_partition_tokens(1000) == 1
+        assert lib.pkv_set_decode_partition_tokens(512) == 1
+    finally:
+        pkv_lib.set_decode_partition_tokens(0)
+    assert pt([100], 32, 8) == 1024
+
+
+def test_plan_table_reference_errors(pkv_lib):
+    """A bad table reference is rejected on the host before the plan launches."""
+    lib = pkv_lib.load()
+    P, T = pkv_lib.PoolDesc, pkv_lib.TableRef
+    d = P(64, 16, 8, 128, 2)
+    ws_bytes = lib.pkv_paged_attention_workspace_bytes(4, 32, 128, 8, 16)
+    fake = ctypes.c_void_p(0x1000)
+    for ref in (T(None, None, 4, 0), T(0x1000, None, 3, 0), T(0x1000, 0x2000, 2, 0), T(0x1002, None, 4, 0),
+                T(0x1000, None, 4, 1)):
+        st = lib.pkv_paged_attention_plan(ctypes.byref(d), 4, 32, 8, fake, ctypes.byref(ref), fake, ws_bytes, None)
+        assert st == 1, (ref.entries, ref.leaf_dir, ref.entry_bytes)
+        assert b"table reference" in lib.pkv_last_error()
+    # two-level: the row width must be whole leaves (32 entries at block 16)
+    st = lib.pkv_paged_attention_plan(ctypes.byref(d), 4, 32, 8, fake, ctypes.byref(T(0x1000, 0x2000, 4, 0)), fake,
+                                      ws_bytes, None)
+    assert st == 1
+    # 16-bit entries cannot address a pool of more than 65536 blocks
+    big = P(70000, 16, 8, 128, 2)
+    st = lib.pkv_decode_prepare(ctypes.byref(big), fake, fake, fake, fake, fake, 4, 4, 32, 8, fake,
+                                ctypes.byref(T(0x1000, None, 2, 0)), fake, ws_bytes, None)
+    assert st == 2

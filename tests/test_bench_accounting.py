@@ -30,6 +30,9 @@ def test_algorithmic_bytes_items():
     assert bench.algorithmic_bytes(w, lens, "int16")["tables"] == H * blocks * 2 + 4 * 4
     leaves = sum(-(-(-(-int(L) // 16)) // 32) for L in lens)
     assert bench.algorithmic_bytes(w, lens, "two_level")["tables"] == H * blocks * 4 + 4 * 4 + H * leaves * 4
+    # with 2048-token partitions only the 3000-token row is split (2 partitions)
+    assert bench.algorithmic_bytes(w, lens, partition_tokens=2048)["partials"] == 2 * 2 * Hq * (D + 2) * 4
+    assert bench.algorithmic_bytes(w, lens, partition_tokens=2048)["out"] == 3 * Hq * D * e
     u = bench.algorithmic_bytes(w, lens, unique=100)
     assert u["kv_unique"] == 2 * 100 * H * D * e and u["total"] == ab["total"] - ab["kv"] + u["kv_unique"]
 
