@@ -129,8 +129,10 @@ struct PlanSeq {
 __device__ __forceinline__ PlanSeq plan_seq(const Params& P, int b) {
   const int lane = threadIdx.x & 63;
   PlanSeq s;
+  // both loads issued before either is used (the table row exists for every b < N)
+  const int fb_row = (b < P.N && P.tables) ? first_block(P, b) : -1;
   s.L = b < P.N ? context_len(P, b) : -1;
-  const int fb = (s.L > 0 && P.tables) ? first_block(P, b) : -1;
+  const int fb = s.L > 0 ? fb_row : -1;
   const int prev_L = __shfl_up(s.L, 1, kGroupRun);
   const int prev_fb = __shfl_up(fb, 1, kGroupRun);
   const bool follows = (lane & (kGroupRun - 1)) != 0 && fb >= 0 && prev_L > 0 && prev_fb == fb;
@@ -207,8 +209,9 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
   // (uniform trip count: every lane takes part in the shuffles)
   unsigned long long tokens = 0;
   int lmax = 0;
+  const PlanSeq s_first = plan_seq(P, tid);  // kept for pass 2 (the whole batch when N <= blockDim)
   for (int b0 = 0; b0 < N; b0 += blockDim.x) {
-    const PlanSeq s = plan_seq(P, b0 + tid);
+    const PlanSeq s = b0 == 0 ? s_first : plan_seq(P, b0 + tid);
     tokens += static_cast<unsigned long long>(max(s.L, 0));
     lmax = max(lmax, s.L);
 #pragma unroll
@@ -255,7 +258,7 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
   // pass 2: write the items
   for (int b0 = 0; b0 < N; b0 += blockDim.x) {
     const int b = b0 + tid;
-    const PlanSeq s = plan_seq(P, b);
+    const PlanSeq s = b0 == 0 ? s_first : plan_seq(P, b);
     const int L = s.L;
     int full, cls;
     tail_class(L, lg, full, cls);
