@@ -136,7 +136,8 @@ def _group_classes(lens, first, pt):
 
 
 def _check_order(tasks, parts, lens, first, pt):
-    """The task list holds every expected item once, full partitions first, tail items in
+    """The task list holds every expected item once, full partitions first (in the top
+    class, with the tails that fill more than 63/64 of a partition), tail items in
     non-increasing group class, each group's tail items together in sequence order.
     Returns the groups."""
     expect = sorted((b * parts + p, int(L)) for b, L in enumerate(lens) for p in range(max(1, -(-int(L) // pt))))
@@ -144,7 +145,7 @@ def _check_order(tasks, parts, lens, first, pt):
     gcls, groups = _group_classes(lens, first, pt)
     b_of, p_of = tasks[:, 0] // parts, tasks[:, 0] % parts
     tail = (p_of == lens[b_of] // pt) & ((lens[b_of] % pt != 0) | (lens[b_of] == 0))
-    key = np.where(tail, gcls[b_of], 65)
+    key = np.where(tail, gcls[b_of], 64)  # full partitions share the top class with tails of > 63/64 of one
     assert (np.diff(key) <= 0).all(), "classes must not increase along the list"
     pos = {int(t): i for i, t in enumerate(tasks[:, 0])}
     for g in groups:
@@ -185,3 +186,51 @@ def test_plan_groups_only_equal_first_blocks():
     b_of, p_of = tasks[:, 0] // parts, tasks[:, 0] % parts
     tails = [int(b) for b, p in zip(b_of, p_of) if p == lens[b] // 1024]
     assert tails == list(range(16, 32)) + list(range(0, 16)) + list(range(32, 40))
+
+
+def _plan_prepare(lens, hq, hkv, tables, d=128, block=16):
+    """The plan as the fused write + plan launch runs it (256 threads; no tokens written)."""
+    n = len(lens)
+    W = tables.shape[1]
+    q = torch.zeros(n, hq, d, dtype=torch.bfloat16, device=DEV)
+    kp, vp = pkv.alloc_pools(1, block, hkv, d, torch.bfloat16, DEV)
+    kv_new = torch.zeros(0, hkv, d, dtype=torch.bfloat16, device=DEV)
+    slots = torch.zeros(0, dtype=torch.int64, device=DEV)
+    ws = pkv.alloc_workspace(n, hq, d, W, block, DEV)
+    lens_d = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(DEV)
+    pkv.decode_prepare(kp, vp, kv_new, kv_new, slots, q, tables, lens_d, ws)
+    torch.cuda.synchronize()
+    cnt = _counters(ws)
+    parts = -(-W * block // pkv.PARTITION_TOKENS)
+    return cnt, _tasks(ws, n, hq, d, parts, int(cnt[0])), parts
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_task_list_on_random_batches(seed):
+    """Random batches (more sequences than either plan launch has threads, empty
+    contexts, contexts that are whole partitions, runs of shared first blocks that cross
+    the aligned runs of 16) through both plan launches: a valid task list in the order
+    the plan promises, and the partition size of the host rule."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.choice([1, 17, 300, 1500]))
+    lens = rng.integers(0, 9000, size=n)
+    lens[rng.random(n) < 0.05] = 0
+    whole = rng.random(n) < 0.05
+    lens[whole] = 2048 * rng.integers(1, 4, size=int(whole.sum()))
+    # first blocks: runs of equal ids of random length (1..40), distinct between runs
+    first = np.zeros(n, dtype=np.int64)
+    b, run_id = 0, 0
+    while b < n:
+        k = int(rng.integers(1, 41))
+        first[b:b + k] = run_id
+        b += k
+        run_id += 1
+    W = max(1, int(-(-lens.max() // 16)))
+    rows = np.repeat(first[:, None], W, axis=1).astype(np.int32)
+    tables = torch.from_numpy(rows).to(DEV)
+    pt = pkv.decode_partition_tokens(lens, 32, 8)
+    for run in (_plan, _plan_prepare):
+        cnt, tasks, parts = run(lens, 32, 8, tables)
+        log(f"seed {seed} {run.__name__}: N={n} partition {1 << int(cnt[1])} (rule {pt}), {cnt[0]} items")
+        assert 1 << int(cnt[1]) == pt
+        _check_order(tasks, parts, lens.astype(np.int64), first, pt)
