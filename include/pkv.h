@@ -153,7 +153,8 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  * past the table row).
  *   q, out        device [num_seqs][num_q_heads][D], pool dtype, contiguous, 16-byte aligned.
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries at index
- *                 >= ceil(context_lens[b] / B) are never read.
+ *                 >= ceil(context_lens[b] / B) are never followed (the plan pass
+ *                 compares entry 0 of every row, an empty context's included).
  *   context_lens  device int32 [num_seqs]; 0 gives a zero output row.
  *   workspace     device, >= pkv_paged_attention_workspace_bytes(...), 256-byte aligned;
  *                 contents on entry do not matter.
@@ -245,7 +246,8 @@ int32_t pkv_paged_attention_prefill_t16(const pkv_pool_desc* pool, const void* k
  * Entry j of sequence b is leaves[leaf_dir[b][j / E]][j % E].  Each call equals the
  * flat-table call with max_blocks_per_seq = dir_width * E on the table those lookups
  * give, bit for bit.  Only the directory entries and leaf entries of a sequence's
- * first ceil(L / B) blocks are read; directory entries read must lie in
+ * first ceil(L / B) blocks are followed (the plan pass also reads, without following
+ * it, directory entry 0 of an empty context's row); directory entries followed must lie in
  * 0 .. num_leaves - 1 (a device precondition, checked by the debug library).  A batch
  * whose longest table sets the width of every row stores dir_width int32 per
  * sequence plus the leaves it uses, instead of dir_width * E per sequence.

@@ -106,12 +106,9 @@ constexpr int kPlanCoopMax = 256;
 constexpr int kPlanClasses = 64;
 constexpr int kGroupRun = 16;  // a group never crosses an aligned run of this many sequences
 
-// First block id of sequence b's table row.
-__device__ __forceinline__ int first_block(const Params& P, int b) {
-  if (P.dir) {
-    const int leaf = P.dir[static_cast<int64_t>(b) * (P.W / P.leaf_e)];
-    return static_cast<const int*>(P.tables)[static_cast<int64_t>(leaf) * P.leaf_e];
-  }
+// Entry 0 of sequence b's flat table row (in the caller's array whatever the context
+// length; only compared, never followed).
+__device__ __forceinline__ int first_entry_flat(const Params& P, int b) {
   if (P.tab_bytes == 2) return static_cast<const uint16_t*>(P.tables)[static_cast<int64_t>(b) * P.W];
   return static_cast<const int*>(P.tables)[static_cast<int64_t>(b) * P.W];
 }
@@ -129,10 +126,14 @@ struct PlanSeq {
 __device__ __forceinline__ PlanSeq plan_seq(const Params& P, int b) {
   const int lane = threadIdx.x & 63;
   PlanSeq s;
-  // both loads issued before either is used (the table row exists for every b < N)
-  const int fb_row = (b < P.N && P.tables) ? first_block(P, b) : -1;
+  // The flat-table entry (or the two-level directory entry) and the length are loaded
+  // together; a two-level leaf is followed only for a non-empty context, whose first
+  // directory entry names a real leaf.
+  const bool tab = b < P.N && P.tables;
+  const int e0 = !tab ? -1 : P.dir ? P.dir[static_cast<int64_t>(b) * (P.W / P.leaf_e)] : first_entry_flat(P, b);
   s.L = b < P.N ? context_len(P, b) : -1;
-  const int fb = s.L > 0 ? fb_row : -1;
+  int fb = -1;
+  if (tab && s.L > 0) fb = P.dir ? static_cast<const int*>(P.tables)[static_cast<int64_t>(e0) * P.leaf_e] : e0;
   const int prev_L = __shfl_up(s.L, 1, kGroupRun);
   const int prev_fb = __shfl_up(fb, 1, kGroupRun);
   const bool follows = (lane & (kGroupRun - 1)) != 0 && fb >= 0 && prev_L > 0 && prev_fb == fb;

@@ -171,3 +171,25 @@ def test_prefill_two_level_matches_flat_tables(case):
     pool, tables, lens_o = replay_prefill(w, synth.NAN_BITS[w.dtype], context=ctx)
     ref = oracle_prefill(w.queries(), w.dtype, pool, tables, lens_o, w.query_start(), w.scale)
     compare(w, c, ref)
+
+
+def test_decode_two_level_empty_contexts_ignore_their_directory():
+    """A sequence with an empty context has its directory row read by the plan pass but
+    never followed: rows naming a leaf past the last one (num_leaves) give the same bits
+    as the flat call with those contexts empty, and zero output rows."""
+    w = synth.gqa_bf16(num_seqs=12, max_len=2100)
+    st = replay_gpu(w, w.all_context_kv(), DEV)
+    pad = nan_block(w, st.bm)
+    ld, lv, tl = _two_level(st.bm, w.batch, w.max_blocks_per_seq, w.block_size, pad, DEV)
+    lens = st.context_lens.clone()
+    empty = [0, 5, 6, 11]
+    lens[empty] = 0
+    dir_bad = tl.leaf_dir.clone()
+    dir_bad[empty] = tl.leaves.shape[0]
+    tl_bad = pkv.TwoLevelTables(dir_bad.contiguous(), tl.leaves)
+    q = to_device(w.queries(), w.dtype, DEV)
+    flat = pkv.paged_attention_decode(q, st.k_pool, st.v_pool, st.tables, lens, w.scale)
+    two = pkv.paged_attention_decode(q, st.k_pool, st.v_pool, tl_bad, lens, w.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(two, w.dtype), to_bits(flat, w.dtype))
+    assert (two[empty].float() == 0).all()
