@@ -77,6 +77,11 @@ struct Params {
   int force_log2;  // 0, or the partition size fixed by the caller (log2)
 };
 
+// Task items (sequence * Pmax + partition, below 2^23 by the host's size checks) carry
+// this bit when their sequence belongs to a group of sequences that share their first
+// block: the partition kernels then read its K/V with cached loads.
+constexpr int kSharedTask = 1 << 30;
+
 // Context length of sequence b, clamped to what its table can address (longer
 // values break the caller's contract; clamping keeps every access in bounds).
 __device__ __forceinline__ int context_len(const Params& P, int b) { return min(max(P.ctx[b], 0), P.Lmax); }
@@ -96,8 +101,10 @@ __device__ __forceinline__ int context_len(const Params& P, int b) { return min(
 // previous sequence's (a forked or cached prefix: parallel samples, beams, a shared
 // prompt) joins that sequence's group, within aligned runs of 16 sequences; the tail
 // items of a group are listed next to each other under the group's largest class, so
-// the workgroups that read the shared blocks run together and find them in L2.  Only
-// the order within a class depends on timing, and no result depends on the order.
+// the workgroups that read the shared blocks run together and find them in L2.  The
+// items of a group of two or more sequences carry kSharedTask, for which the partition
+// kernels read K/V with cached rather than streaming loads.  Only the order within a
+// class depends on timing, and no result depends on the order or the load flavour.
 // ---------------------------------------------------------------------------------
 // Sequences with more full partitions than this have their task entries written by
 // the whole workgroup instead of one thread.
@@ -193,6 +200,7 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
   __shared__ int n_coop, s_lmax;
   __shared__ unsigned long long s_tokens;
   __shared__ int coop_b[kPlanCoopMax], coop_s[kPlanCoopMax], coop_n[kPlanCoopMax], coop_l[kPlanCoopMax];
+  __shared__ int coop_f[kPlanCoopMax];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   if (tid <= NB) {
@@ -264,6 +272,7 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
     int full, cls;
     tail_class(L, lg, full, cls);
     const bool own = cls > 0;
+    const int flag = (s.head && s.last) ? 0 : kSharedTask;  // a group of more than one sequence
     int n = own;
     group_scan(s.head, cls, n);
     if (full) {
@@ -274,20 +283,22 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
         coop_s[k] = st;
         coop_n[k] = full;
         coop_l[k] = L;
+        coop_f[k] = flag;
       } else {
-        for (int q = 0; q < full; ++q) tasks[st + q] = make_int2(b * P.Pmax + q, L);
+        for (int q = 0; q < full; ++q) tasks[st + q] = make_int2((b * P.Pmax + q) | flag, L);
       }
     }
     // the group's last sequence reserves its tail items' places; n - 1 is this
     // sequence's place among them
     int base = (s.last && n) ? atomicAdd(&off[cls], n) : 0;
     base = __shfl(base, s.last_lane, 64);
-    if (own) tasks[base + n - 1] = make_int2(b * P.Pmax + full, L);
+    if (own) tasks[base + n - 1] = make_int2((b * P.Pmax + full) | flag, L);
   }
   __syncthreads();
   const int nc = min(n_coop, kPlanCoopMax);
   for (int k = 0; k < nc; ++k) {
-    for (int q = tid; q < coop_n[k]; q += blockDim.x) tasks[coop_s[k] + q] = make_int2(coop_b[k] * P.Pmax + q, coop_l[k]);
+    for (int q = tid; q < coop_n[k]; q += blockDim.x)
+      tasks[coop_s[k] + q] = make_int2((coop_b[k] * P.Pmax + q) | coop_f[k], coop_l[k]);
   }
 }
 
@@ -429,6 +440,33 @@ __device__ __forceinline__ V load_stream(const char* p) {
 #endif
 }
 
+// K/V tile loads of a workgroup whose sequence shares its first blocks with its
+// neighbours (a task flagged by the plan) are cached loads instead: the group's other
+// workgroups, listed next to it, read the same shared blocks from L2.  They are buffer
+// loads from a resource over the tile (base: the tile's scalar address), so they stay
+// distinct instructions from the streaming global loads on the other side of the
+// workgroup-uniform branch (two loads that differ only in their cache hint would be
+// merged into one plain load).
+using Streamed = std::false_type;
+using Cached = std::true_type;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* tile) {
+  // raw (stride 0) resource; 0x00020000 is the gfx9 word-3 format for untyped access
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile), static_cast<short>(0), 0x7fffffff, 0x00020000);
+}
+template <class V>
+__device__ __forceinline__ V load_cached(__amdgpu_buffer_rsrc_t r, int off) {
+  static_assert(sizeof(V) == 16 || sizeof(V) == 8, "8- or 16-byte K/V fragments");
+  if constexpr (sizeof(V) == 16) return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  else return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+// The same through a per-lane pointer (no tile base to build a resource from): plain
+// loads when cached.
+template <class V, class Temporal>
+__device__ __forceinline__ V load_kv(const char* p) {
+  if constexpr (Temporal::value) return *reinterpret_cast<const V*>(p);
+  else return load_stream<V>(p);
+}
+
 // Rows split into at most this many partitions are merged inside the partition
 // kernel by their last finisher; longer rows (long contexts) are merged by a separate
 // kernel that spreads each row over a whole workgroup.
@@ -566,8 +604,9 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int hy = blockIdx.x - t * HY;
   if (t >= P.counters[0]) return;
   const int2 task = P.tasks[t];
-  const int item = task.x;
-  if (item < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
+  const int item = task.x & ~kSharedTask;
+  const bool shared = (task.x & kSharedTask) != 0;
+  if (task.x < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
   const int b = item / P.Pmax;
   const int p = item - b * P.Pmax;
   const int kvh = hy / P.NHG;
@@ -616,22 +655,38 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int koff = (r * B + m) * 16;       // + ki * 4 * B * 16 + sub * 256
   const int voff = (m * B + 4 * r) * EB;   // + c * 16 * B * EB + sub * 16 * EB
 
-  auto load_blk = [&](int u, int blk, Buf& f) {
+  auto load_blk = [&](auto temporal, int u, int blk, Buf& f) {
     const int sub = u - (u / SUB) * SUB;
     const char* kt = kbase + blk * bstride + sub * 256;
     const char* vt = vbase + blk * bstride + sub * 16 * EB;
+    if constexpr (decltype(temporal)::value) {
+      const auto rk = tile_rsrc(kt);
+      const auto rv = tile_rsrc(vt);
 #pragma unroll
-    for (int ki = 0; ki < KI; ++ki) f.k[ki] = load_stream<u32x4>(kt + koff + ki * 4 * B * 16);
+      for (int ki = 0; ki < KI; ++ki) f.k[ki] = load_cached<u32x4>(rk, koff + ki * 4 * B * 16);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) f.v[c] = load_stream<u32x2>(vt + voff + c * 16 * B * EB);
+      for (int c = 0; c < NC; ++c) f.v[c] = load_cached<u32x2>(rv, voff + c * 16 * B * EB);
+    } else {
+#pragma unroll
+      for (int ki = 0; ki < KI; ++ki) f.k[ki] = load_stream<u32x4>(kt + koff + ki * 4 * B * 16);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) f.v[c] = load_stream<u32x2>(vt + voff + c * 16 * B * EB);
+    }
   };
-  auto load = [&](int u, Buf& f) { load_blk(u, __builtin_amdgcn_readfirstlane(s_tab[u / SUB]), f); };
+  // `shared` is uniform over the workgroup: one scalar branch per unit picks the flavour
+  auto load = [&](int u, Buf& f) {
+    const int blk = __builtin_amdgcn_readfirstlane(s_tab[u / SUB]);
+    if (shared) load_blk(Cached{}, u, blk, f);
+    else load_blk(Streamed{}, u, blk, f);
+  };
   // the wave's first unit takes its block id straight from the table (a scalar load);
   // a wave without units loads unit 0 (unused) so the load stays unconditional
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    load_blk(u0, static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + u0 / SUB)), first);
+    const int blk = static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + u0 / SUB));
+    if (shared) load_blk(Cached{}, u0, blk, first);
+    else load_blk(Streamed{}, u0, blk, first);
   }
   PKV_FENCE();
   if (tid < nblk) s_tab[tid] = tab_val;
@@ -753,8 +808,9 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int hy = blockIdx.x - t * HY;
   if (t >= P.counters[0]) return;
   const int2 task = P.tasks[t];
-  const int item = task.x;
-  if (item < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
+  const int item = task.x & ~kSharedTask;
+  const bool shared = (task.x & kSharedTask) != 0;
+  if (task.x < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
   const int b = item / P.Pmax;
   const int p = item - b * P.Pmax;
   const int kvh = hy / P.NHG;
@@ -816,7 +872,10 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     voff = (m * B + 8 * r) * EB;
   }
 
-  auto load_blk = [&](int blk0, int blk1, Buf& f) {
+  auto load_blk = [&](auto temporal, int blk0, int blk1, Buf& f) {
+    // cached buffer loads need one tile base per wave: units of one 32-token block
+    constexpr bool kBuf = decltype(temporal)::value && BPU == 1;
+    using Tp = std::integral_constant<bool, decltype(temporal)::value && !kBuf>;
     const char* k0 = kbase + blk0 * bstride;
     const char* v0 = vbase + blk0 * bstride;
     const char* kt = k0;
@@ -827,18 +886,32 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
       kt = k_second ? k1 : k0;
       vt = v_second ? v1 : v0;
     }
+    if constexpr (kBuf) {
+      const auto rk = tile_rsrc(kt);
+      const auto rv = tile_rsrc(vt);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int ki = 0; ki < KI; ++ki) f.k[s][ki] = load_stream<u32x4>(kt + koff[s] + ki * 4 * B * 16);
+        for (int ki = 0; ki < KI; ++ki) f.k[s][ki] = load_cached<u32x4>(rk, koff[s] + ki * 4 * B * 16);
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) f.v[c] = load_cached<u32x4>(rv, voff + c * 16 * B * EB);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int ki = 0; ki < KI; ++ki) f.k[s][ki] = load_kv<u32x4, Tp>(kt + koff[s] + ki * 4 * B * 16);
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) f.v[c] = load_kv<u32x4, Tp>(vt + voff + c * 16 * B * EB);
     }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) f.v[c] = load_stream<u32x4>(vt + voff + c * 16 * B * EB);
   };
+  // `shared` is uniform over the workgroup: one scalar branch per unit picks the flavour
   auto load = [&](int u, Buf& f) {
     const int blk0 = __builtin_amdgcn_readfirstlane(s_tab[u * BPU]);
     const int blk1 = BPU == 2 ? __builtin_amdgcn_readfirstlane(s_tab[min(u * BPU + 1, nblk - 1)]) : blk0;
-    load_blk(blk0, blk1, f);
+    if (shared) load_blk(Cached{}, blk0, blk1, f);
+    else load_blk(Streamed{}, blk0, blk1, f);
   };
   Buf first;
   {
@@ -847,7 +920,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     const auto* e0 = table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + u0 * BPU);
     const int blk0 = static_cast<int>(e0[0]);
     const int blk1 = BPU == 2 ? static_cast<int>(e0[u0 * BPU + 1 < nblk ? 1 : 0]) : blk0;
-    load_blk(blk0, blk1, first);
+    if (shared) load_blk(Cached{}, blk0, blk1, first);
+    else load_blk(Streamed{}, blk0, blk1, first);
   }
   PKV_FENCE();
   if (tid < nblk) s_tab[tid] = tab_val;
@@ -959,8 +1033,10 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   const int kvh = blockIdx.x - t * P.Hkv;
   if (t >= P.counters[0]) return;
   const int2 task = P.tasks[t];
-  const int item = task.x;
-  if (item < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
+  const int item = task.x & ~kSharedTask;
+  // (streaming loads whatever the shared flag: a second load flavour would cost this
+  // kernel a wave per SIMD, 136 VGPRs against 128)
+  if (task.x < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
   const int b = item / P.Pmax;
   const int p = item - b * P.Pmax;
   const int hq0 = kvh * G;

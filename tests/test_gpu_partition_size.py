@@ -8,7 +8,8 @@ the plan's task list.
 - The size the device picks equals the host rule (pkv_decode_partition_tokens).
 - The task list is a permutation of the expected (sequence, partition) items, full
   partitions first, tail items in non-increasing length class, and the tail items of
-  sequences that share their first block (copy-on-write samples) listed together.
+  sequences that share their first block (copy-on-write samples) listed together and
+  flagged for cached K/V loads.
 """
 import numpy as np
 import pytest
@@ -62,11 +63,21 @@ def _counters(ws: torch.Tensor) -> np.ndarray:
     return ws[-256:].view(torch.int32)[:2].cpu().numpy()
 
 
+SHARED = 1 << 30  # task flag: the sequence shares its first block with a neighbour
+
+
 def _tasks(ws: torch.Tensor, n: int, hq: int, d: int, parts: int, count: int) -> np.ndarray:
     # workspace regions (each 256-byte aligned): partial outputs, (max, sum) pairs, tasks
     al = lambda x: (x + 255) // 256 * 256
     off = al(n * hq * parts * d * 4) + al(n * hq * parts * 2 * 4)
     return ws[off:off + count * 8].view(torch.int32).view(-1, 2).cpu().numpy()
+
+
+def _items(tasks: np.ndarray) -> np.ndarray:
+    """The (item, length) pairs with the shared-group flag cleared."""
+    t = tasks.copy()
+    t[:, 0] &= ~SHARED
+    return t
 
 
 def _plan(lens, hq, hkv, tables, d=128, block=16):
@@ -107,7 +118,8 @@ def test_device_choice_matches_host_rule(name, lens_fn, hq, hkv):
     log(f"{name}: host rule {pt}, device log2 {cnt[1]}, {cnt[0]} items")
     assert 1 << int(cnt[1]) == pt
     expect = sorted((b * parts + p, int(L)) for b, L in enumerate(lens) for p in range(max(1, -(-int(L) // pt))))
-    assert sorted(map(tuple, tasks.tolist())) == expect
+    assert sorted(map(tuple, _items(tasks).tolist())) == expect
+    assert not (tasks[:, 0] & SHARED).any()  # distinct first blocks: no groups
 
 
 def _group_classes(lens, first, pt):
@@ -139,10 +151,17 @@ def _check_order(tasks, parts, lens, first, pt):
     """The task list holds every expected item once, full partitions first (in the top
     class, with the tails that fill more than 63/64 of a partition), tail items in
     non-increasing group class, each group's tail items together in sequence order.
+    Items of a group of two or more sequences carry the shared flag, the others not.
     Returns the groups."""
+    flags = (tasks[:, 0] & SHARED) != 0
+    tasks = _items(tasks)
     expect = sorted((b * parts + p, int(L)) for b, L in enumerate(lens) for p in range(max(1, -(-int(L) // pt))))
     assert sorted(map(tuple, tasks.tolist())) == expect
     gcls, groups = _group_classes(lens, first, pt)
+    size = np.zeros(len(lens), dtype=np.int64)
+    for g in groups:
+        size[g] = len(g)
+    assert np.array_equal(flags, size[tasks[:, 0] // parts] > 1)
     b_of, p_of = tasks[:, 0] // parts, tasks[:, 0] % parts
     tail = (p_of == lens[b_of] // pt) & ((lens[b_of] % pt != 0) | (lens[b_of] == 0))
     key = np.where(tail, gcls[b_of], 64)  # full partitions share the top class with tails of > 63/64 of one
@@ -183,6 +202,7 @@ def test_plan_groups_only_equal_first_blocks():
         assert len(groups) == n_groups
     # with one first block: runs 16..31 (largest tail class 62), 0..15 (41), 32..39 (33)
     cnt, tasks, parts = _plan(lens, 32, 8, same)
+    tasks = _items(tasks)
     b_of, p_of = tasks[:, 0] // parts, tasks[:, 0] % parts
     tails = [int(b) for b, p in zip(b_of, p_of) if p == lens[b] // 1024]
     assert tails == list(range(16, 32)) + list(range(0, 16)) + list(range(32, 40))
