@@ -120,6 +120,19 @@ __device__ __forceinline__ int first_entry_flat(const Params& P, int b) {
   return static_cast<const int*>(P.tables)[static_cast<int64_t>(b) * P.W];
 }
 
+// Shifts within rows of 16 lanes (DPP row_shr / row_shl): lane l gets lane l - D (up) or
+// l + D (down) of its row, or its own value where that lane is outside the row.
+template <int D>
+__device__ __forceinline__ int row_up(int v) {
+  static_assert(D >= 1 && D <= 15, "row shift");
+  return __builtin_amdgcn_update_dpp(v, v, 0x110 + D, 0xf, 0xf, false);
+}
+template <int D>
+__device__ __forceinline__ int row_down(int v) {
+  static_assert(D >= 1 && D <= 15, "row shift");
+  return __builtin_amdgcn_update_dpp(v, v, 0x100 + D, 0xf, 0xf, false);
+}
+
 // Sequence b as the plan sees it.  Every lane of the workgroup calls this with
 // consecutive b (b = base + threadIdx.x, base a multiple of the workgroup size), so the
 // 16 lanes of each aligned run hold 16 consecutive sequences.
@@ -141,16 +154,19 @@ __device__ __forceinline__ PlanSeq plan_seq(const Params& P, int b) {
   s.L = b < P.N ? context_len(P, b) : -1;
   int fb = -1;
   if (tab && s.L > 0) fb = P.dir ? static_cast<const int*>(P.tables)[static_cast<int64_t>(e0) * P.leaf_e] : e0;
-  const int prev_L = __shfl_up(s.L, 1, kGroupRun);
-  const int prev_fb = __shfl_up(fb, 1, kGroupRun);
+  static_assert(kGroupRun == 16, "groups are found within DPP rows of 16 lanes");
+  const int prev_L = row_up<1>(s.L);
+  const int prev_fb = row_up<1>(fb);
   const bool follows = (lane & (kGroupRun - 1)) != 0 && fb >= 0 && prev_L > 0 && prev_fb == fb;
   s.head = !follows;
-  const bool next_follows = __shfl_down(static_cast<int>(follows), 1, kGroupRun) != 0;
+  const bool next_follows = row_down<1>(static_cast<int>(follows)) != 0;
   s.last = (lane & (kGroupRun - 1)) == kGroupRun - 1 || !next_follows;
   // the first group end at or after this lane (lane 15 of a run always ends one)
   int v = s.last ? lane : 64;
-#pragma unroll
-  for (int d = 1; d < kGroupRun; d <<= 1) v = min(v, __shfl_down(v, d, kGroupRun));
+  v = min(v, row_down<1>(v));
+  v = min(v, row_down<2>(v));
+  v = min(v, row_down<4>(v));
+  v = min(v, row_down<8>(v));
   s.last_lane = v;
   return s;
 }
@@ -171,19 +187,23 @@ __device__ __forceinline__ void tail_class(int L, int lg, int& full, int& cls) {
 
 // Inclusive scan over the lane's group, from its head up to the lane: the largest class
 // and the number of tail items.
+template <int D>
+__device__ __forceinline__ void group_scan_step(int& h, int& cls, int& cnt) {
+  const int c2 = row_up<D>(cls);
+  const int n2 = row_up<D>(cnt);
+  const int h2 = row_up<D>(h);
+  if (!h) {
+    cls = max(cls, c2);
+    cnt += n2;
+  }
+  h |= h2;
+}
 __device__ __forceinline__ void group_scan(bool head, int& cls, int& cnt) {
   int h = head;
-#pragma unroll
-  for (int d = 1; d < kGroupRun; d <<= 1) {
-    const int c2 = __shfl_up(cls, d, kGroupRun);
-    const int n2 = __shfl_up(cnt, d, kGroupRun);
-    const int h2 = __shfl_up(h, d, kGroupRun);
-    if (!h) {
-      cls = max(cls, c2);
-      cnt += n2;
-    }
-    h |= h2;
-  }
+  group_scan_step<1>(h, cls, cnt);
+  group_scan_step<2>(h, cls, cnt);
+  group_scan_step<4>(h, cls, cnt);
+  group_scan_step<8>(h, cls, cnt);
 }
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
