@@ -314,17 +314,16 @@ def long_bf16(block_size: int = 16, seed: int = 1004, num_seqs: int = 8, context
 
 
 def cow_fp16(prompt_len: int = 1020, seed: int = 1003, num_prompts: int = 64, samples: int = 4,
-             max_suffix: int = 256) -> Workload:
+             max_suffix: int = 256, block: int = 16, hq: int = 32, hkv: int = 8) -> Workload:
     """Parallel sampling: prompts of ``prompt_len`` tokens, each forked into ``samples`` samples.
 
     Sample i of prompt k is sequence ``samples*k + i``; sample 0 is the prompt's own
     sequence.  Each sample has generated s ~ U{0..max_suffix} tokens before the
     measured step (one decode step per token, all samples stepping together), then
     the measured step appends one more token to every sample.  32 q / 8 kv heads,
-    D=128, B=16, fp16.
+    D=128, B=16, fp16 (block size and head counts can be changed for test cases).
     """
     rng = np.random.default_rng(seed)
-    block = 16
     n = num_prompts * samples
     suffix = rng.integers(0, max_suffix + 1, size=n)
     lengths = prompt_len + suffix + 1
@@ -339,7 +338,7 @@ def cow_fp16(prompt_len: int = 1020, seed: int = 1003, num_prompts: int = 64, sa
     steps.append(list(range(n)))
     width = -(-(prompt_len + max_suffix + 1) // block)
     return Workload(
-        name=f"cow_fp16_p{prompt_len}", seed=seed, dtype="f16", num_q_heads=32, num_kv_heads=8,
+        name=f"cow_fp16_p{prompt_len}", seed=seed, dtype="f16", num_q_heads=hq, num_kv_heads=hkv,
         head_dim=128, block_size=block, num_blocks=num_blocks, max_blocks_per_seq=width,
         scale=1.0 / math.sqrt(128), free_order=free_order,
         prefill=[(samples * k, prompt_len) for k in range(num_prompts)],

@@ -41,6 +41,10 @@ CASES = [
     ("gqa_bf16", lambda: synth.gqa_bf16(num_seqs=12, max_len=6000)),
     ("f16_g8_d64_b16", lambda: _custom("f16_g8", "f16", 16, 2, 64, 16, [2, 2047, 2048, 2049, 3000, 6143], seed=9)),
     ("cow_fp16_p1020", lambda: synth.cow_fp16(1020, num_prompts=3, max_suffix=200)),
+    # shared-prefix groups (cached K/V loads) in the 32-token-block kernel, and flagged
+    # tasks in the vector-ALU kernel (one query head per kv head), which streams them
+    ("cow_fp16_b32", lambda: synth.cow_fp16(1020, num_prompts=3, max_suffix=200, block=32)),
+    ("cow_fp16_mha", lambda: synth.cow_fp16(1020, num_prompts=3, max_suffix=200, hq=8, hkv=8)),
     ("long_bf16_b16", lambda: synth.long_bf16(16, num_seqs=2, context=5000)),
     ("long_bf16_b32", lambda: synth.long_bf16(32, num_seqs=2, context=5000)),
     # 40 partitions at 1024 (separate merge kernel), 20 at 2048 (merged by the last finisher)
