@@ -14,6 +14,12 @@ algorithmic K+V bytes / step time); ``roofline`` describes the dominant kernel
 (the attention partition pass) against MI355X's 8 TB/s HBM peak; ``cpu_baseline``
 times the fp64 oracle on a bounded sample of the same workload.
 
+Without ``--workload`` the line is the long-context decode step (8 sequences of 131,072
+tokens, block 16: the largest single-GPU configuration), and it carries, as
+sub-records, the GQA batch (256 sequences), long context at block 32, long context at
+512-token partitions, and the device's streaming-read ceiling (``pkv_stream_read`` over
+4 GiB).  ``--workload stream_ceiling`` prints that ceiling as its own line.
+
 With a prefill workload (``--workload prefill_bf16`` or ``chunked_bf16``) a step is
 the KV write of every sequence's chunk followed by the causal chunk attention (its
 plan pass and its attention pass);
@@ -53,6 +59,7 @@ PCIE_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PARTITION_TOKENS = 1024  # the library's shorter decode partition (the plan may pick 2048)
+FUSE_MAX_PARTS = 32  # rows split into more partitions are merged by the separate merge kernel
 LEAF_TOKENS = 512  # the library's two-level leaf
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_attention.hip")
 PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_281_amd", "csrc", "paged_prefill.hip")
@@ -111,7 +118,7 @@ def algorithmic_bytes(w, lens, table_format="int32", unique=None, partition_toke
         tables += int(groups * (-(-(-(-lens // B)) // leaf)).sum() * 4)
     kv_hbm = kv if unique is None else int(2 * unique * H * D * e)
     return {"kv": kv, "kv_unique": kv_hbm, "q": q, "out": out, "partials": partials, "tables": tables,
-            "total": kv_hbm + q + out + partials + tables}
+            "total": kv_hbm + q + out + partials + tables, "merge_long": bool((parts > FUSE_MAX_PARTS).any())}
 
 
 def partition_tokens_of(w, lens):
@@ -682,66 +689,65 @@ def lenclass_main(args, lw, dev):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gqa_bf16")
-    ap.add_argument("--num-seqs", type=int, default=None,
-                    help="override the workload's number of sequences (decode workloads)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--flush-reps", type=int, default=10,
-                    help="extra partition-pass timings, each after a 512 MiB cache flush")
-    ap.add_argument("--eager", action="store_true",
-                    help="time the decode step as stream launches instead of replays of its HIP graph")
-    ap.add_argument("--tables", choices=["int32", "int16", "two_level"], default="int32",
-                    help="block-table format of the decode step (flat int32, flat 16-bit, or two-level)")
-    ap.add_argument("--partition-tokens", type=int, choices=[0, 1024, 2048], default=0,
-                    help="fix the decode partition size (0: the plan pass chooses per batch)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path runs on one GPU, see the design notes for how it would shard)", file=sys.stderr)
-        sys.exit(2)
-
+def stream_ceiling(dev, gib=4, reps=10, configs=None):
+    """The device's streaming-read rate: one read of a ``gib`` GiB buffer by the library's
+    probe kernel (``pkv_stream_read``: 16-byte non-temporal loads, grid-stride), over a
+    sweep of workgroup counts and loads in flight; HIP events around ``reps`` launches."""
     import torch
-    dev = torch.device("cuda:0")
-    if args.copy_calibration:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
+    import paged_kv_cache_281_amd as pkv
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    stream = torch.cuda.current_stream(dev)
+    configs = configs or [(wg, u) for u in (4, 8) for wg in (2048, 4096, 8192, 16384, 32768, 65536)]
+    sink = torch.empty(4 * max(wg for wg, _ in configs), dtype=torch.int32, device=dev)
+    rows = []
+    for wg, u in configs:
+        pkv.stream_read(src, sink, wg, u)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            pkv.stream_read(src, sink, wg, u)
+        e1.record(stream)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "reps": 5}))
-        return
+        ms = e0.elapsed_time(e1) / reps
+        rows.append({"workgroups": wg, "loads_in_flight": u, "ms": round(ms, 4), "gbs": round(n / (ms * 1e-3) / 1e9, 1)})
+    del src, sink
+    torch.cuda.empty_cache()
+    best = max(rows, key=lambda r: r["gbs"])
+    return {"bytes": n, "best_gbs": best["gbs"], "best": best, "frac_of_peak": round(best["gbs"] / HBM_PEAK_GBS, 4),
+            "sweep": rows, "kernel": "stream_read_kernel (pkv_stream_read)"}
 
+
+def stream_main(args, dev):
+    """``--workload stream_ceiling``: the streaming-read ceiling as its own JSON line."""
+    log("streaming-read ceiling: 4 GiB, sweep of launch shapes")
+    t0 = time.perf_counter()
+    c = stream_ceiling(dev, reps=max(1, args.steps))
+    log(f"best {c['best_gbs']} GB/s ({c['best']}) in {time.perf_counter() - t0:.1f} s")
+    res = {"metric": "HBM streaming-read GB/s (% of HBM peak), 1 GPU", "value": c["best_gbs"], "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": 1, "ms_per_step": c["best"]["ms"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+           "config": {"workload": "stream_ceiling", "bytes": c["bytes"]},
+           "roofline": {"kernel": c["kernel"], "bound": "hbm", "achieved": c["best_gbs"], "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": c["frac_of_peak"], "traffic": None, "algorithmic_bytes": c["bytes"]},
+           "sweep": c["sweep"]}
+    print(json.dumps(res), flush=True)
+
+
+def decode_run(args, name, dev, table_format="int32", partition_tokens=0, with_cpu=False, num_seqs=None):
+    """One decode workload: set-up, ``args.steps`` timed steps (graph replays unless
+    ``--eager``), the passes alone, and flushed partition timings.  Returns the bench
+    record (the JSON line's fields) for that workload."""
+    import torch
     import paged_kv_cache_281_amd as pkv
     import synth
-    pkv.load()
-    pkv.set_decode_partition_tokens(args.partition_tokens)
+    pkv.set_decode_partition_tokens(partition_tokens)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
     ti = {"f32": (np.int32, torch.int32), "f16": (np.int16, torch.int16), "bf16": (np.int16, torch.int16)}
-
-    w = synth.by_name(args.workload, **({"num_seqs": args.num_seqs} if args.num_seqs else {}))
-    if args.workload in synth.LENCLASS_WORKLOADS:
-        lenclass_main(args, w, dev)
-        return
-    if args.workload in synth.PREFIX_WORKLOADS:
-        prefix_main(args, w, dev)
-        return
-    if args.workload in synth.SWAP_WORKLOADS:
-        swap_main(args, w, dev)
-        return
-    if args.workload in synth.PREFILL_WORKLOADS:
-        prefill_main(args, w, dev)
-        return
+    w = synth.by_name(name, **({"num_seqs": num_seqs} if num_seqs else {}))
     log(f"workload {w.name}: N={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
-        f"B={w.block_size} {w.dtype} tokens={int(w.context_lens.sum())}")
+        f"B={w.block_size} {w.dtype} tokens={int(w.context_lens.sum())} partition={partition_tokens or 'plan'}")
     t = time.perf_counter()
     ctx = w.all_context_kv()
     log(f"generated context values in {time.perf_counter() - t:.1f} s")
@@ -776,14 +782,14 @@ def main():
     slots_d = torch.from_numpy(slots).to(dev)
     pairs_d = torch.from_numpy(pairs).to(dev)
     width = w.max_blocks_per_seq
-    if args.tables == "two_level":
+    if table_format == "two_level":
         E = LEAF_TOKENS // w.block_size
         ld, lv = bm.block_tables_2l(w.batch, -(-width // E), 0)
         tables = pkv.TwoLevelTables(torch.from_numpy(ld).to(dev), torch.from_numpy(lv).to(dev))
         table_bytes = int(ld.nbytes + lv.nbytes)
         width = ld.shape[1] * E
     else:
-        tab = bm.block_tables16 if args.tables == "int16" else bm.block_tables
+        tab = bm.block_tables16 if table_format == "int16" else bm.block_tables
         tables = torch.from_numpy(tab(w.batch, width, 0)).to(dev)
         table_bytes = int(tables.numel() * tables.element_size())
     lens_np = np.asarray([bm.seq_len(int(s)) for s in w.batch], dtype=np.int32)
@@ -806,7 +812,7 @@ def main():
         if e is not None:
             e[1].record(stream)
 
-    # timed region (eager): exactly `steps` steps; events bracket the partition kernel in each
+    # timed region (eager): exactly `steps` steps; events bracket the partition pass in each
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for _ in range(args.warmup):
         step()
@@ -879,10 +885,12 @@ def main():
 
     uniq = unique_tokens(bm.block_tables(w.batch, w.max_blocks_per_seq, 0), lens_np, w.block_size)
     pt = partition_tokens_of(w, lens_np)
-    ab = algorithmic_bytes(w, lens_np, args.tables, uniq, pt)
+    ab = algorithmic_bytes(w, lens_np, table_format, uniq, pt)
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
+    hbm_gbs = ab["kv_unique"] / (ms_step * 1e-3) / 1e9
     achieved = ab["total"] / (part_ms * 1e-3) / 1e9
-    traffic = stored_traffic(args.workload) if args.tables == "int32" else None
+    tag = w.name if not partition_tokens else f"{w.name}_p{partition_tokens}"
+    traffic = stored_traffic(tag) if table_format == "int32" else None
     res = {
         "metric": METRIC,
         "value": round(kv_gbs, 2),
@@ -899,9 +907,14 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "context_tokens": int(lens_np.sum()), "max_context": int(lens_np.max()),
-                   "partition_tokens": pt, "copy_pairs": int(len(pairs)),
-                   "kv_bytes": ab["kv"], "tables": args.tables, "table_bytes": table_bytes},
-        "pct_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+                   "partition_tokens": pt, "partition_rule": "fixed" if partition_tokens else "plan",
+                   "copy_pairs": int(len(pairs)), "kv_bytes": ab["kv"], "kv_bytes_unique": ab["kv_unique"],
+                   "tables": table_format, "table_bytes": table_bytes},
+        # % of HBM peak counts each distinct block once (the bytes HBM must deliver); the
+        # logical rate counts a block shared by several sequences once per sequence
+        "pct_hbm_peak": round(100.0 * hbm_gbs / HBM_PEAK_GBS, 2),
+        "hbm_kv_gbs": round(hbm_gbs, 2),
+        "logical_kv_gbs": round(kv_gbs, 2),
         "tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "attention_kv_gbs": round(ab["kv"] / ((plan_ms + part_ms) * 1e-3) / 1e9, 2),
         "kernel_ms": {"attn_partitions": round(part_ms, 5), "copy_blocks_alone": round(copy_ms, 5),
@@ -913,15 +926,115 @@ def main():
         "host_block_manager_step_us": round(host_bm_us, 1),
         "step_launch": "eager" if graph_ms is None else "hip_graph",
         "eager_ms_per_step": round(eager_ms, 5),
-        "roofline": {"kernel": "attn_partition", "bound": "hbm", "achieved": round(achieved, 2),
+        "roofline": {"kernel": "attn_partition" + (" + attn_merge_long" if ab["merge_long"] else ""),
+                     "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": ab},
     }
-    if not args.no_cpu_baseline:
+    pkv.set_decode_partition_tokens(0)
+    if with_cpu:
         del kp, vp
         torch.cuda.empty_cache()
         log("timing the oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(w, w.all_context_kv(), args.cpu_seconds)
+    return res
+
+
+def sub_record(r, partition_tokens=0):
+    """The fields of a decode record carried inside the headline line."""
+    return {"workload": r["config"]["workload"], "partition_tokens": r["config"]["partition_tokens"],
+            "partition_rule": r["config"]["partition_rule"], "ms_per_step": r["ms_per_step"],
+            "value": r["value"], "unit": r["unit"], "pct_hbm_peak": r["pct_hbm_peak"],
+            "tokens_per_s": r["tokens_per_s"], "kernel_ms": r["kernel_ms"],
+            "attn_partitions_ms_spread": r["attn_partitions_ms_spread"],
+            "roofline": {k: r["roofline"][k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "traffic")},
+            "algorithmic_bytes": r["roofline"]["algorithmic_bytes"]["total"],
+            "context_tokens": r["config"]["context_tokens"], "block_size": r["config"]["block_size"]}
+
+
+HEADLINE = "long_bf16_b16"
+# other decode configurations the headline line carries: (key, workload, fixed partition size)
+SUB_RECORDS = [("gqa_bf16", "gqa_bf16", 0), ("long_bf16_b32", "long_bf16_b32", 0),
+               ("long_bf16_b16_p512", "long_bf16_b16", 512)]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None,
+                    help=f"one workload's line; default: {HEADLINE} with the other decode configurations "
+                         f"({', '.join(k for k, _, _ in SUB_RECORDS)}) and the streaming-read ceiling as sub-records")
+    ap.add_argument("--num-seqs", type=int, default=None,
+                    help="override the workload's number of sequences (decode workloads)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-reps", type=int, default=10,
+                    help="extra partition-pass timings, each after a 512 MiB cache flush")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the decode step as stream launches instead of replays of its HIP graph")
+    ap.add_argument("--tables", choices=["int32", "int16", "two_level"], default="int32",
+                    help="block-table format of the decode step (flat int32, flat 16-bit, or two-level)")
+    ap.add_argument("--partition-tokens", type=int, choices=[0, 512, 1024, 2048], default=0,
+                    help="fix the decode partition size (0: the plan pass chooses per batch)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path runs on one GPU, see the design notes for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "reps": 5}))
+        return
+
+    import paged_kv_cache_281_amd as pkv
+    import synth
+    pkv.load()
+    if args.workload == "stream_ceiling":
+        stream_main(args, dev)
+        return
+    name = args.workload or HEADLINE
+    if name in synth.LENCLASS_WORKLOADS:
+        lenclass_main(args, synth.by_name(name), dev)
+        return
+    if name in synth.PREFIX_WORKLOADS:
+        prefix_main(args, synth.by_name(name), dev)
+        return
+    if name in synth.SWAP_WORKLOADS:
+        swap_main(args, synth.by_name(name), dev)
+        return
+    if name in synth.PREFILL_WORKLOADS:
+        prefill_main(args, synth.by_name(name, **({"num_seqs": args.num_seqs} if args.num_seqs else {})), dev)
+        return
+    if args.workload is not None:
+        res = decode_run(args, name, dev, args.tables, args.partition_tokens, not args.no_cpu_baseline,
+                         args.num_seqs)
+        print(json.dumps(res), flush=True)
+        return
+    # the headline line: the largest single-GPU configuration, with the other decode
+    # configurations and the streaming-read ceiling carried as sub-records
+    subs = {}
+    for key, wname, pt in SUB_RECORDS:
+        subs[key] = sub_record(decode_run(args, wname, dev, "int32", pt, False))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    ceiling = stream_ceiling(dev, reps=5)
+    log(f"streaming-read ceiling {ceiling['best_gbs']} GB/s ({ceiling['best']})")
+    res = decode_run(args, HEADLINE, dev, "int32", 0, not args.no_cpu_baseline)
+    res["sub_records"] = subs
+    res["hbm_read_ceiling"] = {k: ceiling[k] for k in ("bytes", "best_gbs", "best", "frac_of_peak", "kernel")}
+    res["roofline"]["frac_of_read_ceiling"] = round(res["roofline"]["achieved"] / ceiling["best_gbs"], 4)
     print(json.dumps(res), flush=True)
 
 

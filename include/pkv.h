@@ -123,7 +123,9 @@ int32_t pkv_swap_blocks(const pkv_pool_desc* pool, const void* src_k, const void
 
 /* Context tokens per split-context partition of the attention pass: the plan pass picks
  * PKV_PARTITION_TOKENS or PKV_PARTITION_TOKENS_MAX for each launch (see
- * pkv_decode_partition_tokens); workspaces are sized for the smaller one. */
+ * pkv_decode_partition_tokens); PKV_PARTITION_TOKENS_MIN is used only when fixed with
+ * pkv_set_decode_partition_tokens.  Workspaces are sized for the smallest. */
+#define PKV_PARTITION_TOKENS_MIN 512
 #define PKV_PARTITION_TOKENS 1024
 #define PKV_PARTITION_TOKENS_MAX 2048
 /* Context tokens whose block ids one leaf of a two-level block table holds. */
@@ -346,9 +348,9 @@ int32_t pkv_decode_partition_tokens(const int32_t* context_lens_host, int32_t nu
                                     int32_t num_kv_heads, int32_t* tokens);
 /*
  * Fixes the decode partition size of every later plan pass in the process:
- * PKV_PARTITION_TOKENS or PKV_PARTITION_TOKENS_MAX, or 0 for the per-call choice above
- * (the default).  For tuning and tests; results are the same either way up to fp32
- * rounding of the merge.  Errors: INVALID_ARG (any other value).
+ * PKV_PARTITION_TOKENS_MIN, PKV_PARTITION_TOKENS or PKV_PARTITION_TOKENS_MAX, or 0 for
+ * the per-call choice above (the default).  For tuning and tests; results are the same
+ * either way up to fp32 rounding of the merge.  Errors: INVALID_ARG (any other value).
  */
 int32_t pkv_set_decode_partition_tokens(int32_t tokens);
 
@@ -450,6 +452,21 @@ int32_t pkv_bm_set_prefix_cache(pkv_bm* bm, int32_t enable);
 int32_t pkv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, int32_t n, int32_t* cached_tokens);
 /* Number of blocks registered in the prefix cache (in use or evictable). */
 int32_t pkv_bm_num_cached(const pkv_bm* bm);
+
+/*
+ * Diagnostics: the device's streaming-read rate, the ceiling the bandwidth-bound
+ * attention kernels are measured against (data.6616ai.com "PagedAttention 之外" and
+ * ohmygp.com "先搞清敌人": decode is limited by memory bandwidth, not compute).  Reads
+ * `bytes` bytes from `src` once, with 16-byte non-temporal loads in a grid-stride loop
+ * over `workgroups` workgroups of 256 threads, `unroll` loads in flight per thread, and
+ * stores one xor of what each wave read into `sink`.
+ *   src   device, 16-byte aligned, `bytes` a positive multiple of 16.
+ *   sink  device uint32 [workgroups * 4].
+ * Errors: INVALID_ARG (null or misaligned pointers, bad sizes, unroll not 1, 2, 4 or 8),
+ * LAUNCH.
+ */
+int32_t pkv_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t unroll, void* sink,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,11 +24,12 @@ __all__ = [
     "paged_kv_write", "copy_blocks", "swap_blocks", "workspace_bytes", "alloc_workspace", "TwoLevelTables",
     "paged_attention_decode", "paged_attention_partitions", "paged_attention_plan", "decode_prepare",
     "prefill_workspace_bytes", "alloc_prefill_workspace", "paged_attention_prefill", "BlockManager", "PkvError",
-    "PARTITION_TOKENS", "PARTITION_TOKENS_MAX", "LEAF_TOKENS", "DTYPE_CODES", "decode_partition_tokens", "TableRef",
-    "set_decode_partition_tokens",
+    "PARTITION_TOKENS_MIN", "PARTITION_TOKENS", "PARTITION_TOKENS_MAX", "LEAF_TOKENS", "DTYPE_CODES", "decode_partition_tokens", "TableRef",
+    "set_decode_partition_tokens", "stream_read",
 ]
 
-PARTITION_TOKENS = 1024  # decode split-context partition (PKV_PARTITION_TOKENS; the workspace unit)
+PARTITION_TOKENS_MIN = 512  # smallest decode partition, only when fixed (PKV_PARTITION_TOKENS_MIN; the workspace unit)
+PARTITION_TOKENS = 1024  # decode split-context partition (PKV_PARTITION_TOKENS)
 PARTITION_TOKENS_MAX = 2048  # the longer partition the plan may choose (PKV_PARTITION_TOKENS_MAX)
 LEAF_TOKENS = 512  # tokens whose block ids one two-level leaf holds (PKV_LEAF_TOKENS)
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
@@ -119,6 +120,7 @@ def _bind(lib):
                                             _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp],
                                            _c_i32),
         "pkv_bm_block_tables_2l": ([_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_i32, P(_c_i32)], _c_i32),
+        "pkv_stream_read": ([_c_vp, _c_sz, _c_i32, _c_i32, _c_vp, _c_vp], _c_i32),
         "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
         "pkv_bm_set_prefix_cache": ([_c_vp, _c_i32], _c_i32),
         "pkv_bm_add_seq_tokens": ([_c_vp, _c_i32, _c_vp, _c_i32, P(_c_i32)], _c_i32),
@@ -379,7 +381,7 @@ def decode_partition_tokens(context_lens, num_q_heads: int, num_kv_heads: int) -
 
 
 def set_decode_partition_tokens(tokens: int) -> None:
-    """Fix the decode partition size of later calls (1024 or 2048), or 0 for the plan's choice."""
+    """Fix the decode partition size of later calls (512, 1024 or 2048), or 0 for the plan's choice."""
     _check(load().pkv_set_decode_partition_tokens(int(tokens)))
 
 
@@ -407,6 +409,15 @@ def paged_attention_partitions(q, k_pool, v_pool, block_tables, context_lens, sc
     fn = getattr(load(), "pkv_paged_attention_partitions" + suffix)
     _check(fn(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq, *targs, _ptr(context_lens),
               float(scale), _ptr(ws), ws.numel(), _stream(q.device)))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int, unroll: int = 8) -> None:
+    """Diagnostic: read every byte of the contiguous device tensor ``src`` once
+    (``pkv_stream_read``); ``sink`` is an int32 device tensor of ``4 * workgroups`` entries."""
+    _require(src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32
+             and sink.numel() >= 4 * workgroups, "src must be a contiguous device tensor, sink int32 [4 * workgroups]")
+    _check(load().pkv_stream_read(_ptr(src), src.numel() * src.element_size(), int(workgroups), int(unroll),
+                                  _ptr(sink), _stream(src.device)))
 
 
 # ---- host block manager ----------------------------------------------------------------

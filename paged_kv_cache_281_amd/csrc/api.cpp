@@ -478,9 +478,19 @@ int32_t pkv_decode_partition_tokens(const int32_t* context_lens_host, int32_t nu
 
 int32_t pkv_set_decode_partition_tokens(int32_t tokens) {
   if (tokens == 0) return pkv::set_forced_partition_log2(0);
+  if (tokens == PKV_PARTITION_TOKENS_MIN) return pkv::set_forced_partition_log2(pkv::kLgPartFloor);
   if (tokens == PKV_PARTITION_TOKENS) return pkv::set_forced_partition_log2(pkv::kLgPartMin);
   if (tokens == PKV_PARTITION_TOKENS_MAX) return pkv::set_forced_partition_log2(pkv::kLgPartMax);
-  return pkv::set_error(PKV_ERR_INVALID_ARG, "pkv_set_decode_partition_tokens: 0, 1024 or 2048 expected");
+  return pkv::set_error(PKV_ERR_INVALID_ARG, "pkv_set_decode_partition_tokens: 0, 512, 1024 or 2048 expected");
+}
+
+int32_t pkv_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t unroll, void* sink,
+                        void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !pkv::aligned(src, 16) || !pkv::aligned(sink, 4) ||
+      workgroups <= 0 || workgroups > (1 << 24) || (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8))
+    return set_error(PKV_ERR_INVALID_ARG, "pkv_stream_read: src and sink non-null and aligned, bytes a positive "
+                                          "multiple of 16, workgroups in 1 .. 2^24, unroll 1, 2, 4 or 8 required");
+  return pkv::launch_status(pkv::launch_stream_read(src, bytes, workgroups, unroll, sink, stream), "pkv_stream_read");
 }
 
 size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,

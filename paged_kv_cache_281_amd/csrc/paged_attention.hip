@@ -238,6 +238,9 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
   // (uniform trip count: every lane takes part in the shuffles)
   unsigned long long tokens = 0;
   int lmax = 0;
+  // the two candidate sizes (both the caller's size when it fixed one)
+  const int lg_lo = P.force_log2 ? P.force_log2 : kLgPartMin;
+  const int lg_hi = P.force_log2 ? P.force_log2 : kLgPartMax;
   const PlanSeq s_first = plan_seq(P, tid);  // kept for pass 2 (the whole batch when N <= blockDim)
   for (int b0 = 0; b0 < N; b0 += blockDim.x) {
     const PlanSeq s = b0 == 0 ? s_first : plan_seq(P, b0 + tid);
@@ -246,7 +249,7 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       int full, cls;
-      tail_class(s.L, kLgPartMin + c, full, cls);
+      tail_class(s.L, c ? lg_hi : lg_lo, full, cls);
       int n = cls > 0;
       group_scan(s.head, cls, n);
       if (full) atomicAdd(&cnt[c][NB], full);
@@ -264,7 +267,7 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
   }
   __syncthreads();
   const int lg = choose_partition_log2(s_tokens, s_lmax, P.Hkv * P.NHG, P.slots, P.force_log2);
-  const int* ccnt = cnt[lg - kLgPartMin];
+  const int* ccnt = cnt[lg == lg_lo ? 0 : 1];
   // exclusive offsets of the classes, longest first (class NB, then NB - 1, ...): one
   // wave scans them with lane shuffles, lane i holding class NB - i
   static_assert(NB <= 64, "one wave scans the classes");
@@ -580,10 +583,20 @@ __device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, 
 // Every thread waits until its device-scope partial stores have completed before the
 // workgroup's count is added, so the merging workgroup, whose device-scope loads are
 // issued after it has read the final count, sees every partition's partials.
+//
+// This ordering is the hardware's, not the language memory model's: the partials are
+// relaxed agent-scope atomic stores (on gfx950 they write through the XCD's L2 to the
+// coherent level, sc1), `s_waitcnt 0` holds the thread until they have completed, and
+// the counter add and the merging loads are relaxed too.  A release add paired with an
+// acquire load would be the portable form, but an agent-scope release writes back the
+// whole L2 of the XCD: a __threadfence() version of this protocol was measured 5.5x
+// slower.  The signal fences keep the compiler from moving the stores past the wait.
 template <class T, int D>
 __device__ __forceinline__ void finish_rows(const Params& P, int b, int hq0, int nrows, int np,
                                            MergeSmem<D>& sm, int& s_last) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // all of this thread's memory operations have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (threadIdx.x == 0) s_last = atomicAdd(&P.done[static_cast<int64_t>(b) * P.Hq + hq0], 1) == np - 1;
   __syncthreads();
@@ -638,7 +651,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
     return;
   }
-  const int lg = min(max(P.counters[1], kLgPartMin), kLgPartMax);  // this launch's partition size
+  const int lg = min(max(P.counters[1], kLgPartFloor), kLgPartMax);  // this launch's partition size
   const int np = (L + (1 << lg) - 1) >> lg;
   if (p >= np) return;
 
@@ -842,7 +855,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
     return;
   }
-  const int lg = min(max(P.counters[1], kLgPartMin), kLgPartMax);  // this launch's partition size
+  const int lg = min(max(P.counters[1], kLgPartFloor), kLgPartMax);  // this launch's partition size
   const int np = (L + (1 << lg) - 1) >> lg;
   if (p >= np) return;
 
@@ -1065,7 +1078,7 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
     if (p == 0) zero_rows<T, D>(P, b, hq0, G);
     return;
   }
-  const int lg = min(max(P.counters[1], kLgPartMin), kLgPartMax);  // this launch's partition size
+  const int lg = min(max(P.counters[1], kLgPartFloor), kLgPartMax);  // this launch's partition size
   const int np = (L + (1 << lg) - 1) >> lg;
   if (p >= np) return;
 
@@ -1244,7 +1257,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge_long(Params P) {
   __shared__ MergeSmem<D> s_merge;
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int lg = min(max(P.counters[1], kLgPartMin), kLgPartMax);
+  const int lg = min(max(P.counters[1], kLgPartFloor), kLgPartMax);
   const int np = (context_len(P, b) + (1 << lg) - 1) >> lg;
   if (np <= kFuseMaxParts) return;
   merge_row<T, D, false>(P, static_cast<int64_t>(b) * P.Hq + hq, np, s_merge);

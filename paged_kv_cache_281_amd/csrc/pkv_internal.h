@@ -23,9 +23,10 @@ inline int elem_bytes(int32_t dtype) {
   }
 }
 
-// Partitions of PKV_PARTITION_TOKENS tokens needed for max_blocks_per_seq blocks.
+// Partial-result slots per sequence: partitions of PKV_PARTITION_TOKENS_MIN tokens (the
+// smallest size a launch can use) for max_blocks_per_seq blocks.
 inline int64_t max_partitions(int64_t max_blocks_per_seq, int64_t block_size) {
-  return (max_blocks_per_seq * block_size + PKV_PARTITION_TOKENS - 1) / PKV_PARTITION_TOKENS;
+  return (max_blocks_per_seq * block_size + PKV_PARTITION_TOKENS_MIN - 1) / PKV_PARTITION_TOKENS_MIN;
 }
 
 // Kernel launchers (defined in the .hip files).  They assume validated arguments
@@ -37,6 +38,9 @@ int launch_copy_blocks(const pkv_pool_desc& pool, void* k_pool, void* v_pool, co
 // Whole-block copy from one pool pair to another of the same tile layout.
 int launch_pool_copy(const pkv_pool_desc& pool, const void* src_k, const void* src_v, void* dst_k, void* dst_v,
                      const int64_t* pairs, int32_t num_pairs, void* stream);
+
+// Streaming-read probe (stream_read.hip).
+int launch_stream_read(const void* src, size_t bytes, int32_t workgroups, int32_t unroll, void* sink, void* stream);
 
 struct AttnArgs {
   const void* k_pool;
@@ -59,10 +63,13 @@ struct AttnArgs {
   int32_t force_log2 = 0;  // 0, or the log2 of a partition size fixed by the caller
 };
 
-// Decode partition sizes (log2 of tokens) the plan pass chooses between.
-constexpr int kLgPartMin = 10;  // PKV_PARTITION_TOKENS: the workspace is sized for it
-constexpr int kLgPartMax = 11;  // PKV_PARTITION_TOKENS_MAX
-static_assert((1 << kLgPartMin) == PKV_PARTITION_TOKENS && (1 << kLgPartMax) == PKV_PARTITION_TOKENS_MAX,
+// Decode partition sizes (log2 of tokens): the plan pass chooses between kLgPartMin and
+// kLgPartMax; kLgPartFloor is only used when fixed by the caller, and sizes the workspace.
+constexpr int kLgPartFloor = 9;  // PKV_PARTITION_TOKENS_MIN
+constexpr int kLgPartMin = 10;   // PKV_PARTITION_TOKENS
+constexpr int kLgPartMax = 11;   // PKV_PARTITION_TOKENS_MAX
+static_assert((1 << kLgPartFloor) == PKV_PARTITION_TOKENS_MIN && (1 << kLgPartMin) == PKV_PARTITION_TOKENS &&
+                  (1 << kLgPartMax) == PKV_PARTITION_TOKENS_MAX,
               "partition sizes");
 constexpr int kSlotsPerCU = 3;  // partition workgroups resident per compute unit
 

@@ -36,7 +36,7 @@ def test_workspace_and_pool_sizes(pkv_lib):
     # pairs, the (sequence, partition) task list, per-row counters and a counter block,
     # each 256-byte aligned
     n = lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 8192, 16)
-    parts = 8192 * 16 // 1024
+    parts = 8192 * 16 // 512
     al = lambda x: (x + 255) // 256 * 256
     assert n == al(8 * 32 * parts * 128 * 4) + al(8 * 32 * parts * 2 * 4) + al(8 * parts * 8) + al(8 * 32 * 4) + 256
     assert lib.pkv_paged_attention_workspace_bytes(-1, 32, 128, 8, 16) == 0
@@ -246,7 +246,9 @@ def test_decode_partition_size_rule(pkv_lib):
         pkv_lib.set_decode_partition_tokens(1024)
         assert pt(synth.gqa_bf16().context_lens, 32, 8) == 1024
         assert lib.pkv_set_decode_partition_tokens(1000) == 1
-        assert lib.pkv_set_decode_partition_tokens(512) == 1
+        assert lib.pkv_set_decode_partition_tokens(256) == 1
+        pkv_lib.set_decode_partition_tokens(512)
+        assert pt(synth.gqa_bf16().context_lens, 32, 8) == 512
     finally:
         pkv_lib.set_decode_partition_tokens(0)
     assert pt([100], 32, 8) == 1024

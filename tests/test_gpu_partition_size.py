@@ -1,7 +1,7 @@
-"""Decode partition size (1024 or 2048 tokens, chosen per launch by the plan pass) and
-the plan's task list.
+"""Decode partition size (1024 or 2048 tokens, chosen per launch by the plan pass, or 512
+when fixed by the caller) and the plan's task list.
 
-- Parity against the oracle with the size fixed at 1024 and at 2048 (both launch
+- Parity against the oracle with the size fixed at 512, 1024 and 2048 (both launch
   paths: decode_prepare + partitions, and the one-call decode), on shapes that reach
   every partition kernel, rows of several partitions with a ragged tail, and a row
   that needs the separate merge kernel at 1024 but not at 2048.
@@ -52,7 +52,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("tokens", [1024, 2048])
+@pytest.mark.parametrize("tokens", [512, 1024, 2048])
 @pytest.mark.parametrize("name,make", CASES, ids=[c[0] for c in CASES])
 def test_parity_at_each_partition_size(name, make, tokens, partition_tokens):
     partition_tokens(tokens)
@@ -95,7 +95,7 @@ def _plan(lens, hq, hkv, tables, d=128, block=16):
     pkv.paged_attention_plan(q, kp, vp, tables, lens_d, ws)
     torch.cuda.synchronize()
     cnt = _counters(ws)
-    parts = -(-W * block // pkv.PARTITION_TOKENS)
+    parts = -(-W * block // pkv.PARTITION_TOKENS_MIN)
     return cnt, _tasks(ws, n, hq, d, parts, int(cnt[0])), parts
 
 
@@ -178,7 +178,7 @@ def _check_order(tasks, parts, lens, first, pt):
     return groups
 
 
-@pytest.mark.parametrize("tokens", [1024, 2048])
+@pytest.mark.parametrize("tokens", [512, 1024, 2048])
 def test_task_list_order_and_shared_prefix_groups(tokens, partition_tokens):
     partition_tokens(tokens)
     w = synth.cow_fp16(1020, num_prompts=8, max_suffix=256)
@@ -225,7 +225,7 @@ def _plan_prepare(lens, hq, hkv, tables, d=128, block=16):
     pkv.decode_prepare(kp, vp, kv_new, kv_new, slots, q, tables, lens_d, ws)
     torch.cuda.synchronize()
     cnt = _counters(ws)
-    parts = -(-W * block // pkv.PARTITION_TOKENS)
+    parts = -(-W * block // pkv.PARTITION_TOKENS_MIN)
     return cnt, _tasks(ws, n, hq, d, parts, int(cnt[0])), parts
 
 
