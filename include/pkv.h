@@ -174,6 +174,27 @@ int32_t pkv_paged_attention_decode(const pkv_pool_desc* pool, const void* k_pool
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid allocation).  Same arguments (minus the workspace), kernels and
+ * results as pkv_paged_attention_decode; its workspace is a fixed device array of
+ * PKV_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held from the first
+ * call on that GPU until the process ends.  Nothing in it needs clearing between calls
+ * (the plan pass rewrites what the attention pass reads).  Every call on a GPU uses that
+ * GPU's one array, so calls that overlap in time on one GPU (on different streams, or
+ * from different threads) race and give undefined results; calls ordered on one stream
+ * are safe.  Sizes whose workspace (pkv_paged_attention_workspace_bytes) exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES are rejected with WORKSPACE before anything is enqueued.
+ * Errors: those of pkv_paged_attention_decode; LAUNCH also when the array's device
+ * address cannot be looked up.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (128u << 20)
+int32_t pkv_paged_attention_decode_noalloc(const pkv_pool_desc* pool, const void* k_pool, const void* v_pool,
+                                           void* out, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, float scale, void* stream);
+
+/*
  * Causal attention of chunks of new tokens over the paged pool (prefill and chunked
  * prefill).  Pages: agentalpha.top Q32 follow-up 3 (FlashAttention loads K/V block by
  * block; over paged storage that loading goes through the block table);

@@ -25,7 +25,7 @@ __all__ = [
     "paged_attention_decode", "paged_attention_partitions", "paged_attention_plan", "decode_prepare",
     "prefill_workspace_bytes", "alloc_prefill_workspace", "paged_attention_prefill", "BlockManager", "PkvError",
     "PARTITION_TOKENS_MIN", "PARTITION_TOKENS", "PARTITION_TOKENS_MAX", "LEAF_TOKENS", "DTYPE_CODES", "decode_partition_tokens", "TableRef",
-    "set_decode_partition_tokens", "stream_read",
+    "set_decode_partition_tokens", "stream_read", "paged_attention_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 PARTITION_TOKENS_MIN = 512  # smallest decode partition, only when fixed (PKV_PARTITION_TOKENS_MIN; the workspace unit)
@@ -121,6 +121,8 @@ def _bind(lib):
                                            _c_i32),
         "pkv_bm_block_tables_2l": ([_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_i32, P(_c_i32)], _c_i32),
         "pkv_stream_read": ([_c_vp, _c_sz, _c_i32, _c_i32, _c_vp, _c_vp], _c_i32),
+        "pkv_paged_attention_decode_noalloc": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
+                                                _c_i32, _c_vp, _c_f, _c_vp], _c_i32),
         "pkv_bm_create": ([_c_i32, _c_i32, _c_vp, P(_c_vp)], _c_i32),
         "pkv_bm_set_prefix_cache": ([_c_vp, _c_i32], _c_i32),
         "pkv_bm_add_seq_tokens": ([_c_vp, _c_i32, _c_vp, _c_i32, P(_c_i32)], _c_i32),
@@ -307,6 +309,32 @@ def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
     fn = getattr(load(), "pkv_paged_attention_decode" + suffix)
     _check(fn(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q), N, Hq, *targs, _ptr(context_lens),
               float(scale), _ptr(ws), ws.numel(), _stream(q.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attention_decode_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                                   out: torch.Tensor) -> torch.Tensor:
+    """``paged_attention_decode`` without a workspace and without allocating: the library's
+    fixed per-GPU scratch array holds the partials (``pkv_paged_attention_decode_noalloc``).
+    ``out`` is caller-provided; int32 flat tables only.  Calls that overlap on one GPU race."""
+    d = pool_desc(k_pool, v_pool)
+    _require(q.dim() == 3 and q.shape[2] == d.head_dim and q.dtype == k_pool.dtype and q.is_contiguous()
+             and q.device == k_pool.device, "q must be a contiguous [N, Hq, D] device tensor of the pool dtype")
+    N, Hq, _ = q.shape
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == N
+             and block_tables.is_contiguous() and block_tables.device == q.device,
+             "block_tables must be a contiguous int32 [N, W] device tensor")
+    _require(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (N,) and context_lens.is_contiguous()
+             and context_lens.device == q.device, "context_lens must be a contiguous int32 [N] device tensor")
+    _require(out is not None and out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
+             and out.device == q.device, "out must match q")
+    _check(load().pkv_paged_attention_decode_noalloc(ctypes.byref(d), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(q),
+                                                     N, Hq, _ptr(block_tables), block_tables.shape[1],
+                                                     _ptr(context_lens), float(scale), _stream(q.device)))
     return out
 
 

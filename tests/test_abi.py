@@ -92,6 +92,23 @@ def test_host_side_argument_errors(pkv_lib):
     assert st == 1 and b"misaligned" in lib.pkv_last_error()
 
 
+def test_noalloc_and_stream_read_host_side_errors(pkv_lib):
+    """Sizes beyond the static scratch are rejected before any device call; the
+    streaming-read probe checks its arguments."""
+    lib = pkv_lib.load()
+    d = pkv_lib.PoolDesc(64, 16, 8, 128, 2)
+    fake = ctypes.c_void_p(0x1000)
+    need = lib.pkv_paged_attention_workspace_bytes(4096, 32, 128, 512, 16)
+    assert need > pkv_lib.NOALLOC_SCRATCH_BYTES
+    st = lib.pkv_paged_attention_decode_noalloc(ctypes.byref(d), fake, fake, fake, fake, 4096, 32, fake, 512, fake,
+                                                0.1, None)
+    assert st == 3 and b"static scratch" in lib.pkv_last_error()
+    assert lib.pkv_stream_read(fake, 100, 4, 8, fake, None) == 1     # not a multiple of 16
+    assert lib.pkv_stream_read(fake, 4096, 4, 3, fake, None) == 1    # unroll
+    assert lib.pkv_stream_read(fake, 4096, 0, 8, fake, None) == 1    # workgroups
+    assert lib.pkv_stream_read(None, 4096, 4, 8, fake, None) == 1
+
+
 def test_two_level_host_side_errors(pkv_lib):
     lib = pkv_lib.load()
     P = pkv_lib.PoolDesc
