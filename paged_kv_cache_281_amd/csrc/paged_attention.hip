@@ -66,144 +66,149 @@ struct Params {
   const void* tables;   // int32 or uint16 entries, or two-level leaves (the kernels' Tab parameter)
   const int* dir;       // two-level tables: the leaf directory
   const int* ctx;
-  const int2* tasks;    // {sequence * Pmax + partition, context length} items, longest first
-  const int* counters;  // counters[0] = number of items, counters[1] = log2 of the partition size
+  int4* tasks;          // work items, longest first (written by the plan pass)
+  int* counters;        // counters[0] = number of items, counters[1] = log2 of the partition size
   int* done;            // [N * Hq]: partitions finished per (sequence, first head of a group)
-  int N, Hq, Hkv, G, NHG, W, Pmax, Lmax;
+  int* seq_np;          // [N]: partial results of each sequence's rows
+  int4* seq_grp;        // [N]: shared-prefix group of each sequence (plan pass)
+  int* members;         // [N]: the sequences of each shared-prefix group, group by group
+  int N, Hq, Hkv, G, NHG, W, Pmax, Lmax, B;
   float scale_log2;
   int tab_bytes;   // 4 or 2 (flat tables)
   int leaf_e;      // entries per two-level leaf
   int slots;       // resident partition workgroups (plan's size choice)
   int force_log2;  // 0, or the partition size fixed by the caller (log2)
+  int cm;          // sequences per shared-prefix item (16 / G); below 2: no shared-prefix items
 };
 
-// Task items (sequence * Pmax + partition, below 2^23 by the host's size checks) carry
-// this bit when their sequence belongs to a group of sequences that share their first
-// block: the partition kernels then read its K/V with cached loads.
+// Work items (int4): x = the sequence (an ordinary item) or the offset of the item's
+// sequences in the members list (a shared-prefix item), with the flags below; y = the
+// first context token; z = the number of tokens (0: the zero output of an empty
+// context); w = the partial-result slot of the item | (the partial count of the
+// sequence's rows for an ordinary item, or the number of sequences of a shared-prefix
+// item) << 16.
+constexpr int kPrefixTask = 1 << 29;
+// A shared-prefix item whose group needs several items (more sequences than one item's
+// columns): its K/V loads are cached, so the group's other items, listed next to it,
+// find the shared blocks in L2.
 constexpr int kSharedTask = 1 << 30;
+constexpr int kTaskIndex = kPrefixTask - 1;
 
 // Context length of sequence b, clamped to what its table can address (longer
 // values break the caller's contract; clamping keeps every access in bounds).
 __device__ __forceinline__ int context_len(const Params& P, int b) { return min(max(P.ctx[b], 0), P.Lmax); }
 
+// An item as the partition kernels use it.  `ok` is false for anything a plan pass
+// cannot have written (a workspace without a preceding plan pass): such items do
+// nothing, so every access stays inside the buffers.
+struct Item {
+  bool ok, prefix, shared;
+  int idx;   // sequence, or offset in the members list
+  int tok0, ntok, p;
+  int nm;    // sequences whose rows the item computes
+  int np;    // partial count of an ordinary item's rows
+};
+__device__ __forceinline__ Item decode_item(const Params& P, const int4 t, int unit, int cols_per_seq) {
+  Item it;
+  it.prefix = (t.x & kPrefixTask) != 0;
+  it.shared = (t.x & kSharedTask) != 0;
+  it.idx = t.x & kTaskIndex;
+  it.tok0 = t.y;
+  it.ntok = t.z;
+  it.p = t.w & 0xffff;
+  const int hi = (t.w >> 16) & 0x7fff;
+  it.nm = it.prefix ? hi : 1;
+  it.np = it.prefix ? 0 : hi;
+  it.ok = t.x >= 0 && it.tok0 >= 0 && it.ntok >= 0 && it.tok0 + it.ntok <= P.Lmax && it.tok0 % unit == 0 &&
+          it.p < P.Pmax && it.nm >= 1 && it.idx + it.nm <= P.N &&
+          (it.prefix ? (it.nm * cols_per_seq <= 16 && it.ntok > 0) : (it.np >= 1 && it.np <= P.Pmax));
+  return it;
+}
+
 // ---------------------------------------------------------------------------------
-// Plan kernel (one workgroup).  It picks this launch's partition size, then lists every
-// (sequence, partition) item, longest first so that the short tail partitions of a
-// skewed batch run last.
+// Plan kernel (one workgroup).  It finds sequences that share their leading blocks,
+// picks this launch's partition size, and lists every work item, longest first so
+// that the short tail items of a skewed batch run last.
+//
+// Shared prefixes.  Sequences whose first physical block is the same (forked samples,
+// beams, requests on one cached prompt) form a group, inside aligned windows of
+// kGroupWin sequences.  The group's shared prefix is the run of leading table entries
+// that is equal in every member's row, cut to blocks that every member fills (found by
+// comparing the rows entry by entry, so any table contents give the right result).
+// When it holds at least kMinSharedTokens tokens, its attention is computed once for
+// the group: a shared-prefix item puts the query heads of up to 16 / G members side by
+// side as the columns of the MFMA products, so each prefix block is read once per item
+// instead of once per member.  Each member's own tokens (after the prefix) are
+// ordinary items.  A member's partials are those of the prefix partitions followed by
+// those of its own partitions.  Only the MFMA kernels (16-bit pools, G <= 8) take
+// shared-prefix items.
 //
 // Size: 2048 tokens unless the batch is too small to hide its longest 2048-token item
 // (choose_partition_log2): fewer, longer partitions save each workgroup's fixed start
 // and end, but a batch that cannot fill the chip ends when its longest item does.
 //
 // Order: items are bucketed into 64 classes by their number of tokens (classes of
-// PT/64 tokens; full partitions first, an empty sequence gets one item in class 1,
-// which writes its zero output).  A sequence whose first physical block is the
-// previous sequence's (a forked or cached prefix: parallel samples, beams, a shared
-// prompt) joins that sequence's group, within aligned runs of 16 sequences; the tail
-// items of a group are listed next to each other under the group's largest class, so
-// the workgroups that read the shared blocks run together and find them in L2.  The
-// items of a group of two or more sequences carry kSharedTask, for which the partition
-// kernels read K/V with cached rather than streaming loads.  Only the order within a
-// class depends on timing, and no result depends on the order or the load flavour.
+// PT/64 tokens; full partitions first; an empty sequence gets one item in class 1,
+// which writes its zero output).  Only the order within a class and which members an
+// item of a large group takes depend on timing; no result depends on either (each
+// column of a product, each row's partials and their merge order are fixed).
 // ---------------------------------------------------------------------------------
-// Sequences with more full partitions than this have their task entries written by
-// the whole workgroup instead of one thread.
+// Sequences with more full partitions than this have their items written by the whole
+// workgroup instead of one thread.
 constexpr int kPlanSerialMax = 32;
 constexpr int kPlanCoopMax = 256;
 constexpr int kPlanClasses = 64;
-constexpr int kGroupRun = 16;  // a group never crosses an aligned run of this many sequences
+constexpr int kGroupWin = 512;     // sequences are grouped within aligned windows of this many
+constexpr int kGroupHash = 1024;   // hash slots for a window's first blocks (at most half used)
+constexpr int kGroupWinWords = (65536 / kGroupWin + 31) / 32;  // one bit per window: it has groups
+constexpr int kMinSharedTokens = 256;  // shortest prefix given shared-prefix items
+static_assert((kGroupHash & (kGroupHash - 1)) == 0 && kGroupHash >= 2 * kGroupWin, "hash size");
 
-// Entry 0 of sequence b's flat table row (in the caller's array whatever the context
-// length; only compared, never followed).
-__device__ __forceinline__ int first_entry_flat(const Params& P, int b) {
-  if (P.tab_bytes == 2) return static_cast<const uint16_t*>(P.tables)[static_cast<int64_t>(b) * P.W];
-  return static_cast<const int*>(P.tables)[static_cast<int64_t>(b) * P.W];
-}
-
-// Shifts within rows of 16 lanes (DPP row_shr / row_shl): lane l gets lane l - D (up) or
-// l + D (down) of its row, or its own value where that lane is outside the row.
-template <int D>
-__device__ __forceinline__ int row_up(int v) {
-  static_assert(D >= 1 && D <= 15, "row shift");
-  return __builtin_amdgcn_update_dpp(v, v, 0x110 + D, 0xf, 0xf, false);
-}
-template <int D>
-__device__ __forceinline__ int row_down(int v) {
-  static_assert(D >= 1 && D <= 15, "row shift");
-  return __builtin_amdgcn_update_dpp(v, v, 0x100 + D, 0xf, 0xf, false);
-}
-
-// Sequence b as the plan sees it.  Every lane of the workgroup calls this with
-// consecutive b (b = base + threadIdx.x, base a multiple of the workgroup size), so the
-// 16 lanes of each aligned run hold 16 consecutive sequences.
-struct PlanSeq {
-  int L;          // context length; -1 past the batch
-  bool head;      // first sequence of its group
-  bool last;      // last sequence of its group
-  int last_lane;  // lane of its group's last sequence
-};
-
-__device__ __forceinline__ PlanSeq plan_seq(const Params& P, int b) {
-  const int lane = threadIdx.x & 63;
-  PlanSeq s;
-  // The flat-table entry (or the two-level directory entry) and the length are loaded
-  // together; a two-level leaf is followed only for a non-empty context, whose first
-  // directory entry names a real leaf.
-  const bool tab = b < P.N && P.tables;
-  const int e0 = !tab ? -1 : P.dir ? P.dir[static_cast<int64_t>(b) * (P.W / P.leaf_e)] : first_entry_flat(P, b);
-  s.L = b < P.N ? context_len(P, b) : -1;
-  int fb = -1;
-  if (tab && s.L > 0) fb = P.dir ? static_cast<const int*>(P.tables)[static_cast<int64_t>(e0) * P.leaf_e] : e0;
-  static_assert(kGroupRun == 16, "groups are found within DPP rows of 16 lanes");
-  const int prev_L = row_up<1>(s.L);
-  const int prev_fb = row_up<1>(fb);
-  const bool follows = (lane & (kGroupRun - 1)) != 0 && fb >= 0 && prev_L > 0 && prev_fb == fb;
-  s.head = !follows;
-  const bool next_follows = row_down<1>(static_cast<int>(follows)) != 0;
-  s.last = (lane & (kGroupRun - 1)) == kGroupRun - 1 || !next_follows;
-  // the first group end at or after this lane (lane 15 of a run always ends one)
-  int v = s.last ? lane : 64;
-  v = min(v, row_down<1>(v));
-  v = min(v, row_down<2>(v));
-  v = min(v, row_down<4>(v));
-  v = min(v, row_down<8>(v));
-  s.last_lane = v;
-  return s;
-}
-
-// A sequence's items at partition size 2^lg: `full` whole partitions and, in `cls`
-// (1..64; 0 = none), its tail item.
-__device__ __forceinline__ void tail_class(int L, int lg, int& full, int& cls) {
-  if (L < 0) {
-    full = 0;
-    cls = 0;
-    return;
+// Entry j of sequence b's table, any format (only read below the sequence's length).
+__device__ __forceinline__ int table_entry(const Params& P, int b, int j) {
+  if (P.dir) {
+    const int leaf = P.dir[static_cast<int64_t>(b) * (P.W / P.leaf_e) + j / P.leaf_e];
+    return static_cast<const int*>(P.tables)[static_cast<int64_t>(leaf) * P.leaf_e + j % P.leaf_e];
   }
-  full = L >> lg;
-  const int rem = L - (full << lg);
-  const int sh = lg - 6;  // classes of 2^lg / 64 tokens
-  cls = rem ? (rem + (1 << sh) - 1) >> sh : (L == 0 ? 1 : 0);
+  if (P.tab_bytes == 2) return static_cast<const uint16_t*>(P.tables)[static_cast<int64_t>(b) * P.W + j];
+  return static_cast<const int*>(P.tables)[static_cast<int64_t>(b) * P.W + j];
 }
 
-// Inclusive scan over the lane's group, from its head up to the lane: the largest class
-// and the number of tail items.
-template <int D>
-__device__ __forceinline__ void group_scan_step(int& h, int& cls, int& cnt) {
-  const int c2 = row_up<D>(cls);
-  const int n2 = row_up<D>(cnt);
-  const int h2 = row_up<D>(h);
-  if (!h) {
-    cls = max(cls, c2);
-    cnt += n2;
+// Entries compared by one thread at a time when a group's rows are compared.
+constexpr int kCmpChunk = 16;
+
+// The first j in [j0, min(j0 + kCmpChunk, cap)) at which the table rows of sequences a
+// and b differ, or cap if none (every load issued before the first compare).
+__device__ __forceinline__ int chunk_mismatch(const Params& P, int a, int b, int j0, int cap) {
+  int ea[kCmpChunk], eb[kCmpChunk];
+#pragma unroll
+  for (int k = 0; k < kCmpChunk; ++k) {
+    const int j = min(j0 + k, cap - 1);
+    ea[k] = table_entry(P, a, j);
+    eb[k] = table_entry(P, b, j);
   }
-  h |= h2;
+  int first = cap;
+#pragma unroll
+  for (int k = kCmpChunk - 1; k >= 0; --k) first = (j0 + k < cap && ea[k] != eb[k]) ? j0 + k : first;
+  return first;
 }
-__device__ __forceinline__ void group_scan(bool head, int& cls, int& cnt) {
-  int h = head;
-  group_scan_step<1>(h, cls, cnt);
-  group_scan_step<2>(h, cls, cnt);
-  group_scan_step<4>(h, cls, cnt);
-  group_scan_step<8>(h, cls, cnt);
+
+// The hash slot of first block `key` (inserted if new), or -1 if the table is full.
+__device__ __forceinline__ int hash_slot(int* hkey, int key) {
+  int slot = static_cast<int>((static_cast<unsigned>(key) * 2654435761u) >> 22) & (kGroupHash - 1);
+  for (int probe = 0; probe < kGroupHash; ++probe) {
+    const int prev = atomicCAS(&hkey[slot], -1, key);
+    if (prev == -1 || prev == key) return slot;
+    slot = (slot + 1) & (kGroupHash - 1);
+  }
+  return -1;
+}
+
+// Class of an item of `n` tokens at partition size 2^lg: 1..64 (64: more than 63/64 of
+// a partition, with the full partitions).
+__device__ __forceinline__ int item_class(int n, int lg) {
+  const int sh = lg - 6;
+  return n > 0 ? (n + (1 << sh) - 1) >> sh : 1;
 }
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
@@ -212,48 +217,203 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
 
-__device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ tasks, int* __restrict__ counters) {
+// The items of a shared-prefix group's partition-sized pieces: item k of a run covers
+// prefix partition p0 + k / ncs for the group's column set k % ncs.
+__device__ __forceinline__ int4 prefix_task(const Params& P, int4 g, int ncs, int k, int p0, int lg, int ntok) {
+  const int p = p0 + k / ncs;
+  const int cs = k - (k / ncs) * ncs;
+  const int nm = min(P.cm, g.z - cs * P.cm);
+  const int flag = kPrefixTask | (ncs > 1 ? kSharedTask : 0);
+  return make_int4((g.w + cs * P.cm) | flag, p << lg, ntok, p | (nm << 16));
+}
+
+__device__ __forceinline__ void plan_body(const Params& P) {
   const int N = P.N;
   constexpr int NB = kPlanClasses;
   __shared__ int cnt[2][NB + 1];
   __shared__ int off[NB + 1];
-  __shared__ int n_coop, s_lmax;
+  __shared__ int n_coop, s_lmax, s_nmem, s_any, n_scan;
   __shared__ unsigned long long s_tokens;
-  __shared__ int coop_b[kPlanCoopMax], coop_s[kPlanCoopMax], coop_n[kPlanCoopMax], coop_l[kPlanCoopMax];
-  __shared__ int coop_f[kPlanCoopMax];
+  // items written cooperatively: (first slot, count, sequence or group, kind) and the
+  // group state of a shared-prefix run
+  __shared__ int coop_s[kPlanCoopMax], coop_n[kPlanCoopMax], coop_b[kPlanCoopMax], coop_k[kPlanCoopMax];
+  __shared__ int4 coop_g[kPlanCoopMax];
+  __shared__ int hkey[kGroupHash], hlead[kGroupHash], hcnt[kGroupHash], hS[kGroupHash], hrank[kGroupHash],
+      hbase[kGroupHash];
+  __shared__ int wslot[kGroupWin], wrank[kGroupWin], wscan[kGroupWin], wcap[kGroupWin], wmis[kGroupWin],
+      wpre[kGroupWin + 1];
+  __shared__ unsigned win_any[kGroupWinWords];
   const int tid = threadIdx.x;
+  const int nt = blockDim.x;
   const int lane = tid & 63;
+  // the context length of this thread's first sequence, kept for the passes below (a
+  // batch of at most blockDim sequences is then read once)
+  const int L_first = tid < N ? context_len(P, tid) : 0;
+  auto len_of = [&](int b) { return b == tid ? L_first : context_len(P, b); };
+  int4 g_first = make_int4(0, 0, 1, -1);  // this thread's first sequence's group, once known
   if (tid <= NB) {
     cnt[0][tid] = 0;
     cnt[1][tid] = 0;
   }
+  if (tid < kGroupWinWords) win_any[tid] = 0;
   if (tid == 0) {
     n_coop = 0;
     s_lmax = 0;
     s_tokens = 0;
+    s_nmem = 0;
   }
-  for (int i = tid; i < N * P.Hq; i += blockDim.x) P.done[i] = 0;
+  for (int i = tid; i < N * P.Hq; i += nt) P.done[i] = 0;
   __syncthreads();
-  // pass 1: item counts per class at both partition sizes, total and longest length
-  // (uniform trip count: every lane takes part in the shuffles)
-  unsigned long long tokens = 0;
-  int lmax = 0;
-  // the two candidate sizes (both the caller's size when it fixed one)
+
+  // ---- shared-prefix groups, window by window ----
+  if (P.cm >= 2 && P.tables) {
+    for (int w0 = 0; w0 < N; w0 += kGroupWin) {
+      for (int i = tid; i < kGroupHash; i += nt) {
+        hkey[i] = -1;
+        hlead[i] = 0x7fffffff;
+        hcnt[i] = 0;
+        hS[i] = 0x7fffffff;
+        hrank[i] = 0;
+      }
+      if (tid == 0) {
+        n_scan = 0;
+        s_any = 0;
+      }
+      __syncthreads();
+      for (int i = tid; i < kGroupWin; i += nt) {
+        const int b = w0 + i;
+        int slot = -1;
+        if (b < N && len_of(b) >= kMinSharedTokens) {
+          const int fb = table_entry(P, b, 0);
+          slot = fb >= 0 ? hash_slot(hkey, fb) : -1;
+          if (slot >= 0) {
+            atomicMin(&hlead[slot], b);
+            atomicAdd(&hcnt[slot], 1);
+          }
+        }
+        wslot[i] = slot;
+      }
+      __syncthreads();
+      for (int i = tid; i < kGroupWin; i += nt) {
+        const int slot = wslot[i];
+        if (slot >= 0 && hcnt[slot] >= 2) {
+          const int b = w0 + i;
+          s_any = 1;
+          const int a = hlead[slot];
+          if (a == b) {
+            atomicMin(&hS[slot], context_len(P, b) / P.B);
+          } else {
+            const int k = atomicAdd(&n_scan, 1);
+            wscan[k] = b;
+            wcap[k] = min(context_len(P, a), context_len(P, b)) / P.B;
+            wmis[k] = wcap[k];
+          }
+        }
+      }
+      __syncthreads();
+      if (s_any) {
+        // every member's row against the group's first member's: all threads take
+        // (member, chunk of kCmpChunk entries) pairs; wpre holds each member's first pair
+        if (tid < 64) {
+          constexpr int PER = kGroupWin / 64;
+          int c[PER], sum = 0;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            const int k = tid * PER + e;
+            c[e] = k < n_scan ? (wcap[k] + kCmpChunk - 1) / kCmpChunk : 0;
+            sum += c[e];
+          }
+          int v = sum;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(v, d, 64);
+            v += tid >= d ? t : 0;
+          }
+          int run = v - sum;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            wpre[tid * PER + e] = run;
+            run += c[e];
+          }
+          if (tid == 63) wpre[kGroupWin] = v;
+        }
+        __syncthreads();
+        const int total = wpre[kGroupWin];
+        for (int i = tid; i < total; i += nt) {
+          int lo = 0, hi = n_scan - 1;  // the member: the last k with wpre[k] <= i
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (wpre[mid] <= i) lo = mid;
+            else hi = mid - 1;
+          }
+          const int b = wscan[lo];
+          const int j0 = (i - wpre[lo]) * kCmpChunk;
+          if (j0 >= wmis[lo]) continue;  // an earlier chunk already differs
+          const int j = chunk_mismatch(P, hlead[wslot[b - w0]], b, j0, wcap[lo]);
+          if (j < wcap[lo]) atomicMin(&wmis[lo], j);
+        }
+        __syncthreads();
+        for (int k = tid; k < n_scan; k += nt) atomicMin(&hS[wslot[wscan[k] - w0]], wmis[k]);
+        __syncthreads();
+        for (int i = tid; i < kGroupWin; i += nt) {
+          const int slot = wslot[i];
+          int rank = -1;
+          if (slot >= 0 && hcnt[slot] >= 2 && hS[slot] * P.B >= kMinSharedTokens) {
+            rank = atomicAdd(&hrank[slot], 1);
+            if (hlead[slot] == w0 + i) hbase[slot] = atomicAdd(&s_nmem, hcnt[slot]);
+          }
+          wrank[i] = rank;
+        }
+        __syncthreads();
+        for (int i = tid; i < kGroupWin && w0 + i < N; i += nt) {
+          const int b = w0 + i;
+          const int slot = wslot[i];
+          const int rank = wrank[i];
+          int4 g = make_int4(0, 0, 1, -1);  // {shared tokens, rank, members, members offset}
+          if (rank >= 0) {
+            g = make_int4(hS[slot] * P.B, rank, hcnt[slot], hbase[slot]);
+            P.members[g.w + rank] = b;
+          }
+          P.seq_grp[b] = g;
+          if (b == tid) g_first = g;
+        }
+        if (tid == 0) win_any[(w0 / kGroupWin) >> 5] |= 1u << ((w0 / kGroupWin) & 31);
+      }
+      __syncthreads();
+    }
+  }
+  auto group_of = [&](int b) {
+    const int win = b / kGroupWin;
+    if (b == tid && tid < kGroupWin) return g_first;  // (sequence tid was this thread's in window 0)
+    return (win_any[win >> 5] >> (win & 31)) & 1u ? P.seq_grp[b] : make_int4(0, 0, 1, -1);
+  };
+
+  // ---- item counts per class at both candidate sizes, total tokens, longest length ----
   const int lg_lo = P.force_log2 ? P.force_log2 : kLgPartMin;
   const int lg_hi = P.force_log2 ? P.force_log2 : kLgPartMax;
-  const PlanSeq s_first = plan_seq(P, tid);  // kept for pass 2 (the whole batch when N <= blockDim)
-  for (int b0 = 0; b0 < N; b0 += blockDim.x) {
-    const PlanSeq s = b0 == 0 ? s_first : plan_seq(P, b0 + tid);
-    tokens += static_cast<unsigned long long>(max(s.L, 0));
-    lmax = max(lmax, s.L);
+  unsigned long long tokens = 0;
+  int lmax = 0;
+  for (int b = tid; b < N; b += nt) {
+    const int L = len_of(b);
+    const int4 g = group_of(b);
+    const int own = L - g.x;
+    const int ncs = (g.w >= 0 && g.y == 0) ? (g.z + P.cm - 1) / P.cm : 0;  // the group's item writer
+    tokens += static_cast<unsigned long long>(L);  // the size rule counts every sequence's context (as on the host)
+    lmax = max(lmax, L);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      int full, cls;
-      tail_class(s.L, c ? lg_hi : lg_lo, full, cls);
-      int n = cls > 0;
-      group_scan(s.head, cls, n);
-      if (full) atomicAdd(&cnt[c][NB], full);
-      if (s.last && n) atomicAdd(&cnt[c][cls], n);
+      const int lg = c ? lg_hi : lg_lo;
+      const int full = own >> lg;
+      const int rem = own - (full << lg);
+      int nfull = full;
+      if (rem || L == 0) atomicAdd(&cnt[c][item_class(rem, lg)], 1);
+      if (ncs) {
+        const int fp = g.x >> lg;
+        const int rp = g.x - (fp << lg);
+        nfull += fp * ncs;
+        if (rp) atomicAdd(&cnt[c][item_class(rp, lg)], ncs);
+      }
+      if (nfull) atomicAdd(&cnt[c][NB], nfull);
     }
   }
 #pragma unroll
@@ -282,52 +442,76 @@ __device__ __forceinline__ void plan_body(const Params& P, int2* __restrict__ ta
     }
     if (k >= 1) off[k] = v - c;
     if (tid == 63) {
-      counters[0] = v;
-      counters[1] = lg;
+      P.counters[0] = v;
+      P.counters[1] = lg;
     }
   }
   __syncthreads();
-  // pass 2: write the items
-  for (int b0 = 0; b0 < N; b0 += blockDim.x) {
-    const int b = b0 + tid;
-    const PlanSeq s = b0 == 0 ? s_first : plan_seq(P, b);
-    const int L = s.L;
-    int full, cls;
-    tail_class(L, lg, full, cls);
-    const bool own = cls > 0;
-    const int flag = (s.head && s.last) ? 0 : kSharedTask;  // a group of more than one sequence
-    int n = own;
-    group_scan(s.head, cls, n);
+
+  // ---- the items ----
+  const int PT = 1 << lg;
+  for (int b = tid; b < N; b += nt) {
+    const int L = len_of(b);
+    const int4 g = group_of(b);
+    const int npp = g.w >= 0 ? (g.x + PT - 1) >> lg : 0;
+    const int own = L - g.x;
+    const int full = own >> lg;
+    const int rem = own - (full << lg);
+    const int np = L == 0 ? 1 : npp + full + (rem > 0);
+    P.seq_np[b] = np;
     if (full) {
       const int st = atomicAdd(&off[NB], full);
       const int k = full > kPlanSerialMax ? atomicAdd(&n_coop, 1) : kPlanCoopMax;
       if (k < kPlanCoopMax) {
-        coop_b[k] = b;
         coop_s[k] = st;
         coop_n[k] = full;
-        coop_l[k] = L;
-        coop_f[k] = flag;
+        coop_b[k] = b;
+        coop_k[k] = 0;
+        coop_g[k] = make_int4(g.x, npp, np, 0);
       } else {
-        for (int q = 0; q < full; ++q) tasks[st + q] = make_int2((b * P.Pmax + q) | flag, L);
+        for (int q = 0; q < full; ++q) P.tasks[st + q] = make_int4(b, g.x + (q << lg), PT, (npp + q) | (np << 16));
       }
     }
-    // the group's last sequence reserves its tail items' places; n - 1 is this
-    // sequence's place among them
-    int base = (s.last && n) ? atomicAdd(&off[cls], n) : 0;
-    base = __shfl(base, s.last_lane, 64);
-    if (own) tasks[base + n - 1] = make_int2((b * P.Pmax + full) | flag, L);
+    if (rem || L == 0) {
+      const int pos = atomicAdd(&off[item_class(rem, lg)], 1);
+      P.tasks[pos] = make_int4(b, g.x + (full << lg), rem, (npp + full) | (np << 16));
+    }
+    if (g.w >= 0 && g.y == 0) {  // the group's shared-prefix items
+      const int ncs = (g.z + P.cm - 1) / P.cm;
+      const int fp = g.x >> lg;
+      const int rp = g.x - (fp << lg);
+      if (fp) {
+        const int n = fp * ncs;
+        const int st = atomicAdd(&off[NB], n);
+        const int k = n > kPlanSerialMax ? atomicAdd(&n_coop, 1) : kPlanCoopMax;
+        if (k < kPlanCoopMax) {
+          coop_s[k] = st;
+          coop_n[k] = n;
+          coop_b[k] = ncs;
+          coop_k[k] = 1;
+          coop_g[k] = g;
+        } else {
+          for (int q = 0; q < n; ++q) P.tasks[st + q] = prefix_task(P, g, ncs, q, 0, lg, PT);
+        }
+      }
+      if (rp) {
+        const int st = atomicAdd(&off[item_class(rp, lg)], ncs);
+        for (int q = 0; q < ncs; ++q) P.tasks[st + q] = prefix_task(P, g, ncs, q, fp, lg, rp);
+      }
+    }
   }
   __syncthreads();
   const int nc = min(n_coop, kPlanCoopMax);
   for (int k = 0; k < nc; ++k) {
-    for (int q = tid; q < coop_n[k]; q += blockDim.x)
-      tasks[coop_s[k] + q] = make_int2((coop_b[k] * P.Pmax + q) | coop_f[k], coop_l[k]);
+    const int4 g = coop_g[k];
+    for (int q = tid; q < coop_n[k]; q += nt) {
+      P.tasks[coop_s[k] + q] = coop_k[k] ? prefix_task(P, g, coop_b[k], q, 0, lg, PT)
+                                         : make_int4(coop_b[k], g.x + (q << lg), PT, (g.y + q) | (g.z << 16));
+    }
   }
 }
 
-__global__ __launch_bounds__(1024) void attn_plan(Params P, int2* __restrict__ tasks, int* __restrict__ counters) {
-  plan_body(P, tasks, counters);
-}
+__global__ __launch_bounds__(1024) void attn_plan(Params P) { plan_body(P); }
 
 // The step's KV write and the attention plan in one launch: workgroup 0 plans, the
 // others write (the two touch disjoint memory; the partition pass that follows in
@@ -338,10 +522,9 @@ __global__ __launch_bounds__(1024) void attn_plan(Params P, int2* __restrict__ t
 constexpr int kPrepThreads = PKV_PREP_THREADS;
 
 template <int EB>
-__global__ __launch_bounds__(kPrepThreads) void decode_prepare_kernel(Params P, WriteArgs wa, int2* __restrict__ tasks,
-                                                             int* __restrict__ counters) {
+__global__ __launch_bounds__(kPrepThreads) void decode_prepare_kernel(Params P, WriteArgs wa) {
   if (blockIdx.x == 0) {
-    plan_body(P, tasks, counters);
+    plan_body(P);
     return;
   }
   kv_write_one<EB>(wa, static_cast<int64_t>(blockIdx.x - 1) * blockDim.x + threadIdx.x);
@@ -363,13 +546,23 @@ __device__ __forceinline__ void zero_rows(const Params& P, int b, int hq0, int n
   for (int i = threadIdx.x; i < nrows * D; i += kThreads) o[i] = T::from_float(0.f);
 }
 
-// Merge the four waves' (max, sum, output) in LDS; store the final row or the partials.
-template <class T, int D, int GMAX>
-__device__ __forceinline__ void combine_and_store(const Params& P, const float (*s_m)[GMAX],
-                                                  const float (*s_l)[GMAX], const float (*s_o)[GMAX][D + 4],
-                                                  int b, int hq0, int gcur, int p, int np) {
+// The output row of each column of an item and that row's partial count.
+template <int C>
+struct ColSmem {
+  int64_t row[C];
+  int np[C];
+  int member[C];  // the sequence of each of the item's sequences (by member index)
+  int last[C];    // this workgroup merges that member's rows
+};
+
+// Merge the four waves' (max, sum, output) in LDS; store each column's final row (a row
+// of one partial) or its partial in slot p.
+template <class T, int D, int C>
+__device__ __forceinline__ void combine_and_store(const Params& P, const float (*s_m)[C], const float (*s_l)[C],
+                                                  const float (*s_o)[C][D + 4], const ColSmem<C>& cs, int ncols,
+                                                  int p) {
   typedef typename T::Bits Bits;
-  for (int idx = threadIdx.x; idx < gcur * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
     const int g = idx / D;
     const int d = idx - g * D;
     float M = s_m[0][g];
@@ -382,8 +575,8 @@ __device__ __forceinline__ void combine_and_store(const Params& P, const float (
       num += f * s_o[w][g][d];
       den += f * s_l[w][g];
     }
-    const int64_t row = static_cast<int64_t>(b) * P.Hq + hq0 + g;
-    if (np == 1) {
+    const int64_t row = cs.row[g];
+    if (cs.np[g] == 1) {
       reinterpret_cast<Bits*>(P.out)[row * D + d] = T::from_float(num / den);
     } else {
       // partials are read by whichever workgroup merges the row, possibly on another
@@ -519,9 +712,8 @@ struct MergeSmem {
   f32x4 acc[NG][NCOL];
 };
 
-// kCoherent: the partials were stored by other workgroups of the running kernel, so
-// they are read with device-scope loads; after a kernel boundary plain loads suffice.
-template <class T, int D, bool kCoherent>
+// (the partials were stored by an earlier kernel: plain loads)
+template <class T, int D>
 __device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, MergeSmem<D>& sm) {
   typedef typename T::Bits Bits;
   constexpr int NCOL = MergeSmem<D>::NCOL;
@@ -532,7 +724,7 @@ __device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, 
   const float* ml = P.ws_ml + row * P.Pmax * 2;
   const float* po = P.ws_o + row * P.Pmax * D;
 
-  auto ld = [](const float* p) { return kCoherent ? load_device(p) : *p; };
+  auto ld = [](const float* p) { return *p; };
   float mx = kNegInf;
   for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, ld(&ml[2 * i]));
 #pragma unroll
@@ -556,13 +748,7 @@ __device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, 
   for (int i = grp; i < np; i += NG) {
     const float wgt = fast_exp2(ld(&ml[2 * i]) - M) * ld(&ml[2 * i + 1]);
     const float* src = po + static_cast<int64_t>(i) * D + col * 4;
-    f32x4 v;
-    if constexpr (kCoherent) {
-      v = f32x4{load_device(src), load_device(src + 1), load_device(src + 2), load_device(src + 3)};
-    } else {
-      v = *reinterpret_cast<const f32x4*>(src);
-    }
-    acc += wgt * v;
+    acc += wgt * *reinterpret_cast<const f32x4*>(src);
   }
   sm.acc[grp][col] = acc;
   __syncthreads();
@@ -578,6 +764,31 @@ __device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, 
   __syncthreads();
 }
 
+// Merge of the rows row0 .. row0 + nrows - 1 (each of np <= kFuseMaxParts partials,
+// stored by workgroups of the running kernel) by the calling workgroup, one thread per
+// output element: M = max_p m_p, w_p = exp2(m_p - M) * l_p, out = sum_p w_p o_p / sum_p w_p,
+// summed in partition order.  No barrier: each element is independent.
+template <class T, int D>
+__device__ __forceinline__ void merge_rows_fused(const Params& P, int64_t row0, int nrows, int np) {
+  typedef typename T::Bits Bits;
+  for (int idx = threadIdx.x; idx < nrows * D; idx += kThreads) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    const int64_t row = row0 + g;
+    const float* ml = P.ws_ml + row * P.Pmax * 2;
+    const float* po = P.ws_o + row * P.Pmax * D + d;
+    float M = kNegInf;
+    for (int i = 0; i < np; ++i) M = fmaxf(M, load_device(&ml[2 * i]));
+    float num = 0.f, den = 0.f;
+    for (int i = 0; i < np; ++i) {
+      const float w = fast_exp2(load_device(&ml[2 * i]) - M) * load_device(&ml[2 * i + 1]);
+      num += w * load_device(&po[static_cast<int64_t>(i) * D]);
+      den += w;
+    }
+    reinterpret_cast<Bits*>(P.out)[row * D + d] = T::from_float(num / den);
+  }
+}
+
 // After a partition's partials are stored: the workgroup that finishes a row's last
 // partition (device-scope counter, zeroed by the plan pass) merges its query heads.
 // Every thread waits until its device-scope partial stores have completed before the
@@ -591,17 +802,52 @@ __device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, 
 // acquire load would be the portable form, but an agent-scope release writes back the
 // whole L2 of the XCD: a __threadfence() version of this protocol was measured 5.5x
 // slower.  The signal fences keep the compiler from moving the stores past the wait.
-template <class T, int D>
-__device__ __forceinline__ void finish_rows(const Params& P, int b, int hq0, int nrows, int np,
-                                           MergeSmem<D>& sm, int& s_last) {
+// An item covers `nm` sequences' rows hq0 .. hq0 + nrows - 1 (member i's partial count
+// at cs.np[i * nrows]); each sequence's counter is advanced once per item.
+template <class T, int D, int C>
+__device__ __forceinline__ void finish_rows(const Params& P, ColSmem<C>& cs, int nm, int hq0, int nrows) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // all of this thread's memory operations have completed
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&P.done[static_cast<int64_t>(b) * P.Hq + hq0], 1) == np - 1;
+  if (threadIdx.x < nm) {
+    const int i = threadIdx.x;
+    const int np = cs.np[i * nrows];
+    cs.last[i] = np > 1 && np <= kFuseMaxParts &&
+                 atomicAdd(&P.done[static_cast<int64_t>(cs.member[i]) * P.Hq + hq0], 1) == np - 1;
+  }
   __syncthreads();
-  if (!s_last) return;
-  for (int g = 0; g < nrows; ++g) merge_row<T, D, true>(P, static_cast<int64_t>(b) * P.Hq + hq0 + g, np, sm);
+  for (int i = 0; i < nm; ++i) {
+    if (cs.last[i]) merge_rows_fused<T, D>(P, static_cast<int64_t>(cs.member[i]) * P.Hq + hq0, nrows, cs.np[i * nrows]);
+  }
+}
+
+// Columns of the MFMA kernels' products: lane m (of every 16-lane row) is column m,
+// query head hq0 + m % gcur of the item's sequence m / gcur (an ordinary item has one
+// sequence; a shared-prefix item up to 16 / gcur).  Lanes 0..15 record each column's
+// output row and partial count, and each sequence's id, in LDS for the epilogue.
+struct Cols {
+  bool hv;           // lane's column is used
+  int64_t qrow;      // query row of the lane's column (a used row for unused columns)
+  bool need_finish;  // some covered sequence's rows are merged in this kernel
+};
+template <int C>
+__device__ __forceinline__ Cols setup_columns(const Params& P, const Item& it, int hq0, int gcur, ColSmem<C>& cs) {
+  const int m = threadIdx.x & 15;
+  const int mi = m / gcur;
+  Cols c;
+  c.hv = mi < it.nm;
+  int member = it.prefix ? P.members[it.idx + (c.hv ? mi : 0)] : it.idx;
+  member = min(max(member, 0), P.N - 1);  // (a plan pass writes sequence ids only)
+  const int np = min(max(it.prefix ? P.seq_np[member] : it.np, 1), P.Pmax);
+  c.qrow = static_cast<int64_t>(member) * P.Hq + hq0 + (m - mi * gcur);
+  if (threadIdx.x < 16) {
+    cs.row[m] = c.qrow;
+    cs.np[m] = np;
+    if (c.hv && m == mi * gcur) cs.member[mi] = member;
+  }
+  c.need_finish = __builtin_amdgcn_ballot_w64(c.hv && np > 1 && np <= kFuseMaxParts) != 0;
+  return c;
 }
 
 // ---------------------------------------------------------------------------------
@@ -625,43 +871,38 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     u32x2 v[NC];
   };
 
+  constexpr int C = 16;  // columns of the products
   __shared__ int s_tab[BPP_MAX];
-  __shared__ float s_m[kWaves][GMAX];
-  __shared__ float s_l[kWaves][GMAX];
-  __shared__ float s_o[kWaves][GMAX][D + 4];
-  __shared__ MergeSmem<D> s_merge;
-  __shared__ int s_last;
+  __shared__ float s_m[kWaves][C];
+  __shared__ float s_l[kWaves][C];
+  __shared__ float s_o[kWaves][C][D + 4];
+  __shared__ ColSmem<C> s_cols;
 
   const int HY = P.Hkv * P.NHG;
   const int t = blockIdx.x / HY;
   const int hy = blockIdx.x - t * HY;
   if (t >= P.counters[0]) return;
-  const int2 task = P.tasks[t];
-  const int item = task.x & ~kSharedTask;
-  const bool shared = (task.x & kSharedTask) != 0;
-  if (task.x < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
-  const int b = item / P.Pmax;
-  const int p = item - b * P.Pmax;
   const int kvh = hy / P.NHG;
   const int hg = hy - kvh * P.NHG;
   const int hq0 = kvh * P.G + hg * 16;
   const int gcur = min(16, P.G - hg * 16);
-  const int L = min(max(task.y, 0), P.Lmax);
-  if (L <= 0) {
-    if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
+  const Item it = decode_item(P, P.tasks[t], 16, gcur);
+  if (!it.ok) return;  // only an item list left by the plan pass is valid
+  if (it.ntok == 0) {
+    if (!it.prefix && it.p == 0) zero_rows<T, D>(P, it.idx, hq0, gcur);
     return;
   }
-  const int lg = min(max(P.counters[1], kLgPartFloor), kLgPartMax);  // this launch's partition size
-  const int np = (L + (1 << lg) - 1) >> lg;
-  if (p >= np) return;
+  const bool shared = it.shared;
+  // whose table row the item reads (a shared-prefix item's sequences share these entries)
+  const int lead = it.prefix ? min(max(P.members[it.idx], 0), P.N - 1) : it.idx;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;
   const int m = lane & 15;
-  const int ntok = min(1 << lg, L - (p << lg));
-  const int pe = (p << lg) / B;  // the partition's first table entry
+  const int ntok = it.ntok;
+  const int pe = it.tok0 / B;  // the item's first table entry
   const int nunits = (ntok + 15) >> 4;
   const int nblk = (ntok + B - 1) / B;
 
@@ -671,11 +912,12 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   // (unconditional loads from clamped, always-valid addresses keep the waits exact; a
   // partition may span several two-level leaves, so each lane looks its entry up)
   const int tab_val = static_cast<int>(__builtin_nontemporal_load(
-      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + min(tid, nblk - 1))));
-  const bool hv = m < gcur;
+      table_row<Tab, kLeaf<B>>(P.tables, P.dir, lead, P.W, pe + min(tid, nblk - 1))));
+  const Cols col = setup_columns<C>(P, it, hq0, gcur, s_cols);
+  const bool hv = col.hv;
   u32x4 qf[KI];
   {
-    const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + (hv ? m : 0)) * D * EB;
+    const char* qrow = P.q + col.qrow * D * EB;
 #pragma unroll
     for (int ki = 0; ki < KI; ++ki) qf[ki] = load_stream<u32x4>(qrow + (4 * ki + r) * 16);
 #pragma unroll
@@ -717,7 +959,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   Buf first;
   {
     const int u0 = w < nunits ? w : 0;
-    const int blk = static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + u0 / SUB));
+    const int blk = static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, lead, P.W, pe + u0 / SUB));
     if (shared) load_blk(Cached{}, u0, blk, first);
     else load_blk(Streamed{}, u0, blk, first);
   }
@@ -800,8 +1042,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     }
   }
   __syncthreads();
-  combine_and_store<T, D, GMAX>(P, s_m, s_l, s_o, b, hq0, gcur, p, np);
-  if (np > 1 && np <= kFuseMaxParts) finish_rows<T, D>(P, b, hq0, gcur, np, s_merge, s_last);
+  combine_and_store<T, D, C>(P, s_m, s_l, s_o, s_cols, it.nm * gcur, it.p);
+  if (col.need_finish) finish_rows<T, D, C>(P, s_cols, it.nm, hq0, gcur);
 }
 
 // ---------------------------------------------------------------------------------
@@ -828,54 +1070,50 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     u32x4 v[NC];
   };
 
+  constexpr int C = 16;  // columns of the products
   __shared__ int s_tab[BPP_MAX];
-  __shared__ float s_m[kWaves][GMAX];
-  __shared__ float s_l[kWaves][GMAX];
-  __shared__ float s_o[kWaves][GMAX][D + 4];
-  __shared__ MergeSmem<D> s_merge;
-  __shared__ int s_last;
+  __shared__ float s_m[kWaves][C];
+  __shared__ float s_l[kWaves][C];
+  __shared__ float s_o[kWaves][C][D + 4];
+  __shared__ ColSmem<C> s_cols;
   __shared__ u32x4 s_q[KI][64];
 
   const int HY = P.Hkv * P.NHG;
   const int t = blockIdx.x / HY;
   const int hy = blockIdx.x - t * HY;
   if (t >= P.counters[0]) return;
-  const int2 task = P.tasks[t];
-  const int item = task.x & ~kSharedTask;
-  const bool shared = (task.x & kSharedTask) != 0;
-  if (task.x < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
-  const int b = item / P.Pmax;
-  const int p = item - b * P.Pmax;
   const int kvh = hy / P.NHG;
   const int hg = hy - kvh * P.NHG;
   const int hq0 = kvh * P.G + hg * 16;
   const int gcur = min(16, P.G - hg * 16);
-  const int L = min(max(task.y, 0), P.Lmax);
-  if (L <= 0) {
-    if (p == 0) zero_rows<T, D>(P, b, hq0, gcur);
+  const Item it = decode_item(P, P.tasks[t], 32, gcur);
+  if (!it.ok) return;  // only an item list left by the plan pass is valid
+  if (it.ntok == 0) {
+    if (!it.prefix && it.p == 0) zero_rows<T, D>(P, it.idx, hq0, gcur);
     return;
   }
-  const int lg = min(max(P.counters[1], kLgPartFloor), kLgPartMax);  // this launch's partition size
-  const int np = (L + (1 << lg) - 1) >> lg;
-  if (p >= np) return;
+  const bool shared = it.shared;
+  // whose table row the item reads (a shared-prefix item's sequences share these entries)
+  const int lead = it.prefix ? min(max(P.members[it.idx], 0), P.N - 1) : it.idx;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;
   const int m = lane & 15;
-  const int ntok = min(1 << lg, L - (p << lg));
-  const int pe = (p << lg) / B;  // the partition's first table entry
+  const int ntok = it.ntok;
+  const int pe = it.tok0 / B;  // the item's first table entry
   const int nunits = (ntok + 31) >> 5;
   const int nblk = (ntok + B - 1) / B;
 
   // preamble: all loads first (table entries, queries, first unit), LDS writes after
   const int tab_val = static_cast<int>(__builtin_nontemporal_load(
-      table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + min(tid, nblk - 1))));
-  const bool hv = m < gcur;
+      table_row<Tab, kLeaf<B>>(P.tables, P.dir, lead, P.W, pe + min(tid, nblk - 1))));
+  const Cols col = setup_columns<C>(P, it, hq0, gcur, s_cols);
+  const bool hv = col.hv;
   u32x4 qf[KI];
   {
-    const char* qrow = P.q + (static_cast<int64_t>(b) * P.Hq + hq0 + (hv ? m : 0)) * D * EB;
+    const char* qrow = P.q + col.qrow * D * EB;
 #pragma unroll
     for (int ki = 0; ki < KI; ++ki) qf[ki] = load_stream<u32x4>(qrow + (4 * ki + r) * 16);
 #pragma unroll
@@ -950,7 +1188,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   {
     const int u0 = w < nunits ? w : 0;
     // (the unit's entries lie in one leaf: leaves hold an even number of entries)
-    const auto* e0 = table_row<Tab, kLeaf<B>>(P.tables, P.dir, b, P.W, pe + u0 * BPU);
+    const auto* e0 = table_row<Tab, kLeaf<B>>(P.tables, P.dir, lead, P.W, pe + u0 * BPU);
     const int blk0 = static_cast<int>(e0[0]);
     const int blk1 = BPU == 2 ? static_cast<int>(e0[u0 * BPU + 1 < nblk ? 1 : 0]) : blk0;
     if (shared) load_blk(Cached{}, blk0, blk1, first);
@@ -1031,8 +1269,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     }
   }
   __syncthreads();
-  combine_and_store<T, D, GMAX>(P, s_m, s_l, s_o, b, hq0, gcur, p, np);
-  if (np > 1 && np <= kFuseMaxParts) finish_rows<T, D>(P, b, hq0, gcur, np, s_merge, s_last);
+  combine_and_store<T, D, C>(P, s_m, s_l, s_o, s_cols, it.nm * gcur, it.p);
+  if (col.need_finish) finish_rows<T, D, C>(P, s_cols, it.nm, hq0, gcur);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1040,7 +1278,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
 // pools with G query heads per kv head.  grid = (num_kv_heads, max_partitions, num_seqs)
 // ---------------------------------------------------------------------------------
 template <class T, int D, int B, int G, class Tab>
-__global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
+__global__ __launch_bounds__(kThreads, T::kBytes == 2 ? 4 : 1) void attn_partition_valu(Params P) {
   constexpr int EB = T::kBytes;
   constexpr int X = 16 / EB;
   constexpr int NCH = D / X;
@@ -1059,36 +1297,29 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ float s_o[kWaves][G][D + 4];
-  __shared__ MergeSmem<D> s_merge;
-  __shared__ int s_last;
+  __shared__ ColSmem<G> s_cols;
 
   const int t = blockIdx.x / P.Hkv;
   const int kvh = blockIdx.x - t * P.Hkv;
   if (t >= P.counters[0]) return;
-  const int2 task = P.tasks[t];
-  const int item = task.x & ~kSharedTask;
-  // (streaming loads whatever the shared flag: a second load flavour would cost this
-  // kernel a wave per SIMD, 136 VGPRs against 128)
-  if (task.x < 0 || item >= P.N * P.Pmax) return;  // only a task list left by the plan pass is valid
-  const int b = item / P.Pmax;
-  const int p = item - b * P.Pmax;
+  const Item it = decode_item(P, P.tasks[t], 16, G);
+  // (the plan gives this kernel ordinary items only)
+  if (!it.ok || it.prefix) return;  // only an item list left by the plan pass is valid
+  const int b = it.idx;
   const int hq0 = kvh * G;
-  const int L = min(max(task.y, 0), P.Lmax);
-  if (L <= 0) {
-    if (p == 0) zero_rows<T, D>(P, b, hq0, G);
+  if (it.ntok == 0) {
+    if (it.p == 0) zero_rows<T, D>(P, b, hq0, G);
     return;
   }
-  const int lg = min(max(P.counters[1], kLgPartFloor), kLgPartMax);  // this launch's partition size
-  const int np = (L + (1 << lg) - 1) >> lg;
-  if (p >= np) return;
+  const int np = it.np;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane >> 4;
   const int m = lane & 15;
-  const int ntok = min(1 << lg, L - (p << lg));
-  const int pe = (p << lg) / B;  // the partition's first table entry
+  const int ntok = it.ntok;
+  const int pe = it.tok0 / B;  // the item's first table entry
   const int nunits = (ntok + 15) >> 4;
   const int nblk = (ntok + B - 1) / B;
 
@@ -1246,9 +1477,14 @@ __global__ __launch_bounds__(kThreads) void attn_partition_valu(Params P) {
       for (int c = 0; c < NV; ++c) s_o[w][g][16 * c + m] = o[g][c];
     }
   }
+  if (tid < G) {
+    s_cols.row[tid] = static_cast<int64_t>(b) * P.Hq + hq0 + tid;
+    s_cols.np[tid] = np;
+    if (tid == 0) s_cols.member[0] = b;
+  }
   __syncthreads();
-  combine_and_store<T, D, G>(P, s_m, s_l, s_o, b, hq0, G, p, np);
-  if (np > 1 && np <= kFuseMaxParts) finish_rows<T, D>(P, b, hq0, G, np, s_merge, s_last);
+  combine_and_store<T, D, G>(P, s_m, s_l, s_o, s_cols, G, it.p);
+  if (np > 1 && np <= kFuseMaxParts) finish_rows<T, D, G>(P, s_cols, 1, hq0, G);
 }
 
 // Merge kernel for rows of more than kFuseMaxParts partitions.  grid = (Hq, N)
@@ -1257,10 +1493,9 @@ __global__ __launch_bounds__(kThreads) void attn_merge_long(Params P) {
   __shared__ MergeSmem<D> s_merge;
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int lg = min(max(P.counters[1], kLgPartFloor), kLgPartMax);
-  const int np = (context_len(P, b) + (1 << lg) - 1) >> lg;
+  const int np = min(P.seq_np[b], P.Pmax);
   if (np <= kFuseMaxParts) return;
-  merge_row<T, D, false>(P, static_cast<int64_t>(b) * P.Hq + hq, np, s_merge);
+  merge_row<T, D>(P, static_cast<int64_t>(b) * P.Hq + hq, np, s_merge);
 }
 
 Params make_params(const AttnArgs& a) {
@@ -1274,9 +1509,13 @@ Params make_params(const AttnArgs& a) {
   P.tables = a.block_tables;
   P.dir = a.table_dir;
   P.ctx = a.context_lens;
-  P.tasks = reinterpret_cast<const int2*>(a.tasks);
+  P.tasks = reinterpret_cast<int4*>(a.tasks);
   P.counters = a.counters;
   P.done = a.done;
+  P.seq_np = a.seq_np;
+  P.seq_grp = reinterpret_cast<int4*>(a.seq_grp);
+  P.members = a.members;
+  P.B = a.block_size;
   P.N = a.num_seqs;
   P.Hq = a.num_q_heads;
   P.Hkv = a.num_kv_heads;
@@ -1290,6 +1529,9 @@ Params make_params(const AttnArgs& a) {
   P.leaf_e = PKV_LEAF_TOKENS / a.block_size;
   P.slots = a.slots;
   P.force_log2 = a.force_log2;
+  // shared-prefix items need the MFMA kernels (16-bit pools, 2..16 query heads per kv
+  // head) and at least two sequences per item
+  P.cm = (a.dtype != PKV_F32 && P.G >= 2 && P.G <= 8) ? 16 / P.G : 0;
   return P;
 }
 
@@ -1393,19 +1635,16 @@ int launch_decode_prepare(const AttnArgs& a, const pkv_pool_desc& pool, void* k_
   const unsigned grid = 1 + static_cast<unsigned>((total + kPrepThreads - 1) / kPrepThreads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (eb == 4) {
-    hipLaunchKernelGGL(decode_prepare_kernel<4>, dim3(grid), dim3(kPrepThreads), 0, s, P, wa, reinterpret_cast<int2*>(a.tasks),
-                       a.counters);
+    hipLaunchKernelGGL(decode_prepare_kernel<4>, dim3(grid), dim3(kPrepThreads), 0, s, P, wa);
   } else {
-    hipLaunchKernelGGL(decode_prepare_kernel<2>, dim3(grid), dim3(kPrepThreads), 0, s, P, wa, reinterpret_cast<int2*>(a.tasks),
-                       a.counters);
+    hipLaunchKernelGGL(decode_prepare_kernel<2>, dim3(grid), dim3(kPrepThreads), 0, s, P, wa);
   }
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_attn_plan(const AttnArgs& a, void* stream) {
   const Params P = make_params(a);
-  hipLaunchKernelGGL(attn_plan, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), P,
-                     reinterpret_cast<int2*>(a.tasks), a.counters);
+  hipLaunchKernelGGL(attn_plan, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), P);
   return static_cast<int>(hipGetLastError());
 }
 

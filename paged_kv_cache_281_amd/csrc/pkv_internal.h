@@ -24,9 +24,11 @@ inline int elem_bytes(int32_t dtype) {
 }
 
 // Partial-result slots per sequence: partitions of PKV_PARTITION_TOKENS_MIN tokens (the
-// smallest size a launch can use) for max_blocks_per_seq blocks.
+// smallest size a launch can use) for max_blocks_per_seq blocks, plus one: a sequence
+// whose leading blocks are read with other sequences' (a shared prefix) is split at the
+// end of that prefix, which can cost one more partition.
 inline int64_t max_partitions(int64_t max_blocks_per_seq, int64_t block_size) {
-  return (max_blocks_per_seq * block_size + PKV_PARTITION_TOKENS_MIN - 1) / PKV_PARTITION_TOKENS_MIN;
+  return (max_blocks_per_seq * block_size + PKV_PARTITION_TOKENS_MIN - 1) / PKV_PARTITION_TOKENS_MIN + 1;
 }
 
 // Kernel launchers (defined in the .hip files).  They assume validated arguments
@@ -52,9 +54,12 @@ struct AttnArgs {
   const int32_t* context_lens;
   float* ws_o;   // [num_seqs][num_q_heads][max_partitions][head_dim]
   float* ws_ml;  // [num_seqs][num_q_heads][max_partitions][2]: running max (log2 units), sum
-  int* tasks;    // [num_seqs * max_partitions] x 2 ints: (item, context length), longest first
+  int* tasks;    // [num_seqs * max_partitions] x 4 ints: the plan's work items, longest first
   int* counters; // [64]: counters[0] = number of items
   int* done;     // [num_seqs * num_q_heads]: finished partitions per (sequence, head group)
+  int* seq_np;   // [num_seqs]: partial results of each sequence's rows
+  int* seq_grp;  // [num_seqs] x 4 ints: the plan's shared-prefix group of each sequence
+  int* members;  // [num_seqs]: sequences of each shared-prefix group, group by group
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
   int32_t max_blocks_per_seq, max_parts;
   int32_t table_bytes;  // 4 (int32 entries) or 2 (uint16 entries)
@@ -98,7 +103,7 @@ int32_t set_forced_partition_log2(int32_t log2_tokens);
 
 // Byte offsets of the workspace regions (each 256-byte aligned) and the total size.
 struct WorkspaceLayout {
-  size_t o, ml, tasks, done, counters, total;
+  size_t o, ml, tasks, done, seq_np, seq_grp, members, counters, total;
 };
 inline WorkspaceLayout workspace_layout(int64_t n, int64_t hq, int64_t d, int64_t parts) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -106,8 +111,11 @@ inline WorkspaceLayout workspace_layout(int64_t n, int64_t hq, int64_t d, int64_
   w.o = 0;
   w.ml = al(static_cast<size_t>(n * hq * parts * d) * sizeof(float));
   w.tasks = w.ml + al(static_cast<size_t>(n * hq * parts * 2) * sizeof(float));
-  w.done = w.tasks + al(static_cast<size_t>(n * parts) * 2 * sizeof(int32_t));
-  w.counters = w.done + al(static_cast<size_t>(n * hq) * sizeof(int32_t));
+  w.done = w.tasks + al(static_cast<size_t>(n * parts) * 4 * sizeof(int32_t));
+  w.seq_np = w.done + al(static_cast<size_t>(n * hq) * sizeof(int32_t));
+  w.seq_grp = w.seq_np + al(static_cast<size_t>(n) * sizeof(int32_t));
+  w.members = w.seq_grp + al(static_cast<size_t>(n) * 4 * sizeof(int32_t));
+  w.counters = w.members + al(static_cast<size_t>(n) * sizeof(int32_t));
   w.total = w.counters + 256;
   return w;
 }

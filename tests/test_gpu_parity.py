@@ -198,6 +198,43 @@ def test_cow_samples_agree_bitwise_on_the_shared_prefix():
     assert len({t[i, 63] for i in range(4)}) == 4
 
 
+# forked samples under other shapes: more samples than one shared-prefix item's columns
+# (several items per prefix, cached loads), 8 and 2 query heads per kv head, block 32
+# (the 32-token-unit kernel), 3 query heads per kv head with 6 samples (5 per item), a
+# prefix of several partitions, and one query head per kv head (vector-ALU kernel, no
+# shared-prefix items)
+FORKS = [
+    ("cow_g4_8samples", lambda: synth.cow_fp16(1020, num_prompts=3, samples=8, max_suffix=100)),
+    ("cow_g8", lambda: synth.cow_fp16(1020, num_prompts=3, max_suffix=100, hq=16, hkv=2)),
+    ("cow_g2_b32", lambda: synth.cow_fp16(1020, num_prompts=3, max_suffix=100, hq=8, hkv=4, block=32)),
+    ("cow_g3_6samples", lambda: synth.cow_fp16(1024, num_prompts=2, samples=6, max_suffix=60, hq=12, hkv=4)),
+    ("cow_long_prefix", lambda: synth.cow_fp16(5000, num_prompts=2, max_suffix=64)),
+    ("cow_mha", lambda: synth.cow_fp16(1020, num_prompts=3, max_suffix=100, hq=8, hkv=8)),
+]
+
+
+@pytest.mark.parametrize("name,make", FORKS, ids=[f[0] for f in FORKS])
+def test_forked_samples(name, make):
+    w = make()
+    _run_case(w, fused=True)
+    _run_case(w, check_pools=False)
+
+
+def test_shuffled_forks_give_the_ordered_bits():
+    """The forked batch with its samples scattered through the batch: every row's output
+    bits equal those of the ordered batch (the same groups form), and match the oracle."""
+    w = synth.cow_fp16(1020, num_prompts=6, max_suffix=120)
+    st, ora, out, q_bits = _run_case(w, check_pools=False)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(w.num_seqs)).to(DEV)
+    q = to_device(q_bits, w.dtype, DEV)
+    tables = torch.from_numpy(np.asarray(st.bm.block_tables(w.batch, w.max_blocks_per_seq, nan_block(w, st.bm))))
+    tables = tables.to(DEV)
+    shuffled = pkv.paged_attention_decode(q[perm].contiguous(), st.k_pool, st.v_pool, tables[perm].contiguous(),
+                                          st.context_lens[perm].contiguous(), w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(shuffled.view(torch.int16), out[perm].view(torch.int16))
+
+
 # ---- full-size workloads, in the benchmark's launch configuration -------------------
 FULL = [
     ("tiny_fp32", None),

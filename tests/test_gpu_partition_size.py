@@ -6,10 +6,10 @@ when fixed by the caller) and the plan's task list.
   every partition kernel, rows of several partitions with a ragged tail, and a row
   that needs the separate merge kernel at 1024 but not at 2048.
 - The size the device picks equals the host rule (pkv_decode_partition_tokens).
-- The task list is a permutation of the expected (sequence, partition) items, full
-  partitions first, tail items in non-increasing length class, and the tail items of
-  sequences that share their first block (copy-on-write samples) listed together and
-  flagged for cached K/V loads.
+- The item list holds exactly the expected items, in non-increasing length class:
+  every sequence's own partitions, and for each group of sequences that share their
+  leading blocks (copy-on-write samples, wherever they sit in the batch) the
+  shared-prefix items that read those blocks once for several sequences.
 """
 import numpy as np
 import pytest
@@ -67,36 +67,131 @@ def _counters(ws: torch.Tensor) -> np.ndarray:
     return ws[-256:].view(torch.int32)[:2].cpu().numpy()
 
 
-SHARED = 1 << 30  # task flag: the sequence shares its first block with a neighbour
+PREFIX = 1 << 29  # item flag: a shared-prefix item (x holds the offset of its sequences)
+SHARED = 1 << 30  # item flag: cached K/V loads (a group that needs several items)
+MIN_SHARED = 256  # shortest shared prefix given shared-prefix items
+WIN = 512  # sequences are grouped within aligned windows of this many
 
 
-def _tasks(ws: torch.Tensor, n: int, hq: int, d: int, parts: int, count: int) -> np.ndarray:
-    # workspace regions (each 256-byte aligned): partial outputs, (max, sum) pairs, tasks
+def _regions(n, hq, d, parts):
+    """Byte offsets of the workspace regions (each 256-byte aligned)."""
     al = lambda x: (x + 255) // 256 * 256
-    off = al(n * hq * parts * d * 4) + al(n * hq * parts * 2 * 4)
-    return ws[off:off + count * 8].view(torch.int32).view(-1, 2).cpu().numpy()
+    r = {"o": 0}
+    r["ml"] = al(n * hq * parts * d * 4)
+    r["tasks"] = r["ml"] + al(n * hq * parts * 2 * 4)
+    r["done"] = r["tasks"] + al(n * parts * 16)
+    r["seq_np"] = r["done"] + al(n * hq * 4)
+    r["seq_grp"] = r["seq_np"] + al(n * 4)
+    r["members"] = r["seq_grp"] + al(n * 16)
+    return r
 
 
-def _items(tasks: np.ndarray) -> np.ndarray:
-    """The (item, length) pairs with the shared-group flag cleared."""
-    t = tasks.copy()
-    t[:, 0] &= ~SHARED
-    return t
+def _read_plan(ws, n, hq, d, parts):
+    """(counters, items [count, 4], partial count per sequence, members list)."""
+    cnt = _counters(ws)
+    r = _regions(n, hq, d, parts)
+    i32 = lambda off, k: ws[off:off + 4 * k].view(torch.int32).cpu().numpy()
+    tasks = i32(r["tasks"], 4 * int(cnt[0])).reshape(-1, 4)
+    return cnt, tasks, i32(r["seq_np"], n), i32(r["members"], n)
 
 
-def _plan(lens, hq, hkv, tables, d=128, block=16):
-    """Runs the plan pass alone on a batch; returns the counters and the task list."""
+def _plan(lens, hq, hkv, tables, d=128, block=16, prepare=False):
+    """Runs the plan pass alone (or as the fused write + plan launch runs it, 256
+    threads, no tokens written) on a batch; returns what it wrote."""
     n = len(lens)
     W = tables.shape[1]
     q = torch.zeros(n, hq, d, dtype=torch.bfloat16, device=DEV)
     kp, vp = pkv.alloc_pools(1, block, hkv, d, torch.bfloat16, DEV)  # the plan reads no K/V
     ws = pkv.alloc_workspace(n, hq, d, W, block, DEV)
     lens_d = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(DEV)
-    pkv.paged_attention_plan(q, kp, vp, tables, lens_d, ws)
+    if prepare:
+        kv_new = torch.zeros(0, hkv, d, dtype=torch.bfloat16, device=DEV)
+        slots = torch.zeros(0, dtype=torch.int64, device=DEV)
+        pkv.decode_prepare(kp, vp, kv_new, kv_new, slots, q, tables, lens_d, ws)
+    else:
+        pkv.paged_attention_plan(q, kp, vp, tables, lens_d, ws)
     torch.cuda.synchronize()
-    cnt = _counters(ws)
-    parts = -(-W * block // pkv.PARTITION_TOKENS_MIN)
-    return cnt, _tasks(ws, n, hq, d, parts, int(cnt[0])), parts
+    parts = -(-W * block // pkv.PARTITION_TOKENS_MIN) + 1
+    return _read_plan(ws, n, hq, d, parts)
+
+
+def _groups(lens, rows, block, cm):
+    """The shared-prefix groups the plan must find, restated: within aligned windows of
+    WIN sequences, sequences of at least MIN_SHARED tokens with the same first block;
+    the prefix is the shortest run of leading entries equal to the first member's, cut
+    to blocks both fill; groups of two or more with a prefix of MIN_SHARED tokens or
+    more.  Returns [(members, prefix tokens)]."""
+    out = []
+    if cm < 2:
+        return out
+    n = len(lens)
+    for w0 in range(0, n, WIN):
+        by_first = {}
+        for b in range(w0, min(n, w0 + WIN)):
+            if lens[b] >= MIN_SHARED and rows[b][0] >= 0:
+                by_first.setdefault(int(rows[b][0]), []).append(b)
+        for mem in by_first.values():
+            if len(mem) < 2:
+                continue
+            a = mem[0]
+            S = int(lens[a]) // block
+            for b in mem[1:]:
+                cap = min(int(lens[a]), int(lens[b])) // block
+                j = 0
+                while j < cap and rows[a][j] == rows[b][j]:
+                    j += 1
+                S = min(S, j)
+            if S * block >= MIN_SHARED:
+                out.append((mem, S * block))
+    return out
+
+
+def _check_plan(plan, lens, rows, pt, cm, block=16):
+    """The item list holds exactly the expected items: every sequence's own partitions
+    (after its shared prefix), and for every group ceil(members / cm) shared-prefix items
+    per prefix partition whose sequences are the group's members, each once; partial
+    counts per sequence; items in non-increasing length class.  Returns the groups."""
+    cnt, tasks, seq_np, members = plan
+    lens = np.asarray(lens, dtype=np.int64)
+    groups = _groups(lens, rows, block, cm)
+    sp = {b: S for mem, S in groups for b in mem}
+    own, want_np = [], []
+    for b, L in enumerate(lens):
+        L = int(L)
+        S = sp.get(b, 0)
+        npp = -(-S // pt)
+        full, rem = (L - S) // pt, (L - S) % pt
+        npb = 1 if L == 0 else npp + full + (rem > 0)
+        want_np.append(npb)
+        own += [(b, S + q * pt, pt, npp + q, npb) for q in range(full)]
+        if rem or L == 0:
+            own.append((b, S + full * pt, rem, npp + full, npb))
+    assert np.array_equal(seq_np, want_np)
+    x, tok0, ntok, wv = (tasks[:, i] for i in range(4))
+    is_prefix = (x & PREFIX) != 0
+    got_own = [(int(a), int(t), int(k), int(v & 0xffff), int(v >> 16))
+               for a, t, k, v in zip(x[~is_prefix], tok0[~is_prefix], ntok[~is_prefix], wv[~is_prefix])]
+    assert sorted(got_own) == sorted(own)
+    assert not (x[~is_prefix] & SHARED).any()
+    # shared-prefix items: (group, partition) -> the members its items cover
+    group_of = {b: min(mem) for mem, _ in groups for b in mem}
+    seen = {}
+    for a, t, k, v in zip(x[is_prefix], tok0[is_prefix], ntok[is_prefix], wv[is_prefix]):
+        off, p, nm = int(a) & (PREFIX - 1), int(v) & 0xffff, int(v) >> 16
+        mem = [int(m) for m in members[off:off + nm]]
+        assert 1 <= nm <= cm
+        assert len({group_of.get(m, -1) for m in mem}) == 1 and mem[0] in group_of, "an item mixes groups"
+        seen.setdefault((group_of[mem[0]], p, int(t), int(k), bool(a & SHARED)), []).extend(mem)
+    want = {}
+    for mem, S in groups:
+        ncs = -(-len(mem) // cm)
+        for p in range(-(-S // pt)):
+            want[(min(mem), p, p * pt, min(pt, S - p * pt), ncs > 1)] = sorted(mem)
+    assert {k: sorted(v) for k, v in seen.items()} == want
+    # longest first: classes of pt/64 tokens never increase along the list
+    cls = np.where(ntok > 0, -(-ntok // (pt // 64)), 1)
+    assert (np.diff(cls) <= 0).all(), "classes must not increase along the list"
+    return groups
 
 
 BATCHES = [
@@ -116,145 +211,93 @@ BATCHES = [
 def test_device_choice_matches_host_rule(name, lens_fn, hq, hkv):
     lens = np.asarray(lens_fn(), dtype=np.int64)
     W = max(1, int(-(-lens.max() // 16)))
-    tables = torch.arange(len(lens), dtype=torch.int32, device=DEV).repeat_interleave(W).view(len(lens), W)
-    cnt, tasks, parts = _plan(lens, hq, hkv, tables.contiguous())
+    rows = np.repeat(np.arange(len(lens), dtype=np.int32)[:, None], W, axis=1)
+    plan = _plan(lens, hq, hkv, torch.from_numpy(rows).to(DEV))
     pt = pkv.decode_partition_tokens(lens, hq, hkv)
-    log(f"{name}: host rule {pt}, device log2 {cnt[1]}, {cnt[0]} items")
-    assert 1 << int(cnt[1]) == pt
-    expect = sorted((b * parts + p, int(L)) for b, L in enumerate(lens) for p in range(max(1, -(-int(L) // pt))))
-    assert sorted(map(tuple, _items(tasks).tolist())) == expect
-    assert not (tasks[:, 0] & SHARED).any()  # distinct first blocks: no groups
-
-
-def _group_classes(lens, first, pt):
-    """Tail class of each sequence's group (0: no tail item), the plan's grouping restated:
-    a sequence follows the previous one when both are non-empty, share the first block and
-    lie in the same aligned run of 16."""
-    n = len(lens)
-    cls = np.zeros(n, dtype=np.int64)
-    for b, L in enumerate(lens):
-        rem = int(L) % pt
-        cls[b] = -(-rem // (pt // 64)) if rem else (1 if L == 0 else 0)
-    head = np.ones(n, dtype=bool)
-    for b in range(1, n):
-        head[b] = not (b % 16 and lens[b] > 0 and lens[b - 1] > 0 and first[b] == first[b - 1])
-    groups, g = [], []
-    for b in range(n):
-        if head[b] and g:
-            groups.append(g)
-            g = []
-        g.append(b)
-    groups.append(g)
-    out = np.zeros(n, dtype=np.int64)
-    for g in groups:
-        out[g] = max(cls[g])
-    return out, groups
-
-
-def _check_order(tasks, parts, lens, first, pt):
-    """The task list holds every expected item once, full partitions first (in the top
-    class, with the tails that fill more than 63/64 of a partition), tail items in
-    non-increasing group class, each group's tail items together in sequence order.
-    Items of a group of two or more sequences carry the shared flag, the others not.
-    Returns the groups."""
-    flags = (tasks[:, 0] & SHARED) != 0
-    tasks = _items(tasks)
-    expect = sorted((b * parts + p, int(L)) for b, L in enumerate(lens) for p in range(max(1, -(-int(L) // pt))))
-    assert sorted(map(tuple, tasks.tolist())) == expect
-    gcls, groups = _group_classes(lens, first, pt)
-    size = np.zeros(len(lens), dtype=np.int64)
-    for g in groups:
-        size[g] = len(g)
-    assert np.array_equal(flags, size[tasks[:, 0] // parts] > 1)
-    b_of, p_of = tasks[:, 0] // parts, tasks[:, 0] % parts
-    tail = (p_of == lens[b_of] // pt) & ((lens[b_of] % pt != 0) | (lens[b_of] == 0))
-    key = np.where(tail, gcls[b_of], 64)  # full partitions share the top class with tails of > 63/64 of one
-    assert (np.diff(key) <= 0).all(), "classes must not increase along the list"
-    pos = {int(t): i for i, t in enumerate(tasks[:, 0])}
-    for g in groups:
-        tail_pos = [pos[b * parts + int(lens[b]) // pt] for b in g if lens[b] % pt or lens[b] == 0]
-        if tail_pos:
-            assert tail_pos == list(range(tail_pos[0], tail_pos[0] + len(tail_pos))), (g, tail_pos)
-    return groups
+    log(f"{name}: host rule {pt}, device log2 {plan[0][1]}, {plan[0][0]} items")
+    assert 1 << int(plan[0][1]) == pt
+    assert _check_plan(plan, lens, rows, pt, 16 // (hq // hkv) if 2 <= hq // hkv <= 8 else 0) == []
 
 
 @pytest.mark.parametrize("tokens", [512, 1024, 2048])
-def test_task_list_order_and_shared_prefix_groups(tokens, partition_tokens):
+def test_shared_prefix_groups_of_forked_samples(tokens, partition_tokens):
+    """Copy-on-write samples: each prompt's 4 samples share its first 63 blocks (the
+    tail block was copied for three of them), so every prompt becomes one group with a
+    1008-token prefix and one shared-prefix item per prefix partition."""
     partition_tokens(tokens)
     w = synth.cow_fp16(1020, num_prompts=8, max_suffix=256)
     st = replay_gpu(w, w.all_context_kv(), DEV)
-    tables = st.tables.contiguous()
     lens = st.context_lens.cpu().numpy().astype(np.int64)
-    cnt, tasks, parts = _plan(lens, w.num_q_heads, w.num_kv_heads, tables)
-    assert 1 << int(cnt[1]) == tokens
-    groups = _check_order(tasks, parts, lens, tables[:, 0].cpu().numpy(), tokens)
-    assert len(groups) == 8  # one group per prompt: its 4 samples share the prompt's first block
+    rows = st.tables.cpu().numpy()
+    plan = _plan(lens, w.num_q_heads, w.num_kv_heads, st.tables.contiguous())
+    assert 1 << int(plan[0][1]) == tokens
+    groups = _check_plan(plan, lens, rows, tokens, 4)
+    assert sorted(sorted(m) for m, _ in groups) == [[4 * k + i for i in range(4)] for k in range(8)]
+    assert all(S == 1008 for _, S in groups)
 
 
-def test_plan_groups_only_equal_first_blocks():
-    """Equal first blocks group sequences in aligned runs of 16 (here 3 groups); distinct
-    first blocks leave every sequence on its own (40 groups)."""
-    lens = np.array([100 + 37 * i for i in range(40)], dtype=np.int64)
+def test_groups_form_wherever_members_sit():
+    """The same forked batch with its samples shuffled through the batch gives the same
+    groups (as sets of sequences) and the same prefixes."""
+    w = synth.cow_fp16(1020, num_prompts=8, max_suffix=256)
+    st = replay_gpu(w, w.all_context_kv(), DEV)
+    lens = st.context_lens.cpu().numpy().astype(np.int64)
+    rows = st.tables.cpu().numpy()
+    perm = np.random.default_rng(3).permutation(len(lens))
     pt = pkv.decode_partition_tokens(lens, 32, 8)
-    assert pt == 1024
-    W = int(-(-lens.max() // 16))  # rows wide enough for every context (longer ones are clamped)
-    same = torch.zeros(40, W, dtype=torch.int32, device=DEV)
-    diff = torch.arange(40, dtype=torch.int32, device=DEV).repeat_interleave(W).view(40, W).contiguous()
-    for tables, n_groups in ((same, 3), (diff, 40)):
-        cnt, tasks, parts = _plan(lens, 32, 8, tables)
-        groups = _check_order(tasks, parts, lens, tables[:, 0].cpu().numpy(), pt)
+    ordered = _check_plan(_plan(lens, 32, 8, st.tables.contiguous()), lens, rows, pt, 4)
+    shuffled = _check_plan(_plan(lens[perm], 32, 8, torch.from_numpy(rows[perm]).to(DEV)), lens[perm], rows[perm],
+                           pt, 4)
+    back = sorted((sorted(int(perm[b]) for b in m), S) for m, S in shuffled)
+    assert back == sorted((sorted(m), S) for m, S in ordered)
+
+
+def test_plan_groups_only_equal_leading_blocks():
+    """One first block for all rows: sequences of 256 tokens or more form one group whose
+    prefix is the shortest member's whole blocks (35 members in 9 items of 4); distinct
+    first blocks give no groups, nor do rows that agree on only 160 leading tokens."""
+    lens = np.array([100 + 37 * i for i in range(40)], dtype=np.int64)
+    W = int(-(-lens.max() // 16))
+    pt = pkv.decode_partition_tokens(lens, 32, 8)
+    same = np.zeros((40, W), dtype=np.int32)
+    diff = np.repeat(np.arange(40, dtype=np.int32)[:, None], W, axis=1)
+    early = same.copy()
+    early[:, 10:] = np.arange(40, dtype=np.int32)[:, None]  # rows agree on 10 blocks (160 tokens) only
+    for rows, n_groups in ((same, 1), (diff, 0), (early, 0)):
+        plan = _plan(lens, 32, 8, torch.from_numpy(rows).to(DEV))
+        groups = _check_plan(plan, lens, rows, pt, 4)
         assert len(groups) == n_groups
-    # with one first block: runs 16..31 (largest tail class 62), 0..15 (41), 32..39 (33)
-    cnt, tasks, parts = _plan(lens, 32, 8, same)
-    tasks = _items(tasks)
-    b_of, p_of = tasks[:, 0] // parts, tasks[:, 0] % parts
-    tails = [int(b) for b, p in zip(b_of, p_of) if p == lens[b] // 1024]
-    assert tails == list(range(16, 32)) + list(range(0, 16)) + list(range(32, 40))
-
-
-def _plan_prepare(lens, hq, hkv, tables, d=128, block=16):
-    """The plan as the fused write + plan launch runs it (256 threads; no tokens written)."""
-    n = len(lens)
-    W = tables.shape[1]
-    q = torch.zeros(n, hq, d, dtype=torch.bfloat16, device=DEV)
-    kp, vp = pkv.alloc_pools(1, block, hkv, d, torch.bfloat16, DEV)
-    kv_new = torch.zeros(0, hkv, d, dtype=torch.bfloat16, device=DEV)
-    slots = torch.zeros(0, dtype=torch.int64, device=DEV)
-    ws = pkv.alloc_workspace(n, hq, d, W, block, DEV)
-    lens_d = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(DEV)
-    pkv.decode_prepare(kp, vp, kv_new, kv_new, slots, q, tables, lens_d, ws)
-    torch.cuda.synchronize()
-    cnt = _counters(ws)
-    parts = -(-W * block // pkv.PARTITION_TOKENS_MIN)
-    return cnt, _tasks(ws, n, hq, d, parts, int(cnt[0])), parts
+    g = _groups(lens, same, 16, 4)
+    assert len(g[0][0]) == 35 and g[0][1] == (285 // 16) * 16
 
 
 @pytest.mark.parametrize("seed", range(6))
 def test_task_list_on_random_batches(seed):
-    """Random batches (more sequences than either plan launch has threads, empty
-    contexts, contexts that are whole partitions, runs of shared first blocks that cross
-    the aligned runs of 16) through both plan launches: a valid task list in the order
-    the plan promises, and the partition size of the host rule."""
+    """Random batches (more sequences than either plan launch has threads, several
+    grouping windows, empty contexts, contexts that are whole partitions, groups of
+    sequences with equal leading blocks scattered through the batch, rows that diverge
+    at random places) through both plan launches: the expected items, in the order the
+    plan promises, and the partition size of the host rule."""
     rng = np.random.default_rng(seed)
     n = int(rng.choice([1, 17, 300, 1500]))
     lens = rng.integers(0, 9000, size=n)
     lens[rng.random(n) < 0.05] = 0
     whole = rng.random(n) < 0.05
     lens[whole] = 2048 * rng.integers(1, 4, size=int(whole.sum()))
-    # first blocks: runs of equal ids of random length (1..40), distinct between runs
-    first = np.zeros(n, dtype=np.int64)
-    b, run_id = 0, 0
-    while b < n:
-        k = int(rng.integers(1, 41))
-        first[b:b + k] = run_id
-        b += k
-        run_id += 1
     W = max(1, int(-(-lens.max() // 16)))
-    rows = np.repeat(first[:, None], W, axis=1).astype(np.int32)
+    # rows: a group id per sequence (few groups, scattered), the group's shared entries up
+    # to a random divergence point, then entries of the sequence's own
+    gid = rng.integers(0, max(1, n // 5), size=n)
+    base = rng.integers(0, 1 << 20, size=(int(gid.max()) + 1, W)).astype(np.int32)
+    rows = base[gid].copy()
+    cut = rng.integers(0, W + 1, size=n)
+    own_ids = (np.arange(n, dtype=np.int64)[:, None] * W + np.arange(W)[None, :] + (1 << 21)).astype(np.int32)
+    mask = np.arange(W)[None, :] >= cut[:, None]
+    rows[mask] = own_ids[mask]
     tables = torch.from_numpy(rows).to(DEV)
     pt = pkv.decode_partition_tokens(lens, 32, 8)
-    for run in (_plan, _plan_prepare):
-        cnt, tasks, parts = run(lens, 32, 8, tables)
-        log(f"seed {seed} {run.__name__}: N={n} partition {1 << int(cnt[1])} (rule {pt}), {cnt[0]} items")
-        assert 1 << int(cnt[1]) == pt
-        _check_order(tasks, parts, lens.astype(np.int64), first, pt)
+    for prepare in (False, True):
+        plan = _plan(lens, 32, 8, tables, prepare=prepare)
+        log(f"seed {seed} prepare={prepare}: N={n} partition {1 << int(plan[0][1])} (rule {pt}), {plan[0][0]} items")
+        assert 1 << int(plan[0][1]) == pt
+        _check_plan(plan, lens, rows, pt, 4)
