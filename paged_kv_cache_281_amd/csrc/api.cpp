@@ -135,6 +135,7 @@ AttnCheck check_attention(const char* who, const pkv_pool_desc* pool, const void
   a.seq_np = reinterpret_cast<int*>(ws + L.seq_np);
   a.seq_grp = reinterpret_cast<int*>(ws + L.seq_grp);
   a.members = reinterpret_cast<int*>(ws + L.members);
+  a.member_own = reinterpret_cast<int*>(ws + L.member_own);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;

@@ -166,6 +166,36 @@ __device__ __forceinline__ void pipeline2(int w, int nunits, Buf& A, Load&& load
   }
 }
 
+// The same with a runtime stride: units start, start + stride, ... < nunits.
+template <class Buf, class Load, class Compute>
+__device__ __forceinline__ void pipeline2s(int start, int stride, int nunits, Buf& A, Load&& load,
+                                           Compute&& compute) {
+  const int n = nunits > start ? (nunits - start + stride - 1) / stride : 0;
+  Buf B;
+  int i = 0;
+  for (; i + 2 < n; i += 2) {
+    const int u = start + i * stride;
+    load(u + stride, B);
+    PKV_FENCE();
+    compute(u, A);
+    PKV_FENCE();
+    load(u + 2 * stride, A);
+    PKV_FENCE();
+    compute(u + stride, B);
+    PKV_FENCE();
+  }
+  const int u = start + i * stride;
+  if (n - i == 2) {
+    load(u + stride, B);
+    PKV_FENCE();
+    compute(u, A);
+    PKV_FENCE();
+    compute(u + stride, B);
+  } else if (n - i == 1) {
+    compute(u, A);
+  }
+}
+
 // Block tables.  Flat (Tab = int or uint16_t): entry j of sequence b is
 // tables[b * W + j].  Two-level (Tab = TwoLevel): the sequence's row of the directory,
 // dir[b * (W / LEAF) ..], names for every run of LEAF entries the leaf that holds them,

@@ -72,6 +72,7 @@ struct Params {
   int* seq_np;          // [N]: partial results of each sequence's rows
   int4* seq_grp;        // [N]: shared-prefix group of each sequence (plan pass)
   int* members;         // [N]: the sequences of each shared-prefix group, group by group
+  int* member_own;      // [N]: beside members: each member's own tokens (fused items)
   int N, Hq, Hkv, G, NHG, W, Pmax, Lmax, B;
   float scale_log2;
   int tab_bytes;   // 4 or 2 (flat tables)
@@ -79,6 +80,7 @@ struct Params {
   int slots;       // resident partition workgroups (plan's size choice)
   int force_log2;  // 0, or the partition size fixed by the caller (log2)
   int cm;          // sequences per shared-prefix item (16 / G); below 2: no shared-prefix items
+  int fuse_ok;     // the partition kernel runs fused items (16-token units, one unit per block)
 };
 
 // Work items (int4): x = the sequence (an ordinary item) or the offset of the item's
@@ -92,7 +94,12 @@ constexpr int kPrefixTask = 1 << 29;
 // columns): its K/V loads are cached, so the group's other items, listed next to it,
 // find the shared blocks in L2.
 constexpr int kSharedTask = 1 << 30;
-constexpr int kTaskIndex = kPrefixTask - 1;
+// A shared-prefix item that also computes every member's own tokens (after the prefix):
+// its units are the prefix's, then each member's, and its rows are complete at the end.
+constexpr int kFusedTask = 1 << 28;
+constexpr int kTaskIndex = kFusedTask - 1;
+// Units (16 tokens) of a fused item at most: the prefix and its members' own tokens.
+constexpr int kFusedMaxUnits = 192;
 
 // Context length of sequence b, clamped to what its table can address (longer
 // values break the caller's contract; clamping keeps every access in bounds).
@@ -102,7 +109,7 @@ __device__ __forceinline__ int context_len(const Params& P, int b) { return min(
 // cannot have written (a workspace without a preceding plan pass): such items do
 // nothing, so every access stays inside the buffers.
 struct Item {
-  bool ok, prefix, shared;
+  bool ok, prefix, shared, fused;
   int idx;   // sequence, or offset in the members list
   int tok0, ntok, p;
   int nm;    // sequences whose rows the item computes
@@ -112,6 +119,7 @@ __device__ __forceinline__ Item decode_item(const Params& P, const int4 t, int u
   Item it;
   it.prefix = (t.x & kPrefixTask) != 0;
   it.shared = (t.x & kSharedTask) != 0;
+  it.fused = it.prefix && (t.x & kFusedTask) != 0;
   it.idx = t.x & kTaskIndex;
   it.tok0 = t.y;
   it.ntok = t.z;
@@ -217,14 +225,36 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v,
   return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
 
+// A sequence's shared-prefix group as the plan records it (seq_grp): prefix tokens, the
+// sequence's rank in the group, the group's size, its longest context, and the offset of
+// its members in the members list (-1: no group).
+struct Grp {
+  int sp, rank, cnt, maxl, base;
+};
+__device__ __forceinline__ Grp unpack_grp(int4 r) {
+  return Grp{r.x, r.y & 0xffff, static_cast<int>(static_cast<unsigned>(r.y) >> 16), r.z, r.w};
+}
+__device__ __forceinline__ int4 pack_grp(const Grp& g) { return make_int4(g.sp, g.rank | (g.cnt << 16), g.maxl, g.base); }
+__device__ constexpr Grp kNoGroup = {0, 0, 1, 0, -1};
+
+// Whether a group's items are fused at partition size 2^lg: the prefix fits one partition
+// and, with the own tokens of an item's members (at most maxl - sp each), at most
+// kFusedMaxUnits units.
+__device__ __forceinline__ bool fused_group(const Params& P, const Grp& g, int lg) {
+  if (!P.fuse_ok || g.base < 0 || g.sp > (1 << lg)) return false;
+  const int per = min(P.cm, g.cnt);
+  return (g.sp >> 4) + per * ((g.maxl - g.sp + 15) >> 4) <= kFusedMaxUnits;
+}
+
 // The items of a shared-prefix group's partition-sized pieces: item k of a run covers
 // prefix partition p0 + k / ncs for the group's column set k % ncs.
-__device__ __forceinline__ int4 prefix_task(const Params& P, int4 g, int ncs, int k, int p0, int lg, int ntok) {
+__device__ __forceinline__ int4 prefix_task(const Params& P, const Grp& g, int ncs, int k, int p0, int lg, int ntok,
+                                            bool fused = false) {
   const int p = p0 + k / ncs;
   const int cs = k - (k / ncs) * ncs;
-  const int nm = min(P.cm, g.z - cs * P.cm);
-  const int flag = kPrefixTask | (ncs > 1 ? kSharedTask : 0);
-  return make_int4((g.w + cs * P.cm) | flag, p << lg, ntok, p | (nm << 16));
+  const int nm = min(P.cm, g.cnt - cs * P.cm);
+  const int flag = kPrefixTask | (ncs > 1 ? kSharedTask : 0) | (fused ? kFusedTask : 0);
+  return make_int4((g.base + cs * P.cm) | flag, p << lg, ntok, p | (nm << 16));
 }
 
 __device__ __forceinline__ void plan_body(const Params& P) {
@@ -239,7 +269,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   __shared__ int coop_s[kPlanCoopMax], coop_n[kPlanCoopMax], coop_b[kPlanCoopMax], coop_k[kPlanCoopMax];
   __shared__ int4 coop_g[kPlanCoopMax];
   __shared__ int hkey[kGroupHash], hlead[kGroupHash], hcnt[kGroupHash], hS[kGroupHash], hrank[kGroupHash],
-      hbase[kGroupHash];
+      hbase[kGroupHash], hmaxl[kGroupHash];
   __shared__ int wslot[kGroupWin], wrank[kGroupWin], wscan[kGroupWin], wcap[kGroupWin], wmis[kGroupWin],
       wpre[kGroupWin + 1];
   __shared__ unsigned win_any[kGroupWinWords];
@@ -250,7 +280,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   // batch of at most blockDim sequences is then read once)
   const int L_first = tid < N ? context_len(P, tid) : 0;
   auto len_of = [&](int b) { return b == tid ? L_first : context_len(P, b); };
-  int4 g_first = make_int4(0, 0, 1, -1);  // this thread's first sequence's group, once known
+  Grp g_first = kNoGroup;  // this thread's first sequence's group, once known
   if (tid <= NB) {
     cnt[0][tid] = 0;
     cnt[1][tid] = 0;
@@ -274,6 +304,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
         hcnt[i] = 0;
         hS[i] = 0x7fffffff;
         hrank[i] = 0;
+        hmaxl[i] = 0;
       }
       if (tid == 0) {
         n_scan = 0;
@@ -289,6 +320,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
           if (slot >= 0) {
             atomicMin(&hlead[slot], b);
             atomicAdd(&hcnt[slot], 1);
+            atomicMax(&hmaxl[slot], len_of(b));
           }
         }
         wslot[i] = slot;
@@ -369,12 +401,13 @@ __device__ __forceinline__ void plan_body(const Params& P) {
           const int b = w0 + i;
           const int slot = wslot[i];
           const int rank = wrank[i];
-          int4 g = make_int4(0, 0, 1, -1);  // {shared tokens, rank, members, members offset}
+          Grp g = kNoGroup;
           if (rank >= 0) {
-            g = make_int4(hS[slot] * P.B, rank, hcnt[slot], hbase[slot]);
-            P.members[g.w + rank] = b;
+            g = Grp{hS[slot] * P.B, rank, hcnt[slot], hmaxl[slot], hbase[slot]};
+            P.members[g.base + rank] = b;
+            P.member_own[g.base + rank] = len_of(b) - g.sp;
           }
-          P.seq_grp[b] = g;
+          P.seq_grp[b] = pack_grp(g);
           if (b == tid) g_first = g;
         }
         if (tid == 0) win_any[(w0 / kGroupWin) >> 5] |= 1u << ((w0 / kGroupWin) & 31);
@@ -385,7 +418,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   auto group_of = [&](int b) {
     const int win = b / kGroupWin;
     if (b == tid && tid < kGroupWin) return g_first;  // (sequence tid was this thread's in window 0)
-    return (win_any[win >> 5] >> (win & 31)) & 1u ? P.seq_grp[b] : make_int4(0, 0, 1, -1);
+    return (win_any[win >> 5] >> (win & 31)) & 1u ? unpack_grp(P.seq_grp[b]) : kNoGroup;
   };
 
   // ---- item counts per class at both candidate sizes, total tokens, longest length ----
@@ -395,21 +428,24 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   int lmax = 0;
   for (int b = tid; b < N; b += nt) {
     const int L = len_of(b);
-    const int4 g = group_of(b);
-    const int own = L - g.x;
-    const int ncs = (g.w >= 0 && g.y == 0) ? (g.z + P.cm - 1) / P.cm : 0;  // the group's item writer
+    const Grp g = group_of(b);
+    const int ncs = (g.base >= 0 && g.rank == 0) ? (g.cnt + P.cm - 1) / P.cm : 0;  // the group's item writer
     tokens += static_cast<unsigned long long>(L);  // the size rule counts every sequence's context (as on the host)
     lmax = max(lmax, L);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int lg = c ? lg_hi : lg_lo;
+      const bool fz = fused_group(P, g, lg);
+      const int own = fz ? 0 : L - g.sp;  // (a fused group's own tokens are in its items)
       const int full = own >> lg;
       const int rem = own - (full << lg);
       int nfull = full;
-      if (rem || L == 0) atomicAdd(&cnt[c][item_class(rem, lg)], 1);
-      if (ncs) {
-        const int fp = g.x >> lg;
-        const int rp = g.x - (fp << lg);
+      if ((rem || L == 0) && !fz) atomicAdd(&cnt[c][item_class(rem, lg)], 1);
+      if (ncs && fz) {
+        atomicAdd(&cnt[c][item_class(min(1 << lg, g.sp + min(P.cm, g.cnt) * (g.maxl - g.sp)), lg)], ncs);
+      } else if (ncs) {
+        const int fp = g.sp >> lg;
+        const int rp = g.sp - (fp << lg);
         nfull += fp * ncs;
         if (rp) atomicAdd(&cnt[c][item_class(rp, lg)], ncs);
       }
@@ -452,12 +488,13 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   const int PT = 1 << lg;
   for (int b = tid; b < N; b += nt) {
     const int L = len_of(b);
-    const int4 g = group_of(b);
-    const int npp = g.w >= 0 ? (g.x + PT - 1) >> lg : 0;
-    const int own = L - g.x;
+    const Grp g = group_of(b);
+    const bool fz = fused_group(P, g, lg);
+    const int npp = g.base >= 0 ? (g.sp + PT - 1) >> lg : 0;
+    const int own = fz ? 0 : L - g.sp;
     const int full = own >> lg;
     const int rem = own - (full << lg);
-    const int np = L == 0 ? 1 : npp + full + (rem > 0);
+    const int np = (L == 0 || fz) ? 1 : npp + full + (rem > 0);
     P.seq_np[b] = np;
     if (full) {
       const int st = atomicAdd(&off[NB], full);
@@ -467,19 +504,24 @@ __device__ __forceinline__ void plan_body(const Params& P) {
         coop_n[k] = full;
         coop_b[k] = b;
         coop_k[k] = 0;
-        coop_g[k] = make_int4(g.x, npp, np, 0);
+        coop_g[k] = make_int4(g.sp, npp, np, 0);
       } else {
-        for (int q = 0; q < full; ++q) P.tasks[st + q] = make_int4(b, g.x + (q << lg), PT, (npp + q) | (np << 16));
+        for (int q = 0; q < full; ++q) P.tasks[st + q] = make_int4(b, g.sp + (q << lg), PT, (npp + q) | (np << 16));
       }
     }
-    if (rem || L == 0) {
+    if ((rem || L == 0) && !fz) {
       const int pos = atomicAdd(&off[item_class(rem, lg)], 1);
-      P.tasks[pos] = make_int4(b, g.x + (full << lg), rem, (npp + full) | (np << 16));
+      P.tasks[pos] = make_int4(b, g.sp + (full << lg), rem, (npp + full) | (np << 16));
     }
-    if (g.w >= 0 && g.y == 0) {  // the group's shared-prefix items
-      const int ncs = (g.z + P.cm - 1) / P.cm;
-      const int fp = g.x >> lg;
-      const int rp = g.x - (fp << lg);
+    if (g.base >= 0 && g.rank == 0 && fz) {  // the group's fused items, one per column set
+      const int ncs = (g.cnt + P.cm - 1) / P.cm;
+      const int cls = item_class(min(PT, g.sp + min(P.cm, g.cnt) * (g.maxl - g.sp)), lg);
+      const int st = atomicAdd(&off[cls], ncs);
+      for (int q = 0; q < ncs; ++q) P.tasks[st + q] = prefix_task(P, g, ncs, q, 0, lg, g.sp, true);
+    } else if (g.base >= 0 && g.rank == 0) {  // the group's shared-prefix items
+      const int ncs = (g.cnt + P.cm - 1) / P.cm;
+      const int fp = g.sp >> lg;
+      const int rp = g.sp - (fp << lg);
       if (fp) {
         const int n = fp * ncs;
         const int st = atomicAdd(&off[NB], n);
@@ -489,7 +531,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
           coop_n[k] = n;
           coop_b[k] = ncs;
           coop_k[k] = 1;
-          coop_g[k] = g;
+          coop_g[k] = pack_grp(g);
         } else {
           for (int q = 0; q < n; ++q) P.tasks[st + q] = prefix_task(P, g, ncs, q, 0, lg, PT);
         }
@@ -505,7 +547,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   for (int k = 0; k < nc; ++k) {
     const int4 g = coop_g[k];
     for (int q = tid; q < coop_n[k]; q += nt) {
-      P.tasks[coop_s[k] + q] = coop_k[k] ? prefix_task(P, g, coop_b[k], q, 0, lg, PT)
+      P.tasks[coop_s[k] + q] = coop_k[k] ? prefix_task(P, unpack_grp(g), coop_b[k], q, 0, lg, PT)
                                          : make_int4(coop_b[k], g.x + (q << lg), PT, (g.y + q) | (g.z << 16));
     }
   }
@@ -764,10 +806,21 @@ __device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, 
   __syncthreads();
 }
 
+// (max, sum) of partial i of a row as one 8-byte device-scope load (the pair's two
+// stores have completed before the row's count reaches its last partition).
+__device__ __forceinline__ float2 load_ml(const float* ml, int i) {
+  const unsigned long long v = __hip_atomic_load(
+      reinterpret_cast<unsigned long long*>(const_cast<float*>(ml) + 2 * i), __ATOMIC_RELAXED,
+      __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<unsigned>(v)), __uint_as_float(static_cast<unsigned>(v >> 32)));
+}
+
 // Merge of the rows row0 .. row0 + nrows - 1 (each of np <= kFuseMaxParts partials,
 // stored by workgroups of the running kernel) by the calling workgroup, one thread per
 // output element: M = max_p m_p, w_p = exp2(m_p - M) * l_p, out = sum_p w_p o_p / sum_p w_p,
-// summed in partition order.  No barrier: each element is independent.
+// summed in partition order.  No barrier: each element is independent.  The loads of
+// up to kMergeBatch partials are issued together (one round trip for short rows).
+constexpr int kMergeBatch = 8;
 template <class T, int D>
 __device__ __forceinline__ void merge_rows_fused(const Params& P, int64_t row0, int nrows, int np) {
   typedef typename T::Bits Bits;
@@ -777,13 +830,37 @@ __device__ __forceinline__ void merge_rows_fused(const Params& P, int64_t row0, 
     const int64_t row = row0 + g;
     const float* ml = P.ws_ml + row * P.Pmax * 2;
     const float* po = P.ws_o + row * P.Pmax * D + d;
+    float2 v[kMergeBatch];
+    float o[kMergeBatch];
     float M = kNegInf;
-    for (int i = 0; i < np; ++i) M = fmaxf(M, load_device(&ml[2 * i]));
+    if (np > kMergeBatch) {
+      for (int i0 = 0; i0 < np; i0 += kMergeBatch) {
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) v[k] = load_ml(ml, min(i0 + k, np - 1));
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) M = fmaxf(M, v[k].x);
+      }
+    }
     float num = 0.f, den = 0.f;
-    for (int i = 0; i < np; ++i) {
-      const float w = fast_exp2(load_device(&ml[2 * i]) - M) * load_device(&ml[2 * i + 1]);
-      num += w * load_device(&po[static_cast<int64_t>(i) * D]);
-      den += w;
+    for (int i0 = 0; i0 < np; i0 += kMergeBatch) {
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const int i = min(i0 + k, np - 1);
+        v[k] = load_ml(ml, i);
+        o[k] = load_device(&po[static_cast<int64_t>(i) * D]);
+      }
+      if (np <= kMergeBatch) {
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) M = fmaxf(M, v[k].x);
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        if (i0 + k < np) {
+          const float w = fast_exp2(v[k].x - M) * v[k].y;
+          num = fmaf(w, o[k], num);
+          den += w;
+        }
+      }
     }
     reinterpret_cast<Bits*>(P.out)[row * D + d] = T::from_float(num / den);
   }
@@ -872,7 +949,12 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   };
 
   constexpr int C = 16;  // columns of the products
-  __shared__ int s_tab[BPP_MAX];
+  constexpr int TABN = BPP_MAX > kFusedMaxUnits ? BPP_MAX : kFusedMaxUnits;
+  __shared__ int s_tab[TABN];
+  // fused items: per unit, its valid tokens | (1 + the member whose own tokens it holds) << 8,
+  // and each wave's units in the order it takes them
+  __shared__ int s_uinfo[kFusedMaxUnits];
+  __shared__ int s_wlist[kWaves][kFusedMaxUnits];
   __shared__ float s_m[kWaves][C];
   __shared__ float s_l[kWaves][C];
   __shared__ float s_o[kWaves][C][D + 4];
@@ -888,6 +970,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int gcur = min(16, P.G - hg * 16);
   const Item it = decode_item(P, P.tasks[t], 16, gcur);
   if (!it.ok) return;  // only an item list left by the plan pass is valid
+  if (it.fused && (SUB != 1 || it.tok0 != 0 || it.ntok % 16 != 0)) return;  // (fused items: one unit per block)
   if (it.ntok == 0) {
     if (!it.prefix && it.p == 0) zero_rows<T, D>(P, it.idx, hq0, gcur);
     return;
@@ -903,8 +986,35 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int m = lane & 15;
   const int ntok = it.ntok;
   const int pe = it.tok0 / B;  // the item's first table entry
-  const int nunits = (ntok + 15) >> 4;
+  int nunits = (ntok + 15) >> 4;
   const int nblk = (ntok + B - 1) / B;
+  // A fused item's units: the prefix's (ntok tokens), then each member's own tokens.
+  // Member k's own units start at fstart[k] (lane k of every wave holds its values).
+  int f_own = 0, f_seq = 0, f_start = 0, f_units = 0;
+  int wunits = nunits > w ? (nunits - w + kWaves - 1) / kWaves : 0;  // units this wave takes
+  // a member's own unit j goes to wave j % kWaves (and the prefix's unit u to u % kWaves),
+  // so every column meets its units in the same waves and order whatever the other members
+  auto wave_share = [](int n, int wv) { return n > wv ? (n - wv + kWaves - 1) / kWaves : 0; };
+  if (it.fused) {
+    const int k = min(lane, it.nm - 1);
+    f_seq = min(max(P.members[it.idx + k], 0), P.N - 1);
+    f_own = min(max(P.member_own[it.idx + k], 0), P.Lmax - ntok);
+    f_units = lane < it.nm ? (f_own + 15) >> 4 : 0;
+    // exclusive scan of the members' own units over lanes (nm <= 16)
+    int v = f_units;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int o2 = __shfl_up(v, d, 64);
+      v += (lane & 63) >= d ? o2 : 0;
+    }
+    f_start = nunits + v - f_units;
+    const int total = __shfl(f_start + f_units, it.nm - 1, 64);
+    int mine = wave_share(f_units, w);
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) mine += __shfl_xor(mine, d, 64);
+    wunits = total > kFusedMaxUnits ? 0 : wave_share(nunits, w) + __shfl(mine, 0, 64);
+    nunits = min(total, kFusedMaxUnits);
+  }
 
   // Preamble: issue every load first (the partition's table entries and the queries,
   // then the first unit's block id and its K/V), write LDS afterwards; vmcnt counts
@@ -949,11 +1059,42 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     }
   };
   // `shared` is uniform over the workgroup: one scalar branch per unit picks the flavour
-  auto load = [&](int u, Buf& f) {
+  // the unit of this wave's i-th step
+  auto unit_of = [&](int i) { return it.fused ? __builtin_amdgcn_readfirstlane(s_wlist[w][i]) : w + kWaves * i; };
+  auto load = [&](int i, Buf& f) {
+    const int u = unit_of(i);
     const int blk = __builtin_amdgcn_readfirstlane(s_tab[u / SUB]);
     if (shared) load_blk(Cached{}, u, blk, f);
     else load_blk(Streamed{}, u, blk, f);
   };
+  // a fused item's units after the prefix: thread u stages unit u (its block id and its
+  // valid tokens | member), loaded before the first unit's K/V so the LDS writes wait
+  // only for these table loads
+  static_assert(kFusedMaxUnits <= kThreads, "one thread stages each unit of a fused item");
+  int f_tab = 0, f_info = 16, f_wave = tid % kWaves, f_pos = tid / kWaves;
+  if (it.fused) {
+    int k = 0;
+    for (int q = 1; q < it.nm; ++q) k = tid >= __shfl(f_start, q, 64) ? q : k;
+    const int j = tid - __shfl(f_start, k, 64);
+    const int seq_k = __shfl(f_seq, k, 64);
+    const int own_k = __shfl(f_own, k, 64);
+    // unit j of member k: in wave j % kWaves, after that wave's prefix units and its
+    // units of members 0 .. k-1 (the shuffles run in every lane)
+    const int jw = j % kWaves;
+    int before = wave_share(nblk, jw) + j / kWaves;
+    for (int q = 0; q < it.nm; ++q) {
+      const int uq = __shfl(f_units, q, 64);
+      before += q < k ? wave_share(uq, jw) : 0;
+    }
+    if (tid >= nblk) {
+      f_wave = jw;
+      f_pos = before;
+    }
+    if (tid >= nblk && tid < nunits) {
+      f_tab = static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, seq_k, P.W, nblk + j));
+      f_info = min(16, own_k - 16 * j) | ((k + 1) << 8);
+    }
+  }
   // the wave's first unit takes its block id straight from the table (a scalar load);
   // a wave without units loads unit 0 (unused) so the load stays unconditional
   Buf first;
@@ -965,6 +1106,11 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   }
   PKV_FENCE();
   if (tid < nblk) s_tab[tid] = tab_val;
+  if (it.fused && tid < nunits) {
+    if (tid >= nblk) s_tab[tid] = f_tab;
+    s_uinfo[tid] = f_info;
+    s_wlist[f_wave][f_pos] = tid;
+  }
 #ifdef PKV_Q_IN_LDS
   // query fragments live in LDS (lane-major, conflict-free) and are re-read per unit
   __shared__ u32x4 s_q[KI][64];
@@ -975,13 +1121,15 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
 #endif
   __syncthreads();
 
+  const int mcol = m / gcur;  // the member of this lane's column
   float m_run = kNegInf;
   float l_part = 0.f;
   f32x4 o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int u, Buf& f) {
+  auto compute = [&](int i, Buf& f) {
+    const int u = unit_of(i);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ki = 0; ki < KI; ++ki) {
@@ -993,14 +1141,23 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     }
     float s0 = acc[0] * P.scale_log2, s1 = acc[1] * P.scale_log2;
     float s2 = acc[2] * P.scale_log2, s3 = acc[3] * P.scale_log2;
-    if (16 * u + 16 > ntok) {
-      const int t0 = 16 * u + 4 * r;
-      s0 = (t0 + 0 < ntok) ? s0 : kNegInf;
-      s1 = (t0 + 1 < ntok) ? s1 : kNegInf;
-      s2 = (t0 + 2 < ntok) ? s2 : kNegInf;
-      s3 = (t0 + 3 < ntok) ? s3 : kNegInf;
-      const u32 mlo = (t0 + 0 < ntok ? 0x0000ffffu : 0u) | (t0 + 1 < ntok ? 0xffff0000u : 0u);
-      const u32 mhi = (t0 + 2 < ntok ? 0x0000ffffu : 0u) | (t0 + 3 < ntok ? 0xffff0000u : 0u);
+    // valid tokens of the unit; a fused item's member unit also masks the other members' columns
+    int valid = ntok - 16 * u;
+    int seg = 0;
+    if (it.fused) {
+      const int info = __builtin_amdgcn_readfirstlane(s_uinfo[u]);
+      valid = info & 0xff;
+      seg = info >> 8;
+    }
+    if (valid < 16 || seg) {
+      const int t0 = 4 * r;
+      const bool colok = seg == 0 || mcol == seg - 1;
+      s0 = (colok && t0 + 0 < valid) ? s0 : kNegInf;
+      s1 = (colok && t0 + 1 < valid) ? s1 : kNegInf;
+      s2 = (colok && t0 + 2 < valid) ? s2 : kNegInf;
+      s3 = (colok && t0 + 3 < valid) ? s3 : kNegInf;
+      const u32 mlo = (t0 + 0 < valid ? 0x0000ffffu : 0u) | (t0 + 1 < valid ? 0xffff0000u : 0u);
+      const u32 mhi = (t0 + 2 < valid ? 0x0000ffffu : 0u) | (t0 + 3 < valid ? 0xffff0000u : 0u);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         f.v[c][0] &= mlo;
@@ -1010,13 +1167,15 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     float mx = fmaxf(fmaxf(s0, s1), fmaxf(s2, s3));
     mx = max_xor16(mx);
     mx = max_xor32(mx);
+    // each column (lane m of every row) decides its own rescale, so no column's result
+    // depends on the other columns of the product
     if (wave_any(mx > m_run + kRescaleLog2)) {
-      const float mn = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - mn);
+      const bool raise = mx > m_run + kRescaleLog2;
+      const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;
       l_part *= alpha;
 #pragma unroll
       for (int c = 0; c < NC; ++c) o[c] *= alpha;
-      m_run = mn;
+      m_run = raise ? mx : m_run;
     }
     const u32 p01 = T::pack2(fast_exp2(s0 - m_run), fast_exp2(s1 - m_run));
     const u32 p23 = T::pack2(fast_exp2(s2 - m_run), fast_exp2(s3 - m_run));
@@ -1026,7 +1185,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     for (int c = 0; c < NC; ++c) o[c] = T::mfma_k16(f.v[c], pb, o[c]);
   };
 
-  pipeline<kWaves, Buf>(w, nunits, first, load, compute);
+  pipeline2s(0, 1, wunits, first, load, compute);
 
   float l = sum_xor16(l_part);
   l = sum_xor32(l);
@@ -1087,7 +1246,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int hq0 = kvh * P.G + hg * 16;
   const int gcur = min(16, P.G - hg * 16);
   const Item it = decode_item(P, P.tasks[t], 32, gcur);
-  if (!it.ok) return;  // only an item list left by the plan pass is valid
+  if (!it.ok || it.fused) return;  // only an item list left by the plan pass is valid (no fused items here)
   if (it.ntok == 0) {
     if (!it.prefix && it.p == 0) zero_rows<T, D>(P, it.idx, hq0, gcur);
     return;
@@ -1236,13 +1395,15 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = max_xor16(mx);
     mx = max_xor32(mx);
+    // each column (lane m of every row) decides its own rescale, so no column's result
+    // depends on the other columns of the product
     if (wave_any(mx > m_run + kRescaleLog2)) {
-      const float mn = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - mn);
+      const bool raise = mx > m_run + kRescaleLog2;
+      const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;
       l_part *= alpha;
 #pragma unroll
       for (int c = 0; c < NC; ++c) o[c] *= alpha;
-      m_run = mn;
+      m_run = raise ? mx : m_run;
     }
     u32x4 pb;
 #pragma unroll
@@ -1498,6 +1659,16 @@ __global__ __launch_bounds__(kThreads) void attn_merge_long(Params P) {
   merge_row<T, D>(P, static_cast<int64_t>(b) * P.Hq + hq, np, s_merge);
 }
 
+// Which MFMA kernel a block size uses: 32-token units or 16-token units.
+#ifndef PKV_UNIT32_B16
+#define PKV_UNIT32_B16 0
+#endif
+#ifndef PKV_UNIT32_B32
+#define PKV_UNIT32_B32 1
+#endif
+template <int B>
+constexpr bool kUnit32 = (B == 16) ? PKV_UNIT32_B16 != 0 : PKV_UNIT32_B32 != 0;
+
 Params make_params(const AttnArgs& a) {
   Params P;
   P.q = static_cast<const char*>(a.q);
@@ -1532,18 +1703,11 @@ Params make_params(const AttnArgs& a) {
   // shared-prefix items need the MFMA kernels (16-bit pools, 2..16 query heads per kv
   // head) and at least two sequences per item
   P.cm = (a.dtype != PKV_F32 && P.G >= 2 && P.G <= 8) ? 16 / P.G : 0;
+  P.fuse_ok = (P.cm >= 2 && a.block_size == 16 && !kUnit32<16>) ? 1 : 0;
+  P.member_own = a.member_own;
   return P;
 }
 
-// Which MFMA kernel a block size uses: 32-token units or 16-token units.
-#ifndef PKV_UNIT32_B16
-#define PKV_UNIT32_B16 0
-#endif
-#ifndef PKV_UNIT32_B32
-#define PKV_UNIT32_B32 1
-#endif
-template <int B>
-constexpr bool kUnit32 = (B == 16) ? PKV_UNIT32_B16 != 0 : PKV_UNIT32_B32 != 0;
 
 template <class T, int D, int B, class Tab>
 int launch_partitions_t(const AttnArgs& a, hipStream_t s) {

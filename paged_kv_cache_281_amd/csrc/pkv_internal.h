@@ -60,6 +60,7 @@ struct AttnArgs {
   int* seq_np;   // [num_seqs]: partial results of each sequence's rows
   int* seq_grp;  // [num_seqs] x 4 ints: the plan's shared-prefix group of each sequence
   int* members;  // [num_seqs]: sequences of each shared-prefix group, group by group
+  int* member_own;  // [num_seqs]: beside members, each member's own tokens
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
   int32_t max_blocks_per_seq, max_parts;
   int32_t table_bytes;  // 4 (int32 entries) or 2 (uint16 entries)
@@ -103,7 +104,7 @@ int32_t set_forced_partition_log2(int32_t log2_tokens);
 
 // Byte offsets of the workspace regions (each 256-byte aligned) and the total size.
 struct WorkspaceLayout {
-  size_t o, ml, tasks, done, seq_np, seq_grp, members, counters, total;
+  size_t o, ml, tasks, done, seq_np, seq_grp, members, member_own, counters, total;
 };
 inline WorkspaceLayout workspace_layout(int64_t n, int64_t hq, int64_t d, int64_t parts) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -115,7 +116,8 @@ inline WorkspaceLayout workspace_layout(int64_t n, int64_t hq, int64_t d, int64_
   w.seq_np = w.done + al(static_cast<size_t>(n * hq) * sizeof(int32_t));
   w.seq_grp = w.seq_np + al(static_cast<size_t>(n) * sizeof(int32_t));
   w.members = w.seq_grp + al(static_cast<size_t>(n) * 4 * sizeof(int32_t));
-  w.counters = w.members + al(static_cast<size_t>(n) * sizeof(int32_t));
+  w.member_own = w.members + al(static_cast<size_t>(n) * sizeof(int32_t));
+  w.counters = w.member_own + al(static_cast<size_t>(n) * sizeof(int32_t));
   w.total = w.counters + 256;
   return w;
 }

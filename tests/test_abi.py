@@ -35,13 +35,13 @@ def test_workspace_and_pool_sizes(pkv_lib):
     # partial outputs (8 sequences x 32 heads x 257 slots x 128 floats: 512-token
     # partitions of 131072 tokens, plus one for a split at the end of a shared prefix),
     # (max, sum) pairs, the item list (4 ints an item), per-row counters, per-sequence
-    # partial counts, group records (4 ints) and members, and a counter block, each
-    # 256-byte aligned
+    # partial counts, group records (4 ints), members and their own tokens, and a
+    # counter block, each 256-byte aligned
     n = lib.pkv_paged_attention_workspace_bytes(8, 32, 128, 8192, 16)
     parts = 8192 * 16 // 512 + 1
     al = lambda x: (x + 255) // 256 * 256
     assert n == (al(8 * 32 * parts * 128 * 4) + al(8 * 32 * parts * 2 * 4) + al(8 * parts * 16) + al(8 * 32 * 4)
-                 + al(8 * 4) + al(8 * 16) + al(8 * 4) + 256)
+                 + al(8 * 4) + al(8 * 16) + al(8 * 4) + al(8 * 4) + 256)
     assert lib.pkv_paged_attention_workspace_bytes(-1, 32, 128, 8, 16) == 0
     d = pkv_lib.PoolDesc(65536, 16, 8, 128, 2)
     assert lib.pkv_pool_bytes(ctypes.byref(d)) == 2 * 2 ** 30

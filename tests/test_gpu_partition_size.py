@@ -67,6 +67,8 @@ def _counters(ws: torch.Tensor) -> np.ndarray:
     return ws[-256:].view(torch.int32)[:2].cpu().numpy()
 
 
+FUSED = 1 << 28  # item flag: a shared-prefix item that also computes its members' own tokens
+FUSED_MAX_UNITS = 192  # 16-token units of a fused item at most
 PREFIX = 1 << 29  # item flag: a shared-prefix item (x holds the offset of its sequences)
 SHARED = 1 << 30  # item flag: cached K/V loads (a group that needs several items)
 MIN_SHARED = 256  # shortest shared prefix given shared-prefix items
@@ -83,16 +85,17 @@ def _regions(n, hq, d, parts):
     r["seq_np"] = r["done"] + al(n * hq * 4)
     r["seq_grp"] = r["seq_np"] + al(n * 4)
     r["members"] = r["seq_grp"] + al(n * 16)
+    r["member_own"] = r["members"] + al(n * 4)
     return r
 
 
 def _read_plan(ws, n, hq, d, parts):
-    """(counters, items [count, 4], partial count per sequence, members list)."""
+    """(counters, items [count, 4], partial count per sequence, members list, their own tokens)."""
     cnt = _counters(ws)
     r = _regions(n, hq, d, parts)
     i32 = lambda off, k: ws[off:off + 4 * k].view(torch.int32).cpu().numpy()
     tasks = i32(r["tasks"], 4 * int(cnt[0])).reshape(-1, 4)
-    return cnt, tasks, i32(r["seq_np"], n), i32(r["members"], n)
+    return cnt, tasks, i32(r["seq_np"], n), i32(r["members"], n), i32(r["member_own"], n)
 
 
 def _plan(lens, hq, hkv, tables, d=128, block=16, prepare=False):
@@ -146,19 +149,34 @@ def _groups(lens, rows, block, cm):
     return out
 
 
+def _fused(mem, S, lens, pt, cm, block):
+    """A group whose items also compute its members' own tokens: block 16, the prefix in
+    one partition, and the prefix plus min(cm, members) members of the group's longest
+    context in at most FUSED_MAX_UNITS units."""
+    per = min(cm, len(mem))
+    maxl = max(int(lens[b]) for b in mem)
+    return block == 16 and S <= pt and S // 16 + per * (-(-(maxl - S) // 16)) <= FUSED_MAX_UNITS
+
+
 def _check_plan(plan, lens, rows, pt, cm, block=16):
     """The item list holds exactly the expected items: every sequence's own partitions
     (after its shared prefix), and for every group ceil(members / cm) shared-prefix items
-    per prefix partition whose sequences are the group's members, each once; partial
-    counts per sequence; items in non-increasing length class.  Returns the groups."""
-    cnt, tasks, seq_np, members = plan
+    per prefix partition whose sequences are the group's members, each once (a fused
+    group: one item per column set that also holds its members' own tokens, and no own
+    items); partial counts per sequence; items in non-increasing length class.  Returns
+    the groups."""
+    cnt, tasks, seq_np, members, member_own = plan
     lens = np.asarray(lens, dtype=np.int64)
     groups = _groups(lens, rows, block, cm)
     sp = {b: S for mem, S in groups for b in mem}
+    fused = {b for mem, S in groups if _fused(mem, S, lens, pt, cm, block) for b in mem}
     own, want_np = [], []
     for b, L in enumerate(lens):
         L = int(L)
         S = sp.get(b, 0)
+        if b in fused:
+            want_np.append(1)
+            continue
         npp = -(-S // pt)
         full, rem = (L - S) // pt, (L - S) % pt
         npb = 1 if L == 0 else npp + full + (rem > 0)
@@ -177,19 +195,32 @@ def _check_plan(plan, lens, rows, pt, cm, block=16):
     group_of = {b: min(mem) for mem, _ in groups for b in mem}
     seen = {}
     for a, t, k, v in zip(x[is_prefix], tok0[is_prefix], ntok[is_prefix], wv[is_prefix]):
-        off, p, nm = int(a) & (PREFIX - 1), int(v) & 0xffff, int(v) >> 16
+        off, p, nm = int(a) & (FUSED - 1), int(v) & 0xffff, int(v) >> 16
         mem = [int(m) for m in members[off:off + nm]]
         assert 1 <= nm <= cm
         assert len({group_of.get(m, -1) for m in mem}) == 1 and mem[0] in group_of, "an item mixes groups"
-        seen.setdefault((group_of[mem[0]], p, int(t), int(k), bool(a & SHARED)), []).extend(mem)
+        if a & FUSED:  # the members' own tokens, beside their ids
+            assert [int(o) for o in member_own[off:off + nm]] == [int(lens[m]) - sp[m] for m in mem]
+        seen.setdefault((group_of[mem[0]], p, int(t), int(k), bool(a & SHARED), bool(a & FUSED)), []).extend(mem)
     want = {}
     for mem, S in groups:
         ncs = -(-len(mem) // cm)
+        if _fused(mem, S, lens, pt, cm, block):
+            want[(min(mem), 0, 0, S, ncs > 1, True)] = sorted(mem)
+            continue
         for p in range(-(-S // pt)):
-            want[(min(mem), p, p * pt, min(pt, S - p * pt), ncs > 1)] = sorted(mem)
+            want[(min(mem), p, p * pt, min(pt, S - p * pt), ncs > 1, False)] = sorted(mem)
     assert {k: sorted(v) for k, v in seen.items()} == want
-    # longest first: classes of pt/64 tokens never increase along the list
-    cls = np.where(ntok > 0, -(-ntok // (pt // 64)), 1)
+    # longest first: classes of pt/64 tokens never increase along the list (a fused item
+    # is classed by its prefix plus its members' longest own tokens, at most a partition)
+    size = ntok.astype(np.int64).copy()
+    for i, (a, v) in enumerate(zip(x, wv)):
+        if a & FUSED:
+            mem = [int(m) for m in members[int(a) & (FUSED - 1):][:int(v) >> 16]]
+            S = sp[mem[0]]
+            g = next(g for g, _ in groups if mem[0] in g)
+            size[i] = min(pt, S + min(cm, len(g)) * (max(int(lens[b]) for b in g) - S))
+    cls = np.where(size > 0, -(-size // (pt // 64)), 1)
     assert (np.diff(cls) <= 0).all(), "classes must not increase along the list"
     return groups
 
