@@ -217,4 +217,21 @@ __device__ __forceinline__ const typename TabEntry<Tab>::type* table_row(const v
   }
 }
 
+// Entry e of sequence b's table loaded through the scalar cache (b and e must be
+// uniform over the wave): 32-bit entries (flat int32 or two-level) are read from the
+// constant address space, so the load is counted apart from the vector-memory loads in
+// flight; 16-bit entries use an ordinary load.
+template <class Tab, int LEAF>
+__device__ __forceinline__ int table_entry_uniform(const void* tables, const int* dir, int b, int W, int e) {
+  typedef const __attribute__((address_space(4))) int* cint;
+  if constexpr (std::is_same<Tab, TwoLevel>::value) {
+    const int leaf = ((cint)(dir))[static_cast<int64_t>(b) * (W / LEAF) + e / LEAF];
+    return ((cint)(static_cast<const int*>(tables)))[static_cast<int64_t>(leaf) * LEAF + e % LEAF];
+  } else if constexpr (std::is_same<Tab, int>::value) {
+    return ((cint)(static_cast<const int*>(tables)))[static_cast<int64_t>(b) * W + e];
+  } else {
+    return static_cast<int>(*table_row<Tab, LEAF>(tables, dir, b, W, e));
+  }
+}
+
 }  // namespace pkv

@@ -50,7 +50,7 @@ constexpr float kPfRescaleLog2 = 8.f;  // lazy rescale threshold (log2 units)
 // Row groups (16 rows each) per wave: kRGBig when the chunks fill whole workgroup
 // tiles, 1 for short chunks (fewer idle rows).
 #ifndef PKV_PREFILL_RG_BIG
-#define PKV_PREFILL_RG_BIG 2
+#define PKV_PREFILL_RG_BIG 3
 #endif
 constexpr int kRGBig = PKV_PREFILL_RG_BIG;
 constexpr int kRGSmall = 1;
@@ -157,22 +157,29 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan(PrefillParams P) {
   });
 }
 
-// The 4 waves of a workgroup share each 32-token K/V unit.  All
-// 256 threads copy the next unit from the pool into an LDS double buffer (its global
-// loads are issued before the current unit is computed), one barrier per unit.  K is
-// stored as [chunk][half s][m] 16-byte pieces, where slot (s, m) holds token tau_s(m),
-// so the 16 lanes of a fragment read touch 256 contiguous bytes; V rows (32 tokens,
-// 64 bytes) are padded to 80 bytes so the 16 rows of a fragment read fall in distinct
-// banks.  Each wave reads its fragments for the unit once and uses them for all RG of
-// its 16-row groups.
+// The 4 waves of a workgroup share each 32-token K/V unit.  The unit is copied from
+// the pool straight into LDS (global_load_lds: every lane moves 16 bytes to its place in
+// a 1 KiB run), in a ring of kPfStages buffers: unit u + 2 is in flight while unit u is
+// computed, and one barrier per unit both publishes unit u + 1 and frees the buffer of
+// unit u - 1.  K is stored as [chunk][half s][m] 16-byte pieces, where slot (s, m)
+// holds token tau_s(m), so the 16 lanes of a fragment read touch 256 contiguous bytes;
+// a V row (32 tokens, 64 bytes) holds its four 16-byte pieces in the order
+// q ^ ((row / 4) % 4), so the 16 rows of a fragment read fall in distinct banks.  Each
+// wave reads a fragment just before the products that use it, once for all RG of its
+// 16-row groups.
 template <int D>
-struct PrefillSmem {
-  static constexpr int kChunks = D / 8;  // 16-byte K chunks per token
-  static constexpr int kVRow = 80;       // bytes per padded V row
-  static constexpr int kKBytes = kChunks * 32 * 16;
-  static constexpr int kBytes = kKBytes + D * kVRow;
-  char buf[2][kBytes];
+struct PrefillLds {
+  static constexpr int kKPieces = D / 8 * 32;  // 16-byte K pieces per unit
+  static constexpr int kVPieces = D * 4;       // 16-byte V pieces per unit
+  static constexpr int kKBytes = kKPieces * 16;
+  static constexpr int kBytes = (kKPieces + kVPieces) * 16;
+  static constexpr int kRuns = (kKPieces + kVPieces) / 64;  // 64-piece runs (one load instruction each)
 };
+constexpr int kPfStages = 3;
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt at their maxima)
+constexpr int vmcnt_only(int n) { return (n & 0xf) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xf << 8); }
 
 template <class T, int D, int B, int RG, class Tab>
 __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) {
@@ -182,17 +189,14 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
   constexpr int NC = D / 16;
   constexpr int BPU = 32 / B;
   constexpr int ROWS = 16 * RG * kPfWaves;
-  constexpr int CH = PrefillSmem<D>::kChunks;
-  constexpr int VROW = PrefillSmem<D>::kVRow;
-  constexpr int KB = PrefillSmem<D>::kKBytes;
-  constexpr int KPIECES = CH * 32;   // 16-byte K pieces per unit
-  constexpr int VPIECES = D * 4;     // 16-byte V pieces per unit
-  constexpr int KPT = KPIECES / kPfThreads;  // per thread
-  constexpr int VPT = VPIECES / kPfThreads;
-  static_assert(KPIECES % kPfThreads == 0 && VPIECES % kPfThreads == 0, "pieces must divide evenly");
+  constexpr int KB = PrefillLds<D>::kKBytes;
+  constexpr int KRUNS = PrefillLds<D>::kKPieces / 64;
+  constexpr int RUNS = PrefillLds<D>::kRuns;
+  constexpr int NX = RUNS / kPfWaves;  // load instructions per thread per unit
+  static_assert(RUNS % kPfWaves == 0 && KRUNS % kPfWaves == 0, "runs must divide over the waves");
   constexpr int64_t TILE = static_cast<int64_t>(B) * D * EB;
   typedef typename T::Bits Bits;
-  __shared__ PrefillSmem<D> sm;
+  __shared__ __align__(16) char s_kv[kPfStages][PrefillLds<D>::kBytes];
 
   // task t = blockIdx / Hkv from the plan's list (longest first); KV heads vary
   // fastest, so with 8 KV heads each XCD serves one head's K/V from its L2
@@ -242,59 +246,50 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     for (int ki = 0; ki < KI; ++ki) qf[k][ki] = *reinterpret_cast<const u32x4*>(qrow + (4 * ki + r) * 16);
   }
 
-  // this thread's pieces of every unit: K piece i = tid + 256 x -> chunk i / 32, slot i % 32
-  // (slot = 16 s + mm holds token tau_s(mm)); V piece i -> row i / 4, tokens 8 (i % 4) ..
+  // This thread's piece of each of its NX runs: run x*kPfWaves + w, piece (run * 64 + lane).
+  // K piece i -> chunk i / 32, slot i % 32 (slot = 16 s + mm holds token tau_s(mm)); V
+  // piece j -> row j / 4, position j % 4 holding tokens 8 q .. 8 q + 7, q = pos ^ ((row / 4) % 4).
   constexpr int LEAF = PKV_LEAF_TOKENS / B;  // two-level leaf entries
   const int64_t bstride = static_cast<int64_t>(P.Hkv) * TILE;
   const char* kbase = P.kp + kvh * TILE;
   const char* vbase = P.vp + kvh * TILE;
-  int kg_off[KPT], kl_off[KPT], vg_off[VPT], vl_off[VPT];
-  bool kg_hi[KPT], vg_hi[VPT];  // (16-token blocks) piece comes from the unit's second block
+  int g_off[NX];
+  bool g_hi[NX];  // (16-token blocks) the piece comes from the unit's second block
 #pragma unroll
-  for (int x = 0; x < KPT; ++x) {
-    const int i = tid + kPfThreads * x;
-    const int c = i >> 5;
-    const int slot = i & 31;
-    const int ss = slot >> 4;
-    const int mm = slot & 15;
-    const int tok = 8 * (mm >> 2) + 4 * ss + (mm & 3);
-    kg_hi[x] = BPU == 2 && tok >= 16;
-    kg_off[x] = (c * B + (BPU == 2 ? (tok & 15) : tok)) * 16;
-    kl_off[x] = (c * 32 + slot) * 16;
+  for (int x = 0; x < NX; ++x) {
+    const int run = x * kPfWaves + w;
+    const int i = run * 64 + lane;
+    if (run < KRUNS) {
+      const int c = i >> 5;
+      const int slot = i & 31;
+      const int ss = slot >> 4;
+      const int mm = slot & 15;
+      const int tok = 8 * (mm >> 2) + 4 * ss + (mm & 3);
+      g_hi[x] = BPU == 2 && tok >= 16;
+      g_off[x] = (c * B + (BPU == 2 ? (tok & 15) : tok)) * 16;
+    } else {
+      const int j = i - PrefillLds<D>::kKPieces;
+      const int d = j >> 2;
+      const int q = (j & 3) ^ ((d >> 2) & 3);
+      g_hi[x] = BPU == 2 && q >= 2;
+      g_off[x] = (d * B + 8 * (BPU == 2 ? (q & 1) : q)) * EB;
+    }
   }
+  auto fetch = [&](int u, int stage) {
+    const int e0 = u * BPU;
+    // block ids through the scalar cache (the waits for them leave the K/V loads in flight);
+    // an absent second block reuses the first
+    const int blk0 = table_entry_uniform<Tab, LEAF>(P.tables, P.dir, b, P.W, e0);
+    const int blk1 = BPU == 2 ? table_entry_uniform<Tab, LEAF>(P.tables, P.dir, b, P.W, min(e0 + 1, nblk - 1)) : blk0;
 #pragma unroll
-  for (int x = 0; x < VPT; ++x) {
-    const int i = tid + kPfThreads * x;
-    const int d = i >> 2;
-    const int qq = i & 3;
-    vg_hi[x] = BPU == 2 && qq >= 2;
-    vg_off[x] = (d * B + 8 * (BPU == 2 ? (qq & 1) : qq)) * EB;
-    vl_off[x] = KB + d * VROW + qq * 16;
-  }
-  struct Stage {
-    u32x4 k[KPT];
-    u32x4 v[VPT];
-  };
-  auto fetch = [&](int u, Stage& st) {
-    const int e0 = u * BPU;  // a unit's entries lie in one leaf (LEAF is a multiple of BPU)
-    const auto* trow = table_row<Tab, LEAF>(P.tables, P.dir, b, P.W, e0);
-    const int blk0 = static_cast<int>(trow[0]);  // uniform: scalar loads
-    const int blk1 = BPU == 2 ? static_cast<int>(trow[e0 + 1 < nblk ? 1 : 0]) : blk0;  // absent second block: reuse the first
-    const char* k0 = kbase + blk0 * bstride;
-    const char* v0 = vbase + blk0 * bstride;
-    const char* k1 = kbase + blk1 * bstride;
-    const char* v1 = vbase + blk1 * bstride;
-#pragma unroll
-    for (int x = 0; x < KPT; ++x) st.k[x] = *reinterpret_cast<const u32x4*>((kg_hi[x] ? k1 : k0) + kg_off[x]);
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) st.v[x] = *reinterpret_cast<const u32x4*>((vg_hi[x] ? v1 : v0) + vg_off[x]);
-  };
-  auto deposit = [&](int bi, const Stage& st) {
-    char* base = sm.buf[bi];
-#pragma unroll
-    for (int x = 0; x < KPT; ++x) *reinterpret_cast<u32x4*>(base + kl_off[x]) = st.k[x];
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) *reinterpret_cast<u32x4*>(base + vl_off[x]) = st.v[x];
+    for (int x = 0; x < NX; ++x) {
+      const int run = x * kPfWaves + w;
+      const char* base = run < KRUNS ? kbase : vbase;
+      const char* src = base + (g_hi[x] ? blk1 : blk0) * bstride + g_off[x];
+      // (typed pointers: with char pointers the host pass drops the kernel's launch stub)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(src),
+                                       reinterpret_cast<u32x4*>(&s_kv[stage][run * 64 * 16]), 16, 0, 0);
+    }
   };
 
   float m_run[RG], l_run[RG];
@@ -307,27 +302,48 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     for (int c = 0; c < NC; ++c) o[k][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float cs = P.scale_log2;
+  const int vsw = (m >> 2) & 3;  // V piece swizzle of this lane's fragment rows
 
-  auto compute = [&](int u, int bi) {
-    const char* base = sm.buf[bi];
-    u32x4 kf[2][KI], vf[NC];
+  // LDS fragment reads are issued one step ahead of the products that use them (two
+  // register buffers), so each read has a step of MFMAs to land.
+  auto kfrag = [&](const char* base, int ki, int s2) {
+    return *reinterpret_cast<const u32x4*>(base + ((4 * ki + r) * 32 + 16 * s2 + m) * 16);
+  };
+  auto vfrag = [&](const char* base, int c) {
+    return *reinterpret_cast<const u32x4*>(base + KB + ((16 * c + m) * 4 + (r ^ vsw)) * 16);
+  };
+  // P.V over the unit (V of tokens past the context was zeroed in LDS)
+  auto pv = [&](const char* base, const u32x4 (&pb)[RG]) {
+    u32x4 vb[2];
+    vb[0] = vfrag(base, 0);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int c = 0; c < NC; ++c) {
+      if (c + 1 < NC) vb[(c + 1) & 1] = vfrag(base, c + 1);
 #pragma unroll
-      for (int ki = 0; ki < KI; ++ki)
-        kf[s2][ki] = *reinterpret_cast<const u32x4*>(base + ((4 * ki + r) * 32 + 16 * s2 + m) * 16);
+      for (int k = 0; k < RG; ++k) o[k][c] = T::mfma_k32(vb[c & 1], pb[k], o[k][c]);
     }
+  };
+  // V elements of tokens past the context (t >= L) in the unit of stage `stage` become 0
+  // before they meet p = 0 (a NaN in an unused slot would survive 0 * NaN)
+  auto zero_v_tail = [&](int u, int stage) {
+    char* base = s_kv[stage] + KB;
+    const int t0 = L - 32 * u;  // first local token past the context
+    for (int i = tid; i < D * 4; i += kPfThreads) {
+      const int d = i >> 2;
+      const int q = (i & 3) ^ ((d >> 2) & 3);  // tokens 8q .. 8q + 7 at position i % 4
+      if (8 * q + 8 <= t0) continue;
+      u32x4* pc = reinterpret_cast<u32x4*>(base + i * 16);
+      u32x4 v = *pc;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vf[c] = *reinterpret_cast<const u32x4*>(base + KB + (16 * c + m) * VROW + r * 16);
+      for (int kk = 0; kk < 4; ++kk)
+        v[kk] &= (8 * q + 2 * kk < t0 ? 0x0000ffffu : 0u) | (8 * q + 2 * kk + 1 < t0 ? 0xffff0000u : 0u);
+      *pc = v;
+    }
+  };
+
+  auto compute = [&](int u, int stage) {
+    const char* base = s_kv[stage];
     const int j0 = 32 * u + 8 * r;
-    if (32 * u + 32 > L) {  // tokens past the context: zero V
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u32 msk = (j0 + 2 * kk < L ? 0x0000ffffu : 0u) | (j0 + 2 * kk + 1 < L ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) vf[c][kk] &= msk;
-      }
-    }
     const bool diag = 32 * u + 31 > w_first;
     // scores of every group: independent MFMA chains, interleaved
     f32x4 acc[RG][2];
@@ -336,12 +352,19 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
       acc[k][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc[k][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    u32x4 kb[2][2];
+    kb[0][0] = kfrag(base, 0, 0);
+    kb[0][1] = kfrag(base, 0, 1);
 #pragma unroll
     for (int ki = 0; ki < KI; ++ki) {
+      if (ki + 1 < KI) {
+        kb[(ki + 1) & 1][0] = kfrag(base, ki + 1, 0);
+        kb[(ki + 1) & 1][1] = kfrag(base, ki + 1, 1);
+      }
 #pragma unroll
       for (int k = 0; k < RG; ++k) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) acc[k][s2] = T::mfma_k32(kf[s2][ki], qf[k][ki], acc[k][s2]);
+        for (int s2 = 0; s2 < 2; ++s2) acc[k][s2] = T::mfma_k32(kb[ki & 1][s2], qf[k][ki], acc[k][s2]);
       }
     }
     float sc[RG][8];  // raw scores of tokens 8r + e, e = 4 s + j
@@ -370,14 +393,12 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     if (wave_any(grow)) {  // rare: some row's max rose by more than the threshold
 #pragma unroll
       for (int k = 0; k < RG; ++k) {
-        if (wave_any(mx[k] > m_run[k] + kPfRescaleLog2)) {
-          const float mn = fmaxf(m_run[k], mx[k]);
-          const float alpha = fast_exp2(m_run[k] - mn);
-          l_run[k] *= alpha;
+        const bool raise = mx[k] > m_run[k] + kPfRescaleLog2;  // each row (lane m) on its own
+        const float alpha = raise ? fast_exp2(m_run[k] - mx[k]) : 1.f;
+        l_run[k] *= alpha;
 #pragma unroll
-          for (int c = 0; c < NC; ++c) o[k][c] *= alpha;
-          m_run[k] = mn;
-        }
+        for (int c = 0; c < NC; ++c) o[k][c] *= alpha;
+        m_run[k] = raise ? mx[k] : m_run[k];
       }
     }
     u32x4 pb[RG];
@@ -390,32 +411,32 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) pb[k][kk] = T::pack2(p[2 * kk], p[2 * kk + 1]);
     }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-#pragma unroll
-      for (int k = 0; k < RG; ++k) o[k][c] = T::mfma_k32(vf[c], pb[k], o[k][c]);
-    }
+    pv(base, pb);
   };
 
-  // Unit u is computed from LDS buffer u % 2 while unit u + 1 waits in registers and
-  // unit u + 2 is being loaded: each unit's loads have two units of compute to land.
-  Stage s0, s1;
-  auto step = [&](int u, Stage& cur, Stage& nxt) {
-    // on entry `cur` is free and `nxt` holds unit u + 1 (if any)
-    // unconditional (the last unit again near the end): a load issued on only some
-    // paths would make the deposit below wait for every outstanding load
-    fetch(min(u + 2, nunits - 1), cur);
-    if (wave_rows && 32 * u <= w_last) compute(u, u & 1);  // units this wave's rows can see
-    if (u + 1 < nunits) deposit((u + 1) & 1, nxt);
-    __syncthreads();
-  };
-  fetch(0, s0);
-  if (nunits > 1) fetch(1, s1);
-  deposit(0, s0);
-  __syncthreads();
-  for (int u = 0; u < nunits; u += 2) {
-    step(u, s0, s1);
-    if (u + 1 < nunits) step(u + 1, s1, s0);
+  // Ring of kPfStages LDS buffers: unit u computed from buffer u % 3 while units u + 1
+  // and u + 2 load.  Before unit u: this thread's loads of unit u have landed (its later
+  // unit's NX loads may still be in flight), and the barrier makes every thread's
+  // loads visible and ends every wave's use of buffer (u - 1) % 3, which unit u + 2 then fills.
+  // (the barrier is s_barrier alone: a full __syncthreads would also wait for the loads
+  // of unit u + 1; the signal fences keep the compiler from moving LDS reads across it)
+  fetch(0, 0);
+  if (nunits > 1) fetch(1, 1);
+  for (int u = 0; u < nunits; ++u) {
+    if (u + 1 < nunits) __builtin_amdgcn_s_waitcnt(vmcnt_only(NX));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (u + 2 < nunits) fetch(u + 2, (u + 2) % kPfStages);
+    if (32 * u + 32 > L) {  // the unit holding the context's end (workgroup-uniform)
+      zero_v_tail(u, u % kPfStages);
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(63) & ~(0xf << 8));  // (lgkmcnt 0: the LDS writes are done)
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    if (wave_rows && 32 * u <= w_last) compute(u, u % kPfStages);  // units this wave's rows can see
   }
 
 #pragma unroll
