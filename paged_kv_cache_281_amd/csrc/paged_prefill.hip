@@ -50,7 +50,7 @@ constexpr float kPfRescaleLog2 = 8.f;  // lazy rescale threshold (log2 units)
 // Row groups (16 rows each) per wave: kRGBig when the chunks fill whole workgroup
 // tiles, 1 for short chunks (fewer idle rows).
 #ifndef PKV_PREFILL_RG_BIG
-#define PKV_PREFILL_RG_BIG 3
+#define PKV_PREFILL_RG_BIG 2
 #endif
 constexpr int kRGBig = PKV_PREFILL_RG_BIG;
 constexpr int kRGSmall = 1;
