@@ -281,11 +281,15 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     // an absent second block reuses the first
     const int blk0 = table_entry_uniform<Tab, LEAF>(P.tables, P.dir, b, P.W, e0);
     const int blk1 = BPU == 2 ? table_entry_uniform<Tab, LEAF>(P.tables, P.dir, b, P.W, min(e0 + 1, nblk - 1)) : blk0;
+    // the unit's tiles (scalar addresses); each lane then picks its tile and adds its offset
+    const char* kt0 = kbase + blk0 * bstride;
+    const char* kt1 = kbase + blk1 * bstride;
+    const char* vt0 = vbase + blk0 * bstride;
+    const char* vt1 = vbase + blk1 * bstride;
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
       const int run = x * kPfWaves + w;
-      const char* base = run < KRUNS ? kbase : vbase;
-      const char* src = base + (g_hi[x] ? blk1 : blk0) * bstride + g_off[x];
+      const char* src = (run < KRUNS ? (g_hi[x] ? kt1 : kt0) : (g_hi[x] ? vt1 : vt0)) + g_off[x];
       // (typed pointers: with char pointers the host pass drops the kernel's launch stub)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(src),
                                        reinterpret_cast<u32x4*>(&s_kv[stage][run * 64 * 16]), 16, 0, 0);
