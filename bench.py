@@ -5,9 +5,9 @@ copies of the step (if any), then one launch that writes the step's new tokens
 into their slots (from the host block manager) and plans the attention, then the
 attention partition pass, whose last finisher per row does the log-sum-exp merge
 (a separate merge kernel for rows of more than 32 partitions).  Inputs are seeded
-synthetic data already resident in HBM.  The step's launches are captured once as
-a HIP graph and the timed steps are graph replays (``--eager`` times stream
-launches instead; both are reported).
+synthetic data already resident in HBM.  The timed steps are stream launches; the
+same step captured as a HIP graph is replayed afterwards and reported beside them
+(``--eager`` skips the replays).
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole step (attention's
 algorithmic K+V bytes / step time); ``roofline`` describes the dominant kernel
@@ -575,9 +575,12 @@ def lenclass_main(args, lw, dev):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        for i in range(args.steps):
             step(evs[i])
         torch.cuda.synchronize()
-        eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         part_ms = [float(np.mean([e[i][0].elapsed_time(e[i][1]) for e in evs])) for i in range(len(parts))]
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream(device=dev)
@@ -632,7 +635,8 @@ def lenclass_main(args, lw, dev):
                 g2.replay()
             torch.cuda.synchronize()
             conc_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-            log(f"{name}: pools as parallel graph branches {conc_ms:.4f} ms (one branch {graph_ms:.4f})")
+            log(f"{name}: pools as parallel graph branches {conc_ms:.4f} ms (one branch {graph_ms:.4f}, "
+                f"stream launches {step_ms:.4f})")
         abs_ = [algorithmic_bytes(p["w"], p["lens_np"], partition_tokens=partition_tokens_of(p["w"], p["lens_np"]))
                 for p in parts]
         kv = sum(a["kv"] for a in abs_)
@@ -641,16 +645,16 @@ def lenclass_main(args, lw, dev):
         per_slot = 2 * base.num_kv_heads * base.head_dim * base.elem_bytes
         results[name] = {
             "block_sizes": [p["w"].block_size for p in parts], "sequences": [p["w"].num_seqs for p in parts],
-            "ms_per_step": round(graph_ms, 5), "eager_ms_per_step": round(eager_ms, 5),
+            "ms_per_step": round(step_ms, 5), "graph_ms_per_step": round(graph_ms, 5),
             "parallel_branches_ms_per_step": None if conc_ms is None else round(conc_ms, 5),
             "partition_kernel_ms": [round(x, 5) for x in part_ms],
-            "kv_gbs": round(kv / (graph_ms * 1e-3) / 1e9, 2),
+            "kv_gbs": round(kv / (step_ms * 1e-3) / 1e9, 2),
             "partition_kernel_gbs": round(sum(a["total"] for a in abs_) / (sum(part_ms) * 1e-3) / 1e9, 2),
             "tokens": used, "allocated_slots": alloc, "wasted_slots": alloc - used,
             "kv_bytes_allocated": alloc * per_slot, "table_entries": sum(p["blocks"] for p in parts),
             "kv_bytes": kv, "algorithmic_bytes": sum(a["total"] for a in abs_),
         }
-        log(f"{name}: step {graph_ms:.4f} ms (eager {eager_ms:.4f}), partition kernels {part_ms}, "
+        log(f"{name}: step {step_ms:.4f} ms (graph replays {graph_ms:.4f}), partition kernels {part_ms}, "
             f"waste {alloc - used} slots, {results[name]['table_entries']} table entries")
         del parts, g
         torch.cuda.synchronize()
@@ -676,7 +680,7 @@ def lenclass_main(args, lw, dev):
                    "kv_bytes": r["kv_bytes"]},
         "pct_hbm_peak": round(100.0 * r["kv_gbs"] / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(base.num_seqs / (r["ms_per_step"] * 1e-3), 1),
-        "step_launch": "hip_graph",
+        "step_launch": "stream",
         "configurations": results,
         "roofline": {"kernel": "attn_partition (block-16 and block-32 launches)", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -812,23 +816,29 @@ def decode_run(args, name, dev, table_format="int32", partition_tokens=0, with_c
         if e is not None:
             e[1].record(stream)
 
-    # timed region (eager): exactly `steps` steps; events bracket the partition pass in each
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # timed region: exactly `steps` steps launched on the stream, nothing else in it
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the same steps again with HIP events around each partition pass (on the stream it
+    # is launched on): the kernel's duration for the roofline (the events add a little
+    # time to each step, so these steps are not the ones timed above)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
     for i in range(args.steps):
         step(ev[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    eager_ms = wall * 1e3 / args.steps
-    ms_step = eager_ms
+    events_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     graph_ms = None
     if not args.eager:
-        # The decode step has a fixed shape, so it is captured once as a HIP graph and
-        # replayed: one launch per step instead of three (data.6616ai.com
-        # "PagedAttention 之外": graph capture removes the per-launch CPU cost of decode).
+        # the same step captured once as a HIP graph and replayed (data.6616ai.com
+        # "PagedAttention 之外": graph capture removes the per-launch CPU cost of decode);
+        # on this device a replay costs a few microseconds more than the stream launches
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream(device=dev)
         side.wait_stream(stream)
@@ -846,8 +856,8 @@ def decode_run(args, name, dev, table_format="int32", partition_tokens=0, with_c
             g.replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        ms_step = graph_ms
-        log(f"graph replay: {graph_ms:.4f} ms per step (stream launches {eager_ms:.4f} ms)")
+    log(f"step {ms_step:.4f} ms as stream launches (with events {events_ms:.4f}, graph replays "
+        f"{graph_ms if graph_ms is None else round(graph_ms, 4)})")
     part_all = [e[0].elapsed_time(e[1]) for e in ev]
     part_ms = float(np.mean(part_all))
 
@@ -924,8 +934,9 @@ def decode_run(args, name, dev, table_format="int32", partition_tokens=0, with_c
         "attn_partitions_ms_spread": spread(part_all),
         "attn_partitions_ms_after_cache_flush_spread": spread(flushed) if flushed else None,
         "host_block_manager_step_us": round(host_bm_us, 1),
-        "step_launch": "eager" if graph_ms is None else "hip_graph",
-        "eager_ms_per_step": round(eager_ms, 5),
+        "step_launch": "stream",
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "events_ms_per_step": round(events_ms, 5),
         "roofline": {"kernel": "attn_partition" + (" + attn_merge_long" if ab["merge_long"] else ""),
                      "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -973,7 +984,7 @@ def main():
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="extra partition-pass timings, each after a 512 MiB cache flush")
     ap.add_argument("--eager", action="store_true",
-                    help="time the decode step as stream launches instead of replays of its HIP graph")
+                    help="skip the HIP-graph replays of the decode step (the timed steps are stream launches)")
     ap.add_argument("--tables", choices=["int32", "int16", "two_level"], default="int32",
                     help="block-table format of the decode step (flat int32, flat 16-bit, or two-level)")
     ap.add_argument("--partition-tokens", type=int, choices=[0, 512, 1024, 2048], default=0,

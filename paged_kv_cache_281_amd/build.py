@@ -31,7 +31,10 @@ def _flags(debug: bool):
          # no packed-fp32 instructions in device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          # MFMA accumulators in VGPRs: the online-softmax rescale works on them with VALU ops
-         "-mllvm", "-amdgpu-mfma-vgpr-form"]
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
+         # atomics exactly as written: the plan's counting atomics on one LDS word are
+         # faster issued from every lane than turned into a lane-by-lane loop
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
     f += ["-O1", "-g", "-DPKV_DEBUG=1"] if debug else ["-O3"]
     return f
 

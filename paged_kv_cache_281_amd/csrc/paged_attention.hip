@@ -182,23 +182,74 @@ __device__ __forceinline__ int table_entry(const Params& P, int b, int j) {
   return static_cast<const int*>(P.tables)[static_cast<int64_t>(b) * P.W + j];
 }
 
-// Entries compared by one thread at a time when a group's rows are compared.
-constexpr int kCmpChunk = 16;
+// Group rows are compared in segments of one entry per lane of a wave (64 consecutive
+// entries, so each load instruction reads neighbouring words); a wave keeps kCmpBatch
+// segments in flight.
+constexpr int kCmpSeg = 64;
+constexpr int kCmpBatch = 24;
 
-// The first j in [j0, min(j0 + kCmpChunk, cap)) at which the table rows of sequences a
-// and b differ, or cap if none (every load issued before the first compare).
-__device__ __forceinline__ int chunk_mismatch(const Params& P, int a, int b, int j0, int cap) {
-  int ea[kCmpChunk], eb[kCmpChunk];
-#pragma unroll
-  for (int k = 0; k < kCmpChunk; ++k) {
-    const int j = min(j0 + k, cap - 1);
-    ea[k] = table_entry(P, a, j);
-    eb[k] = table_entry(P, b, j);
+// Entry j of row b in one table format, without branches (so that a batch of such loads
+// is issued back to back): 0 = int32 rows, 1 = uint16 rows, 2 = two-level.
+template <int F>
+__device__ __forceinline__ int table_entry_fmt(const Params& P, int b, int j) {
+  if constexpr (F == 2) {
+    const int leaf = P.dir[static_cast<int64_t>(b) * (P.W / P.leaf_e) + j / P.leaf_e];
+    return static_cast<const int*>(P.tables)[static_cast<int64_t>(leaf) * P.leaf_e + j % P.leaf_e];
+  } else if constexpr (F == 1) {
+    return static_cast<const uint16_t*>(P.tables)[static_cast<int64_t>(b) * P.W + j];
+  } else {
+    return static_cast<const int*>(P.tables)[static_cast<int64_t>(b) * P.W + j];
   }
-  int first = cap;
+}
+
+// One batch of row segments of a window.  Lane i < kCmpBatch holds segment i: its
+// member's index k in the window's list, first entry j0 (-1: none), the two rows (the
+// member's and its group's first member's) and the number of entries to compare.  Every
+// lane compares entry j0 + lane of the two rows; the first differing entry of each
+// segment lowers `mis` of its member.  Addresses come from lane reads, so the loads of
+// the whole batch are issued back to back.
+template <int F>
+__device__ __forceinline__ void compare_segments(const Params& P, int rk, int rj, int ra, int rb, int rc, int* mis) {
+  const int lane = threadIdx.x & 63;
+  int ea[kCmpBatch], eb[kCmpBatch];
+  unsigned in = 0;  // bit i: this lane's entry of segment i exists
+  static_assert(kCmpBatch <= 32, "one bit per segment");
+  // the entry this lane reads for segment i: its own if it exists, else one that does
+  // (entry 0 of both rows always exists)
+  auto entry = [&](int i) {
+    const int j0 = __builtin_amdgcn_readlane(rj, i);
+    return j0 < 0 ? 0 : min(j0 + lane, __builtin_amdgcn_readlane(rc, i) - 1);
+  };
 #pragma unroll
-  for (int k = kCmpChunk - 1; k >= 0; --k) first = (j0 + k < cap && ea[k] != eb[k]) ? j0 + k : first;
-  return first;
+  for (int i = 0; i < kCmpBatch; ++i) {
+    const int j0 = __builtin_amdgcn_readlane(rj, i);
+    in |= static_cast<unsigned>(j0 >= 0 && j0 + lane < __builtin_amdgcn_readlane(rc, i)) << i;
+    const int a = __builtin_amdgcn_readlane(ra, i);
+    const int b = __builtin_amdgcn_readlane(rb, i);
+    const int jj = entry(i);
+    if constexpr (F == 2) {  // the leaves first, then their entries
+      const int64_t dw = P.W / P.leaf_e;
+      ea[i] = P.dir[a * dw + jj / P.leaf_e];
+      eb[i] = P.dir[b * dw + jj / P.leaf_e];
+    } else {
+      ea[i] = table_entry_fmt<F>(P, a, jj);
+      eb[i] = table_entry_fmt<F>(P, b, jj);
+    }
+  }
+  if constexpr (F == 2) {
+    const int* leaves = static_cast<const int*>(P.tables);
+#pragma unroll
+    for (int i = 0; i < kCmpBatch; ++i) {
+      const int e = entry(i) % P.leaf_e;
+      ea[i] = leaves[static_cast<int64_t>(ea[i]) * P.leaf_e + e];
+      eb[i] = leaves[static_cast<int64_t>(eb[i]) * P.leaf_e + e];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kCmpBatch; ++i) {
+    const unsigned long long m = __ballot(((in >> i) & 1u) && ea[i] != eb[i]);
+    if (m && lane == 0) atomicMin(&mis[__builtin_amdgcn_readlane(rk, i)], __builtin_amdgcn_readlane(rj, i) + __builtin_ctzll(m));
+  }
 }
 
 // The hash slot of first block `key` (inserted if new), or -1 if the table is full.
@@ -270,8 +321,8 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   __shared__ int4 coop_g[kPlanCoopMax];
   __shared__ int hkey[kGroupHash], hlead[kGroupHash], hcnt[kGroupHash], hS[kGroupHash], hrank[kGroupHash],
       hbase[kGroupHash], hmaxl[kGroupHash];
-  __shared__ int wslot[kGroupWin], wrank[kGroupWin], wscan[kGroupWin], wcap[kGroupWin], wmis[kGroupWin],
-      wpre[kGroupWin + 1];
+  __shared__ int wslot[kGroupWin], wrank[kGroupWin], wscan[kGroupWin], wlead[kGroupWin], wcap[kGroupWin],
+      wmis[kGroupWin], wpre[kGroupWin + 1];
   __shared__ unsigned win_any[kGroupWinWords];
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
@@ -280,6 +331,9 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   // batch of at most blockDim sequences is then read once)
   const int L_first = tid < N ? context_len(P, tid) : 0;
   auto len_of = [&](int b) { return b == tid ? L_first : context_len(P, b); };
+  // and its first table entry, read together with the length (plain tables only: a
+  // two-level row is followed only for a sequence long enough to be grouped)
+  const int fb_first = (tid < N && P.cm >= 2 && P.tables && !P.dir) ? table_entry(P, tid, 0) : -1;
   Grp g_first = kNoGroup;  // this thread's first sequence's group, once known
   if (tid <= NB) {
     cnt[0][tid] = 0;
@@ -315,7 +369,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
         const int b = w0 + i;
         int slot = -1;
         if (b < N && len_of(b) >= kMinSharedTokens) {
-          const int fb = table_entry(P, b, 0);
+          const int fb = (b == tid && !P.dir) ? fb_first : table_entry(P, b, 0);
           slot = fb >= 0 ? hash_slot(hkey, fb) : -1;
           if (slot >= 0) {
             atomicMin(&hlead[slot], b);
@@ -337,6 +391,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
           } else {
             const int k = atomicAdd(&n_scan, 1);
             wscan[k] = b;
+            wlead[k] = a;
             wcap[k] = min(context_len(P, a), context_len(P, b)) / P.B;
             wmis[k] = wcap[k];
           }
@@ -344,15 +399,15 @@ __device__ __forceinline__ void plan_body(const Params& P) {
       }
       __syncthreads();
       if (s_any) {
-        // every member's row against the group's first member's: all threads take
-        // (member, chunk of kCmpChunk entries) pairs; wpre holds each member's first pair
+        // every member's row against the group's first member's, in segments of kCmpSeg
+        // entries: wpre holds each member's first segment in the window's segment list
         if (tid < 64) {
           constexpr int PER = kGroupWin / 64;
           int c[PER], sum = 0;
 #pragma unroll
           for (int e = 0; e < PER; ++e) {
             const int k = tid * PER + e;
-            c[e] = k < n_scan ? (wcap[k] + kCmpChunk - 1) / kCmpChunk : 0;
+            c[e] = k < n_scan ? (wcap[k] + kCmpSeg - 1) / kCmpSeg : 0;
             sum += c[e];
           }
           int v = sum;
@@ -371,18 +426,29 @@ __device__ __forceinline__ void plan_body(const Params& P) {
         }
         __syncthreads();
         const int total = wpre[kGroupWin];
-        for (int i = tid; i < total; i += nt) {
-          int lo = 0, hi = n_scan - 1;  // the member: the last k with wpre[k] <= i
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (wpre[mid] <= i) lo = mid;
-            else hi = mid - 1;
+        const int wave = tid >> 6;
+        const int nwaves = nt >> 6;
+        for (int u0 = wave * kCmpBatch; u0 < total; u0 += nwaves * kCmpBatch) {
+          // lane i < kCmpBatch resolves segment u0 + i: its member k and first entry
+          int rk = 0, rj = -1, ra = 0, rb = 0, rc = 1;  // (rj = -1: no segment)
+          if (lane < kCmpBatch && u0 + lane < total) {
+            const int u = u0 + lane;
+            int lo = 0, hi = n_scan - 1;  // the member: the last k with wpre[k] <= u
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (wpre[mid] <= u) lo = mid;
+              else hi = mid - 1;
+            }
+            rk = lo;
+            rj = (u - wpre[lo]) * kCmpSeg;
+            if (rj >= wmis[lo]) rj = -1;  // an earlier segment already differs
+            ra = wlead[lo];
+            rb = wscan[lo];
+            rc = wcap[lo];
           }
-          const int b = wscan[lo];
-          const int j0 = (i - wpre[lo]) * kCmpChunk;
-          if (j0 >= wmis[lo]) continue;  // an earlier chunk already differs
-          const int j = chunk_mismatch(P, hlead[wslot[b - w0]], b, j0, wcap[lo]);
-          if (j < wcap[lo]) atomicMin(&wmis[lo], j);
+          if (P.dir) compare_segments<2>(P, rk, rj, ra, rb, rc, wmis);
+          else if (P.tab_bytes == 2) compare_segments<1>(P, rk, rj, ra, rb, rc, wmis);
+          else compare_segments<0>(P, rk, rj, ra, rb, rc, wmis);
         }
         __syncthreads();
         for (int k = tid; k < n_scan; k += nt) atomicMin(&hS[wslot[wscan[k] - w0]], wmis[k]);
@@ -559,9 +625,13 @@ __global__ __launch_bounds__(1024) void attn_plan(Params P) { plan_body(P); }
 // others write (the two touch disjoint memory; the partition pass that follows in
 // stream order sees both).
 #ifndef PKV_PREP_THREADS
-#define PKV_PREP_THREADS 256
+#define PKV_PREP_THREADS 1024
 #endif
 constexpr int kPrepThreads = PKV_PREP_THREADS;
+#ifndef PKV_WRITE_THREADS
+#define PKV_WRITE_THREADS 256
+#endif
+constexpr int kWriteThreads = PKV_WRITE_THREADS;
 
 template <int EB>
 __global__ __launch_bounds__(kPrepThreads) void decode_prepare_kernel(Params P, WriteArgs wa) {
@@ -569,7 +639,8 @@ __global__ __launch_bounds__(kPrepThreads) void decode_prepare_kernel(Params P, 
     plan_body(P);
     return;
   }
-  kv_write_one<EB>(wa, static_cast<int64_t>(blockIdx.x - 1) * blockDim.x + threadIdx.x);
+  if (threadIdx.x >= kWriteThreads) return;
+  kv_write_one<EB>(wa, static_cast<int64_t>(blockIdx.x - 1) * kWriteThreads + threadIdx.x);
 }
 
 // Device-scope (relaxed) stores and loads of the partition partials: coherent across
@@ -1796,7 +1867,7 @@ int launch_decode_prepare(const AttnArgs& a, const pkv_pool_desc& pool, void* k_
   wa.H = pool.num_kv_heads;
   wa.D = pool.head_dim;
   wa.B = pool.block_size;
-  const unsigned grid = 1 + static_cast<unsigned>((total + kPrepThreads - 1) / kPrepThreads);
+  const unsigned grid = 1 + static_cast<unsigned>((total + kWriteThreads - 1) / kWriteThreads);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (eb == 4) {
     hipLaunchKernelGGL(decode_prepare_kernel<4>, dim3(grid), dim3(kPrepThreads), 0, s, P, wa);

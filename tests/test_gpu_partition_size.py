@@ -99,7 +99,7 @@ def _read_plan(ws, n, hq, d, parts):
 
 
 def _plan(lens, hq, hkv, tables, d=128, block=16, prepare=False):
-    """Runs the plan pass alone (or as the fused write + plan launch runs it, 256
+    """Runs the plan pass alone (or as the fused write + plan launch runs it, 1024
     threads, no tokens written) on a batch; returns what it wrote."""
     n = len(lens)
     W = tables.shape[1]
