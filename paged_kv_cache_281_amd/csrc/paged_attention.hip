@@ -100,6 +100,8 @@ constexpr int kFusedTask = 1 << 28;
 constexpr int kTaskIndex = kFusedTask - 1;
 // Units (16 tokens) of a fused item at most: the prefix and its members' own tokens.
 constexpr int kFusedMaxUnits = 192;
+// Parts a fused group's work is cut into at most (each part a workgroup of its own).
+constexpr int kFusedMaxParts = 4;
 
 // Context length of sequence b, clamped to what its table can address (longer
 // values break the caller's contract; clamping keeps every access in bounds).
@@ -114,6 +116,7 @@ struct Item {
   int tok0, ntok, p;
   int nm;    // sequences whose rows the item computes
   int np;    // partial count of an ordinary item's rows
+  int parts; // a fused item: the parts of its group's work (it computes part p)
 };
 __device__ __forceinline__ Item decode_item(const Params& P, const int4 t, int unit, int cols_per_seq) {
   Item it;
@@ -125,11 +128,13 @@ __device__ __forceinline__ Item decode_item(const Params& P, const int4 t, int u
   it.ntok = t.z;
   it.p = t.w & 0xffff;
   const int hi = (t.w >> 16) & 0x7fff;
-  it.nm = it.prefix ? hi : 1;
+  it.nm = it.prefix ? (hi & 0xff) : 1;
+  it.parts = it.prefix ? (hi >> 8) : 0;
   it.np = it.prefix ? 0 : hi;
   it.ok = t.x >= 0 && it.tok0 >= 0 && it.ntok >= 0 && it.tok0 + it.ntok <= P.Lmax && it.tok0 % unit == 0 &&
           it.p < P.Pmax && it.nm >= 1 && it.idx + it.nm <= P.N &&
-          (it.prefix ? (it.nm * cols_per_seq <= 16 && it.ntok > 0) : (it.np >= 1 && it.np <= P.Pmax));
+          (it.prefix ? (it.nm * cols_per_seq <= 16 && it.ntok > 0) : (it.np >= 1 && it.np <= P.Pmax)) &&
+          (it.fused ? (it.parts >= 1 && it.parts <= kFusedMaxParts && it.p < it.parts) : it.parts == 0);
   return it;
 }
 
@@ -149,7 +154,11 @@ __device__ __forceinline__ Item decode_item(const Params& P, const int4 t, int u
 // instead of once per member.  Each member's own tokens (after the prefix) are
 // ordinary items.  A member's partials are those of the prefix partitions followed by
 // those of its own partitions.  Only the MFMA kernels (16-bit pools, G <= 8) take
-// shared-prefix items.
+// shared-prefix items.  A group whose prefix fits one partition and whose members' own
+// tokens are short is fused: one item per column set computes the prefix and every
+// member's own tokens (masking each own unit to its member's columns), cut into parts
+// when the batch has few such items (fused_parts); a member's partials are then one per
+// part.
 //
 // Size: 2048 tokens unless the batch is too small to hide its longest 2048-token item
 // (choose_partition_log2): fewer, longer partitions save each workgroup's fixed start
@@ -299,13 +308,44 @@ __device__ __forceinline__ bool fused_group(const Params& P, const Grp& g, int l
 
 // The items of a shared-prefix group's partition-sized pieces: item k of a run covers
 // prefix partition p0 + k / ncs for the group's column set k % ncs.
-__device__ __forceinline__ int4 prefix_task(const Params& P, const Grp& g, int ncs, int k, int p0, int lg, int ntok,
-                                            bool fused = false) {
+__device__ __forceinline__ int4 prefix_task(const Params& P, const Grp& g, int ncs, int k, int p0, int lg, int ntok) {
   const int p = p0 + k / ncs;
   const int cs = k - (k / ncs) * ncs;
   const int nm = min(P.cm, g.cnt - cs * P.cm);
-  const int flag = kPrefixTask | (ncs > 1 ? kSharedTask : 0) | (fused ? kFusedTask : 0);
+  const int flag = kPrefixTask | (ncs > 1 ? kSharedTask : 0);
   return make_int4((g.base + cs * P.cm) | flag, p << lg, ntok, p | (nm << 16));
+}
+
+// Part s of `parts` of a fused group's column set cs.
+__device__ __forceinline__ int4 fused_task(const Params& P, const Grp& g, int ncs, int cs, int s, int parts) {
+  const int nm = min(P.cm, g.cnt - cs * P.cm);
+  const int flag = kPrefixTask | (ncs > 1 ? kSharedTask : 0) | kFusedTask;
+  return make_int4((g.base + cs * P.cm) | flag, 0, g.sp, s | (nm << 16) | (parts << 24));
+}
+
+// Parts per fused item.  A batch of few groups gives few workgroups, each a long chain
+// of dependent loads; cutting each group's work into parts (merged like partitions) runs
+// it on more of the device.  Measured on forked batches of 1020-token prompts (4 samples,
+// 8 KV heads, 768 resident slots): 4 parts ran 15-22% faster with 32 or 64 workgroups,
+// 2 parts about even with 128, and any split slower from 256 workgroups (each part then
+// pays a dependent partial store and merge while the device is already busy).  So: one
+// part per three resident slots' worth of workgroups, at most four, and at least one
+// prefix unit per wave and part.
+__device__ __forceinline__ int fused_parts(const Params& P, int fused_sets, int prefix_units) {
+#ifdef PKV_FUSED_PARTS
+  const int want = PKV_FUSED_PARTS;
+#else
+  const int wg = max(fused_sets, 1) * P.Hkv * P.NHG;
+  const int want = P.slots / (3 * wg);
+#endif
+  return max(1, min(min(want, kFusedMaxParts), min(P.Pmax, prefix_units / kWaves)));
+}
+
+// The class of one part of a fused column set: its share of the prefix plus min(cm,
+// members) times the group's longest own tokens, at most a partition.
+__device__ __forceinline__ int fused_class(const Params& P, const Grp& g, int lg, int parts) {
+  const int size = g.sp + min(P.cm, g.cnt) * (g.maxl - g.sp);
+  return item_class(min(1 << lg, (size + parts - 1) / parts), lg);
 }
 
 __device__ __forceinline__ void plan_body(const Params& P) {
@@ -313,7 +353,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   constexpr int NB = kPlanClasses;
   __shared__ int cnt[2][NB + 1];
   __shared__ int off[NB + 1];
-  __shared__ int n_coop, s_lmax, s_nmem, s_any, n_scan;
+  __shared__ int n_coop, s_lmax, s_nmem, s_any, n_scan, s_fsets[2];
   __shared__ unsigned long long s_tokens;
   // items written cooperatively: (first slot, count, sequence or group, kind) and the
   // group state of a shared-prefix run
@@ -345,6 +385,8 @@ __device__ __forceinline__ void plan_body(const Params& P) {
     s_lmax = 0;
     s_tokens = 0;
     s_nmem = 0;
+    s_fsets[0] = 0;
+    s_fsets[1] = 0;
   }
   for (int i = tid; i < N * P.Hq; i += nt) P.done[i] = 0;
   __syncthreads();
@@ -508,7 +550,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
       int nfull = full;
       if ((rem || L == 0) && !fz) atomicAdd(&cnt[c][item_class(rem, lg)], 1);
       if (ncs && fz) {
-        atomicAdd(&cnt[c][item_class(min(1 << lg, g.sp + min(P.cm, g.cnt) * (g.maxl - g.sp)), lg)], ncs);
+        atomicAdd(&s_fsets[c], ncs);  // (counted by class once the number of parts is known)
       } else if (ncs) {
         const int fp = g.sp >> lg;
         const int rp = g.sp - (fp << lg);
@@ -529,7 +571,20 @@ __device__ __forceinline__ void plan_body(const Params& P) {
   }
   __syncthreads();
   const int lg = choose_partition_log2(s_tokens, s_lmax, P.Hkv * P.NHG, P.slots, P.force_log2);
-  const int* ccnt = cnt[lg == lg_lo ? 0 : 1];
+  const int csel = lg == lg_lo ? 0 : 1;
+  const int* ccnt = cnt[csel];
+  // fused groups: each column set's work in `parts` items, counted by class
+  const int fsets = s_fsets[csel];
+  if (fsets) {
+    for (int b = tid; b < N; b += nt) {
+      const Grp g = group_of(b);
+      if (g.base >= 0 && g.rank == 0 && fused_group(P, g, lg)) {
+        const int parts = fused_parts(P, fsets, g.sp >> 4);
+        atomicAdd(&cnt[csel][fused_class(P, g, lg, parts)], ((g.cnt + P.cm - 1) / P.cm) * parts);
+      }
+    }
+    __syncthreads();
+  }
   // exclusive offsets of the classes, longest first (class NB, then NB - 1, ...): one
   // wave scans them with lane shuffles, lane i holding class NB - i
   static_assert(NB <= 64, "one wave scans the classes");
@@ -556,11 +611,12 @@ __device__ __forceinline__ void plan_body(const Params& P) {
     const int L = len_of(b);
     const Grp g = group_of(b);
     const bool fz = fused_group(P, g, lg);
+    const int parts = fz ? fused_parts(P, fsets, g.sp >> 4) : 1;
     const int npp = g.base >= 0 ? (g.sp + PT - 1) >> lg : 0;
     const int own = fz ? 0 : L - g.sp;
     const int full = own >> lg;
     const int rem = own - (full << lg);
-    const int np = (L == 0 || fz) ? 1 : npp + full + (rem > 0);
+    const int np = fz ? parts : L == 0 ? 1 : npp + full + (rem > 0);
     P.seq_np[b] = np;
     if (full) {
       const int st = atomicAdd(&off[NB], full);
@@ -579,11 +635,10 @@ __device__ __forceinline__ void plan_body(const Params& P) {
       const int pos = atomicAdd(&off[item_class(rem, lg)], 1);
       P.tasks[pos] = make_int4(b, g.sp + (full << lg), rem, (npp + full) | (np << 16));
     }
-    if (g.base >= 0 && g.rank == 0 && fz) {  // the group's fused items, one per column set
+    if (g.base >= 0 && g.rank == 0 && fz) {  // the group's fused items: parts per column set
       const int ncs = (g.cnt + P.cm - 1) / P.cm;
-      const int cls = item_class(min(PT, g.sp + min(P.cm, g.cnt) * (g.maxl - g.sp)), lg);
-      const int st = atomicAdd(&off[cls], ncs);
-      for (int q = 0; q < ncs; ++q) P.tasks[st + q] = prefix_task(P, g, ncs, q, 0, lg, g.sp, true);
+      const int st = atomicAdd(&off[fused_class(P, g, lg, parts)], ncs * parts);
+      for (int q = 0; q < ncs * parts; ++q) P.tasks[st + q] = fused_task(P, g, ncs, q / parts, q % parts, parts);
     } else if (g.base >= 0 && g.rank == 0) {  // the group's shared-prefix items
       const int ncs = (g.cnt + P.cm - 1) / P.cm;
       const int fp = g.sp >> lg;
@@ -799,7 +854,10 @@ __device__ __forceinline__ V load_kv(const char* p) {
 // Rows split into at most this many partitions are merged inside the partition
 // kernel by their last finisher; longer rows (long contexts) are merged by a separate
 // kernel that spreads each row over a whole workgroup.
-constexpr int kFuseMaxParts = 32;
+#ifndef PKV_FUSE_MAX_PARTS
+#define PKV_FUSE_MAX_PARTS 32
+#endif
+constexpr int kFuseMaxParts = PKV_FUSE_MAX_PARTS;
 
 // The query fragments of the MFMA path are kept in LDS (re-read per unit), which
 // lowers register use enough for three waves per SIMD.
@@ -1041,7 +1099,8 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int gcur = min(16, P.G - hg * 16);
   const Item it = decode_item(P, P.tasks[t], 16, gcur);
   if (!it.ok) return;  // only an item list left by the plan pass is valid
-  if (it.fused && (SUB != 1 || it.tok0 != 0 || it.ntok % 16 != 0)) return;  // (fused items: one unit per block)
+  // (fused items: one unit per block, at least one prefix unit per wave in every part)
+  if (it.fused && (SUB != 1 || it.tok0 != 0 || it.ntok % 16 != 0 || it.parts * kWaves * 16 > it.ntok)) return;
   if (it.ntok == 0) {
     if (!it.prefix && it.p == 0) zero_rows<T, D>(P, it.idx, hq0, gcur);
     return;
@@ -1059,18 +1118,27 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   const int pe = it.tok0 / B;  // the item's first table entry
   int nunits = (ntok + 15) >> 4;
   const int nblk = (ntok + B - 1) / B;
-  // A fused item's units: the prefix's (ntok tokens), then each member's own tokens.
-  // Member k's own units start at fstart[k] (lane k of every wave holds its values).
-  int f_own = 0, f_seq = 0, f_start = 0, f_units = 0;
+  // A fused item computes part it.p of its group's work: the prefix units [ps0, ps1) and
+  // each member's own units [os0, os0 + f_units) (its share of them), listed locally as
+  // the part's prefix units, then each member's own units; member k's start at local
+  // index f_start (lane k of every wave holds a member's values).
+  int f_own = 0, f_seq = 0, f_start = 0, f_units = 0, f_os0 = 0;
+  int ps0 = 0, ps1 = nblk;
   int wunits = nunits > w ? (nunits - w + kWaves - 1) / kWaves : 0;  // units this wave takes
   // a member's own unit j goes to wave j % kWaves (and the prefix's unit u to u % kWaves),
   // so every column meets its units in the same waves and order whatever the other members
   auto wave_share = [](int n, int wv) { return n > wv ? (n - wv + kWaves - 1) / kWaves : 0; };
+  auto wave_range = [&](int a, int b, int wv) { return wave_share(b, wv) - wave_share(a, wv); };
   if (it.fused) {
+    const int S = it.parts, sp = it.p;
+    ps0 = sp * nblk / S;
+    ps1 = (sp + 1) * nblk / S;
     const int k = min(lane, it.nm - 1);
     f_seq = min(max(P.members[it.idx + k], 0), P.N - 1);
     f_own = min(max(P.member_own[it.idx + k], 0), P.Lmax - ntok);
-    f_units = lane < it.nm ? (f_own + 15) >> 4 : 0;
+    const int uk = (f_own + 15) >> 4;
+    f_os0 = lane < it.nm ? sp * uk / S : 0;
+    f_units = lane < it.nm ? (sp + 1) * uk / S - f_os0 : 0;
     // exclusive scan of the members' own units over lanes (nm <= 16)
     int v = f_units;
 #pragma unroll
@@ -1078,14 +1146,16 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
       const int o2 = __shfl_up(v, d, 64);
       v += (lane & 63) >= d ? o2 : 0;
     }
-    f_start = nunits + v - f_units;
+    f_start = (ps1 - ps0) + v - f_units;
     const int total = __shfl(f_start + f_units, it.nm - 1, 64);
-    int mine = wave_share(f_units, w);
+    int mine = wave_range(f_os0, f_os0 + f_units, w);
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) mine += __shfl_xor(mine, d, 64);
-    wunits = total > kFusedMaxUnits ? 0 : wave_share(nunits, w) + __shfl(mine, 0, 64);
+    wunits = total > kFusedMaxUnits ? 0 : wave_range(ps0, ps1, w) + __shfl(mine, 0, 64);
     nunits = min(total, kFusedMaxUnits);
   }
+  // the prefix entries staged from the lead's row: [ps0, ps1) of the item's blocks
+  const int nloc = ps1 - ps0;
 
   // Preamble: issue every load first (the partition's table entries and the queries,
   // then the first unit's block id and its K/V), write LDS afterwards; vmcnt counts
@@ -1093,7 +1163,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   // (unconditional loads from clamped, always-valid addresses keep the waits exact; a
   // partition may span several two-level leaves, so each lane looks its entry up)
   const int tab_val = static_cast<int>(__builtin_nontemporal_load(
-      table_row<Tab, kLeaf<B>>(P.tables, P.dir, lead, P.W, pe + min(tid, nblk - 1))));
+      table_row<Tab, kLeaf<B>>(P.tables, P.dir, lead, P.W, pe + ps0 + min(tid, nloc - 1))));
   const Cols col = setup_columns<C>(P, it, hq0, gcur, s_cols);
   const bool hv = col.hv;
   u32x4 qf[KI];
@@ -1146,22 +1216,27 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   if (it.fused) {
     int k = 0;
     for (int q = 1; q < it.nm; ++q) k = tid >= __shfl(f_start, q, 64) ? q : k;
-    const int j = tid - __shfl(f_start, k, 64);
+    const int os0k = __shfl(f_os0, k, 64);
+    const int j = os0k + tid - __shfl(f_start, k, 64);  // member k's own unit (of all its units)
     const int seq_k = __shfl(f_seq, k, 64);
     const int own_k = __shfl(f_own, k, 64);
-    // unit j of member k: in wave j % kWaves, after that wave's prefix units and its
-    // units of members 0 .. k-1 (the shuffles run in every lane)
+    // own unit j of member k: in wave j % kWaves, after that wave's prefix units of the
+    // part and its units of members 0 .. k-1 (the shuffles run in every lane)
     const int jw = j % kWaves;
-    int before = wave_share(nblk, jw) + j / kWaves;
+    int before = wave_range(ps0, ps1, jw) + wave_range(os0k, j, jw);
     for (int q = 0; q < it.nm; ++q) {
+      const int o0 = __shfl(f_os0, q, 64);
       const int uq = __shfl(f_units, q, 64);
-      before += q < k ? wave_share(uq, jw) : 0;
+      before += q < k ? wave_range(o0, o0 + uq, jw) : 0;
     }
-    if (tid >= nblk) {
+    if (tid >= nloc) {
       f_wave = jw;
       f_pos = before;
+    } else {  // the part's prefix unit ps0 + tid
+      f_wave = (ps0 + tid) % kWaves;
+      f_pos = wave_range(ps0, ps0 + tid, f_wave);
     }
-    if (tid >= nblk && tid < nunits) {
+    if (tid >= nloc && tid < nunits) {
       f_tab = static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, seq_k, P.W, nblk + j));
       f_info = min(16, own_k - 16 * j) | ((k + 1) << 8);
     }
@@ -1170,15 +1245,16 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   // a wave without units loads unit 0 (unused) so the load stays unconditional
   Buf first;
   {
-    const int u0 = w < nunits ? w : 0;
-    const int blk = static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, lead, P.W, pe + u0 / SUB));
+    // (a fused part's wave w starts with its prefix unit ps0 + u0, the first one in wave w)
+    const int u0 = it.fused ? (w - ps0 % kWaves + kWaves) % kWaves : w < nunits ? w : 0;
+    const int blk = static_cast<int>(*table_row<Tab, kLeaf<B>>(P.tables, P.dir, lead, P.W, pe + ps0 + u0 / SUB));
     if (shared) load_blk(Cached{}, u0, blk, first);
     else load_blk(Streamed{}, u0, blk, first);
   }
   PKV_FENCE();
-  if (tid < nblk) s_tab[tid] = tab_val;
+  if (tid < nloc) s_tab[tid] = tab_val;
   if (it.fused && tid < nunits) {
-    if (tid >= nblk) s_tab[tid] = f_tab;
+    if (tid >= nloc) s_tab[tid] = f_tab;
     s_uinfo[tid] = f_info;
     s_wlist[f_wave][f_pos] = tid;
   }

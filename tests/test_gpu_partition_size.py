@@ -69,6 +69,7 @@ def _counters(ws: torch.Tensor) -> np.ndarray:
 
 FUSED = 1 << 28  # item flag: a shared-prefix item that also computes its members' own tokens
 FUSED_MAX_UNITS = 192  # 16-token units of a fused item at most
+FUSED_MAX_PARTS = 4  # parts a fused group's work is cut into at most
 PREFIX = 1 << 29  # item flag: a shared-prefix item (x holds the offset of its sequences)
 SHARED = 1 << 30  # item flag: cached K/V loads (a group that needs several items)
 MIN_SHARED = 256  # shortest shared prefix given shared-prefix items
@@ -158,24 +159,48 @@ def _fused(mem, S, lens, pt, cm, block):
     return block == 16 and S <= pt and S // 16 + per * (-(-(maxl - S) // 16)) <= FUSED_MAX_UNITS
 
 
+def _fused_parts(tasks, members, groups):
+    """The parts of each fused group's work, read from its items (every item of a group
+    carries the same count); checks that the batch has one count, cut to what each
+    group's prefix allows (four prefix units per wave and part at least)."""
+    x, wv = tasks[:, 0], tasks[:, 3]
+    gid = {b: i for i, (mem, _) in enumerate(groups) for b in mem}
+    parts = {}
+    for a, v in zip(x, wv):
+        if a & FUSED:
+            g = gid[int(members[int(a) & (FUSED - 1)])]
+            parts.setdefault(g, set()).add(int(v) >> 24)
+    assert all(len(v) == 1 for v in parts.values()), "one part count per group"
+    parts = {g: v.pop() for g, v in parts.items()}
+    if parts:
+        top = max(parts.values())
+        assert 1 <= top <= FUSED_MAX_PARTS
+        for g, n in parts.items():
+            cap = groups[g][1] // 16 // 4  # four prefix units per wave
+            assert n == min(top, cap), (n, top, cap)
+    return {groups[g][0][0]: n for g, n in parts.items()}
+
+
 def _check_plan(plan, lens, rows, pt, cm, block=16):
     """The item list holds exactly the expected items: every sequence's own partitions
     (after its shared prefix), and for every group ceil(members / cm) shared-prefix items
     per prefix partition whose sequences are the group's members, each once (a fused
-    group: one item per column set that also holds its members' own tokens, and no own
-    items); partial counts per sequence; items in non-increasing length class.  Returns
-    the groups."""
+    group: per column set, one item per part of its work, which also holds its members'
+    own tokens, and no own items); partial counts per sequence; items in non-increasing
+    length class.  Returns the groups."""
     cnt, tasks, seq_np, members, member_own = plan
     lens = np.asarray(lens, dtype=np.int64)
     groups = _groups(lens, rows, block, cm)
     sp = {b: S for mem, S in groups for b in mem}
     fused = {b for mem, S in groups if _fused(mem, S, lens, pt, cm, block) for b in mem}
+    parts_by_first = _fused_parts(tasks, members, [(m, S) for m, S in groups if _fused(m, S, lens, pt, cm, block)])
+    parts_of = {b: parts_by_first[mem[0]] for mem, S in groups if mem[0] in parts_by_first for b in mem}
     own, want_np = [], []
     for b, L in enumerate(lens):
         L = int(L)
         S = sp.get(b, 0)
         if b in fused:
-            want_np.append(1)
+            want_np.append(parts_of[b])
             continue
         npp = -(-S // pt)
         full, rem = (L - S) // pt, (L - S) % pt
@@ -195,7 +220,7 @@ def _check_plan(plan, lens, rows, pt, cm, block=16):
     group_of = {b: min(mem) for mem, _ in groups for b in mem}
     seen = {}
     for a, t, k, v in zip(x[is_prefix], tok0[is_prefix], ntok[is_prefix], wv[is_prefix]):
-        off, p, nm = int(a) & (FUSED - 1), int(v) & 0xffff, int(v) >> 16
+        off, p, nm = int(a) & (FUSED - 1), int(v) & 0xffff, (int(v) >> 16) & 0xff
         mem = [int(m) for m in members[off:off + nm]]
         assert 1 <= nm <= cm
         assert len({group_of.get(m, -1) for m in mem}) == 1 and mem[0] in group_of, "an item mixes groups"
@@ -206,20 +231,23 @@ def _check_plan(plan, lens, rows, pt, cm, block=16):
     for mem, S in groups:
         ncs = -(-len(mem) // cm)
         if _fused(mem, S, lens, pt, cm, block):
-            want[(min(mem), 0, 0, S, ncs > 1, True)] = sorted(mem)
+            for p in range(parts_of[mem[0]]):
+                want[(min(mem), p, 0, S, ncs > 1, True)] = sorted(mem)
             continue
         for p in range(-(-S // pt)):
             want[(min(mem), p, p * pt, min(pt, S - p * pt), ncs > 1, False)] = sorted(mem)
     assert {k: sorted(v) for k, v in seen.items()} == want
     # longest first: classes of pt/64 tokens never increase along the list (a fused item
-    # is classed by its prefix plus its members' longest own tokens, at most a partition)
+    # is classed by its share of the prefix plus its members' longest own tokens, at most
+    # a partition)
     size = ntok.astype(np.int64).copy()
     for i, (a, v) in enumerate(zip(x, wv)):
         if a & FUSED:
-            mem = [int(m) for m in members[int(a) & (FUSED - 1):][:int(v) >> 16]]
+            mem = [int(m) for m in members[int(a) & (FUSED - 1):][:(int(v) >> 16) & 0xff]]
             S = sp[mem[0]]
             g = next(g for g, _ in groups if mem[0] in g)
-            size[i] = min(pt, S + min(cm, len(g)) * (max(int(lens[b]) for b in g) - S))
+            whole = S + min(cm, len(g)) * (max(int(lens[b]) for b in g) - S)
+            size[i] = min(pt, -(-whole // parts_of[mem[0]]))
     cls = np.where(size > 0, -(-size // (pt // 64)), 1)
     assert (np.diff(cls) <= 0).all(), "classes must not increase along the list"
     return groups
