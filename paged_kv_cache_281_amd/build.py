@@ -39,6 +39,13 @@ def _flags(debug: bool):
     return f
 
 
+# Flags of single sources.  The prefill kernel's scores are never NaN where they count
+# (masked scores are selected to -inf, pool slots past a context are zeroed bitwise):
+# without NaN semantics each fmaxf is one v_max (no canonicalising of its inputs), which
+# cuts the softmax's VALU work on a path that is bound by VALU and MFMA issue.
+FILE_FLAGS = {"paged_prefill.hip": ["-fno-honor-nans"]}
+
+
 def build(debug: bool = False, jobs: int = 8, verbose: bool = False, extra_flags=(), out: str = None) -> str:
     """Compile every source under csrc/ and link libpkv.so (or ``out``); returns its path."""
     hipcc = _hipcc()
@@ -52,7 +59,7 @@ def build(debug: bool = False, jobs: int = 8, verbose: bool = False, extra_flags
 
     def compile_one(src):
         obj = os.path.join(out_dir, os.path.basename(src) + ".o")
-        cmd = [hipcc] + flags + ["-c", src, "-o", obj]
+        cmd = [hipcc] + flags + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
         if src.endswith(".cpp"):
             cmd = [hipcc] + flags + ["-x", "hip", "-c", src, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)

@@ -388,8 +388,9 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     bool grow = false;
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
-      float v = fmaxf(fmaxf(fmaxf(sc[k][0], sc[k][1]), fmaxf(sc[k][2], sc[k][3])),
-                      fmaxf(fmaxf(sc[k][4], sc[k][5]), fmaxf(sc[k][6], sc[k][7])));
+      // (three-input groups: each becomes one v_max3)
+      float v = fmaxf(fmaxf(fmaxf(sc[k][0], sc[k][1]), sc[k][2]),
+                      fmaxf(fmaxf(fmaxf(sc[k][3], sc[k][4]), sc[k][5]), fmaxf(sc[k][6], sc[k][7])));
       v = max_xor16(v);
       mx[k] = max_xor32(v) * cs;  // scale > 0: the max of the scaled scores
       grow = grow || (mx[k] > m_run[k] + kPfRescaleLog2);
@@ -426,6 +427,10 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
   // of unit u + 1; the signal fences keep the compiler from moving LDS reads across it)
   fetch(0, 0);
   if (nunits > 1) fetch(1, 1);
+  // Everything issued so far has landed before the loop (the query fragments with the
+  // first two units): with the queries known complete, the compiler has no reason to
+  // wait for every copy in flight before each unit's first product.
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   for (int u = 0; u < nunits; ++u) {
     if (u + 1 < nunits) __builtin_amdgcn_s_waitcnt(vmcnt_only(NX));
     else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
