@@ -966,7 +966,8 @@ def sub_record(r, partition_tokens=0):
 HEADLINE = "long_bf16_b16"
 # other decode configurations the headline line carries: (key, workload, fixed partition size)
 SUB_RECORDS = [("gqa_bf16", "gqa_bf16", 0), ("long_bf16_b32", "long_bf16_b32", 0),
-               ("long_bf16_b16_p512", "long_bf16_b16", 512)]
+               ("long_bf16_b16_p512", "long_bf16_b16", 512), ("cow_fp16_p1020", "cow_fp16_p1020", 0),
+               ("cow_fp16_p1020_shuffled", "cow_fp16_p1020_shuffled", 0)]
 
 
 def main():
@@ -1044,6 +1045,10 @@ def main():
     log(f"streaming-read ceiling {ceiling['best_gbs']} GB/s ({ceiling['best']})")
     res = decode_run(args, HEADLINE, dev, "int32", 0, not args.no_cpu_baseline)
     res["sub_records"] = subs
+    # the forked batch with its samples scattered through the batch, against the same
+    # batch in prompt order (shared prefixes are found wherever their sequences sit)
+    res["cow_shuffled_over_ordered"] = round(subs["cow_fp16_p1020_shuffled"]["ms_per_step"] /
+                                             subs["cow_fp16_p1020"]["ms_per_step"], 4)
     res["hbm_read_ceiling"] = {k: ceiling[k] for k in ("bytes", "best_gbs", "best", "frac_of_peak", "kernel")}
     res["roofline"]["frac_of_read_ceiling"] = round(res["roofline"]["achieved"] / ceiling["best_gbs"], 4)
     print(json.dumps(res), flush=True)

@@ -314,7 +314,7 @@ def long_bf16(block_size: int = 16, seed: int = 1004, num_seqs: int = 8, context
 
 
 def cow_fp16(prompt_len: int = 1020, seed: int = 1003, num_prompts: int = 64, samples: int = 4,
-             max_suffix: int = 256, block: int = 16, hq: int = 32, hkv: int = 8) -> Workload:
+             max_suffix: int = 256, block: int = 16, hq: int = 32, hkv: int = 8, shuffle: bool = False) -> Workload:
     """Parallel sampling: prompts of ``prompt_len`` tokens, each forked into ``samples`` samples.
 
     Sample i of prompt k is sequence ``samples*k + i``; sample 0 is the prompt's own
@@ -322,6 +322,8 @@ def cow_fp16(prompt_len: int = 1020, seed: int = 1003, num_prompts: int = 64, sa
     measured step (one decode step per token, all samples stepping together), then
     the measured step appends one more token to every sample.  32 q / 8 kv heads,
     D=128, B=16, fp16 (block size and head counts can be changed for test cases).
+    With ``shuffle`` the attention batch lists the same sequences in a seeded random
+    order (a prompt's samples scattered through the batch); everything else is equal.
     """
     rng = np.random.default_rng(seed)
     n = num_prompts * samples
@@ -337,13 +339,16 @@ def cow_fp16(prompt_len: int = 1020, seed: int = 1003, num_prompts: int = 64, sa
         steps.append([i for i in range(n) if suffix[i] > tau])
     steps.append(list(range(n)))
     width = -(-(prompt_len + max_suffix + 1) // block)
+    batch = np.arange(n, dtype=np.int32)
+    if shuffle:
+        batch = np.random.default_rng((seed, 1)).permutation(n).astype(np.int32)
     return Workload(
-        name=f"cow_fp16_p{prompt_len}", seed=seed, dtype="f16", num_q_heads=hq, num_kv_heads=hkv,
+        name=f"cow_fp16_p{prompt_len}" + ("_shuffled" if shuffle else ""), seed=seed, dtype="f16", num_q_heads=hq, num_kv_heads=hkv,
         head_dim=128, block_size=block, num_blocks=num_blocks, max_blocks_per_seq=width,
         scale=1.0 / math.sqrt(128), free_order=free_order,
         prefill=[(samples * k, prompt_len) for k in range(num_prompts)],
         forks=[(samples * k, samples * k + i) for k in range(num_prompts) for i in range(1, samples)],
-        steps=steps, batch=np.arange(n, dtype=np.int32), context_lens=lengths.astype(np.int32),
+        steps=steps, batch=batch, context_lens=lengths[batch].astype(np.int32),
         notes=f"suffix lengths {suffix.tolist()}")
 
 
@@ -353,6 +358,7 @@ WORKLOADS = {
     "gqa_bf16": gqa_bf16,
     "cow_fp16_p1020": lambda **kw: cow_fp16(1020, **kw),
     "cow_fp16_p1024": lambda **kw: cow_fp16(1024, **kw),
+    "cow_fp16_p1020_shuffled": lambda **kw: cow_fp16(1020, shuffle=True, **kw),
     "long_bf16_b16": lambda **kw: long_bf16(16, **kw),
     "long_bf16_b32": lambda **kw: long_bf16(32, **kw),
 }
