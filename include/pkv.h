@@ -156,7 +156,9 @@ size_t pkv_paged_attention_workspace_bytes(int32_t num_seqs, int32_t num_q_heads
  *   q, out        device [num_seqs][num_q_heads][D], pool dtype, contiguous, 16-byte aligned.
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries at index
  *                 >= ceil(context_lens[b] / B) are never followed (the plan pass
- *                 compares entry 0 of every row, an empty context's included).
+ *                 reads entry 0 of every row, an empty context's included, and compares
+ *                 the leading entries of rows whose first entries are equal, up to the
+ *                 shorter context's full blocks, without following them).
  *   context_lens  device int32 [num_seqs]; 0 gives a zero output row.
  *   workspace     device, >= pkv_paged_attention_workspace_bytes(...), 256-byte aligned;
  *                 contents on entry do not matter.
@@ -269,8 +271,7 @@ int32_t pkv_paged_attention_prefill_t16(const pkv_pool_desc* pool, const void* k
  * Entry j of sequence b is leaves[leaf_dir[b][j / E]][j % E].  Each call equals the
  * flat-table call with max_blocks_per_seq = dir_width * E on the table those lookups
  * give, bit for bit.  Only the directory entries and leaf entries of a sequence's
- * first ceil(L / B) blocks are followed (the plan pass also reads, without following
- * it, directory entry 0 of an empty context's row); directory entries followed must lie in
+ * first ceil(L / B) blocks are followed; directory entries followed must lie in
  * 0 .. num_leaves - 1 (a device precondition, checked by the debug library).  A batch
  * whose longest table sets the width of every row stores dir_width int32 per
  * sequence plus the leaves it uses, instead of dir_width * E per sequence.
@@ -302,17 +303,23 @@ size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num
  * The two passes of pkv_paged_attention_decode, exposed separately (same arguments,
  * same results when called in this order on one stream with the same workspace and
  * context_lens) so that each pass can be timed on its own:
- *  - plan: picks the partition size, lists the (sequence, partition) items in the
- *    workspace, longest first, and clears the per-row completion counters.  `tables`
- *    (a host struct; NULL allowed) lets it read the first block id of each sequence:
- *    a sequence whose first block equals the previous sequence's (a forked or cached
- *    prefix) has its last partition listed next to that sequence's, so the workgroups
- *    that read the shared blocks run together.  It changes the order only, never a
- *    result;
+ *  - plan: picks the partition size, lists the work items in the workspace, longest
+ *    first, and clears the per-row completion counters.  `tables` (a host struct; NULL
+ *    allowed, which skips this) lets it find shared prefixes (agentalpha.top "Q32：
+ *    vLLM PagedAttention 原理", standard answer part 3; data.6616ai.com
+ *    "PagedAttention：把虚拟内存搬进 KV Cache", copy-on-write sharing): sequences of
+ *    256 tokens or more whose rows start with the same blocks, anywhere within windows
+ *    of 512 sequences, form a group whose common leading blocks (compared entry by
+ *    entry, cut to blocks every member fills) are attended once for the whole group on
+ *    16-bit pools with 2 to 8 query heads per kv head, the members' query heads side by
+ *    side in one item.  Each column of a result depends only on its own sequence's
+ *    tokens and on how its work is split, never on its position in the batch or on the
+ *    other members of its group; a grouped call and an ungrouped one (NULL `tables`)
+ *    split the work differently and may differ in the last bits;
  *  - partitions: one workgroup per item and kv-head group; writes the final output of
- *    sequences that fit one partition and partial results of the others; the
- *    workgroup that completes the last partition of a row merges that row's partials
- *    with log-sum-exp weights.
+ *    sequences that fit one item and partial results of the others; the workgroup
+ *    that completes the last partial of a row merges that row's partials with
+ *    log-sum-exp weights.
  * A partitions pass without a preceding plan pass on that workspace gives undefined
  * output values (but stays within the buffers).  Errors as pkv_paged_attention_decode.
  */
