@@ -880,8 +880,12 @@ struct MergeSmem {
   static constexpr int NCOL = D / 4;
   static constexpr int NG = kThreads / NCOL;
   float red[kWaves];
+  float w[kThreads];  // weights of one chunk of kThreads partials
   f32x4 acc[NG][NCOL];
 };
+
+// Partials whose loads one thread of the merge keeps in flight together.
+constexpr int kMergeUnroll = 8;
 
 // (the partials were stored by an earlier kernel: plain loads)
 template <class T, int D>
@@ -895,9 +899,23 @@ __device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, 
   const float* ml = P.ws_ml + row * P.Pmax * 2;
   const float* po = P.ws_o + row * P.Pmax * D;
 
-  auto ld = [](const float* p) { return *p; };
-  float mx = kNegInf;
-  for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, ld(&ml[2 * i]));
+  const int col = tid % NCOL;
+  const int grp = tid / NCOL;
+  // this thread's first partials (they do not depend on the max: their loads go out
+  // with the (max, sum) loads) and its (max, sum) of the first chunk
+  f32x4 v0[kMergeUnroll];
+  {
+    const int n0 = min(np, kThreads);
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int j = min(grp + u * NG, n0 - 1);
+      v0[u] = *reinterpret_cast<const f32x4*>(po + static_cast<int64_t>(j) * D + col * 4);
+    }
+  }
+  float2 ml0 = make_float2(kNegInf, 0.f);
+  if (tid < np) ml0 = *reinterpret_cast<const float2*>(&ml[2 * tid]);
+  float mx = ml0.x;
+  for (int i = tid + kThreads; i < np; i += kThreads) mx = fmaxf(mx, ml[2 * i]);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, shfl_xor(mx, k));
   if (lane == 0) sm.red[w] = mx;
@@ -905,22 +923,49 @@ __device__ __forceinline__ void merge_row(const Params& P, int64_t row, int np, 
   const float M = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
   __syncthreads();
 
+  // chunks of kThreads partials: each thread's weight into LDS, then every thread adds
+  // its partials (p = grp, grp + NG, ... in order), all of its loads issued together
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int i = tid; i < np; i += kThreads) den += fast_exp2(ld(&ml[2 * i]) - M) * ld(&ml[2 * i + 1]);
+  for (int c0 = 0; c0 < np; c0 += kThreads) {
+    const int i = c0 + tid;
+    float wi = 0.f;
+    if (i < np) {
+      const float2 v = c0 == 0 ? ml0 : *reinterpret_cast<const float2*>(&ml[2 * i]);
+      wi = fast_exp2(v.x - M) * v.y;
+    }
+    den += wi;
+    sm.w[tid] = wi;
+    __syncthreads();
+    const int n = min(np - c0, kThreads);
+    int j0 = grp;
+    if (c0 == 0) {  // the batch loaded up front
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        if (j0 + u * NG < n) acc += sm.w[j0 + u * NG] * v0[u];
+      }
+      j0 += NG * kMergeUnroll;
+    }
+    for (; j0 < n; j0 += NG * kMergeUnroll) {
+      f32x4 v[kMergeUnroll];
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const int j = min(j0 + u * NG, n - 1);  // (an existing partial; its weight is not used)
+        v[u] = *reinterpret_cast<const f32x4*>(po + static_cast<int64_t>(c0 + j) * D + col * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        if (j0 + u * NG < n) acc += sm.w[j0 + u * NG] * v[u];
+      }
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) den += shfl_xor(den, k);
   if (lane == 0) sm.red[w] = den;
   __syncthreads();
   const float DEN = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
 
-  const int col = tid % NCOL;
-  const int grp = tid / NCOL;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int i = grp; i < np; i += NG) {
-    const float wgt = fast_exp2(ld(&ml[2 * i]) - M) * ld(&ml[2 * i + 1]);
-    const float* src = po + static_cast<int64_t>(i) * D + col * 4;
-    acc += wgt * *reinterpret_cast<const f32x4*>(src);
-  }
   sm.acc[grp][col] = acc;
   __syncthreads();
   if (tid < NCOL) {
