@@ -1167,11 +1167,13 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
   // each member's own units [os0, os0 + f_units) (its share of them), listed locally as
   // the part's prefix units, then each member's own units; member k's start at local
   // index f_start (lane k of every wave holds a member's values).
-  int f_own = 0, f_seq = 0, f_start = 0, f_units = 0, f_os0 = 0;
+  int f_own = 0, f_seq = 0, f_start = 0, f_units = 0, f_os0 = 0, f_off = 0;
   int ps0 = 0, ps1 = nblk;
   int wunits = nunits > w ? (nunits - w + kWaves - 1) / kWaves : 0;  // units this wave takes
-  // a member's own unit j goes to wave j % kWaves (and the prefix's unit u to u % kWaves),
-  // so every column meets its units in the same waves and order whatever the other members
+  // A member's own unit j goes to wave (j + off) % kWaves, off a hash of the number of its
+  // own units (and the prefix's unit u to u % kWaves), so every column meets its units in
+  // the same waves and order whatever the other members; the hash spreads the members'
+  // uneven last units over the waves instead of piling them on the first ones.
   auto wave_share = [](int n, int wv) { return n > wv ? (n - wv + kWaves - 1) / kWaves : 0; };
   auto wave_range = [&](int a, int b, int wv) { return wave_share(b, wv) - wave_share(a, wv); };
   if (it.fused) {
@@ -1184,6 +1186,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     const int uk = (f_own + 15) >> 4;
     f_os0 = lane < it.nm ? sp * uk / S : 0;
     f_units = lane < it.nm ? (sp + 1) * uk / S - f_os0 : 0;
+    f_off = static_cast<int>((static_cast<unsigned>(uk) * 2654435761u >> 7) & (kWaves - 1));
     // exclusive scan of the members' own units over lanes (nm <= 16)
     int v = f_units;
 #pragma unroll
@@ -1193,7 +1196,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     }
     f_start = (ps1 - ps0) + v - f_units;
     const int total = __shfl(f_start + f_units, it.nm - 1, 64);
-    int mine = wave_range(f_os0, f_os0 + f_units, w);
+    int mine = wave_range(f_os0 + f_off, f_os0 + f_units + f_off, w);
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) mine += __shfl_xor(mine, d, 64);
     wunits = total > kFusedMaxUnits ? 0 : wave_range(ps0, ps1, w) + __shfl(mine, 0, 64);
@@ -1265,12 +1268,13 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
     const int j = os0k + tid - __shfl(f_start, k, 64);  // member k's own unit (of all its units)
     const int seq_k = __shfl(f_seq, k, 64);
     const int own_k = __shfl(f_own, k, 64);
-    // own unit j of member k: in wave j % kWaves, after that wave's prefix units of the
-    // part and its units of members 0 .. k-1 (the shuffles run in every lane)
-    const int jw = j % kWaves;
-    int before = wave_range(ps0, ps1, jw) + wave_range(os0k, j, jw);
+    const int offk = __shfl(f_off, k, 64);
+    // own unit j of member k: in wave (j + offk) % kWaves, after that wave's prefix units
+    // of the part and its units of members 0 .. k-1 (the shuffles run in every lane)
+    const int jw = (j + offk) % kWaves;
+    int before = wave_range(ps0, ps1, jw) + wave_range(os0k + offk, j + offk, jw);
     for (int q = 0; q < it.nm; ++q) {
-      const int o0 = __shfl(f_os0, q, 64);
+      const int o0 = __shfl(f_os0, q, 64) + __shfl(f_off, q, 64);
       const int uq = __shfl(f_units, q, 64);
       before += q < k ? wave_range(o0, o0 + uq, jw) : 0;
     }
