@@ -160,9 +160,10 @@ def test_two_runs_are_bitwise_identical_and_passes_compose():
     assert torch.equal(a.view(torch.int16), out.view(torch.int16))
 
 
-def test_mfma_group_path_matches_vector_path_on_replicated_heads():
-    """GQA (4 query heads per kv head, MFMA) vs the same data with kv heads
-    replicated into an MHA pool (one query head per kv head, vector ALU)."""
+def test_query_group_matches_replicated_single_heads():
+    """GQA (4 query heads per kv head: 4 columns of each MFMA product) vs the same data
+    with kv heads replicated into an MHA pool (one query head per kv head: one column
+    per product)."""
     w = synth.gqa_bf16(num_seqs=6, max_len=2000)
     st = replay_gpu(w, w.all_context_kv(), DEV)
     q = to_device(w.queries(), w.dtype, DEV)

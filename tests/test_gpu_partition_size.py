@@ -275,7 +275,7 @@ def test_device_choice_matches_host_rule(name, lens_fn, hq, hkv):
     pt = pkv.decode_partition_tokens(lens, hq, hkv)
     log(f"{name}: host rule {pt}, device log2 {plan[0][1]}, {plan[0][0]} items")
     assert 1 << int(plan[0][1]) == pt
-    assert _check_plan(plan, lens, rows, pt, 16 // (hq // hkv) if 2 <= hq // hkv <= 8 else 0) == []
+    assert _check_plan(plan, lens, rows, pt, 16 // (hq // hkv) if 1 <= hq // hkv <= 8 else 0) == []
 
 
 @pytest.mark.parametrize("tokens", [512, 1024, 2048])
