@@ -311,7 +311,7 @@ size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num
  *    256 tokens or more whose rows start with the same blocks, anywhere within windows
  *    of 512 sequences, form a group whose common leading blocks (compared entry by
  *    entry, cut to blocks every member fills) are attended once for the whole group on
- *    16-bit pools with 2 to 8 query heads per kv head, the members' query heads side by
+ *    16-bit pools with 1 to 8 query heads per kv head, the members' query heads side by
  *    side in one item.  Each column of a result depends only on its own sequence's
  *    tokens and on how its work is split, never on its position in the batch or on the
  *    other members of its group; a grouped call and an ungrouped one (NULL `tables`)

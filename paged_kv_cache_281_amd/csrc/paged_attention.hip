@@ -1402,7 +1402,7 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
 }
 
 // ---------------------------------------------------------------------------------
-// MFMA partition kernel with 32-token units (bf16/fp16, 2..16 query heads): one unit
+// MFMA partition kernel with 32-token units (bf16/fp16, 1..16 query heads): one unit
 // is one 32-token block, or two consecutive 16-token blocks.  The scores of a unit are
 // two 16x16x32 MFMA chains over D whose rows are the tokens tau_s(i) =
 // 8*(i/4) + 4*s + i%4 (s = 0, 1), so that lane (r, m) ends up holding the scores of
@@ -1896,8 +1896,8 @@ Params make_params(const AttnArgs& a) {
   P.leaf_e = PKV_LEAF_TOKENS / a.block_size;
   P.slots = a.slots;
   P.force_log2 = a.force_log2;
-  // shared-prefix items need the MFMA kernels (16-bit pools, 2..16 query heads per kv
-  // head) and at least two sequences per item
+  // shared-prefix items need the MFMA kernels (16-bit pools, 1..8 query heads per kv
+  // head, so that an item holds at least two sequences)
   P.cm = (a.dtype != PKV_F32 && P.G >= 1 && P.G <= 8) ? 16 / P.G : 0;
   P.fuse_ok = (P.cm >= 2 && a.block_size == 16 && !kUnit32<16>) ? 1 : 0;
   P.member_own = a.member_own;
