@@ -412,9 +412,15 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(sc[k][e], cs, -m_run[k]));
-      l_run[k] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) pb[k][kk] = T::pack2(p[2 * kk], p[2 * kk + 1]);
+      // the row's sum gathers the probabilities as rounded for the P.V product (two per
+      // dot2 with ones: half the VALU operations of separate adds)
+      const u32 one2 = T::pack2(1.f, 1.f);
+      float lk = T::dot2(pb[k][0], one2, l_run[k]);
+      lk = T::dot2(pb[k][1], one2, lk);
+      lk = T::dot2(pb[k][2], one2, lk);
+      l_run[k] = T::dot2(pb[k][3], one2, lk);
     }
     pv(base, pb);
   };
