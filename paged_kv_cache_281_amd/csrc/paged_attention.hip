@@ -1360,12 +1360,13 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
         f.v[c][1] &= mhi;
       }
     }
+    // This lane's max over its scores; a column's four lanes are combined only when one
+    // of them is above the threshold (the column's max then is too: the same decisions
+    // and values as combining them on every unit).  Each column (lane m of every row)
+    // decides its own rescale, so no column's result depends on the other columns.
     float mx = fmaxf(fmaxf(s0, s1), fmaxf(s2, s3));
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    // each column (lane m of every row) decides its own rescale, so no column's result
-    // depends on the other columns of the product
     if (wave_any(mx > m_run + kRescaleLog2)) {
+      mx = max_xor32(max_xor16(mx));
       const bool raise = mx > m_run + kRescaleLog2;
       const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;
       l_part *= alpha;
@@ -1588,12 +1589,11 @@ __global__ __launch_bounds__(kThreads, PKV_MFMA_WAVES_PER_EU) void attn_partitio
         for (int c = 0; c < NC; ++c) f.v[c][k] &= msk;
       }
     }
+    // (a column's lanes are combined only when a rescale may be due, as in the 16-token
+    // kernel; each column decides its own rescale)
     float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    // each column (lane m of every row) decides its own rescale, so no column's result
-    // depends on the other columns of the product
     if (wave_any(mx > m_run + kRescaleLog2)) {
+      mx = max_xor32(max_xor16(mx));
       const bool raise = mx > m_run + kRescaleLog2;
       const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;
       l_part *= alpha;
@@ -1781,9 +1781,10 @@ __global__ __launch_bounds__(kThreads, T::kBytes == 2 ? 4 : 1) void attn_partiti
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float mx = row_max16(s[g]);
-      if (wave_any(mx > m_run[g] + kRescaleLog2)) {
-        const float mn = fmaxf(m_run[g], mx);
+      // (the row's max only when a lane's score may call for a rescale: the row's max
+      // is above the threshold exactly when one of its lanes is)
+      if (wave_any(s[g] > m_run[g] + kRescaleLog2)) {
+        const float mn = fmaxf(m_run[g], row_max16(s[g]));
         const float alpha = fast_exp2(m_run[g] - mn);
         l_part[g] *= alpha;
 #pragma unroll

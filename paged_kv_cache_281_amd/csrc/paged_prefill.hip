@@ -384,26 +384,29 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
         for (int e = 0; e < 8; ++e) sc[k][e] = (j0 + e <= pos[k]) ? sc[k][e] : kNegInf;
       }
     }
+    // This lane's max over its 8 scores first; a row's four lanes are combined only when
+    // one of them is above the threshold, since the row's max then is too: the same
+    // decisions and values as combining them on every unit.
     float mx[RG];
     bool grow = false;
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
       // (three-input groups: each becomes one v_max3)
-      float v = fmaxf(fmaxf(fmaxf(sc[k][0], sc[k][1]), sc[k][2]),
-                      fmaxf(fmaxf(fmaxf(sc[k][3], sc[k][4]), sc[k][5]), fmaxf(sc[k][6], sc[k][7])));
-      v = max_xor16(v);
-      mx[k] = max_xor32(v) * cs;  // scale > 0: the max of the scaled scores
+      const float v = fmaxf(fmaxf(fmaxf(sc[k][0], sc[k][1]), sc[k][2]),
+                            fmaxf(fmaxf(fmaxf(sc[k][3], sc[k][4]), sc[k][5]), fmaxf(sc[k][6], sc[k][7])));
+      mx[k] = v * cs;  // scale > 0: the max of the scaled scores
       grow = grow || (mx[k] > m_run[k] + kPfRescaleLog2);
     }
     if (wave_any(grow)) {  // rare: some row's max rose by more than the threshold
 #pragma unroll
       for (int k = 0; k < RG; ++k) {
-        const bool raise = mx[k] > m_run[k] + kPfRescaleLog2;  // each row (lane m) on its own
-        const float alpha = raise ? fast_exp2(m_run[k] - mx[k]) : 1.f;
+        const float rmx = max_xor32(max_xor16(mx[k]));       // the row's max
+        const bool raise = rmx > m_run[k] + kPfRescaleLog2;  // each row (lane m) on its own
+        const float alpha = raise ? fast_exp2(m_run[k] - rmx) : 1.f;
         l_run[k] *= alpha;
 #pragma unroll
         for (int c = 0; c < NC; ++c) o[k][c] *= alpha;
-        m_run[k] = raise ? mx[k] : m_run[k];
+        m_run[k] = raise ? rmx : m_run[k];
       }
     }
     u32x4 pb[RG];
