@@ -161,16 +161,21 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan(PrefillParams P) {
 // the pool straight into LDS (global_load_lds: every lane moves 16 bytes to its place in
 // a 1 KiB run), in a ring of kPfStages buffers: unit u + 2 is in flight while unit u is
 // computed, and one barrier per unit both publishes unit u + 1 and frees the buffer of
-// unit u - 1.  K is stored as [chunk][half s][m] 16-byte pieces, where slot (s, m)
-// holds token tau_s(m), so the 16 lanes of a fragment read touch 256 contiguous bytes;
-// a V row (32 tokens, 64 bytes) holds its four 16-byte pieces in the order
-// q ^ ((row / 4) % 4), so the 16 rows of a fragment read fall in distinct banks.  Each
-// wave reads a fragment just before the products that use it, once for all RG of its
-// 16-row groups.
+// unit u - 1.  Each half of K and of V holds the tokens of one 16-token half of the
+// unit (one block at block size 16), so every 1 KiB copy run reads a single block: its
+// tile address is the same for all lanes (scalar), and each lane only adds a fixed
+// offset.  K half h: chunk c (8 elements of d), token t of the half at 16-byte piece
+// c * 16 + (t ^ 4h); V half h: row d, tokens 8 q .. 8 q + 7 of the half (q = 0, 1) at
+// piece d * 2 + (q ^ ((d / 8) % 2)).  The XORs put the 16 lanes of a fragment read
+// (8 tokens from each half, or 16 rows) in distinct banks.  Each wave reads a fragment
+// just before the products that use it, once for all RG of its 16-row groups.
 template <int D>
 struct PrefillLds {
   static constexpr int kKPieces = D / 8 * 32;  // 16-byte K pieces per unit
   static constexpr int kVPieces = D * 4;       // 16-byte V pieces per unit
+  static constexpr int kKHalf = kKPieces / 2;  // pieces of one token half
+  static constexpr int kVHalf = kVPieces / 2;
+  static_assert(kKHalf % 64 == 0 && kVHalf % 64 == 0, "a copy run lies in one half");
   static constexpr int kKBytes = kKPieces * 16;
   static constexpr int kBytes = (kKPieces + kVPieces) * 16;
   static constexpr int kRuns = (kKPieces + kVPieces) / 64;  // 64-piece runs (one load instruction each)
@@ -247,32 +252,35 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
   }
 
   // This thread's piece of each of its NX runs: run x*kPfWaves + w, piece (run * 64 + lane).
-  // K piece i -> chunk i / 32, slot i % 32 (slot = 16 s + mm holds token tau_s(mm)); V
-  // piece j -> row j / 4, position j % 4 holding tokens 8 q .. 8 q + 7, q = pos ^ ((row / 4) % 4).
+  // K piece i -> half h = i / KH, chunk c, token 16 h + t of the unit (layout above); V
+  // piece j -> half h, row d, tokens 16 h + 8 q .. + 7.  The half of a run is the same for
+  // all its lanes (g_hi: a scalar choice of the tile at block size 16).
+  constexpr int KH = PrefillLds<D>::kKHalf;
+  constexpr int VH = PrefillLds<D>::kVHalf;
   constexpr int LEAF = PKV_LEAF_TOKENS / B;  // two-level leaf entries
   const int64_t bstride = static_cast<int64_t>(P.Hkv) * TILE;
   const char* kbase = P.kp + kvh * TILE;
   const char* vbase = P.vp + kvh * TILE;
   int g_off[NX];
-  bool g_hi[NX];  // (16-token blocks) the piece comes from the unit's second block
+  bool g_hi[NX];  // (16-token blocks) the run comes from the unit's second block
 #pragma unroll
   for (int x = 0; x < NX; ++x) {
     const int run = x * kPfWaves + w;
-    const int i = run * 64 + lane;
     if (run < KRUNS) {
-      const int c = i >> 5;
-      const int slot = i & 31;
-      const int ss = slot >> 4;
-      const int mm = slot & 15;
-      const int tok = 8 * (mm >> 2) + 4 * ss + (mm & 3);
-      g_hi[x] = BPU == 2 && tok >= 16;
-      g_off[x] = (c * B + (BPU == 2 ? (tok & 15) : tok)) * 16;
+      const int h = run * 64 / KH;
+      const int wi = run * 64 - h * KH + lane;
+      const int c = wi >> 4;
+      const int t = (wi & 15) ^ (4 * h);
+      g_hi[x] = BPU == 2 && h == 1;
+      g_off[x] = (c * B + (BPU == 2 ? t : 16 * h + t)) * 16;
     } else {
-      const int j = i - PrefillLds<D>::kKPieces;
-      const int d = j >> 2;
-      const int q = (j & 3) ^ ((d >> 2) & 3);
-      g_hi[x] = BPU == 2 && q >= 2;
-      g_off[x] = (d * B + 8 * (BPU == 2 ? (q & 1) : q)) * EB;
+      const int j0 = run * 64 - PrefillLds<D>::kKPieces;
+      const int h = j0 / VH;
+      const int wi = j0 - h * VH + lane;
+      const int d = wi >> 1;
+      const int q = (wi & 1) ^ ((d >> 3) & 1);
+      g_hi[x] = BPU == 2 && h == 1;
+      g_off[x] = (d * B + (BPU == 2 ? 8 * q : 16 * h + 8 * q)) * EB;
     }
   }
   auto fetch = [&](int u, int stage) {
@@ -281,7 +289,8 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     // an absent second block reuses the first
     const int blk0 = table_entry_uniform<Tab, LEAF>(P.tables, P.dir, b, P.W, e0);
     const int blk1 = BPU == 2 ? table_entry_uniform<Tab, LEAF>(P.tables, P.dir, b, P.W, min(e0 + 1, nblk - 1)) : blk0;
-    // the unit's tiles (scalar addresses); each lane then picks its tile and adds its offset
+    // the unit's tiles (scalar addresses); each run takes one of them (a scalar choice)
+    // and each lane adds its fixed offset
     const char* kt0 = kbase + blk0 * bstride;
     const char* kt1 = kbase + blk1 * bstride;
     const char* vt0 = vbase + blk0 * bstride;
@@ -306,15 +315,20 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     for (int c = 0; c < NC; ++c) o[k][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float cs = P.scale_log2;
-  const int vsw = (m >> 2) & 3;  // V piece swizzle of this lane's fragment rows
+  // this lane's pieces in the fragment reads (layout above): K fragment (ki, s2) reads
+  // chunk 4 ki + r, token tau_s2(m) = 8 (m / 4) + 4 s2 + m % 4 of the unit, which lies in
+  // half m / 8; V fragment c reads row 16 c + m, tokens 8 r .. 8 r + 7 (half r / 2)
+  const int kh = m >> 3;
+  const int kpiece = kh * KH + r * 16 + 8 * ((m >> 2) & 1) + (m & 3);
+  const int vpiece = PrefillLds<D>::kKPieces + (r >> 1) * VH + m * 2 + ((r & 1) ^ ((m >> 3) & 1));
 
   // LDS fragment reads are issued one step ahead of the products that use them (two
   // register buffers), so each read has a step of MFMAs to land.
   auto kfrag = [&](const char* base, int ki, int s2) {
-    return *reinterpret_cast<const u32x4*>(base + ((4 * ki + r) * 32 + 16 * s2 + m) * 16);
+    return *reinterpret_cast<const u32x4*>(base + (kpiece + 64 * ki + 4 * (s2 ^ kh)) * 16);
   };
   auto vfrag = [&](const char* base, int c) {
-    return *reinterpret_cast<const u32x4*>(base + KB + ((16 * c + m) * 4 + (r ^ vsw)) * 16);
+    return *reinterpret_cast<const u32x4*>(base + (vpiece + 32 * c) * 16);
   };
   // P.V over the unit (V of tokens past the context was zeroed in LDS)
   auto pv = [&](const char* base, const u32x4 (&pb)[RG]) {
@@ -333,8 +347,9 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     char* base = s_kv[stage] + KB;
     const int t0 = L - 32 * u;  // first local token past the context
     for (int i = tid; i < D * 4; i += kPfThreads) {
-      const int d = i >> 2;
-      const int q = (i & 3) ^ ((d >> 2) & 3);  // tokens 8q .. 8q + 7 at position i % 4
+      const int h = i / VH;
+      const int d = (i - h * VH) >> 1;
+      const int q = 2 * h + ((i & 1) ^ ((d >> 3) & 1));  // tokens 8q .. 8q + 7 of the unit
       if (8 * q + 8 <= t0) continue;
       u32x4* pc = reinterpret_cast<u32x4*>(base + i * 16);
       u32x4 v = *pc;
