@@ -305,30 +305,37 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     }
   };
 
-  float m_run[RG], l_run[RG];
+  const float cs = P.scale_log2;
+  const float inv_cs = 1.f / cs;
+  // m_run: the row's running max of the scaled scores; lim: the raw score above which a
+  // rescale is due, (m_run + threshold) / cs, kept beside it so that the common case
+  // compares raw scores without scaling them
+  float m_run[RG], lim[RG], l_run[RG];
   f32x4 o[RG][NC];
 #pragma unroll
   for (int k = 0; k < RG; ++k) {
     m_run[k] = kNegInf;
+    lim[k] = kNegInf;
     l_run[k] = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) o[k][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float cs = P.scale_log2;
   // this lane's pieces in the fragment reads (layout above): K fragment (ki, s2) reads
   // chunk 4 ki + r, token tau_s2(m) = 8 (m / 4) + 4 s2 + m % 4 of the unit, which lies in
   // half m / 8; V fragment c reads row 16 c + m, tokens 8 r .. 8 r + 7 (half r / 2)
   const int kh = m >> 3;
   const int kpiece = kh * KH + r * 16 + 8 * ((m >> 2) & 1) + (m & 3);
-  const int vpiece = PrefillLds<D>::kKPieces + (r >> 1) * VH + m * 2 + ((r & 1) ^ ((m >> 3) & 1));
+  const int kbyte[2] = {(kpiece + 4 * kh) * 16, (kpiece + 4 * (kh ^ 1)) * 16};  // s2 = 0, 1
+  const int vbyte = (PrefillLds<D>::kKPieces + (r >> 1) * VH + m * 2 + ((r & 1) ^ ((m >> 3) & 1))) * 16;
 
   // LDS fragment reads are issued one step ahead of the products that use them (two
   // register buffers), so each read has a step of MFMAs to land.
+  // (a lane offset per unit, the rest an immediate of the read)
   auto kfrag = [&](const char* base, int ki, int s2) {
-    return *reinterpret_cast<const u32x4*>(base + (kpiece + 64 * ki + 4 * (s2 ^ kh)) * 16);
+    return *reinterpret_cast<const u32x4*>(base + kbyte[s2] + 1024 * ki);
   };
   auto vfrag = [&](const char* base, int c) {
-    return *reinterpret_cast<const u32x4*>(base + (vpiece + 32 * c) * 16);
+    return *reinterpret_cast<const u32x4*>(base + vbyte + 512 * c);
   };
   // P.V over the unit (V of tokens past the context was zeroed in LDS)
   auto pv = [&](const char* base, const u32x4 (&pb)[RG]) {
@@ -399,29 +406,29 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
         for (int e = 0; e < 8; ++e) sc[k][e] = (j0 + e <= pos[k]) ? sc[k][e] : kNegInf;
       }
     }
-    // This lane's max over its 8 scores first; a row's four lanes are combined only when
-    // one of them is above the threshold, since the row's max then is too: the same
-    // decisions and values as combining them on every unit.
+    // This lane's max over its 8 raw scores first; a row's four lanes are combined only
+    // when one of them is above the row's limit, since the row's max then is too.
     float mx[RG];
-    bool grow = false;
+    unsigned long long grow = 0;
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
       // (three-input groups: each becomes one v_max3)
-      const float v = fmaxf(fmaxf(fmaxf(sc[k][0], sc[k][1]), sc[k][2]),
-                            fmaxf(fmaxf(fmaxf(sc[k][3], sc[k][4]), sc[k][5]), fmaxf(sc[k][6], sc[k][7])));
-      mx[k] = v * cs;  // scale > 0: the max of the scaled scores
-      grow = grow || (mx[k] > m_run[k] + kPfRescaleLog2);
+      mx[k] = fmaxf(fmaxf(fmaxf(sc[k][0], sc[k][1]), sc[k][2]),
+                    fmaxf(fmaxf(fmaxf(sc[k][3], sc[k][4]), sc[k][5]), fmaxf(sc[k][6], sc[k][7])));
+      grow |= __builtin_amdgcn_ballot_w64(mx[k] > lim[k]);
     }
-    if (wave_any(grow)) {  // rare: some row's max rose by more than the threshold
+    if (grow != 0) {  // rare: some row's max passed its limit
 #pragma unroll
       for (int k = 0; k < RG; ++k) {
-        const float rmx = max_xor32(max_xor16(mx[k]));       // the row's max
-        const bool raise = rmx > m_run[k] + kPfRescaleLog2;  // each row (lane m) on its own
-        const float alpha = raise ? fast_exp2(m_run[k] - rmx) : 1.f;
+        const float rmx = max_xor32(max_xor16(mx[k]));  // the row's max (raw)
+        const bool raise = rmx > lim[k];                 // each row (lane m) on its own
+        const float nm = rmx * cs;                       // scale > 0: the max of the scaled scores
+        const float alpha = raise ? fast_exp2(m_run[k] - nm) : 1.f;
         l_run[k] *= alpha;
 #pragma unroll
         for (int c = 0; c < NC; ++c) o[k][c] *= alpha;
-        m_run[k] = raise ? rmx : m_run[k];
+        m_run[k] = raise ? nm : m_run[k];
+        lim[k] = raise ? (nm + kPfRescaleLog2) * inv_cs : lim[k];
       }
     }
     u32x4 pb[RG];
