@@ -412,9 +412,10 @@ __global__ __launch_bounds__(kPfThreads) void attn_prefill_lds(PrefillParams P) 
     unsigned long long grow = 0;
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
-      // (three-input groups: each becomes one v_max3)
-      mx[k] = fmaxf(fmaxf(fmaxf(sc[k][0], sc[k][1]), sc[k][2]),
-                    fmaxf(fmaxf(fmaxf(sc[k][3], sc[k][4]), sc[k][5]), fmaxf(sc[k][6], sc[k][7])));
+      // (nested pairs of fmaxf become v_max3: three of them and one v_max for 8 values)
+      const float a = fmaxf(fmaxf(sc[k][0], sc[k][1]), sc[k][2]);
+      const float bb = fmaxf(fmaxf(sc[k][3], sc[k][4]), sc[k][5]);
+      mx[k] = fmaxf(fmaxf(fmaxf(a, bb), sc[k][6]), sc[k][7]);
       grow |= __builtin_amdgcn_ballot_w64(mx[k] > lim[k]);
     }
     if (grow != 0) {  // rare: some row's max passed its limit
