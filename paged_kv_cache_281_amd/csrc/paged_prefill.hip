@@ -17,9 +17,9 @@
 // tasks that exist, those reading the most K/V first.
 // The workgroup walks 32-token units of K/V (one 32-token block or two 16-token
 // blocks) from position 0 up to the last position its rows can see.  All 256 threads
-// copy each unit from the pool into an LDS double buffer, issuing the next unit's
-// loads before the current one is computed, with one barrier per unit; each wave
-// reads the unit's fragments once and uses them for all of its RG groups of 16 rows.
+// copy each unit from the pool into a ring of three LDS buffers, two units ahead of
+// the one being computed, with one barrier per unit; each wave reads the unit's
+// fragments once and uses them for all of its RG groups of 16 rows.
 //
 // Products (16x16x32 bf16/fp16 MFMA, fp32 accumulate), per 16 rows:
 //   S^T[token][row] = K[token][:] . Q[row][:]   (K fragment as A, Q^T as B)
@@ -28,7 +28,7 @@
 // tau_s(i) = 8*(i/4) + 4*s + i%4 (s = 0, 1), so lane (r, m) holds the scores of
 // tokens 8r..8r+7 of row m: after the softmax, rounded to the pool type, they are the
 // B operand of the P.V product as they stand, and its A operand (V^T) is 16
-// contiguous bytes of a V row.
+// bytes of a V row (the 16 bytes of tokens 8r..8r+7, contiguous in LDS).
 //
 // Masking: a score is kept when its token is <= the row's position (a select, so a
 // NaN in a masked slot never propagates; applied only on units that reach past a
