@@ -35,6 +35,23 @@ def to_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
     return b.view(np.uint32 if dtype == "f32" else np.uint16)
 
 
+def value_bits(values: np.ndarray, dtype: str) -> np.ndarray:
+    """Bits of float values rounded to the pool type (as the library stores them)."""
+    t = torch.from_numpy(np.ascontiguousarray(values, dtype=np.float32)).to(TORCH_DTYPE[dtype])
+    return to_bits(t, dtype)
+
+
+def rising_keys(context, dtype: str, head_dim: int, step: float):
+    """The context with every element of the key at position t set to step * t / head_dim
+    (values unchanged): with all-ones queries the score of position t is step * t, so
+    every later block raises a row's maximum past the lazy-rescale threshold."""
+    out = {}
+    for s, (k, v) in context.items():
+        vals = np.broadcast_to((step * np.arange(k.shape[0], dtype=np.float32) / head_dim)[:, None, None], k.shape)
+        out[s] = (value_bits(vals, dtype), v)
+    return out
+
+
 @dataclasses.dataclass
 class GpuState:
     bm: pkv.BlockManager
@@ -110,8 +127,9 @@ def run_attention(w, st: GpuState, q_bits: np.ndarray, device="cuda") -> torch.T
     return out
 
 
-def compare(w, got: torch.Tensor, ref: np.ndarray, rows=None):
-    """Assert the GPU output matches the oracle: fp32 max-abs 1e-5; 16-bit types
+def compare(w, got: torch.Tensor, ref: np.ndarray, rows=None, f32_atol: float = 1e-5):
+    """Assert the GPU output matches the oracle: fp32 max-abs f32_atol (1e-5 unless a
+    case derives a larger bound from its logits); 16-bit types
     |gpu - oracle| <= 2e-2 + 1e-2 |oracle| elementwise and relative L2 error per
     (sequence, head) below 1e-2.  Returns (max abs error, max relative L2 error)."""
     g = widen(to_bits(got, w.dtype), w.dtype)
@@ -123,7 +141,7 @@ def compare(w, got: torch.Tensor, ref: np.ndarray, rows=None):
     rel = np.linalg.norm(g - ref, axis=-1) / np.maximum(nrm, 1e-30)
     rel = np.where(nrm > 0, rel, 0.0)
     if w.dtype == "f32":
-        assert err.max() <= 1e-5, f"max abs err {err.max()}"
+        assert err.max() <= f32_atol, f"max abs err {err.max()}"
     else:
         bad = err > 2e-2 + 1e-2 * np.abs(ref)
         assert not bad.any(), f"{bad.sum()} elements out of tolerance, max abs err {err.max()}"

@@ -14,9 +14,10 @@ import torch
 
 import synth
 from oracle.attention import paged_attention_decode as oracle_attention
+from oracle.numerics import widen
 from oracle.replay import replay as oracle_replay
-from gpu_harness import (compare, log, nan_block, replay_gpu, run_attention, to_bits, to_device,
-                         TORCH_DTYPE)
+from gpu_harness import (compare, log, nan_block, replay_gpu, rising_keys, run_attention, to_bits, to_device,
+                         value_bits, TORCH_DTYPE)
 import paged_kv_cache_281_amd as pkv
 
 pytestmark = pytest.mark.gpu
@@ -115,6 +116,46 @@ def test_shape_variants(v):
 def test_peaked_queries_need_max_subtraction():
     """q x 30: logits of order 1e2..1e3, exp overflows without the running max."""
     _run_case(synth.gqa_bf16(num_seqs=6, max_len=1400), q_scale=30.0)
+
+
+RISING = [
+    # name, workload: keys that grow with position (rising_keys), all-ones queries
+    ("rise_gqa_b16", lambda n: _custom(n, "bf16", 8, 2, 128, 16, [40, 700, 2100], seed=21)),
+    ("rise_mha_b16", lambda n: _custom(n, "bf16", 4, 4, 128, 16, [33, 1500], seed=22)),
+    ("rise_gqa_b32", lambda n: _custom(n, "bf16", 8, 2, 128, 32, [100, 1300], seed=23)),
+    ("rise_f32_b16", lambda n: _custom(n, "f32", 4, 2, 128, 16, [20, 900], seed=24)),
+    ("rise_forked", lambda n: synth.cow_fp16(1020, num_prompts=2, max_suffix=40)),
+]
+
+
+@pytest.mark.parametrize("name,make", RISING, ids=[r[0] for r in RISING])
+def test_scores_rising_on_every_unit(name, make):
+    """A row's score rises by 8 / sqrt(D) per token (about 16 in log2 units per 16-token
+    unit at D = 128), so its running maximum passes the lazy-rescale threshold on every
+    unit of the context: the rescale path of every kernel runs unit after unit.  The
+    forked case puts the rising keys in the shared prompt (fused items).
+
+    fp32 bound: the logits reach L = 8 * max(context) * scale * log2(e) (about 900 here)
+    in the kernel's log2 units, where one fp32 rounding of a logit, or of the running
+    maximum, moves a weight by L * 2^-24 relative; the output, a mean of values of at
+    most |V|max, then moves by up to 2 * 2 * L * 2^-24 * |V|max (two roundings, both
+    signs of error), so the case allows 1e-5 + 8 * 2^-24 * L * |V|max."""
+    w = make(name)
+    ctx = rising_keys(w.all_context_kv(), w.dtype, w.head_dim, 8.0)
+    q = value_bits(np.ones((w.num_seqs, w.num_q_heads, w.head_dim), np.float32), w.dtype)
+    log(f"case {name}: N={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} B={w.block_size} dtype={w.dtype}")
+    st = replay_gpu(w, ctx, DEV)
+    pad = nan_block(w, st.bm)
+    ora = oracle_replay(w, synth.NAN_BITS[w.dtype], pad=pad, context=ctx)
+    tables = np.asarray(st.bm.block_tables(w.batch, w.max_blocks_per_seq, pad))
+    assert (tables == ora.block_tables).all()
+    st.tables = torch.from_numpy(tables).to(DEV)
+    out = run_attention(w, st, q, DEV)
+    ref = oracle_attention(q, w.dtype, ora.pool, tables, ora.context_lens, w.scale)
+    L = 8.0 * float(ora.context_lens.max()) * w.scale * np.log2(np.e)
+    vmax = max(float(np.abs(widen(v, w.dtype)).max()) for _, v in ctx.values())
+    err, rel = compare(w, out, ref, f32_atol=1e-5 + 8 * 2.0 ** -24 * L * vmax)
+    log(f"case {name}: max abs err {err:.3e}, max rel L2 {rel:.3e} (logits up to {L:.0f})")
 
 
 def test_empty_context_gives_zero_rows():
