@@ -319,7 +319,9 @@ size_t pkv_paged_attention_prefill_workspace_bytes(int32_t num_seqs, int32_t num
  *  - partitions: one workgroup per item and kv-head group; writes the final output of
  *    sequences that fit one item and partial results of the others; the workgroup
  *    that completes the last partial of a row merges that row's partials with
- *    log-sum-exp weights.
+ *    log-sum-exp weights.  Its grid holds as many items as the last plan pass this
+ *    process launched on the workspace could list (half as many when that plan could
+ *    not use 512-token partitions), so the partition size may change between the calls.
  * A partitions pass without a preceding plan pass on that workspace gives undefined
  * output values (but stays within the buffers).  Errors as pkv_paged_attention_decode.
  */

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -188,6 +189,48 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int32_t> g_slots[kMaxDevices];
 std::atomic<int32_t> g_force_log2{0};
+
+// The smallest partition (log2 of tokens) that each workspace's last plan pass could
+// use, so that a partition pass launched on its own sizes its grid for that plan's item
+// list even if the partition size was changed in between.  A workspace that is not on
+// record gets the grid of 512-token partitions, which holds any list.
+struct PlanFloor {
+  const void* ws = nullptr;
+  int32_t lg = 0;
+};
+constexpr int kPlanFloors = 64;
+std::mutex g_plan_mu;
+PlanFloor g_plan_floor[kPlanFloors];
+int g_plan_next = 0;
+
+int32_t plan_floor_log2(int32_t force_log2) { return force_log2 ? force_log2 : kLgPartMin; }
+
+void record_plan(const void* ws, int32_t force_log2) {
+  const int32_t lg = plan_floor_log2(force_log2);
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  for (PlanFloor& r : g_plan_floor) {
+    if (r.ws == ws) {
+      r.lg = lg;
+      return;
+    }
+  }
+  g_plan_floor[g_plan_next] = {ws, lg};
+  g_plan_next = (g_plan_next + 1) % kPlanFloors;
+}
+
+int32_t recorded_plan_floor(const void* ws) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  for (const PlanFloor& r : g_plan_floor)
+    if (r.ws == ws) return r.lg;
+  return kLgPartFloor;
+}
+
+// Items per sequence in the partition grid after a plan whose partitions hold at least
+// 2^floor_lg tokens.
+int32_t grid_parts_for(const AttnArgs& a, int32_t floor_lg) {
+  return floor_lg >= kLgPartMin ? static_cast<int32_t>(grid_partitions(a.max_blocks_per_seq, a.block_size))
+                                : a.max_parts;
+}
 }  // namespace
 
 int32_t resident_slots() {
@@ -425,6 +468,7 @@ int32_t pkv_decode_prepare(const pkv_pool_desc* pool, void* k_pool, void* v_pool
                                       num_seqs, stream)) != PKV_OK)
       return st;
   }
+  pkv::record_plan(workspace, c.args.force_log2);
   return pkv::launch_status(pkv::launch_decode_prepare(c.args, *pool, k_pool, v_pool, k_new, v_new, slot_mapping,
                                                        num_tokens, stream),
                             "pkv_decode_prepare");
@@ -567,7 +611,16 @@ int32_t partitions_impl(const char* who, const pkv_pool_desc* pool, const void* 
     if (st != PKV_OK) return st;
   }
   c.args.table_dir = two.dir;
+  c.args.grid_parts =
+      grid_parts_for(c.args, with_plan ? plan_floor_log2(c.args.force_log2) : recorded_plan_floor(workspace));
+  if (kDebugChecks && !with_plan) {
+    std::vector<int32_t> cnt;
+    if (!fetch_host(c.args.counters, 1, stream, cnt)) return debug_fail(who, "cannot read the plan's item count");
+    if (cnt[0] < 0 || static_cast<int64_t>(cnt[0]) > static_cast<int64_t>(num_seqs) * c.args.grid_parts)
+      return debug_fail(who, "the plan's item list does not fit the partition grid");
+  }
   if (with_plan) {
+    record_plan(workspace, c.args.force_log2);
     const int rc = launch_attn_plan(c.args, stream);
     if (rc != 0) return launch_status(rc, who);
   }
@@ -631,6 +684,7 @@ int32_t pkv_paged_attention_plan(const pkv_pool_desc* pool, int32_t num_seqs, in
                                                context_lens, num_seqs, stream);
     if (st != PKV_OK) return st;
   }
+  pkv::record_plan(workspace, c.args.force_log2);
   return pkv::launch_status(pkv::launch_attn_plan(c.args, stream), "pkv_paged_attention_plan");
 }
 

@@ -1910,7 +1910,7 @@ template <class T, int D, int B, class Tab>
 int launch_partitions_t(const AttnArgs& a, hipStream_t s) {
   const Params P = make_params(a);
   const dim3 block(kThreads);
-  const int64_t items = static_cast<int64_t>(a.num_seqs) * a.max_parts;
+  const int64_t items = static_cast<int64_t>(a.num_seqs) * (a.grid_parts > 0 ? a.grid_parts : a.max_parts);
   // fp32 pools run on the vector ALU; 16-bit pools on the MFMA kernel, MHA (one query
   // head per KV head) included: its idle product columns then hold the query heads of
   // forked sequences that share a prefix.  Measured: a forked MHA batch (64 prompts x 4

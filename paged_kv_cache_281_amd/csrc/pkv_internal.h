@@ -31,6 +31,16 @@ inline int64_t max_partitions(int64_t max_blocks_per_seq, int64_t block_size) {
   return (max_blocks_per_seq * block_size + PKV_PARTITION_TOKENS_MIN - 1) / PKV_PARTITION_TOKENS_MIN + 1;
 }
 
+// Items per sequence the plan can list when its partitions hold at least
+// PKV_PARTITION_TOKENS tokens: a sequence's own partitions plus one for a split at the
+// end of a shared prefix; a fused group of c members lists ceil(c / cm) column sets
+// (cm >= 2) of at most min(4, max_partitions) parts, which stays within c times this
+// count.  The partition kernels' grid holds this many items per sequence then, half of
+// what 512-token partitions need.
+inline int64_t grid_partitions(int64_t max_blocks_per_seq, int64_t block_size) {
+  return (max_blocks_per_seq * block_size + PKV_PARTITION_TOKENS - 1) / PKV_PARTITION_TOKENS + 1;
+}
+
 // Kernel launchers (defined in the .hip files).  They assume validated arguments
 // and return a hipError_t value as int.
 int launch_kv_write(const pkv_pool_desc& pool, void* k_pool, void* v_pool, const void* k_new,
@@ -63,6 +73,7 @@ struct AttnArgs {
   int* member_own;  // [num_seqs]: beside members, each member's own tokens
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dtype;
   int32_t max_blocks_per_seq, max_parts;
+  int32_t grid_parts = 0;  // items per sequence in the partition grid (0: max_parts)
   int32_t table_bytes;  // 4 (int32 entries) or 2 (uint16 entries)
   float scale;
   int32_t slots = 768;     // resident partition workgroups on the device (plan's size choice)

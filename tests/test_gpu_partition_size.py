@@ -17,7 +17,7 @@ import torch
 
 import paged_kv_cache_281_amd as pkv
 import synth
-from gpu_harness import log, replay_gpu
+from gpu_harness import log, replay_gpu, to_device
 from test_gpu_parity import _custom, _run_case
 
 pytestmark = pytest.mark.gpu
@@ -190,6 +190,8 @@ def _check_plan(plan, lens, rows, pt, cm, block=16):
     length class.  Returns the groups."""
     cnt, tasks, seq_np, members, member_own = plan
     lens = np.asarray(lens, dtype=np.int64)
+    if pt >= 1024:  # the partition kernels' grid then holds ceil(W * B / 1024) + 1 items per sequence
+        assert int(cnt[0]) <= len(lens) * (-(-np.asarray(rows).shape[1] * block // 1024) + 1)
     groups = _groups(lens, rows, block, cm)
     sp = {b: S for mem, S in groups for b in mem}
     fused = {b for mem, S in groups if _fused(mem, S, lens, pt, cm, block) for b in mem}
@@ -360,3 +362,44 @@ def test_task_list_on_random_batches(seed):
         log(f"seed {seed} prepare={prepare}: N={n} partition {1 << int(plan[0][1])} (rule {pt}), {plan[0][0]} items")
         assert 1 << int(plan[0][1]) == pt
         _check_plan(plan, lens, rows, pt, 4)
+
+
+def test_grid_holds_the_longest_item_list():
+    """With partitions of 1024 tokens or more the partition grid holds ceil(W * B / 1024)
+    + 1 items per sequence.  Three samples of one 512-token prompt at 8 query heads per KV
+    head (two members per column set) form one fused group of two column sets, each cut
+    into three parts: six items, exactly the grid of three sequences with 45-block rows.
+    Both launch paths match the oracle."""
+    w = synth.cow_fp16(512, num_prompts=1, samples=3, max_suffix=200, hq=16, hkv=2)
+    st = replay_gpu(w, w.all_context_kv(), DEV)
+    lens = st.context_lens.cpu().numpy().astype(np.int64)
+    rows = st.tables.cpu().numpy()
+    plan = _plan(lens, w.num_q_heads, w.num_kv_heads, st.tables.contiguous())
+    assert 1 << int(plan[0][1]) == 1024
+    groups = _check_plan(plan, lens, rows, 1024, 2)
+    assert len(groups) == 1
+    assert int(plan[0][0]) == len(lens) * (-(-rows.shape[1] * 16 // 1024) + 1) == 6
+    _run_case(w, fused=True)
+    _run_case(w, check_pools=False)
+
+
+def test_partition_size_changed_between_plan_and_partitions(partition_tokens):
+    """A plan made with 512-token partitions lists more items (20) than the grid of
+    1024-token partitions holds (12); the partition pass sizes its grid from its
+    workspace's plan, not from the size set when it is launched, so the output equals
+    the one-call decode at 512 bit for bit."""
+    w = synth.long_bf16(16, num_seqs=2, context=5000)
+    st = replay_gpu(w, w.all_context_kv(), DEV)
+    q = to_device(w.queries(), w.dtype, DEV)
+    partition_tokens(512)
+    ref = pkv.paged_attention_decode(q, st.k_pool, st.v_pool, st.tables, st.context_lens, w.scale)
+    ws = pkv.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_blocks_per_seq, w.block_size, DEV)
+    pkv.paged_attention_plan(q, st.k_pool, st.v_pool, st.tables, st.context_lens, ws)
+    partition_tokens(0)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_partitions(q, st.k_pool, st.v_pool, st.tables, st.context_lens, w.scale, out, ws)
+    torch.cuda.synchronize()
+    cnt = _counters(ws)
+    log(f"plan at 512: {cnt[0]} items, partitions launched with the plan's choice in force")
+    assert int(cnt[1]) == 9 and int(cnt[0]) == 20
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
