@@ -124,7 +124,7 @@ def algorithmic_bytes(w, lens, table_format="int32", unique=None, partition_toke
 def partition_tokens_of(w, lens):
     """The decode partition size the library's plan pass picks for this batch."""
     import paged_kv_cache_281_amd as pkv
-    return pkv.decode_partition_tokens(lens, w.num_q_heads, w.num_kv_heads)
+    return pkv.decode_partition_tokens(lens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size)
 
 
 def stored_traffic(workload, kernel="attn_partition", src=KERNEL_SRC):
@@ -739,7 +739,7 @@ def stream_main(args, dev):
     print(json.dumps(res), flush=True)
 
 
-def decode_run(args, name, dev, table_format="int32", partition_tokens=0, with_cpu=False, num_seqs=None):
+def decode_run(args, name, dev, table_format="int32", partition_tokens=0, with_cpu=False, num_seqs=None, shape=None):
     """One decode workload: set-up, ``args.steps`` timed steps (graph replays unless
     ``--eager``), the passes alone, and flushed partition timings.  Returns the bench
     record (the JSON line's fields) for that workload."""
@@ -749,7 +749,7 @@ def decode_run(args, name, dev, table_format="int32", partition_tokens=0, with_c
     pkv.set_decode_partition_tokens(partition_tokens)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
     ti = {"f32": (np.int32, torch.int32), "f16": (np.int16, torch.int16), "bf16": (np.int16, torch.int16)}
-    w = synth.by_name(name, **({"num_seqs": num_seqs} if num_seqs else {}))
+    w = synth.by_name(name, **({"num_seqs": num_seqs} if num_seqs else {}), **(shape or {}))
     log(f"workload {w.name}: N={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
         f"B={w.block_size} {w.dtype} tokens={int(w.context_lens.sum())} partition={partition_tokens or 'plan'}")
     t = time.perf_counter()
@@ -988,6 +988,10 @@ def main():
                     help="skip the HIP-graph replays of the decode step (the timed steps are stream launches)")
     ap.add_argument("--tables", choices=["int32", "int16", "two_level"], default="int32",
                     help="block-table format of the decode step (flat int32, flat 16-bit, or two-level)")
+    ap.add_argument("--head-dim", type=int, choices=[64, 128], default=None,
+                    help="gqa_bf16 / mha_bf16 at another head size (same lengths)")
+    ap.add_argument("--block-size", type=int, choices=[16, 32], default=None,
+                    help="gqa_bf16 / mha_bf16 at another block size (same lengths)")
     ap.add_argument("--partition-tokens", type=int, choices=[0, 512, 1024, 2048], default=0,
                     help="fix the decode partition size (0: the plan pass chooses per batch)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -1030,8 +1034,9 @@ def main():
         prefill_main(args, synth.by_name(name, **({"num_seqs": args.num_seqs} if args.num_seqs else {})), dev)
         return
     if args.workload is not None:
+        shape = {k: v for k, v in (("head_dim", args.head_dim), ("block", args.block_size)) if v}
         res = decode_run(args, name, dev, args.tables, args.partition_tokens, not args.no_cpu_baseline,
-                         args.num_seqs)
+                         args.num_seqs, shape)
         print(json.dumps(res), flush=True)
         return
     # the headline line: the largest single-GPU configuration, with the other decode

@@ -366,16 +366,19 @@ int32_t pkv_decode_prepare(const pkv_pool_desc* pool, void* k_pool, void* v_pool
  * combine, partial stores, merge), but a batch too small to keep the chip busy ends
  * when its longest items do.  The plan takes PKV_PARTITION_TOKENS_MAX when some
  * context exceeds PKV_PARTITION_TOKENS and
- *     3 * sum_b(context_lens[b]) * workgroups_per_item >= 2 * min(max_b context_lens[b], PKV_PARTITION_TOKENS_MAX) * slots
- * (the token work per resident workgroup slot reaches two thirds of the longest item),
- * with workgroups_per_item = H * ceil(G / 16) and slots = 3 resident workgroups per
- * compute unit (768 on MI355X); else PKV_PARTITION_TOKENS.  A value set with
- * pkv_set_decode_partition_tokens takes precedence.  Host-only and synchronous; no
- * device is needed (without one, 256 compute units are assumed).
- * Errors: INVALID_ARG (null pointers, num_seqs < 0, heads not positive or not a multiple).
+ *     3 * sum_b(context_lens[b]) * workgroups_per_item >= k * min(max_b context_lens[b], PKV_PARTITION_TOKENS_MAX) * slots
+ * with k = 3 for pools of head_dim 64 and block_size 16 (the token work per resident
+ * workgroup slot reaches the longest item) and k = 2 otherwise (two thirds of it),
+ * workgroups_per_item = H * ceil(G / 16) and slots = 3 resident workgroups per compute
+ * unit (768 on MI355X); else PKV_PARTITION_TOKENS.  A value set with
+ * pkv_set_decode_partition_tokens takes precedence.  The pool descriptor gives H,
+ * head_dim and block_size (num_blocks and dtype are checked, not used).  Host-only and
+ * synchronous; no device is needed (without one, 256 compute units are assumed).
+ * Errors: INVALID_ARG (bad pool descriptor, null pointers, num_seqs < 0, num_q_heads
+ * not a positive multiple of H), UNSUPPORTED (head_dim or block_size).
  */
-int32_t pkv_decode_partition_tokens(const int32_t* context_lens_host, int32_t num_seqs, int32_t num_q_heads,
-                                    int32_t num_kv_heads, int32_t* tokens);
+int32_t pkv_decode_partition_tokens(const pkv_pool_desc* pool, const int32_t* context_lens_host, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t* tokens);
 /*
  * Fixes the decode partition size of every later plan pass in the process:
  * PKV_PARTITION_TOKENS_MIN, PKV_PARTITION_TOKENS or PKV_PARTITION_TOKENS_MAX, or 0 for

@@ -98,7 +98,7 @@ def _bind(lib):
                                      _c_i32),
         "pkv_decode_prepare": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp,
                                 P(TableRef), _c_vp, _c_sz, _c_vp], _c_i32),
-        "pkv_decode_partition_tokens": ([_c_vp, _c_i32, _c_i32, _c_i32, P(_c_i32)], _c_i32),
+        "pkv_decode_partition_tokens": ([P(PoolDesc), _c_vp, _c_i32, _c_i32, P(_c_i32)], _c_i32),
         "pkv_set_decode_partition_tokens": ([_c_i32], _c_i32),
         "pkv_paged_attention_prefill": ([P(PoolDesc), _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_i32,
                                          _c_i32, _c_vp, _c_i32, _c_vp, _c_f, _c_vp, _c_sz, _c_vp], _c_i32),
@@ -399,12 +399,15 @@ def paged_attention_plan(q, k_pool, v_pool, block_tables, context_lens, workspac
                                            ws.numel(), _stream(q.device)))
 
 
-def decode_partition_tokens(context_lens, num_q_heads: int, num_kv_heads: int) -> int:
-    """The partition size the plan pass picks for these context lengths (host values)."""
+def decode_partition_tokens(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int = 128,
+                            block_size: int = 16) -> int:
+    """The partition size the plan pass picks for these context lengths (host values) on
+    a 16-bit pool of this head and block size."""
     lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
     out = _c_i32()
-    _check(load().pkv_decode_partition_tokens(lens.ctypes.data if lens.size else None, lens.size, int(num_q_heads),
-                                              int(num_kv_heads), ctypes.byref(out)))
+    pool = PoolDesc(1, int(block_size), int(num_kv_heads), int(head_dim), DTYPE_CODES[torch.bfloat16])
+    _check(load().pkv_decode_partition_tokens(ctypes.byref(pool), lens.ctypes.data if lens.size else None, lens.size,
+                                              int(num_q_heads), ctypes.byref(out)))
     return out.value
 
 

@@ -506,11 +506,14 @@ int32_t pkv_swap_blocks(const pkv_pool_desc* pool, const void* src_k, const void
       pkv::launch_pool_copy(*pool, src_k, src_v, dst_k, dst_v, src_dst_pairs, num_pairs, stream), "pkv_swap_blocks");
 }
 
-int32_t pkv_decode_partition_tokens(const int32_t* context_lens_host, int32_t num_seqs, int32_t num_q_heads,
-                                    int32_t num_kv_heads, int32_t* tokens) {
-  if (!tokens || num_seqs < 0 || (num_seqs > 0 && !context_lens_host) || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      num_q_heads % num_kv_heads != 0)
+int32_t pkv_decode_partition_tokens(const pkv_pool_desc* pool, const int32_t* context_lens_host, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t* tokens) {
+  const int32_t st = pkv::check_pool(pool, "pkv_decode_partition_tokens");
+  if (st != PKV_OK) return st;
+  if (!tokens || num_seqs < 0 || (num_seqs > 0 && !context_lens_host) || num_q_heads <= 0 ||
+      num_q_heads % pool->num_kv_heads != 0)
     return pkv::set_error(PKV_ERR_INVALID_ARG, "pkv_decode_partition_tokens: bad arguments");
+  const int32_t num_kv_heads = pool->num_kv_heads;
   unsigned long long total = 0;
   int lmax = 0;
   for (int32_t b = 0; b < num_seqs; ++b) {
@@ -520,7 +523,8 @@ int32_t pkv_decode_partition_tokens(const int32_t* context_lens_host, int32_t nu
   }
   const int G = num_q_heads / num_kv_heads;
   const int hy = num_kv_heads * ((G + 15) / 16);
-  *tokens = 1 << pkv::choose_partition_log2(total, lmax, hy, pkv::resident_slots(), pkv::forced_partition_log2());
+  *tokens = 1 << pkv::choose_partition_log2(total, lmax, hy, pool->head_dim, pool->block_size, pkv::resident_slots(),
+                                            pkv::forced_partition_log2());
   return PKV_OK;
 }
 

@@ -73,7 +73,7 @@ struct Params {
   int4* seq_grp;        // [N]: shared-prefix group of each sequence (plan pass)
   int* members;         // [N]: the sequences of each shared-prefix group, group by group
   int* member_own;      // [N]: beside members: each member's own tokens (fused items)
-  int N, Hq, Hkv, G, NHG, W, Pmax, Lmax, B;
+  int N, Hq, Hkv, G, NHG, W, Pmax, Lmax, B, D;
   float scale_log2;
   int tab_bytes;   // 4 or 2 (flat tables)
   int leaf_e;      // entries per two-level leaf
@@ -570,7 +570,7 @@ __device__ __forceinline__ void plan_body(const Params& P) {
     atomicMax(&s_lmax, lmax);
   }
   __syncthreads();
-  const int lg = choose_partition_log2(s_tokens, s_lmax, P.Hkv * P.NHG, P.slots, P.force_log2);
+  const int lg = choose_partition_log2(s_tokens, s_lmax, P.Hkv * P.NHG, P.D, P.B, P.slots, P.force_log2);
   const int csel = lg == lg_lo ? 0 : 1;
   const int* ccnt = cnt[csel];
   // fused groups: each column set's work in `parts` items, counted by class
@@ -1892,6 +1892,7 @@ Params make_params(const AttnArgs& a) {
   P.W = a.max_blocks_per_seq;
   P.Pmax = a.max_parts;
   P.Lmax = a.max_blocks_per_seq * a.block_size;
+  P.D = a.head_dim;
   P.scale_log2 = a.scale * kLog2e;
   P.tab_bytes = a.table_bytes;
   P.leaf_e = PKV_LEAF_TOKENS / a.block_size;

@@ -93,16 +93,22 @@ constexpr int kSlotsPerCU = 3;  // partition workgroups resident per compute uni
 // The plan's partition size for a batch of `tokens` context tokens in total, the longest
 // `lmax`, with `hy` workgroups per (sequence, partition) item: the larger size once the
 // batch's token work per resident workgroup slot reaches two thirds of its longest item
-// (capped at the larger size), else the smaller one.  Measured on MI355X: batches below
-// that ratio (GQA batches of 32 to 96 sequences) ran 1-19% faster with the smaller size,
-// batches at or above it (a 64-sequence MHA batch, a 256-sequence GQA batch, 256 forked
-// samples, one or eight 128K-token sequences) 1-5% faster with the larger one.
-__host__ __device__ inline int choose_partition_log2(unsigned long long tokens, int lmax, int hy, int slots,
-                                                     int force_log2) {
+// (capped at the larger size), or the whole longest item at head size 64 with 16-token
+// blocks, else the smaller one.  Measured on MI355X: at head size 128, batches below
+// that ratio (GQA batches of 32 to 96 sequences) ran 1-19% faster with the smaller
+// size, batches at or above it (GQA batches of 112 to 256 sequences, a 64-sequence MHA
+// batch, 256 forked samples, one or eight 128K-token sequences) up to 5% faster with
+// the larger one; block 32 at head size 64 or 128 changed over at the same ratio.  At
+// head size 64 with 16-token blocks the GQA batches changed over later: 112 and 128
+// sequences (ratios 1.05 and 1.2) 2-5% faster with the smaller size, 160 and 192 (1.6
+// and 2.0) 0.5-1.2% faster with the larger one; MHA batches there ran alike with either.
+__host__ __device__ inline int choose_partition_log2(unsigned long long tokens, int lmax, int hy, int head_dim,
+                                                     int block_size, int slots, int force_log2) {
   if (force_log2) return force_log2;
   if (lmax <= (1 << kLgPartMin)) return kLgPartMin;
   const unsigned long long longest = lmax < (1 << kLgPartMax) ? lmax : (1 << kLgPartMax);
-  return 3ull * tokens * static_cast<unsigned long long>(hy) >= 2ull * longest * static_cast<unsigned long long>(slots)
+  const unsigned long long need = head_dim <= 64 && block_size == 16 ? 3ull : 2ull;
+  return 3ull * tokens * static_cast<unsigned long long>(hy) >= need * longest * static_cast<unsigned long long>(slots)
              ? kLgPartMax
              : kLgPartMin;
 }

@@ -280,24 +280,33 @@ def tiny_fp32(seed: int = 1000, num_seqs: int = 4) -> Workload:
                             num_blocks=64, width=4)
 
 
-def mha_bf16(seed: int = 1001, num_seqs: int = 64, max_len: Optional[int] = None) -> Workload:
-    """MHA 32 q = 32 kv heads, D=128, B=16, skewed mix, pool = need + 10%, bf16."""
+def _shape_tag(head_dim: int, block: int) -> str:
+    """Name suffix of a batch built at another head size or block size than its default."""
+    return (f"_d{head_dim}" if head_dim != 128 else "") + (f"_b{block}" if block != 16 else "")
+
+
+def mha_bf16(seed: int = 1001, num_seqs: int = 64, max_len: Optional[int] = None, head_dim: int = 128,
+             block: int = 16) -> Workload:
+    """MHA 32 q = 32 kv heads, D=128, B=16, skewed mix, pool = need + 10%, bf16 (head and
+    block size can be changed; the lengths stay the same)."""
     rng = np.random.default_rng(seed)
     lengths = skewed_lengths(rng, num_seqs, 1)
     if max_len is not None:
         lengths = np.minimum(lengths, max_len)
-    return _decode_workload("mha_bf16", seed, "bf16", lengths, 32, 32, 128, 16, rng,
-                            width=256 if max_len is None else None)
+    return _decode_workload("mha_bf16" + _shape_tag(head_dim, block), seed, "bf16", lengths, 32, 32, head_dim,
+                            block, rng, width=4096 // block if max_len is None else None)
 
 
-def gqa_bf16(seed: int = 1002, num_seqs: int = 256, max_len: Optional[int] = None) -> Workload:
-    """GQA 32 q over 8 kv heads (4 per group), D=128, B=16, skewed mix x2 (up to 8191), bf16."""
+def gqa_bf16(seed: int = 1002, num_seqs: int = 256, max_len: Optional[int] = None, head_dim: int = 128,
+             block: int = 16) -> Workload:
+    """GQA 32 q over 8 kv heads (4 per group), D=128, B=16, skewed mix x2 (up to 8191), bf16
+    (head and block size can be changed; the lengths stay the same)."""
     rng = np.random.default_rng(seed)
     lengths = skewed_lengths(rng, num_seqs, 2)
     if max_len is not None:
         lengths = np.minimum(lengths, max_len)
-    return _decode_workload("gqa_bf16", seed, "bf16", lengths, 32, 8, 128, 16, rng,
-                            width=512 if max_len is None else None)
+    return _decode_workload("gqa_bf16" + _shape_tag(head_dim, block), seed, "bf16", lengths, 32, 8, head_dim,
+                            block, rng, width=8192 // block if max_len is None else None)
 
 
 def long_bf16(block_size: int = 16, seed: int = 1004, num_seqs: int = 8, context: int = 131072) -> Workload:

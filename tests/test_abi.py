@@ -235,8 +235,8 @@ def test_prefix_cache_switch_and_plain_fallback(pkv_lib):
 
 def test_decode_partition_size_rule(pkv_lib):
     """The plan's partition size: 2048 when some context exceeds 1024 tokens and the token
-    work per workgroup slot reaches two thirds of the longest item (768 slots without a
-    device: 256 compute units x 3)."""
+    work per workgroup slot reaches two thirds of the longest item at head size 128, the
+    whole longest item at head size 64 (768 slots without a device: 256 compute units x 3)."""
     import synth
     pt = pkv_lib.decode_partition_tokens
     assert pt([], 32, 8) == 1024
@@ -256,10 +256,26 @@ def test_decode_partition_size_rule(pkv_lib):
     assert pt([3000] + [500] * 257, 32, 8) == 2048         # 131500 tokens
     assert pt([2048] * 64, 64, 2) == 1024                  # 32 query heads per kv head: 4 workgroups per item
     assert pt([2048] * 128, 64, 2) == 2048
+    # head size 64 with 16-token blocks: 3 * tokens * workgroups per item against
+    # 3 * longest * slots; with 32-token blocks the head size-128 threshold
+    assert pt([2048] * 64, 32, 8, 64) == 1024
+    assert pt([2048] * 96, 32, 8, 64) == 2048              # 3 * 196608 * 8 == 3 * 2048 * 768
+    assert pt([2048] * 95, 32, 8, 64) == 1024
+    assert pt([2048] * 64, 32, 8, 64, 32) == 2048
+    assert pt([2048] * 63, 32, 8, 128, 32) == 1024
+    assert pt(synth.gqa_bf16(num_seqs=128).context_lens, 32, 8) == 2048
+    assert pt(synth.gqa_bf16(num_seqs=128).context_lens, 32, 8, 64) == 1024
+    assert pt(synth.gqa_bf16(num_seqs=128).context_lens, 32, 8, 64, 32) == 2048
+    assert pt(synth.gqa_bf16(num_seqs=160).context_lens, 32, 8, 64) == 2048
     lib = pkv_lib.load()
     out = ctypes.c_int32()
-    assert lib.pkv_decode_partition_tokens(None, 3, 32, 8, ctypes.byref(out)) == 1
-    assert lib.pkv_decode_partition_tokens(None, 0, 30, 8, ctypes.byref(out)) == 1
+    pool = pkv_lib.PoolDesc(1, 16, 8, 128, 2)
+    assert lib.pkv_decode_partition_tokens(ctypes.byref(pool), None, 3, 32, ctypes.byref(out)) == 1
+    assert lib.pkv_decode_partition_tokens(ctypes.byref(pool), None, 0, 30, ctypes.byref(out)) == 1
+    assert lib.pkv_decode_partition_tokens(None, None, 0, 32, ctypes.byref(out)) == 1
+    assert lib.pkv_decode_partition_tokens(ctypes.byref(pool), None, 0, 32, ctypes.byref(out)) == 0
+    odd = pkv_lib.PoolDesc(1, 16, 8, 96, 2)
+    assert lib.pkv_decode_partition_tokens(ctypes.byref(odd), None, 0, 32, ctypes.byref(out)) == 2
     try:
         pkv_lib.set_decode_partition_tokens(2048)
         assert pt([100], 32, 8) == 2048

@@ -403,3 +403,19 @@ def test_partition_size_changed_between_plan_and_partitions(partition_tokens):
     log(f"plan at 512: {cnt[0]} items, partitions launched with the plan's choice in force")
     assert int(cnt[1]) == 9 and int(cnt[0]) == 20
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("n,block,want", [(128, 16, 1024), (160, 16, 2048), (128, 32, 2048)])
+def test_device_choice_at_head_size_64(n, block, want):
+    """At head size 64 with 16-token blocks the plan needs the token work per slot to
+    reach the whole longest item (not two thirds of it) before it takes 2048-token
+    partitions: GQA batches of 128 and 160 sequences fall on either side; with 32-token
+    blocks 128 sequences already take 2048.  The device agrees with the host rule."""
+    lens = np.asarray(synth.gqa_bf16(num_seqs=n).context_lens, dtype=np.int64)
+    W = int(-(-lens.max() // block))
+    rows = np.repeat(np.arange(len(lens), dtype=np.int32)[:, None], W, axis=1)
+    plan = _plan(lens, 32, 8, torch.from_numpy(rows).to(DEV), d=64, block=block)
+    pt = pkv.decode_partition_tokens(lens, 32, 8, 64, block)
+    log(f"D=64 B={block}, {n} sequences: host rule {pt}, device log2 {plan[0][1]}")
+    assert pt == want and 1 << int(plan[0][1]) == want
+    _check_plan(plan, lens, rows, pt, 4, block)
