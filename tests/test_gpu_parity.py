@@ -279,20 +279,26 @@ def test_shuffled_forks_give_the_ordered_bits():
 
 # ---- full-size workloads, in the benchmark's launch configuration -------------------
 FULL = [
-    ("tiny_fp32", None),
-    ("mha_bf16", None),
-    ("gqa_bf16", None),
-    ("cow_fp16_p1020", None),
-    ("cow_fp16_p1024", None),
-    ("long_bf16_b16", [0, 5]),
-    ("long_bf16_b32", [3]),
+    ("tiny_fp32", "tiny_fp32", {}, None),
+    ("mha_bf16", "mha_bf16", {}, None),
+    ("gqa_bf16", "gqa_bf16", {}, None),
+    ("cow_fp16_p1020", "cow_fp16_p1020", {}, None),
+    ("cow_fp16_p1024", "cow_fp16_p1024", {}, None),
+    ("long_bf16_b16", "long_bf16_b16", {}, [0, 5]),
+    ("long_bf16_b32", "long_bf16_b32", {}, [3]),
+    # the GQA batch on pools of head size 64 and of block 32 (the benchmark's
+    # --head-dim / --block-size), and at 128 sequences, where head size 64 keeps
+    # 1024-token partitions
+    ("gqa_bf16_d64", "gqa_bf16", {"head_dim": 64}, None),
+    ("gqa_bf16_b32", "gqa_bf16", {"block": 32}, None),
+    ("gqa_bf16_d64_n128", "gqa_bf16", {"head_dim": 64, "num_seqs": 128}, None),
 ]
 
 
-@pytest.mark.parametrize("name,rows", FULL, ids=[f[0] for f in FULL])
-def test_full_size_workloads(name, rows):
+@pytest.mark.parametrize("name,kw,rows", [f[1:] for f in FULL], ids=[f[0] for f in FULL])
+def test_full_size_workloads(name, kw, rows):
     """Full sizes, last step run as the benchmark runs it (decode_prepare + partitions)."""
-    w = synth.by_name(name)
+    w = synth.by_name(name, **kw)
     _run_case(w, rows=rows, fused=True)
 
 
