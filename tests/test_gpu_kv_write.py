@@ -1,9 +1,10 @@
 """GPU parity of paged_kv_write with mixed slot patterns against the oracle write.
 
-Groups of B tokens whose slots are one whole block in order are stored as whole
-tiles; everything else (runs that start inside a block, runs crossing a block
-boundary, a shuffled block, gaps, padding slots, a short last group) goes token by
-token.  Both must leave the pools bit-identical to the oracle's.
+Segments of B tokens whose slots are one whole block in order are stored as whole
+tiles, wherever they start in the token list; everything else (runs that start inside
+a block, runs crossing a block boundary, a shuffled block, gaps, padding slots, a
+short last run) goes token by token.  Both must leave the pools bit-identical to the
+oracle's.
 """
 import numpy as np
 import pytest
@@ -42,6 +43,52 @@ def test_kv_write_mixed_slots(dtype, B, D):
     log(f"kv write {dtype} B={B} D={D}: {T} tokens")
     k = synth.normal_bits((77, 1), (T, H, D), dtype)
     v = synth.normal_bits((77, 2), (T, H, D), dtype)
+    kp, vp = pkv.alloc_pools(nb, B, H, D, TORCH_DTYPE[dtype], DEV)
+    fill = synth.NAN_BITS[dtype]
+    npi, ti = INT_VIEW[dtype]
+    fv = np.array([fill], dtype=np.uint32 if dtype == "f32" else np.uint16).view(npi)[0]
+    kp.view(ti).fill_(int(fv))
+    vp.view(ti).fill_(int(fv))
+    pkv.paged_kv_write(kp, vp, to_device(k, dtype, DEV), to_device(v, dtype, DEV), torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    pool = Pool(nb, H, D, B, dtype, fill)
+    oracle_write(pool, k, v, slots)
+    assert (to_bits(kp, dtype) == pool.k).all(), "K pool differs"
+    assert (to_bits(vp, dtype) == pool.v).all(), "V pool differs"
+
+
+def _prompt_slots(rng, nb, B):
+    """Prefill-like slots: sequences of random lengths laid end to end in the token list,
+    each filling blocks of its own from the block offset where its chunk starts (0 for
+    a new prompt, else inside a partly filled block), block ids shuffled, with padding
+    tokens between some of them."""
+    ids = rng.permutation(nb)
+    out, used = [], 0
+    for q in range(12):
+        L = int(rng.integers(1, 3 * B + 6))
+        o = 0 if q % 3 else int(rng.integers(1, B))
+        need = -(-(o + L) // B)
+        blocks = ids[used:used + need]
+        used += need
+        pos = o + np.arange(L)
+        out.append(blocks[pos // B] * B + pos % B)
+        if q % 4 == 3:
+            out.append(np.array([-1]))
+    s = np.concatenate(out).astype(np.int64)
+    assert used <= nb and len(np.unique(s[s >= 0])) == (s >= 0).sum()
+    return s
+
+
+@pytest.mark.parametrize("dtype,B,D", [("bf16", 16, 128), ("f16", 32, 64), ("f32", 16, 64), ("f32", 32, 128)])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_kv_write_prompt_layout(dtype, B, D, seed):
+    rng = np.random.default_rng(100 + seed)
+    nb, H = 64, 2
+    slots = _prompt_slots(rng, nb, B)
+    T = len(slots)
+    log(f"kv write, prompt layout, {dtype} B={B} D={D} seed {seed}: {T} tokens")
+    k = synth.normal_bits((78, seed, 1), (T, H, D), dtype)
+    v = synth.normal_bits((78, seed, 2), (T, H, D), dtype)
     kp, vp = pkv.alloc_pools(nb, B, H, D, TORCH_DTYPE[dtype], DEV)
     fill = synth.NAN_BITS[dtype]
     npi, ti = INT_VIEW[dtype]
