@@ -91,10 +91,13 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_tiles_kernel(const cha
     u32x4 kr[NP], vr[NP];
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
-      const int j = min(tid + NT * x, n * CH - 1);
-      const int i = a + j / CH, c = j - (j / CH) * CH;
-      kr[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ksrc + i * row + c * 16));
-      vr[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vsrc + i * row + c * 16));
+      const int j = tid + NT * x;
+      if (x == 0 || j < n * CH) {  // (a range of one whole block needs one piece per thread)
+        const int jj = min(j, n * CH - 1);
+        const int i = a + jj / CH, c = jj - (jj / CH) * CH;
+        kr[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ksrc + i * row + c * 16));
+        vr[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vsrc + i * row + c * 16));
+      }
     }
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
