@@ -101,3 +101,40 @@ def test_kv_write_prompt_layout(dtype, B, D, seed):
     oracle_write(pool, k, v, slots)
     assert (to_bits(kp, dtype) == pool.k).all(), "K pool differs"
     assert (to_bits(vp, dtype) == pool.v).all(), "V pool differs"
+
+
+EDGE = {
+    "all_padding": lambda B: np.full(2 * B + 3, -1),
+    "one_token": lambda B: np.array([5 * B + 7]),
+    # a whole block starting at the second token: the first range owns it and writes
+    # one token past its own range
+    "block_after_one": lambda B: np.concatenate([[9 * B + 3], np.arange(4 * B, 5 * B)]),
+    # the first range's last token opens a whole block: it reaches B - 1 tokens into
+    # the next range, whose own first segment starts right after
+    "longest_reach": lambda B: np.concatenate([np.arange(2 * B + 1, 3 * B), np.arange(6 * B, 7 * B),
+                                               np.arange(11 * B + 2, 11 * B + 5)]),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+@pytest.mark.parametrize("dtype,B,D", [("bf16", 16, 128), ("f16", 32, 64), ("f32", 32, 128)])
+def test_kv_write_segment_edges(case, dtype, B, D):
+    slots = EDGE[case](B).astype(np.int64)
+    nb, H = 16, 2
+    assert slots.max() < nb * B
+    T = len(slots)
+    log(f"kv write edge case {case}, {dtype} B={B} D={D}: {T} tokens")
+    k = synth.normal_bits((79, 1), (T, H, D), dtype)
+    v = synth.normal_bits((79, 2), (T, H, D), dtype)
+    kp, vp = pkv.alloc_pools(nb, B, H, D, TORCH_DTYPE[dtype], DEV)
+    fill = synth.NAN_BITS[dtype]
+    npi, ti = INT_VIEW[dtype]
+    fv = np.array([fill], dtype=np.uint32 if dtype == "f32" else np.uint16).view(npi)[0]
+    kp.view(ti).fill_(int(fv))
+    vp.view(ti).fill_(int(fv))
+    pkv.paged_kv_write(kp, vp, to_device(k, dtype, DEV), to_device(v, dtype, DEV), torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    pool = Pool(nb, H, D, B, dtype, fill)
+    oracle_write(pool, k, v, slots)
+    assert (to_bits(kp, dtype) == pool.k).all(), "K pool differs"
+    assert (to_bits(vp, dtype) == pool.v).all(), "V pool differs"
