@@ -989,9 +989,9 @@ def main():
     ap.add_argument("--tables", choices=["int32", "int16", "two_level"], default="int32",
                     help="block-table format of the decode step (flat int32, flat 16-bit, or two-level)")
     ap.add_argument("--head-dim", type=int, choices=[64, 128], default=None,
-                    help="gqa_bf16 / mha_bf16 at another head size (same lengths)")
+                    help="gqa_bf16 / mha_bf16 / prefill_bf16 / chunked_bf16 at another head size (same lengths)")
     ap.add_argument("--block-size", type=int, choices=[16, 32], default=None,
-                    help="gqa_bf16 / mha_bf16 at another block size (same lengths)")
+                    help="gqa_bf16 / mha_bf16 / prefill_bf16 / chunked_bf16 at another block size (same lengths)")
     ap.add_argument("--partition-tokens", type=int, choices=[0, 512, 1024, 2048], default=0,
                     help="fix the decode partition size (0: the plan pass chooses per batch)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -1031,7 +1031,9 @@ def main():
         swap_main(args, synth.by_name(name), dev)
         return
     if name in synth.PREFILL_WORKLOADS:
-        prefill_main(args, synth.by_name(name, **({"num_seqs": args.num_seqs} if args.num_seqs else {})), dev)
+        shape = {k: v for k, v in (("head_dim", args.head_dim), ("block", args.block_size)) if v}
+        kw = dict(shape, **({"num_seqs": args.num_seqs} if args.num_seqs else {}))
+        prefill_main(args, synth.by_name(name, **kw), dev)
         return
     if args.workload is not None:
         shape = {k: v for k, v in (("head_dim", args.head_dim), ("block", args.block_size)) if v}

@@ -231,24 +231,26 @@ def prefill_workload(name: str, seed: int, dtype: str, context_lens, chunk_lens,
                            context_lens=L.astype(np.int32), chunk_lens=C.astype(np.int32), notes=notes)
 
 
-def prefill_bf16(seed: int = 1005, num_seqs: int = 64) -> PrefillWorkload:
+def prefill_bf16(seed: int = 1005, num_seqs: int = 64, head_dim: int = 128, block: int = 16) -> PrefillWorkload:
     """Whole-prompt prefill: 64 prompts with lengths from the interview post's request
-    mix (each prompt is its own chunk), 32 q / 8 kv heads, D=128, B=16, bf16."""
+    mix (each prompt is its own chunk), 32 q / 8 kv heads, D=128, B=16, bf16 (head and
+    block size can be changed; the lengths stay the same)."""
     rng = np.random.default_rng(seed)
     L = skewed_lengths(rng, num_seqs, 1)
-    return prefill_workload("prefill_bf16", seed, "bf16", L, L, 32, 8, 128, 16,
+    return prefill_workload("prefill_bf16" + _shape_tag(head_dim, block), seed, "bf16", L, L, 32, 8, head_dim, block,
                             notes="prompt lengths from the skewed request mix; chunk = whole prompt")
 
 
-def chunked_bf16(seed: int = 1006, num_seqs: int = 16, chunk: int = 512) -> PrefillWorkload:
+def chunked_bf16(seed: int = 1006, num_seqs: int = 16, chunk: int = 512, head_dim: int = 128,
+                 block: int = 16) -> PrefillWorkload:
     """Chunked prefill: 16 sequences whose earlier tokens (the skewed mix scaled x2, up
     to 8191) are already cached, each appending a chunk of 512 tokens; 32 q / 8 kv
-    heads, D=128, B=16, bf16."""
+    heads, D=128, B=16, bf16 (head and block size can be changed)."""
     rng = np.random.default_rng(seed)
     prefix = skewed_lengths(rng, num_seqs, 2)
     C = np.full(num_seqs, chunk, dtype=np.int64)
-    return prefill_workload("chunked_bf16", seed, "bf16", prefix + C, C, 32, 8, 128, 16,
-                            notes="cached prefix from the x2 skewed mix, then a 512-token chunk")
+    return prefill_workload("chunked_bf16" + _shape_tag(head_dim, block), seed, "bf16", prefix + C, C, 32, 8,
+                            head_dim, block, notes="cached prefix from the x2 skewed mix, then a 512-token chunk")
 
 
 def _decode_workload(name: str, seed: int, dtype: str, lengths: np.ndarray, hq: int, hkv: int,
