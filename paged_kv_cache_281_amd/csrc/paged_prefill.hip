@@ -96,25 +96,38 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = 1024;
 static_assert(kPlanBuckets == kPlanThreads, "one bucket per plan thread");
 
+// Inclusive sum over the workgroup's threads in thread order: lane shuffles within each
+// wave, then each thread adds the totals of the waves before its own (two barriers,
+// where a step-by-step scan over the whole workgroup takes two per doubling).
+__device__ __forceinline__ int plan_scan(int v, int* s_wsum) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d, 64);
+    v += lane >= d ? t : 0;
+  }
+  if (lane == 63) s_wsum[tid >> 6] = v;
+  __syncthreads();
+  for (int w = 0; w < (tid >> 6); ++w) v += s_wsum[w];
+  __syncthreads();  // s_wsum is free again
+  return v;
+}
+
 // Calls f(b, t, C, L) for every (sequence b, tile t) the chunks have.  Sequences are
 // taken kPlanThreads at a time; their tiles are spread over all threads (a block-wide
 // scan of the tile counts, then a binary search per tile), so a long chunk's many
 // tiles do not fall on one thread.
 template <class F>
-__device__ __forceinline__ void plan_tiles(const PrefillParams& P, int* s_end, int* s_c, int* s_l, F&& f) {
+__device__ __forceinline__ void plan_tiles(const PrefillParams& P, int* s_end, int* s_c, int* s_l, int* s_wsum,
+                                           F&& f) {
   const int tid = threadIdx.x;
   for (int b0 = 0; b0 < P.N; b0 += kPlanThreads) {
     int q0, C = 0, L = 0, nt = 0;
     if (b0 + tid < P.N && chunk_of(P, b0 + tid, q0, C, L)) nt = (C * P.G + P.rows - 1) / P.rows;
     s_c[tid] = C;
     s_l[tid] = L;
-    s_end[tid] = nt;
-    for (int d = 1; d < kPlanThreads; d <<= 1) {  // inclusive scan: s_end[i] = tiles of sequences b0 .. b0 + i
-      __syncthreads();
-      const int add = tid >= d ? s_end[tid - d] : 0;
-      __syncthreads();
-      s_end[tid] += add;
-    }
+    s_end[tid] = plan_scan(nt, s_wsum);  // inclusive: tiles of sequences b0 .. b0 + tid
     __syncthreads();
     const int total = s_end[kPlanThreads - 1];
     for (int g = tid; g < total; g += kPlanThreads) {
@@ -132,26 +145,22 @@ __device__ __forceinline__ void plan_tiles(const PrefillParams& P, int* s_end, i
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan(PrefillParams P) {
   __shared__ int cnt[kPlanBuckets];
   __shared__ int s_end[kPlanThreads], s_c[kPlanThreads], s_l[kPlanThreads];
+  __shared__ int s_wsum[kPlanThreads / 64];
   const int tid = threadIdx.x;
   cnt[tid] = 0;
   __syncthreads();
   auto bucket = [&](int t, int C, int L) {
     return kPlanBuckets - 1 - min(tile_units(P, C, L, t), kPlanBuckets - 1);
   };
-  plan_tiles(P, s_end, s_c, s_l, [&](int b, int t, int C, int L) { atomicAdd(&cnt[bucket(t, C, L)], 1); });
+  plan_tiles(P, s_end, s_c, s_l, s_wsum, [&](int b, int t, int C, int L) { atomicAdd(&cnt[bucket(t, C, L)], 1); });
   // exclusive scan of the bucket counts (bucket 0 = most units)
-  int v = cnt[tid];
-  for (int d = 1; d < kPlanBuckets; d <<= 1) {
-    __syncthreads();
-    const int add = tid >= d ? cnt[tid - d] : 0;
-    __syncthreads();
-    cnt[tid] += add;
-  }
   __syncthreads();
-  if (tid == kPlanBuckets - 1) P.counters[0] = min(cnt[tid], P.cap);
-  cnt[tid] -= v;  // exclusive offsets
+  const int v = cnt[tid];
+  const int incl = plan_scan(v, s_wsum);
+  if (tid == kPlanBuckets - 1) P.counters[0] = min(incl, P.cap);
+  cnt[tid] = incl - v;  // exclusive offsets
   __syncthreads();
-  plan_tiles(P, s_end, s_c, s_l, [&](int b, int t, int C, int L) {
+  plan_tiles(P, s_end, s_c, s_l, s_wsum, [&](int b, int t, int C, int L) {
     const int slot = atomicAdd(&cnt[bucket(t, C, L)], 1);
     if (slot < P.cap) P.tasks[slot] = make_int2(b, t);  // overlapping chunks could overflow the bound
   });
