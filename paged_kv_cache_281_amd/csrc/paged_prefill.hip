@@ -117,18 +117,21 @@ __device__ __forceinline__ int plan_scan(int v, int* s_wsum) {
 // Calls f(b, t, C, L) for every (sequence b, tile t) the chunks have.  Sequences are
 // taken kPlanThreads at a time; their tiles are spread over all threads (a block-wide
 // scan of the tile counts, then a binary search per tile), so a long chunk's many
-// tiles do not fall on one thread.
+// tiles do not fall on one thread.  With `loaded`, a batch of at most kPlanThreads
+// sequences reuses the chunks and tile offsets an earlier call left in LDS.
 template <class F>
 __device__ __forceinline__ void plan_tiles(const PrefillParams& P, int* s_end, int* s_c, int* s_l, int* s_wsum,
-                                           F&& f) {
+                                           bool loaded, F&& f) {
   const int tid = threadIdx.x;
   for (int b0 = 0; b0 < P.N; b0 += kPlanThreads) {
-    int q0, C = 0, L = 0, nt = 0;
-    if (b0 + tid < P.N && chunk_of(P, b0 + tid, q0, C, L)) nt = (C * P.G + P.rows - 1) / P.rows;
-    s_c[tid] = C;
-    s_l[tid] = L;
-    s_end[tid] = plan_scan(nt, s_wsum);  // inclusive: tiles of sequences b0 .. b0 + tid
-    __syncthreads();
+    if (!loaded) {
+      int q0, C = 0, L = 0, nt = 0;
+      if (b0 + tid < P.N && chunk_of(P, b0 + tid, q0, C, L)) nt = (C * P.G + P.rows - 1) / P.rows;
+      s_c[tid] = C;
+      s_l[tid] = L;
+      s_end[tid] = plan_scan(nt, s_wsum);  // inclusive: tiles of sequences b0 .. b0 + tid
+      __syncthreads();
+    }
     const int total = s_end[kPlanThreads - 1];
     for (int g = tid; g < total; g += kPlanThreads) {
       int lo = 0, hi = kPlanThreads - 1;  // first sequence whose range ends past g
@@ -152,7 +155,8 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan(PrefillParams P) {
   auto bucket = [&](int t, int C, int L) {
     return kPlanBuckets - 1 - min(tile_units(P, C, L, t), kPlanBuckets - 1);
   };
-  plan_tiles(P, s_end, s_c, s_l, s_wsum, [&](int b, int t, int C, int L) { atomicAdd(&cnt[bucket(t, C, L)], 1); });
+  plan_tiles(P, s_end, s_c, s_l, s_wsum, false,
+             [&](int b, int t, int C, int L) { atomicAdd(&cnt[bucket(t, C, L)], 1); });
   // exclusive scan of the bucket counts (bucket 0 = most units)
   __syncthreads();
   const int v = cnt[tid];
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan(PrefillParams P) {
   if (tid == kPlanBuckets - 1) P.counters[0] = min(incl, P.cap);
   cnt[tid] = incl - v;  // exclusive offsets
   __syncthreads();
-  plan_tiles(P, s_end, s_c, s_l, s_wsum, [&](int b, int t, int C, int L) {
+  plan_tiles(P, s_end, s_c, s_l, s_wsum, P.N <= kPlanThreads, [&](int b, int t, int C, int L) {
     const int slot = atomicAdd(&cnt[bucket(t, C, L)], 1);
     if (slot < P.cap) P.tasks[slot] = make_int2(b, t);  // overlapping chunks could overflow the bound
   });
